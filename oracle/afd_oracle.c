@@ -1,0 +1,452 @@
+/*
+ * afd_oracle.c -- plain, slow CPU oracle for the FFN-rank hot path of
+ * Attention-FFN Disaggregation (AFD).
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path may link, load or
+ * call this file.  Only the test suite, the smoke check and the CPU-baseline
+ * leg of the benchmark use it.  It shares no code, header, table or helper
+ * with the HIP library: it is written from the pages, step by step, in their
+ * order, with no blocking, fusion or reordering beyond what they state.
+ *
+ * Precision: every accumulation is in double.  Inputs are bf16 bit patterns
+ * (hidden states, weights; upcast exactly) and fp32 router logits.
+ *
+ * Sources (titles of the pages, with the section used):
+ *   [RFC-GPU]  "[RFC]: Async GPU Connector" (vllm-project/afd-plugin #233):
+ *              "Data flow" (plan_dispatch: flatten topk_ids, stable argsort,
+ *              bincount, cumsum; shared rows; weighted index_add_ combine),
+ *              "Attention gate and FFN expert compute" (grouped_topk gate,
+ *              fused_experts over expert-grouped rows, shared expert,
+ *              routed_scaling_factor).
+ *   [WIRE]     "Data on the wire: tensors per layer and stage": Step 2
+ *              (total_tokens is the sum of seq_lens), Step 3 (fan-in: peers
+ *              concatenated along tokens in subgroup order), Step 4 (split
+ *              back by the recorded seq_lens).
+ *   [P2P-UG]   "NCCL_P2P_CONNECTOR_USER_GUIDE.md", Configuration
+ *              (compute_gate_on_attention=true: router logits travel to the
+ *              FFN, which runs the expert path).
+ *
+ * Readings taken where the pages are silent (each also listed in the design
+ * notes): softmax scoring renormalised over the top-K; selection by fp32 logit
+ * value, larger first, equal values to the lower expert index; SwiGLU expert
+ * with W13 = [gate rows; up rows] of shape [2I][H] and W2 of shape [H][I];
+ * silu(z) = z / (1 + exp(-z)); the shared expert is unweighted and added after
+ * the routed sum; with one FFN replica every token is a shared row.
+ *
+ * Parity status: every function below is pinned by the CPU tests (invariants,
+ * library special cases, a float64 dense brute force with no permutation).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define ORC_OK 0
+#define ORC_ERR_ARG (-1)
+#define ORC_ERR_NONFINITE (-2)
+#define ORC_ERR_CAPACITY (-3)
+
+/* bf16 bit pattern -> double.  bf16 is the top half of an IEEE binary32, so
+ * the conversion is exact. */
+static double bf16_to_double(uint16_t b) {
+    uint32_t u = ((uint32_t)b) << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+int oracle_num_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+void oracle_set_threads(int n) {
+#ifdef _OPENMP
+    if (n > 0) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
+/* ---------------------------------------------------------------------------
+ * Step a1: fan-in offsets.  [WIRE] Step 2 / Step 3: peers are concatenated in
+ * subgroup order; total_tokens = sum(seq_lens).  off[p] is where peer p's
+ * first token lands in the concatenation, off[P] = total_tokens.
+ * ------------------------------------------------------------------------- */
+int oracle_fanin(int P, const int32_t* seq_lens, int32_t token_cap, int32_t* off) {
+    if (P < 1 || !seq_lens || !off) return ORC_ERR_ARG;
+    off[0] = 0;
+    for (int p = 0; p < P; ++p) {
+        if (seq_lens[p] < 0) return ORC_ERR_ARG;
+        if (token_cap > 0 && seq_lens[p] > token_cap) return ORC_ERR_CAPACITY;
+        off[p + 1] = off[p] + seq_lens[p];
+    }
+    return ORC_OK;
+}
+
+/* Fan-in of a row-major per-peer tensor: out = concat_p src_p along rows. */
+int oracle_concat_rows(int P, const int32_t* seq_lens, const void* const* src,
+                       int64_t row_bytes, void* out) {
+    if (P < 1 || !seq_lens || !src || !out) return ORC_ERR_ARG;
+    char* dst = (char*)out;
+    for (int p = 0; p < P; ++p) {
+        int64_t nb = (int64_t)seq_lens[p] * row_bytes;
+        if (nb > 0) memcpy(dst, src[p], (size_t)nb);
+        dst += nb;
+    }
+    return ORC_OK;
+}
+
+/* ---------------------------------------------------------------------------
+ * Step a2: top-k routing.  [RFC-GPU] "Attention gate and FFN expert compute"
+ * names vLLM's grouped_topk as the gate; with one expert group that is a plain
+ * softmax top-k.  For each token the experts are sorted by (logit descending,
+ * expert index ascending) and the first K are kept in that order.  Weights:
+ * the softmax over all E experts, restricted to the K kept experts and (when
+ * renorm != 0) divided by their sum, which is
+ *   w_k = exp(L[ids_k] - L[ids_0]) / sum_j exp(L[ids_j] - L[ids_0]).
+ * ------------------------------------------------------------------------- */
+
+/* true when expert a ranks before expert b for this token */
+static int ranks_before(const float* l, int a, int b) {
+    /* -0.0 == +0.0 under IEEE comparison, so both compare as equal values. */
+    if (l[a] > l[b]) return 1;
+    if (l[a] < l[b]) return 0;
+    return a < b;
+}
+
+int oracle_route(int64_t T, int E, int K, int renorm, const float* logits,
+                 int32_t* ids, double* w) {
+    if (T < 0 || E < 1 || K < 1 || K > E || (T > 0 && (!logits || !ids || !w)))
+        return ORC_ERR_ARG;
+    for (int64_t i = 0; i < T * (int64_t)E; ++i)
+        if (!isfinite(logits[i])) return ORC_ERR_NONFINITE;
+    int bad = 0;
+#pragma omp parallel
+    {
+        int* order = (int*)malloc(sizeof(int) * (size_t)E);
+        if (!order) {
+#pragma omp atomic write
+            bad = 1;
+        } else {
+#pragma omp for schedule(static)
+            for (int64_t t = 0; t < T; ++t) {
+                const float* l = logits + t * E;
+                /* insertion sort of the expert indices by rank */
+                for (int e = 0; e < E; ++e) {
+                    int j = e;
+                    while (j > 0 && ranks_before(l, e, order[j - 1])) {
+                        order[j] = order[j - 1];
+                        --j;
+                    }
+                    order[j] = e;
+                }
+                for (int k = 0; k < K; ++k) ids[t * K + k] = order[k];
+                double m = (double)l[order[0]];
+                if (renorm) {
+                    double s = 0.0;
+                    for (int k = 0; k < K; ++k) s += exp((double)l[order[k]] - m);
+                    for (int k = 0; k < K; ++k) w[t * K + k] = exp((double)l[order[k]] - m) / s;
+                } else {
+                    double s = 0.0; /* full softmax denominator over all E */
+                    for (int e = 0; e < E; ++e) s += exp((double)l[e] - m);
+                    for (int k = 0; k < K; ++k) w[t * K + k] = exp((double)l[order[k]] - m) / s;
+                }
+            }
+            free(order);
+        }
+    }
+    return bad ? ORC_ERR_ARG : ORC_OK;
+}
+
+/* ---------------------------------------------------------------------------
+ * Step a3: dispatch plan.  [RFC-GPU] "Data flow", plan_dispatch: flatten the
+ * [T,K] expert ids to pairs f = t*K + k, argsort them stably by expert id,
+ * bincount for the per-expert group sizes, cumsum for the group offsets.
+ * The stable argsort over a small integer key is written as a counting sort:
+ * pairs are visited in increasing f and each goes to the next free position
+ * of its expert's group, which is exactly the stable order.
+ *   counts[e]          = #{f : ids_f == e}
+ *   expert_offsets[e]  = sum_{e' < e} counts[e']      (E+1 entries)
+ *   perm[pos] = f, inv[f] = pos.
+ * ------------------------------------------------------------------------- */
+int oracle_dispatch(int64_t T, int E, int K, const int32_t* ids, int32_t* counts,
+                    int32_t* expert_offsets, int32_t* perm, int32_t* inv) {
+    if (T < 0 || E < 1 || K < 1 || !counts || !expert_offsets) return ORC_ERR_ARG;
+    int64_t n = T * (int64_t)K;
+    for (int e = 0; e < E; ++e) counts[e] = 0;
+    for (int64_t f = 0; f < n; ++f) {
+        if (ids[f] < 0 || ids[f] >= E) return ORC_ERR_ARG;
+        counts[ids[f]] += 1;
+    }
+    expert_offsets[0] = 0;
+    for (int e = 0; e < E; ++e) expert_offsets[e + 1] = expert_offsets[e] + counts[e];
+    int32_t* next = (int32_t*)malloc(sizeof(int32_t) * (size_t)E);
+    if (!next) return ORC_ERR_ARG;
+    for (int e = 0; e < E; ++e) next[e] = expert_offsets[e];
+    for (int64_t f = 0; f < n; ++f) {
+        int32_t pos = next[ids[f]]++;
+        perm[pos] = (int32_t)f;
+        inv[f] = pos;
+    }
+    free(next);
+    return ORC_OK;
+}
+
+/* ---------------------------------------------------------------------------
+ * Steps a4/a5 for one row: a SwiGLU expert (the expert FFN that vLLM's
+ * fused_experts applies, [RFC-GPU] "Attention gate and FFN expert compute").
+ *   g_j = sum_h x_h W13[j][h],  u_j = sum_h x_h W13[I+j][h]      (j < I)
+ *   a_j = silu(g_j) * u_j,      silu(z) = z / (1 + exp(-z))
+ *   y_c = sum_j a_j W2[c][j]                                      (c < H)
+ * x: H bf16; w13: [2I][H] bf16; w2: [H][I] bf16; y: H doubles.
+ * scratch: I doubles.
+ * ------------------------------------------------------------------------- */
+static void swiglu_row(int64_t H, int64_t I, const uint16_t* x, const uint16_t* w13,
+                       const uint16_t* w2, double* act, double* y) {
+    for (int64_t j = 0; j < I; ++j) {
+        const uint16_t* wg = w13 + j * H;
+        const uint16_t* wu = w13 + (I + j) * H;
+        double g = 0.0, u = 0.0;
+        for (int64_t h = 0; h < H; ++h) {
+            double xv = bf16_to_double(x[h]);
+            g += xv * bf16_to_double(wg[h]);
+            u += xv * bf16_to_double(wu[h]);
+        }
+        act[j] = (g / (1.0 + exp(-g))) * u;
+    }
+    for (int64_t c = 0; c < H; ++c) {
+        const uint16_t* wr = w2 + c * I;
+        double s = 0.0;
+        for (int64_t j = 0; j < I; ++j) s += act[j] * bf16_to_double(wr[j]);
+        y[c] = s;
+    }
+}
+
+/* One SwiGLU row, exposed so that tests can pin it against a textbook
+ * formula. */
+int oracle_swiglu_row(int64_t H, int64_t I, const uint16_t* x, const uint16_t* w13,
+                      const uint16_t* w2, double* y) {
+    if (H < 1 || I < 1 || !x || !w13 || !w2 || !y) return ORC_ERR_ARG;
+    double* act = (double*)malloc(sizeof(double) * (size_t)I);
+    if (!act) return ORC_ERR_ARG;
+    swiglu_row(H, I, x, w13, w2, act, y);
+    free(act);
+    return ORC_OK;
+}
+
+/* ---------------------------------------------------------------------------
+ * Step a4/a5 over the dispatch plan: every expert e runs over its group
+ * [expert_offsets[e], expert_offsets[e+1]) of the permuted pairs; the row of
+ * pair perm[i] is token perm[i] / K.  Y[i] is the expert output for permuted
+ * position i.  (The rows inside a group are independent, so they may run in
+ * parallel without changing any result.)
+ * ------------------------------------------------------------------------- */
+int oracle_experts(int64_t T, int64_t H, int E, int K, int64_t I, const uint16_t* X,
+                   const int32_t* expert_offsets, const int32_t* perm,
+                   const uint16_t* W13, const uint16_t* W2, double* Y) {
+    if (T < 0 || H < 1 || E < 1 || K < 1 || I < 1) return ORC_ERR_ARG;
+    int bad = 0;
+    for (int e = 0; e < E; ++e) {
+        const uint16_t* w13 = W13 + (int64_t)e * 2 * I * H;
+        const uint16_t* w2 = W2 + (int64_t)e * H * I;
+        int64_t lo = expert_offsets[e], hi = expert_offsets[e + 1];
+#pragma omp parallel
+        {
+            double* act = (double*)malloc(sizeof(double) * (size_t)I);
+            if (!act) {
+#pragma omp atomic write
+                bad = 1;
+            } else {
+#pragma omp for schedule(dynamic, 1)
+                for (int64_t i = lo; i < hi; ++i) {
+                    int64_t t = perm[i] / K;
+                    swiglu_row(H, I, X + t * H, w13, w2, act, Y + i * H);
+                }
+                free(act);
+            }
+        }
+    }
+    return bad ? ORC_ERR_ARG : ORC_OK;
+}
+
+/* ---------------------------------------------------------------------------
+ * Step a6: the shared expert over the shared rows.  [RFC-GPU] "Data flow":
+ * the shared rows of FFN rank r are arange(r, num_tokens, ffn_size); with one
+ * FFN replica that is every token, carried in the slot's shared_x field.
+ * S[t] = SwiGLU_shared(Xs[t]), Ws13 [2Is][H], Ws2 [H][Is].
+ * ------------------------------------------------------------------------- */
+int oracle_shared(int64_t T, int64_t H, int64_t Is, const uint16_t* Xs,
+                  const uint16_t* Ws13, const uint16_t* Ws2, double* S) {
+    if (T < 0 || H < 1 || Is < 1) return ORC_ERR_ARG;
+    int bad = 0;
+#pragma omp parallel
+    {
+        double* act = (double*)malloc(sizeof(double) * (size_t)Is);
+        if (!act) {
+#pragma omp atomic write
+            bad = 1;
+        } else {
+#pragma omp for schedule(dynamic, 1)
+            for (int64_t t = 0; t < T; ++t) swiglu_row(H, Is, Xs + t * H, Ws13, Ws2, act, S + t * H);
+            free(act);
+        }
+    }
+    return bad ? ORC_ERR_ARG : ORC_OK;
+}
+
+/* ---------------------------------------------------------------------------
+ * Step a7: combine.  [RFC-GPU] "Data flow": each token's expert outputs are
+ * accumulated with its router weights (a weighted index_add_), and the shared
+ * branch is added by shared_idx.
+ *   out[t] = rsf * sum_{k<K} w[t,k] * Y[inv[t*K+k]]  +  S[t]      (k in order)
+ * S may be NULL (no shared expert).
+ * ------------------------------------------------------------------------- */
+int oracle_combine(int64_t T, int64_t H, int K, double rsf, const double* w,
+                   const int32_t* inv, const double* Y, const double* S, double* out) {
+    if (T < 0 || H < 1 || K < 1) return ORC_ERR_ARG;
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; ++t) {
+        for (int64_t c = 0; c < H; ++c) {
+            double r = 0.0;
+            for (int k = 0; k < K; ++k) r += w[t * K + k] * Y[(int64_t)inv[t * K + k] * H + c];
+            out[t * H + c] = rsf * r + (S ? S[t * H + c] : 0.0);
+        }
+    }
+    return ORC_OK;
+}
+
+/* ---------------------------------------------------------------------------
+ * The whole path, a1..a7, on per-peer inputs.  Outputs the concatenated
+ * result out[T][H] (split back per peer by off[], [WIRE] Step 4) and the
+ * routing/dispatch artefacts for bit-exact comparison.
+ *   x[p]: [seq_lens[p]][H] bf16;  l[p]: [seq_lens[p]][E] fp32
+ *   ids [T*K], w [T*K], counts [E], expert_offsets [E+1], perm/inv [T*K],
+ *   off [P+1], out [T*H] (all caller-allocated; any may be NULL except out,
+ *   which the computation needs).
+ * ------------------------------------------------------------------------- */
+int oracle_ffn(int P, const int32_t* seq_lens, const uint16_t* const* x, const float* const* l,
+               int64_t H, int E, int K, int64_t I, int64_t Is, double rsf, int renorm,
+               const uint16_t* W13, const uint16_t* W2, const uint16_t* Ws13, const uint16_t* Ws2,
+               int32_t* ids_out, double* w_out, int32_t* counts_out, int32_t* eoff_out,
+               int32_t* perm_out, int32_t* inv_out, int32_t* off_out, double* out) {
+    if (P < 1 || !seq_lens || H < 1 || E < 1 || K < 1 || K > E || I < 1 || !out) return ORC_ERR_ARG;
+    int rc;
+    int32_t* off = (int32_t*)malloc(sizeof(int32_t) * (size_t)(P + 1));
+    if (!off) return ORC_ERR_ARG;
+    rc = oracle_fanin(P, seq_lens, 0, off);
+    if (rc) { free(off); return rc; }
+    int64_t T = off[P], n = T * K;
+    uint16_t* X = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)(T * H + 1));
+    float* L = (float*)malloc(sizeof(float) * (size_t)(T * E + 1));
+    int32_t* ids = (int32_t*)malloc(sizeof(int32_t) * (size_t)(n + 1));
+    double* w = (double*)malloc(sizeof(double) * (size_t)(n + 1));
+    int32_t* counts = (int32_t*)malloc(sizeof(int32_t) * (size_t)E);
+    int32_t* eoff = (int32_t*)malloc(sizeof(int32_t) * (size_t)(E + 1));
+    int32_t* perm = (int32_t*)malloc(sizeof(int32_t) * (size_t)(n + 1));
+    int32_t* inv = (int32_t*)malloc(sizeof(int32_t) * (size_t)(n + 1));
+    double* Y = (double*)malloc(sizeof(double) * (size_t)(n * H + 1));
+    double* S = (Is > 0) ? (double*)malloc(sizeof(double) * (size_t)(T * H + 1)) : NULL;
+    if (!X || !L || !ids || !w || !counts || !eoff || !perm || !inv || !Y || (Is > 0 && !S)) {
+        rc = ORC_ERR_ARG;
+        goto done;
+    }
+    /* a1: fan-in -- concatenate the peers along the token dimension */
+    rc = oracle_concat_rows(P, seq_lens, (const void* const*)x, H * (int64_t)sizeof(uint16_t), X);
+    if (rc) goto done;
+    rc = oracle_concat_rows(P, seq_lens, (const void* const*)l, E * (int64_t)sizeof(float), L);
+    if (rc) goto done;
+    /* a2: route */
+    rc = oracle_route(T, E, K, renorm, L, ids, w);
+    if (rc) goto done;
+    /* a3: dispatch */
+    rc = oracle_dispatch(T, E, K, ids, counts, eoff, perm, inv);
+    if (rc) goto done;
+    /* a4/a5: routed experts over their groups */
+    rc = oracle_experts(T, H, E, K, I, X, eoff, perm, W13, W2, Y);
+    if (rc) goto done;
+    /* a6: shared expert over the shared rows (all tokens with one replica) */
+    if (Is > 0) {
+        rc = oracle_shared(T, H, Is, X, Ws13, Ws2, S);
+        if (rc) goto done;
+    }
+    /* a7: weighted combine (+ shared); the split is off[] */
+    rc = oracle_combine(T, H, K, rsf, w, inv, Y, S, out);
+    if (rc) goto done;
+    if (ids_out) memcpy(ids_out, ids, sizeof(int32_t) * (size_t)n);
+    if (w_out) memcpy(w_out, w, sizeof(double) * (size_t)n);
+    if (counts_out) memcpy(counts_out, counts, sizeof(int32_t) * (size_t)E);
+    if (eoff_out) memcpy(eoff_out, eoff, sizeof(int32_t) * (size_t)(E + 1));
+    if (perm_out) memcpy(perm_out, perm, sizeof(int32_t) * (size_t)n);
+    if (inv_out) memcpy(inv_out, inv, sizeof(int32_t) * (size_t)n);
+    if (off_out) memcpy(off_out, off, sizeof(int32_t) * (size_t)(P + 1));
+done:
+    free(off); free(X); free(L); free(ids); free(w); free(counts); free(eoff);
+    free(perm); free(inv); free(Y); free(S);
+    return rc;
+}
+
+/* ---------------------------------------------------------------------------
+ * Output rows for a chosen list of tokens, one token at a time, for sizes
+ * where the whole path is too slow on the CPU.  For token t (an index into
+ * the fan-in) it routes t alone (step a2 on one row), applies each selected
+ * expert to x_t, and combines in k order with the shared row:
+ *   out = rsf * sum_k w_k * SwiGLU_{ids_k}(x_t) + SwiGLU_shared(x_t)
+ * which is the same value the grouped path gives for that token (the expert
+ * output of pair t*K+k sits at inv[t*K+k]).
+ *   X: [T][H] bf16 fan-in rows; L: [T][E]; tok: n token indices;
+ *   out: [n][H]; ids: [n][K]; w: [n][K].
+ * ------------------------------------------------------------------------- */
+int oracle_token_rows(int64_t T, int64_t H, int E, int K, int64_t I, int64_t Is, double rsf,
+                      int renorm, const uint16_t* X, const float* L, const uint16_t* W13,
+                      const uint16_t* W2, const uint16_t* Ws13, const uint16_t* Ws2,
+                      int64_t n, const int64_t* tok, double* out, int32_t* ids, double* w) {
+    if (T < 0 || H < 1 || E < 1 || K < 1 || K > E || I < 1 || n < 0) return ORC_ERR_ARG;
+    for (int64_t q = 0; q < n; ++q)
+        if (tok[q] < 0 || tok[q] >= T) return ORC_ERR_ARG;
+    int bad = 0;
+#pragma omp parallel
+    {
+        int64_t amax = I > Is ? I : Is;
+        double* act = (double*)malloc(sizeof(double) * (size_t)amax);
+        double* y = (double*)malloc(sizeof(double) * (size_t)H);
+        if (!act || !y) {
+#pragma omp atomic write
+            bad = 1;
+        } else {
+#pragma omp for schedule(dynamic, 1)
+            for (int64_t q = 0; q < n; ++q) {
+                int64_t t = tok[q];
+                int rc = oracle_route(1, E, K, renorm, L + t * E, ids + q * K, w + q * K);
+                if (rc) {
+#pragma omp atomic write
+                    bad = 1;
+                    continue;
+                }
+                double* o = out + q * H;
+                for (int64_t c = 0; c < H; ++c) o[c] = 0.0;
+                for (int k = 0; k < K; ++k) {
+                    int e = ids[q * K + k];
+                    swiglu_row(H, I, X + t * H, W13 + (int64_t)e * 2 * I * H,
+                               W2 + (int64_t)e * H * I, act, y);
+                    for (int64_t c = 0; c < H; ++c) o[c] += w[q * K + k] * y[c];
+                }
+                for (int64_t c = 0; c < H; ++c) o[c] = rsf * o[c];
+                if (Is > 0) {
+                    swiglu_row(H, Is, X + t * H, Ws13, Ws2, act, y);
+                    for (int64_t c = 0; c < H; ++c) o[c] += y[c];
+                }
+            }
+        }
+        free(act);
+        free(y);
+    }
+    return bad ? ORC_ERR_ARG : ORC_OK;
+}
