@@ -1,0 +1,195 @@
+"""Benchmark: FFN-side tokens/s per MoE layer on one MI355X.
+
+A step is one afd_ffn_run -- the whole FFN-side hot path (wait + fan-in,
+top-k routing, dispatch permutation, gate/up SwiGLU grouped GEMM, down grouped
+GEMM with the shared expert, weighted combine + split + return publish) over
+one work item of P peers.  Before each step the peers pack their messages on
+their own streams and are synchronized, so the inputs are resident in HBM
+when the step starts; after it they unpack.  Each step is timed with HIP
+events on the FFN stream, one event between every two kernels, so the same
+timed region gives the per-kernel durations used for the roofline.
+
+Prints one JSON line.  Default workload: the prefill shape (2 peers,
+seq_lens [1024, 3072], H=2048, 64 experts, top-6, I=1408, shared 2816).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, published
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def algorithmic(wl, counts):
+    """Algorithmic flops and bytes of one FFN step and of its kernels."""
+    T, H, E, K, I, Is = (wl.total_tokens, wl.hidden, wl.num_experts, wl.top_k, wl.intermediate,
+                         wl.shared_intermediate)
+    pairs = T * K
+    touched = int((np.asarray(counts) > 0).sum())
+    g1_flops = 4.0 * H * I * pairs + 4.0 * H * Is * T
+    g2_flops = 2.0 * H * I * pairs + 2.0 * H * Is * T
+    w13_bytes = touched * 2 * I * H * 2 + (2 * Is * H * 2 if Is else 0)
+    w2_bytes = touched * H * I * 2 + (H * Is * 2 if Is else 0)
+    io_bytes = T * H * 2 + T * E * 4 + T * H * 2
+    return {
+        "flops": g1_flops + g2_flops,
+        "bytes": w13_bytes + w2_bytes + io_bytes,
+        "gemm_gate_up_swiglu": {"flops": g1_flops, "bytes": w13_bytes + T * H * 2 * (K + 1) + 2 * pairs * I},
+        "gemm_down": {"flops": g2_flops, "bytes": w2_bytes + 2 * pairs * I + 2 * T * Is},
+        "touched_experts": touched,
+    }
+
+
+def cpu_baseline(wl, inp, target_s=15.0):
+    """The oracle as it stands, timed on a bounded prefix sample of each peer."""
+    from oracle import oracle
+    oracle.lib()
+    T = wl.total_tokens
+
+    def run(frac):
+        n = [max(1, int(round(s * frac))) if s else 0 for s in wl.seq_lens]
+        x = [inp["x"][p][:n[p]] for p in range(wl.num_peers)]
+        l = [inp["l"][p][:n[p]] for p in range(wl.num_peers)]
+        t0 = time.perf_counter()
+        oracle.ffn(x, l, inp["W13"], inp["W2"], inp.get("Ws13"), inp.get("Ws2"), K=wl.top_k,
+                   rsf=wl.routed_scaling_factor, renorm=wl.renormalize)
+        return sum(n), time.perf_counter() - t0
+
+    frac = min(1.0, 32.0 / T)
+    n, dt = run(frac)
+    if dt < target_s / 4 and frac < 1.0:
+        frac = min(1.0, frac * target_s / max(dt, 1e-3))
+        n, dt = run(frac)
+    return {"value": n / dt, "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"first {n} of {T} tokens (each peer's leading {frac:.4f} share), whole oracle path "
+                      f"a1-a7 in float64, {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="prefill")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-profile", action="store_true", help="no per-kernel events (pure step timing)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: the FFN-rank path here runs on a single MI355X "
+              "(no collectives); run it with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from combine_afd_slot_amd import afd
+    from combine_afd_slot_amd.driver import FfnSession
+    from combine_afd_slot_amd.inputs import WORKLOADS, make_inputs
+
+    wl = WORKLOADS[args.workload]
+    log(f"[bench] workload {wl.name}: seq_lens={wl.seq_lens} H={wl.hidden} E={wl.num_experts} "
+        f"K={wl.top_k} I={wl.intermediate} Is={wl.shared_intermediate}")
+    t0 = time.time()
+    inp = make_inputs(wl)
+    log(f"[bench] inputs drawn in {time.time() - t0:.1f} s")
+
+    sess = FfnSession(wl, inp)
+    for i in range(args.warmup):
+        sess.step()
+    st = sess.status()
+    if st.status != 0:
+        raise RuntimeError(f"warmup run failed: {afd.status_string(st.status)}")
+    counts = sess.routing()["counts"]
+    log(f"[bench] warmup done ({args.warmup} steps); expert counts min/max {counts.min()}/{counts.max()}")
+
+    if not args.no_profile:
+        afd.afd_profile_enable(sess.win, True)
+        afd.afd_profile_read(sess.win, reset=True)
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    step_ms = []
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    for i in range(args.steps):
+        sess.pack_all()
+        ev0.record(sess.ffn_stream)
+        sess.run()
+        ev1.record(sess.ffn_stream)
+        sess.ffn_stream.synchronize()
+        step_ms.append(ev0.elapsed_time(ev1))
+        sess.unpack_all()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    st = sess.status()
+    if st.status != 0:
+        raise RuntimeError(f"timed run failed: {afd.status_string(st.status)}")
+    kern = {}
+    if not args.no_profile:
+        tot, runs = afd.afd_profile_read(sess.win, reset=True)
+        afd.afd_profile_enable(sess.win, False)
+        kern = {k: v / max(runs, 1) for k, v in tot.items()}
+    sess.close()
+
+    ms = float(np.mean(step_ms))
+    T = wl.total_tokens
+    alg = algorithmic(wl, counts)
+    value = T / (ms * 1e-3)
+    line = {
+        "metric": "FFN-side tokens/sec per MoE layer (dispatch+GEMM+combine); % of MFMA/HBM roofline",
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "ms_per_step_p10_p50_p90": [round(float(np.percentile(step_ms, q)), 4) for q in (10, 50, 90)],
+        "wall_ms_per_step_incl_pack_unpack": round(wall * 1e3 / args.steps, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "peers": wl.num_peers, "seq_lens": list(wl.seq_lens),
+                   "total_tokens": T, "hidden": wl.hidden, "experts": wl.num_experts, "top_k": wl.top_k,
+                   "intermediate": wl.intermediate, "shared_intermediate": wl.shared_intermediate,
+                   "token_cap": wl.token_cap, "parallelism": "single GPU"},
+        "mfma_frac_step": round(alg["flops"] / (ms * 1e-3) / (MFMA_BF16_PEAK_TFLOPS * 1e12), 4),
+        "hbm_frac_step": round(alg["bytes"] / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9), 4),
+        "expert_counts_min_max": [int(counts.min()), int(counts.max())],
+    }
+    if kern:
+        line["kernel_ms"] = {k: round(v, 4) for k, v in kern.items()}
+        dom = max(("gemm_gate_up_swiglu", "gemm_down"), key=lambda k: kern[k])
+        # decode-shaped steps stream weights: bound by HBM; prefill steps by MFMA
+        ai = alg[dom]["flops"] / alg[dom]["bytes"]
+        ridge = MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+        if ai >= ridge:
+            ach = alg[dom]["flops"] / (kern[dom] * 1e-3) / 1e12
+            line["roofline"] = {"kernel": dom, "bound": "mfma", "achieved": round(ach, 1),
+                                "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                                "frac": round(ach / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None}
+        else:
+            ach = alg[dom]["bytes"] / (kern[dom] * 1e-3) / 1e9
+            line["roofline"] = {"kernel": dom, "bound": "hbm", "achieved": round(ach, 1),
+                                "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None}
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on a bounded sample")
+        line["cpu_baseline"] = cpu_baseline(wl, inp)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,550 @@
+// afd_host.cpp -- the C ABI of libafd.so (include/afd.h): configuration
+// checks, the window layout, the per-(peer, stage) sequence and ring state
+// kept by the host, and the launches.  Host-detectable errors return before
+// anything is enqueued.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "afd_internal.h"
+
+namespace {
+
+thread_local std::string g_err = "";
+
+int32_t fail(int32_t code, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return code;
+}
+
+int32_t hip_fail(hipError_t e, const char* what) {
+    return fail(AFD_ERR_DEVICE, "%s: %s", what, hipGetErrorString(e));
+}
+
+const char* kProfileNames[AFD_PROFILE_SLOTS] = {"wait_fanin", "route_topk", "scan_offsets", "permute",
+                                                "gemm_gate_up_swiglu", "gemm_down", "combine_split_publish",
+                                                "unused"};
+constexpr int kProfileUsed = 7;
+
+int32_t validate(const afd_window_config* c) {
+    if (!c) return fail(AFD_ERR_INVALID, "config is NULL");
+    if (c->struct_size != sizeof(afd_window_config))
+        return fail(AFD_ERR_INVALID, "struct_size %u != %zu", c->struct_size, sizeof(afd_window_config));
+    for (int i = 0; i < 4; ++i)
+        if (c->reserved[i] != 0) return fail(AFD_ERR_INVALID, "reserved[%d] must be 0", i);
+    if (c->num_peers < 1 || c->num_peers > afd::kMaxPeers) return fail(AFD_ERR_INVALID, "num_peers out of [1,64]");
+    if (c->ring_depth < 1 || c->ring_depth > 4) return fail(AFD_ERR_INVALID, "ring_depth out of [1,4]");
+    if (c->token_cap < 1) return fail(AFD_ERR_INVALID, "token_cap must be >= 1");
+    if (c->hidden < 8 || c->hidden % 8) return fail(AFD_ERR_INVALID, "hidden must be a positive multiple of 8");
+    if (c->num_experts < 1 || c->num_experts > afd::kMaxExperts)
+        return fail(AFD_ERR_INVALID, "num_experts out of [1,1024]");
+    if (c->top_k < 1 || c->top_k > c->num_experts || c->top_k > afd::kMaxTopK)
+        return fail(AFD_ERR_INVALID, "top_k out of [1, min(num_experts,16)]");
+    if (c->intermediate < 8 || c->intermediate % 8)
+        return fail(AFD_ERR_INVALID, "intermediate must be a positive multiple of 8");
+    if (c->shared_intermediate < 0 || c->shared_intermediate % 8)
+        return fail(AFD_ERR_INVALID, "shared_intermediate must be a non-negative multiple of 8");
+    if (c->renormalize != 0 && c->renormalize != 1) return fail(AFD_ERR_INVALID, "renormalize must be 0 or 1");
+    if (c->poll_timeout_us < 1) return fail(AFD_ERR_INVALID, "poll_timeout_us must be >= 1");
+    if (!(c->routed_scaling_factor == c->routed_scaling_factor)) return fail(AFD_ERR_INVALID, "rsf is NaN");
+    const int64_t tmax = (int64_t)c->num_peers * c->token_cap;
+    if (tmax * c->top_k > (int64_t)1 << 30) return fail(AFD_ERR_INVALID, "num_peers*token_cap*top_k too large");
+    return AFD_OK;
+}
+
+// Workspace carve-up, in bytes from the workspace start.
+struct WsLayout {
+    int64_t ctrl, peer_counts, blk_counts, blk_base, counts, eoff, grp_M, grp_row0, tstart1, tstart2;
+    int64_t ids, wts, perm, inv, tok_src, sh_src, sh_dst, h, hs, y, ys, bytes;
+    int64_t ctrl_ints;
+    // control-word offsets inside ctrl (in ints)
+    int64_t c_seen_in, c_ret_seq, c_seen_ret, c_cur_seq, c_off, c_T, c_done, c_run_status, c_peer_status;
+};
+
+WsLayout ws_layout(const afd_window_config& c) {
+    WsLayout w{};
+    const int64_t P = c.num_peers, R = c.ring_depth, E = c.num_experts, K = c.top_k;
+    const int64_t tmax = P * c.token_cap, np = tmax * K;
+    const int64_t nb = (tmax + afd::kRouteChunk - 1) / afd::kRouteChunk;
+    const int64_t G = E + (c.shared_intermediate > 0 ? 1 : 0);
+    int64_t ci = 0;
+    w.c_seen_in = ci; ci += P * R;
+    w.c_ret_seq = ci; ci += P * R;
+    w.c_seen_ret = ci; ci += P * R;
+    w.c_cur_seq = ci; ci += P;
+    w.c_off = ci; ci += P + 1;
+    w.c_T = ci; ci += 1;
+    w.c_done = ci; ci += 1;
+    w.c_run_status = ci; ci += R * afd::kStatusWords;
+    w.c_peer_status = ci; ci += P * R * afd::kStatusWords;
+    w.ctrl_ints = ci;
+    int64_t cur = 0;
+    auto take = [&](int64_t bytes) {
+        const int64_t o = cur;
+        cur += afd::align_up(bytes > 0 ? bytes : 1);
+        return o;
+    };
+    w.ctrl = take(4 * ci);
+    w.peer_counts = take(4 * P * E);
+    w.blk_counts = take(4 * nb * E);
+    w.blk_base = take(4 * nb * E);
+    w.counts = take(4 * E);
+    w.eoff = take(4 * (E + 1));
+    w.grp_M = take(4 * G);
+    w.grp_row0 = take(4 * G);
+    w.tstart1 = take(4 * (G + 1));
+    w.tstart2 = take(4 * (G + 1));
+    w.ids = take(4 * np);
+    w.wts = take(4 * np);
+    w.perm = take(4 * np);
+    w.inv = take(4 * np);
+    w.tok_src = take(8 * tmax);
+    w.sh_src = take(8 * tmax);
+    w.sh_dst = take(4 * tmax);
+    w.h = take(2 * np * c.intermediate);
+    w.hs = take(2 * tmax * (c.shared_intermediate > 0 ? c.shared_intermediate : 1));
+    w.y = take(2 * np * c.hidden);
+    w.ys = take(4 * tmax * c.hidden);
+    w.bytes = cur;
+    return w;
+}
+
+void layout_from(const afd_window_config& c, afd_layout* L, WsLayout* wl) {
+    std::memset(L, 0, sizeof *L);
+    int64_t fb[AFD_NUM_FIELDS];
+    afd::slot_field_bytes(c.token_cap, c.hidden, c.num_experts, fb);
+    int64_t cur = 0;
+    for (int i = 0; i < AFD_NUM_FIELDS; ++i) {
+        L->field_off[i] = cur;
+        L->field_bytes[i] = fb[i];
+        cur += afd::align_up(fb[i]);
+    }
+    L->slot_bytes = cur;
+    const int64_t nflags = (int64_t)c.num_peers * c.ring_depth;
+    const int64_t first_slot = afd::align_up(4 * nflags);
+    L->window_bytes = first_slot + nflags * L->slot_bytes;
+    L->in_off = 0;
+    L->in_slots_off = first_slot;
+    L->ret_off = afd::align_up(L->window_bytes);
+    L->ret_slots_off = L->ret_off + first_slot;
+    const WsLayout w = ws_layout(c);
+    L->workspace_off = L->ret_off + afd::align_up(L->window_bytes);
+    L->workspace_bytes = w.bytes;
+    L->total_bytes = L->workspace_off + w.bytes;
+    if (wl) *wl = w;
+}
+
+}  // namespace
+
+struct afd_window {
+    afd_window_config cfg;
+    afd_layout lay;
+    WsLayout wl;
+    int device = 0;
+    int num_cu = 0;
+    long long ticks_per_us = 100;
+    char* base = nullptr;
+    afd::DevCtx ctx{};
+    std::vector<int32_t> pack_seq;    // [P*R] last seq sent by the peer (host side of the peer)
+    std::vector<int32_t> packed_len;  // [P*R]
+    std::vector<uint8_t> inflight;    // [P*R]
+    bool profile = false;
+    hipEvent_t ev[AFD_PROFILE_SLOTS + 1] = {};
+    bool ev_pending = false;
+    double prof_ms[AFD_PROFILE_SLOTS] = {};
+    int prof_runs = 0;
+    std::mutex prof_mu;
+};
+
+namespace {
+
+void fill_ctx(afd_window* w) {
+    const afd_window_config& c = w->cfg;
+    const WsLayout& L = w->wl;
+    afd::DevCtx& d = w->ctx;
+    d.P = c.num_peers;
+    d.R = c.ring_depth;
+    d.token_cap = c.token_cap;
+    d.H = c.hidden;
+    d.E = c.num_experts;
+    d.K = c.top_k;
+    d.I = c.intermediate;
+    d.Is = c.shared_intermediate;
+    d.renorm = c.renormalize;
+    d.rsf = c.routed_scaling_factor;
+    d.has_shared = c.shared_intermediate > 0 ? 1 : 0;
+    d.G = c.num_experts + d.has_shared;
+    const int64_t tmax = (int64_t)c.num_peers * c.token_cap;
+    d.NB = (int)((tmax + afd::kRouteChunk - 1) / afd::kRouteChunk);
+    {
+        // sum over groups of ceil(M_g / BM) <= (pairs + E*(BM-1)) / BM, plus the shared group
+        const int64_t pairs = tmax * c.top_k;
+        const int64_t mt_r = (pairs + (int64_t)c.num_experts * (afd::kBM - 1)) / afd::kBM;
+        const int64_t mt_s = d.has_shared ? (tmax + afd::kBM - 1) / afd::kBM : 0;
+        const int64_t nt1_r = (c.intermediate + afd::kBN / 2 - 1) / (afd::kBN / 2);
+        const int64_t nt1_s = (c.shared_intermediate + afd::kBN / 2 - 1) / (afd::kBN / 2);
+        const int64_t nt2 = (c.hidden + afd::kBN - 1) / afd::kBN;
+        d.max_tiles1 = (int)(mt_r * nt1_r + mt_s * nt1_s);
+        d.max_tiles2 = (int)((mt_r + mt_s) * nt2);
+    }
+    d.slot_bytes = w->lay.slot_bytes;
+    for (int i = 0; i < AFD_NUM_FIELDS; ++i) d.foff[i] = w->lay.field_off[i];
+    d.in_win = w->base + w->lay.in_off;
+    d.ret_win = w->base + w->lay.ret_off;
+    d.slots_off = w->lay.in_slots_off - w->lay.in_off;
+    char* ws = w->base + w->lay.workspace_off;
+    int* ctrl = (int*)(ws + L.ctrl);
+    d.seen_in = ctrl + L.c_seen_in;
+    d.ret_seq = ctrl + L.c_ret_seq;
+    d.seen_ret = ctrl + L.c_seen_ret;
+    d.cur_seq = ctrl + L.c_cur_seq;
+    d.off = ctrl + L.c_off;
+    d.Tptr = ctrl + L.c_T;
+    d.done_ctr = ctrl + L.c_done;
+    d.run_status = ctrl + L.c_run_status;
+    d.peer_status = ctrl + L.c_peer_status;
+    d.peer_counts = (int*)(ws + L.peer_counts);
+    d.blk_counts = (int*)(ws + L.blk_counts);
+    d.blk_base = (int*)(ws + L.blk_base);
+    d.counts = (int*)(ws + L.counts);
+    d.eoff = (int*)(ws + L.eoff);
+    d.grp_M = (int*)(ws + L.grp_M);
+    d.grp_row0 = (int*)(ws + L.grp_row0);
+    d.tstart1 = (int*)(ws + L.tstart1);
+    d.tstart2 = (int*)(ws + L.tstart2);
+    d.ids = (int*)(ws + L.ids);
+    d.wts = (float*)(ws + L.wts);
+    d.perm = (int*)(ws + L.perm);
+    d.inv = (int*)(ws + L.inv);
+    d.tok_src = (uint64_t*)(ws + L.tok_src);
+    d.sh_src = (uint64_t*)(ws + L.sh_src);
+    d.sh_dst = (int*)(ws + L.sh_dst);
+    d.h = (uint16_t*)(ws + L.h);
+    d.hs = (uint16_t*)(ws + L.hs);
+    d.y = (uint16_t*)(ws + L.y);
+    d.ys = (float*)(ws + L.ys);
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+// Fold the previous run's events into the accumulated times.
+void prof_collect(afd_window* w) {
+    if (!w->ev_pending) return;
+    for (int i = 0; i <= kProfileUsed; ++i) (void)hipEventSynchronize(w->ev[i]);
+    for (int i = 0; i < kProfileUsed; ++i) {
+        float ms = 0.f;
+        if (hipEventElapsedTime(&ms, w->ev[i], w->ev[i + 1]) == hipSuccess) w->prof_ms[i] += ms;
+    }
+    w->prof_runs += 1;
+    w->ev_pending = false;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t afd_abi_version(void) { return AFD_ABI_VERSION; }
+
+const char* afd_last_error(void) { return g_err.c_str(); }
+
+const char* afd_status_string(int32_t s) {
+    switch (s) {
+        case AFD_OK: return "AFD_OK";
+        case AFD_SHUTDOWN: return "AFD_SHUTDOWN";
+        case AFD_ERR_INVALID: return "AFD_ERR_INVALID";
+        case AFD_ERR_CAPACITY: return "AFD_ERR_CAPACITY";
+        case AFD_ERR_SHAPE: return "AFD_ERR_SHAPE";
+        case AFD_ERR_RING: return "AFD_ERR_RING";
+        case AFD_ERR_TIMEOUT: return "AFD_ERR_TIMEOUT";
+        case AFD_ERR_HEADER: return "AFD_ERR_HEADER";
+        case AFD_ERR_SEQ: return "AFD_ERR_SEQ";
+        case AFD_ERR_DEVICE: return "AFD_ERR_DEVICE";
+        default: return "AFD_UNKNOWN";
+    }
+}
+
+int32_t afd_layout_compute(const afd_window_config* cfg, afd_layout* out) {
+    const int32_t rc = validate(cfg);
+    if (rc) return rc;
+    if (!out) return fail(AFD_ERR_INVALID, "out is NULL");
+    layout_from(*cfg, out, nullptr);
+    return AFD_OK;
+}
+
+int32_t afd_header_encode(const afd_header_fields* f, const int32_t* counts, int32_t* words_out) {
+    if (!f || !words_out || f->n_counts < 0) return fail(AFD_ERR_INVALID, "bad header arguments");
+    afd::header_encode(*f, counts, words_out);
+    return AFD_OK;
+}
+
+int32_t afd_header_decode(const int32_t* words, int32_t nwords, int32_t expect_counts, afd_header_fields* out) {
+    if (!words || !out || nwords < AFD_HDR_WORDS) return fail(AFD_ERR_INVALID, "bad header arguments");
+    if (nwords < AFD_HDR_WORDS + expect_counts) return fail(AFD_ERR_HEADER, "header shorter than its counts");
+    const int32_t rc = afd::header_decode(words, expect_counts, out);
+    if (rc) return fail(rc, "header failed its magic/version/length check");
+    return AFD_OK;
+}
+
+int32_t afd_window_create(const afd_window_config* cfg, afd_window** out) {
+    if (!out) return fail(AFD_ERR_INVALID, "out is NULL");
+    *out = nullptr;
+    int32_t rc = validate(cfg);
+    if (rc) return rc;
+    afd_window* w = new (std::nothrow) afd_window();
+    if (!w) return fail(AFD_ERR_INVALID, "out of host memory");
+    w->cfg = *cfg;
+    layout_from(*cfg, &w->lay, &w->wl);
+    hipError_t e = hipGetDevice(&w->device);
+    if (e != hipSuccess) {
+        delete w;
+        return hip_fail(e, "hipGetDevice");
+    }
+    (void)hipDeviceGetAttribute(&w->num_cu, hipDeviceAttributeMultiprocessorCount, w->device);
+    if (w->num_cu < 1) w->num_cu = 1;
+    int khz = 0;
+    if (hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, w->device) == hipSuccess && khz > 0)
+        w->ticks_per_us = khz / 1000 > 0 ? khz / 1000 : 1;
+    e = hipMalloc((void**)&w->base, (size_t)w->lay.total_bytes);
+    if (e != hipSuccess) {
+        delete w;
+        return hip_fail(e, "hipMalloc(window)");
+    }
+    // Flags, mirrors and status words start at zero; the slots are left as
+    // they are (a slot is only read after its flag announces it).
+    const afd_layout& L = w->lay;
+    e = hipMemset(w->base + L.in_off, 0, (size_t)(L.in_slots_off - L.in_off));
+    if (e == hipSuccess) e = hipMemset(w->base + L.ret_off, 0, (size_t)(L.ret_slots_off - L.ret_off));
+    if (e == hipSuccess) e = hipMemset(w->base + L.workspace_off + w->wl.ctrl, 0, (size_t)(4 * w->wl.ctrl_ints));
+    if (e == hipSuccess) e = hipDeviceSynchronize();
+    if (e != hipSuccess) {
+        (void)hipFree(w->base);
+        delete w;
+        return hip_fail(e, "window init");
+    }
+    const int pr = cfg->num_peers * cfg->ring_depth;
+    w->pack_seq.assign(pr, 0);
+    w->packed_len.assign(pr, 0);
+    w->inflight.assign(pr, 0);
+    fill_ctx(w);
+    for (int i = 0; i <= AFD_PROFILE_SLOTS; ++i) (void)hipEventCreate(&w->ev[i]);
+    const char* lg = getenv("AFD_LOG");
+    if (lg && lg[0] == '1')
+        fprintf(stderr, "[afd] window: P=%d R=%d token_cap=%d slot=%lld B window=%lld B workspace=%lld B total=%lld B\n",
+                cfg->num_peers, cfg->ring_depth, cfg->token_cap, (long long)L.slot_bytes, (long long)L.window_bytes,
+                (long long)L.workspace_bytes, (long long)L.total_bytes);
+    *out = w;
+    return AFD_OK;
+}
+
+int32_t afd_window_destroy(afd_window* w) {
+    if (!w) return AFD_OK;
+    int32_t rc = AFD_OK;
+    if (w->base) {
+        hipError_t e = hipDeviceSynchronize();
+        if (e != hipSuccess) rc = hip_fail(e, "hipDeviceSynchronize");
+        (void)hipFree(w->base);
+    }
+    for (int i = 0; i <= AFD_PROFILE_SLOTS; ++i)
+        if (w->ev[i]) (void)hipEventDestroy(w->ev[i]);
+    delete w;
+    return rc;
+}
+
+int32_t afd_window_layout(const afd_window* w, afd_layout* out) {
+    if (!w || !out) return fail(AFD_ERR_INVALID, "NULL argument");
+    *out = w->lay;
+    return AFD_OK;
+}
+
+int32_t afd_slot_pack(afd_window* w, int32_t peer, int32_t stage, int32_t layer_idx, int32_t seq_len,
+                      const void* hidden, const float* logits, uint32_t flags, void* peer_stream) {
+    if (!w) return fail(AFD_ERR_INVALID, "window is NULL");
+    const afd_window_config& c = w->cfg;
+    if (peer < 0 || peer >= c.num_peers) return fail(AFD_ERR_INVALID, "peer %d out of range", peer);
+    if (stage < 0 || stage >= c.ring_depth) return fail(AFD_ERR_INVALID, "stage %d out of range", stage);
+    if (seq_len < 0) return fail(AFD_ERR_INVALID, "seq_len < 0");
+    if (seq_len > c.token_cap)
+        return fail(AFD_ERR_CAPACITY, "seq_len %d exceeds token_cap %d", seq_len, c.token_cap);
+    if (flags & ~AFD_FLAG_SHUTDOWN) return fail(AFD_ERR_INVALID, "unknown flag bits 0x%x", flags);
+    if (seq_len > 0 && (!hidden || !logits)) return fail(AFD_ERR_INVALID, "hidden/logits NULL");
+    if (seq_len > 0 && (!aligned(hidden, 16) || !aligned(logits, 4)))
+        return fail(AFD_ERR_INVALID, "hidden must be 16-byte aligned, logits 4-byte aligned");
+    const int idx = peer * c.ring_depth + stage;
+    if (w->inflight[idx])
+        return fail(AFD_ERR_RING, "(peer %d, stage %d) still in flight: unpack it before packing again", peer, stage);
+    const int seq = w->pack_seq[idx] + 1;
+    hipError_t e = afd::launch_pack(w->ctx, peer, stage, layer_idx, seq_len, hidden, logits, flags, seq,
+                                    (hipStream_t)peer_stream);
+    if (e != hipSuccess) return hip_fail(e, "pack launch");
+    w->pack_seq[idx] = seq;
+    w->packed_len[idx] = seq_len;
+    // a shutdown message gets no reply; an empty one neither
+    w->inflight[idx] = (seq_len > 0 && !(flags & AFD_FLAG_SHUTDOWN)) ? 1 : 0;
+    return AFD_OK;
+}
+
+int32_t afd_ffn_run(afd_window* w, int32_t stage, int32_t layer_idx, const afd_moe_weights* weights,
+                    void* ffn_stream) {
+    if (!w || !weights) return fail(AFD_ERR_INVALID, "NULL argument");
+    const afd_window_config& c = w->cfg;
+    if (stage < 0 || stage >= c.ring_depth) return fail(AFD_ERR_INVALID, "stage %d out of range", stage);
+    if (!weights->w13 || !weights->w2) return fail(AFD_ERR_INVALID, "routed weights are NULL");
+    if (c.shared_intermediate > 0 && (!weights->ws13 || !weights->ws2))
+        return fail(AFD_ERR_INVALID, "shared weights are NULL");
+    if (!aligned(weights->w13, 16) || !aligned(weights->w2, 16) ||
+        (c.shared_intermediate > 0 && (!aligned(weights->ws13, 16) || !aligned(weights->ws2, 16))))
+        return fail(AFD_ERR_INVALID, "weights must be 16-byte aligned");
+    afd::Weights wt{(const uint16_t*)weights->w13, (const uint16_t*)weights->w2, (const uint16_t*)weights->ws13,
+                    (const uint16_t*)weights->ws2};
+    hipEvent_t* ev = nullptr;
+    if (w->profile) {
+        std::lock_guard<std::mutex> g(w->prof_mu);
+        prof_collect(w);
+        ev = w->ev;
+        w->ev_pending = true;
+    }
+    const long long timeout = (long long)c.poll_timeout_us * w->ticks_per_us;
+    hipError_t e = afd::launch_ffn(w->ctx, stage, layer_idx, wt, timeout, w->num_cu, ev, (hipStream_t)ffn_stream);
+    if (e != hipSuccess) return hip_fail(e, "ffn launch");
+    return AFD_OK;
+}
+
+int32_t afd_slot_unpack(afd_window* w, int32_t peer, int32_t stage, int32_t seq_len, void* out,
+                        void* peer_stream) {
+    if (!w) return fail(AFD_ERR_INVALID, "window is NULL");
+    const afd_window_config& c = w->cfg;
+    if (peer < 0 || peer >= c.num_peers) return fail(AFD_ERR_INVALID, "peer %d out of range", peer);
+    if (stage < 0 || stage >= c.ring_depth) return fail(AFD_ERR_INVALID, "stage %d out of range", stage);
+    const int idx = peer * c.ring_depth + stage;
+    if (seq_len != w->packed_len[idx])
+        return fail(AFD_ERR_SHAPE, "seq_len %d differs from the packed length %d", seq_len, w->packed_len[idx]);
+    if (seq_len == 0) {
+        w->inflight[idx] = 0;
+        return AFD_OK;  // nothing was sent, nothing to wait for
+    }
+    if (!w->inflight[idx]) return fail(AFD_ERR_INVALID, "(peer %d, stage %d) has no message in flight", peer, stage);
+    if (!out || !aligned(out, 16)) return fail(AFD_ERR_INVALID, "out must be a 16-byte aligned device pointer");
+    const long long timeout = (long long)c.poll_timeout_us * w->ticks_per_us;
+    hipError_t e = afd::launch_unpack(w->ctx, peer, stage, seq_len, w->pack_seq[idx], out, timeout,
+                                      (hipStream_t)peer_stream);
+    if (e != hipSuccess) return hip_fail(e, "unpack launch");
+    w->inflight[idx] = 0;
+    return AFD_OK;
+}
+
+static int32_t read_status(afd_window* w, const int* dev_words, void* stream, afd_run_info* info) {
+    if (!info) return fail(AFD_ERR_INVALID, "info is NULL");
+    hipError_t e = hipStreamSynchronize((hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+    int32_t words[afd::kStatusWords];
+    e = hipMemcpy(words, dev_words, sizeof words, hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return hip_fail(e, "status copy");
+    info->status = words[0];
+    info->failed_peer = words[1];
+    info->last_seq = words[2];
+    info->total_tokens = words[3];
+    (void)w;
+    return AFD_OK;
+}
+
+int32_t afd_window_status(afd_window* w, int32_t stage, void* stream, afd_run_info* info) {
+    if (!w) return fail(AFD_ERR_INVALID, "window is NULL");
+    if (stage < 0 || stage >= w->cfg.ring_depth) return fail(AFD_ERR_INVALID, "stage out of range");
+    return read_status(w, w->ctx.run_status + stage * afd::kStatusWords, stream, info);
+}
+
+int32_t afd_peer_status(afd_window* w, int32_t peer, int32_t stage, void* stream, afd_run_info* info) {
+    if (!w) return fail(AFD_ERR_INVALID, "window is NULL");
+    if (peer < 0 || peer >= w->cfg.num_peers || stage < 0 || stage >= w->cfg.ring_depth)
+        return fail(AFD_ERR_INVALID, "peer/stage out of range");
+    return read_status(w, w->ctx.peer_status + (peer * w->cfg.ring_depth + stage) * afd::kStatusWords, stream, info);
+}
+
+int32_t afd_window_poll(afd_window* w, int32_t which, int32_t* flags_out) {
+    if (!w || !flags_out || (which != 0 && which != 1)) return fail(AFD_ERR_INVALID, "bad poll arguments");
+    const char* src = which == 0 ? w->ctx.in_win : w->ctx.ret_win;
+    hipError_t e = hipMemcpy(flags_out, src, sizeof(int32_t) * w->cfg.num_peers * w->cfg.ring_depth,
+                             hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return hip_fail(e, "poll copy");
+    return AFD_OK;
+}
+
+int32_t afd_debug_routing(afd_window* w, void* stream, int32_t* ids, float* wts, int32_t* counts,
+                          int32_t* expert_offsets, int32_t* perm, int32_t* inv, int32_t* split_offsets) {
+    if (!w) return fail(AFD_ERR_INVALID, "window is NULL");
+    hipError_t e = hipStreamSynchronize((hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+    const afd::DevCtx& d = w->ctx;
+    const afd_window_config& c = w->cfg;
+    int32_t T = 0;
+    e = hipMemcpy(&T, d.Tptr, 4, hipMemcpyDeviceToHost);
+    const size_t np = (size_t)T * c.top_k;
+    auto cp = [&](void* dst, const void* src, size_t bytes) {
+        if (e == hipSuccess && dst && bytes) e = hipMemcpy(dst, src, bytes, hipMemcpyDeviceToHost);
+    };
+    cp(ids, d.ids, 4 * np);
+    cp(wts, d.wts, 4 * np);
+    cp(counts, d.counts, 4 * (size_t)c.num_experts);
+    cp(expert_offsets, d.eoff, 4 * ((size_t)c.num_experts + 1));
+    cp(perm, d.perm, 4 * np);
+    cp(inv, d.inv, 4 * np);
+    cp(split_offsets, d.off, 4 * ((size_t)c.num_peers + 1));
+    if (e != hipSuccess) return hip_fail(e, "debug copy");
+    return AFD_OK;
+}
+
+int32_t afd_debug_read(afd_window* w, int64_t offset, int64_t bytes, void* host_dst) {
+    if (!w || !host_dst || offset < 0 || bytes < 0 || offset + bytes > w->lay.total_bytes)
+        return fail(AFD_ERR_INVALID, "debug read out of range");
+    hipError_t e = hipMemcpy(host_dst, w->base + offset, (size_t)bytes, hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return hip_fail(e, "debug read");
+    return AFD_OK;
+}
+
+int32_t afd_debug_write(afd_window* w, int64_t offset, int64_t bytes, const void* host_src) {
+    if (!w || !host_src || offset < 0 || bytes < 0 || offset + bytes > w->lay.total_bytes)
+        return fail(AFD_ERR_INVALID, "debug write out of range");
+    hipError_t e = hipMemcpy(w->base + offset, host_src, (size_t)bytes, hipMemcpyHostToDevice);
+    if (e == hipSuccess) e = hipDeviceSynchronize();
+    if (e != hipSuccess) return hip_fail(e, "debug write");
+    return AFD_OK;
+}
+
+int32_t afd_profile_enable(afd_window* w, int32_t on) {
+    if (!w) return fail(AFD_ERR_INVALID, "window is NULL");
+    std::lock_guard<std::mutex> g(w->prof_mu);
+    if (!on) prof_collect(w);
+    w->profile = on != 0;
+    return AFD_OK;
+}
+
+int32_t afd_profile_read(afd_window* w, float* ms, int32_t n, int32_t* runs, int32_t reset) {
+    if (!w) return fail(AFD_ERR_INVALID, "window is NULL");
+    std::lock_guard<std::mutex> g(w->prof_mu);
+    prof_collect(w);
+    for (int i = 0; i < n && i < AFD_PROFILE_SLOTS; ++i) ms[i] = (float)w->prof_ms[i];
+    if (runs) *runs = w->prof_runs;
+    if (reset) {
+        for (double& v : w->prof_ms) v = 0.0;
+        w->prof_runs = 0;
+    }
+    return AFD_OK;
+}
+
+const char* afd_profile_kernel_name(int32_t i) {
+    if (i < 0 || i >= AFD_PROFILE_SLOTS) return "";
+    return kProfileNames[i];
+}
+
+}  // extern "C"

@@ -1,0 +1,95 @@
+// afd_internal.h -- device context shared by the host launcher code and the
+// kernels of libafd.so.  Not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "afd_proto.h"
+
+namespace afd {
+
+// Tokens handled by one routing / permutation workgroup.  The per-block
+// expert histograms of the routing kernel and the stable ranks of the
+// permutation kernel are both taken over these chunks, in token order.
+constexpr int kRouteChunk = 64;
+constexpr int kMaxTopK = 16;
+constexpr int kMaxPeers = 64;
+constexpr int kMaxExperts = 1024;
+
+// Grouped-GEMM macro tile (rows x columns x depth).  For the gate/up GEMM
+// the BN columns are BN/2 gate columns and the same BN/2 up columns.
+constexpr int kBM = 128;
+constexpr int kBN = 128;
+constexpr int kBK = 64;
+
+// Per-stage run status words: [status, failed_peer, seq of peer 0, T].
+constexpr int kStatusWords = 4;
+
+// Everything a kernel needs, passed by value.
+struct DevCtx {
+    // configuration
+    int P, R, token_cap, H, E, K, I, Is, renorm;
+    float rsf;
+    int has_shared;  // Is > 0
+    int G;           // GEMM groups: shared first (when present), then experts
+    int NB;          // routing chunks for P*token_cap tokens
+    int max_tiles1, max_tiles2;  // upper bounds of the GEMM tile counts (sanity limits)
+    int64_t slot_bytes;
+    int64_t foff[AFD_NUM_FIELDS];
+    // windows (flags at offset 0 of each window)
+    char* in_win;
+    char* ret_win;
+    int64_t slots_off;  // first slot, relative to a window's start
+    // control words
+    int* seen_in;      // [P*R] FFN-side mirror of the inbound flags
+    int* ret_seq;      // [P*R] FFN-side return sequence counters
+    int* seen_ret;     // [P*R] peer-side mirror of the return flags
+    int* cur_seq;      // [P]   inbound seq consumed by the current run
+    int* off;          // [P+1] fan-in offsets
+    int* Tptr;         // [1]   total tokens of the current run
+    int* done_ctr;     // [1]   combine completion counter
+    int* run_status;   // [R][kStatusWords]
+    int* peer_status;  // [P*R][kStatusWords]
+    // routing / dispatch
+    int* peer_counts;  // [P][E]
+    int* blk_counts;   // [NB][E]
+    int* blk_base;     // [NB][E]
+    int* counts;       // [E]
+    int* eoff;         // [E+1]
+    int* grp_M;        // [G]
+    int* grp_row0;     // [G]
+    int* tstart1;      // [G+1] gate/up GEMM tile prefix
+    int* tstart2;      // [G+1] down GEMM tile prefix
+    int* ids;          // [Tmax*K]
+    float* wts;        // [Tmax*K]
+    int* perm;         // [Tmax*K]
+    int* inv;          // [Tmax*K]
+    uint64_t* tok_src; // [Tmax] address of token t's routed_x row
+    uint64_t* sh_src;  // [Tmax] address of shared row t's shared_x row
+    int* sh_dst;       // [Tmax] fan-in token index of shared row t
+    // expert activations
+    uint16_t* h;       // [Tmax*K][I]  bf16 SwiGLU activations, permuted order
+    uint16_t* hs;      // [Tmax][Is]   bf16 shared activations
+    uint16_t* y;       // [Tmax*K][H]  bf16 routed expert outputs, permuted order
+    float* ys;         // [Tmax][H]    fp32 shared expert output, token order
+};
+
+struct Weights {
+    const uint16_t* w13;
+    const uint16_t* w2;
+    const uint16_t* ws13;
+    const uint16_t* ws2;
+};
+
+// Launchers (afd_kernels.hip).  All return the launch's hipError_t.
+hipError_t launch_pack(const DevCtx& c, int peer, int stage, int layer, int seq_len, const void* hidden,
+                       const float* logits, uint32_t flags, int seq, hipStream_t st);
+hipError_t launch_unpack(const DevCtx& c, int peer, int stage, int seq_len, int expect_echo, void* out,
+                         long long timeout_ticks, hipStream_t st);
+// One FFN run; `ev` (may be null) holds kProfileSlots+1 events recorded
+// between the launches.
+hipError_t launch_ffn(const DevCtx& c, int stage, int layer, const Weights& w, long long timeout_ticks,
+                      int num_cu, hipEvent_t* ev, hipStream_t st);
+
+}  // namespace afd

@@ -1,0 +1,127 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Routing ids, per-expert counts and offsets, the dispatch permutation and its
+inverse, and the split offsets must match bit for bit; outputs within 2e-2
+per-row relative error.  Small workloads are checked on every output row;
+the full-size workloads on every routing artefact and on sampled output
+rows that the oracle computes one token at a time.
+"""
+import numpy as np
+import pytest
+
+from combine_afd_slot_amd.driver import FfnSession
+from combine_afd_slot_amd.inputs import WORKLOADS, make_inputs, small_workload
+from gpu_util import ROW_REL_TOL, check_routing, row_rel_err, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _run_and_check_full(orc, wl):
+    say(f"[parity] {wl.name} seq_lens={wl.seq_lens} H={wl.hidden} E={wl.num_experts} K={wl.top_k} "
+        f"I={wl.intermediate} Is={wl.shared_intermediate}")
+    inp = make_inputs(wl)
+    ref = orc.ffn(inp["x"], inp["l"], inp["W13"], inp["W2"], inp.get("Ws13"), inp.get("Ws2"),
+                  K=wl.top_k, rsf=wl.routed_scaling_factor, renorm=wl.renormalize)
+    with FfnSession(wl, inp) as s:
+        s.step()
+        st = s.status()
+        assert st.status == 0, st.status
+        assert st.total_tokens == wl.total_tokens
+        check_routing(s.routing(), ref, wl)
+        outs = s.outputs_f32()
+        for p in range(wl.num_peers):
+            assert s.peer_status(p).status == 0
+            err = row_rel_err(outs[p], ref["out_p"][p])
+            assert err <= ROW_REL_TOL, (p, err)
+    return ref
+
+
+def test_tiny(orc):
+    _run_and_check_full(orc, WORKLOADS["tiny"])
+
+
+SMALL = [
+    # empty peer, widths that are not multiples of the 64-wide tile halves
+    small_workload(),
+    # several row tiles per expert, ragged tails everywhere
+    small_workload("multi_tile", seq_lens=(300, 173), hidden=192, num_experts=6, top_k=2,
+                   intermediate=136, shared_intermediate=264, token_cap=300),
+    # no shared expert, K = E, routed scaling factor
+    small_workload("k_eq_e", seq_lens=(33, 1), hidden=64, num_experts=5, top_k=5, intermediate=48,
+                   shared_intermediate=0, token_cap=40, routed_scaling_factor=2.5),
+    # top-1, many experts (two logits per lane), no renormalisation
+    small_workload("top1_e100", seq_lens=(50, 70, 9), hidden=128, num_experts=100, top_k=1,
+                   intermediate=64, shared_intermediate=64, token_cap=80, renormalize=0),
+    # many peers, E=256 (four logits per lane), K=8
+    small_workload("e256", seq_lens=(5, 17, 0, 29, 3, 64, 1, 40), hidden=256, num_experts=256, top_k=8,
+                   intermediate=128, shared_intermediate=128, token_cap=64),
+]
+
+
+@pytest.mark.parametrize("wl", SMALL, ids=[w.name for w in SMALL])
+def test_small_workloads(orc, wl):
+    _run_and_check_full(orc, wl)
+
+
+def test_ties_and_negative_zero(orc):
+    wl = small_workload("ties", seq_lens=(40, 24), hidden=64, num_experts=16, top_k=4, intermediate=64,
+                        shared_intermediate=0, token_cap=64)
+    inp = make_inputs(wl)
+    L = inp["L"]
+    L[::2] = np.round(L[::2])          # many exact ties
+    L[1::4] = 0.5                       # all-equal rows
+    L[3::8, 3] = -0.0
+    L[3::8, 5] = 0.0
+    off = np.concatenate([[0], np.cumsum(wl.seq_lens)])
+    inp["l"] = [L[off[p]:off[p + 1]] for p in range(wl.num_peers)]
+    ref = orc.ffn(inp["x"], inp["l"], inp["W13"], inp["W2"], K=wl.top_k)
+    with FfnSession(wl, inp) as s:
+        s.step()
+        assert s.status().status == 0
+        check_routing(s.routing(), ref, wl)
+
+
+def _sampled_tokens(wl, per_peer=4):
+    off = np.concatenate([[0], np.cumsum(wl.seq_lens)])
+    rng = np.random.default_rng(7)
+    tok = []
+    for p in range(wl.num_peers):
+        n = wl.seq_lens[p]
+        if n == 0:
+            continue
+        pick = {off[p], off[p + 1] - 1}
+        pick.update(int(off[p] + v) for v in rng.integers(0, n, per_peer))
+        tok.extend(sorted(pick))
+    return np.array(tok, dtype=np.int64)
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name", ["decode", "prefill", "fanin4", "skew"])
+def test_full_size_sampled(orc, name):
+    wl = WORKLOADS[name]
+    say(f"[parity-full] {name}: generating inputs")
+    inp = make_inputs(wl, progress=lambda what: say(f"[parity-full] {name}: drawing {what}"))
+    say(f"[parity-full] {name}: oracle routing + dispatch on all {wl.total_tokens} tokens")
+    ids, w = orc.route(inp["L"], wl.top_k, wl.renormalize)
+    counts, eoff, perm, inv = orc.dispatch(ids, wl.num_experts)
+    ref = {"ids": ids, "w": w, "counts": counts, "expert_offsets": eoff, "perm": perm, "inv": inv}
+    tok = _sampled_tokens(wl)
+    say(f"[parity-full] {name}: oracle output rows for {len(tok)} sampled tokens")
+    out_ref, ids_t, _ = orc.token_rows(inp["X"], inp["L"], tok, inp["W13"], inp["W2"], inp.get("Ws13"),
+                                       inp.get("Ws2"), K=wl.top_k, rsf=wl.routed_scaling_factor,
+                                       renorm=wl.renormalize)
+    np.testing.assert_array_equal(ids_t, ids[tok])
+    say(f"[parity-full] {name}: GPU run")
+    with FfnSession(wl, inp) as s:
+        del inp["W13"], inp["W2"]
+        s.step()
+        st = s.status()
+        assert st.status == 0 and st.total_tokens == wl.total_tokens
+        check_routing(s.routing(), ref, wl)
+        out = np.concatenate(s.outputs_f32())
+        err = row_rel_err(out[tok], out_ref)
+        say(f"[parity-full] {name}: max row rel err {err:.3e} over {len(tok)} rows")
+        assert err <= ROW_REL_TOL
+        # properties that hold on every row: finite, and the same scale as the sample
+        assert np.isfinite(out).all()
+        assert 0.25 < np.abs(out).mean() / np.abs(out_ref).mean() < 4.0

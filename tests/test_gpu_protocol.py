@@ -1,0 +1,234 @@
+"""GPU protocol tests: slot contents, flags, and the failure paths, each forced
+from the host (a withheld publish, a corrupted header written with
+afd_debug_write, a repeated flag value).  Every kernel still exits normally:
+waits are bounded by a short poll timeout.
+
+Sources: "[RFC]: Async GPU Connector" ("Window and slot layout": slot fields,
+header self-check, shutdown bit, seq flags; "Capacity and ring depth":
+overflow raises, ring exhaustion is an error; "Risks and alternatives":
+echo_seq turns a mismatched reply into an explicit error) and "Data on the
+wire" (shape checks).
+"""
+import numpy as np
+import pytest
+
+from combine_afd_slot_amd import afd
+from combine_afd_slot_amd.driver import FfnSession
+from combine_afd_slot_amd.inputs import WORKLOADS, make_inputs, small_workload, bf16_to_f32
+from gpu_util import ROW_REL_TOL, row_rel_err, say
+from oracle import protocol as ref
+
+pytestmark = pytest.mark.gpu
+
+TINY = WORKLOADS["tiny"]
+
+
+def _session(wl=TINY, timeout_us=20_000, inp=None):
+    inp = make_inputs(wl) if inp is None else inp
+    return FfnSession(wl, inp, poll_timeout_us=timeout_us), inp
+
+
+def _slot_off(s, win_off, peer, stage):
+    L = s.layout
+    first = L.in_slots_off - L.in_off
+    return win_off + first + (peer * s.wl.ring_depth + stage) * L.slot_bytes
+
+
+def _read_header(s, which, peer, stage=0):
+    L = s.layout
+    base = L.in_off if which == 0 else L.ret_off
+    off = _slot_off(s, base, peer, stage) + L.field_off[0]
+    raw = afd.afd_debug_read(s.win, off, 4 * (12 + s.wl.num_experts))
+    return np.frombuffer(raw, np.int32).copy(), off
+
+
+def _oracle_out(orc, wl, inp):
+    return orc.ffn(inp["x"], inp["l"], inp["W13"], inp["W2"], inp.get("Ws13"), inp.get("Ws2"), K=wl.top_k)
+
+
+def test_pack_writes_slot_fields_and_flag():
+    say("[protocol] pack slot contents")
+    s, inp = _session()
+    with s:
+        s.pack_all(layer=3)
+        L = s.layout
+        E, H = TINY.num_experts, TINY.hidden
+        for p, n in enumerate(TINY.seq_lens):
+            so = _slot_off(s, L.in_off, p, 0)
+            rx = np.frombuffer(afd.afd_debug_read(s.win, so + L.field_off[2], 2 * n * H), np.uint16)
+            sx = np.frombuffer(afd.afd_debug_read(s.win, so + L.field_off[4], 2 * n * H), np.uint16)
+            rt = np.frombuffer(afd.afd_debug_read(s.win, so + L.field_off[1], 4 * n * E), np.float32)
+            si = np.frombuffer(afd.afd_debug_read(s.win, so + L.field_off[3], 4 * n), np.int32)
+            np.testing.assert_array_equal(rx.reshape(n, H), inp["x"][p])
+            np.testing.assert_array_equal(sx.reshape(n, H), inp["x"][p])
+            np.testing.assert_array_equal(rt.reshape(n, E), inp["l"][p])
+            np.testing.assert_array_equal(si, np.arange(n))
+            hw, _ = _read_header(s, 0, p)
+            d = ref.decode_header(hw, E)
+            assert d["seq"] == 1 and d["layer_idx"] == 3 and d["stage_idx"] == 0
+            assert d["num_tokens"] == n and d["shared_tokens"] == n and d["src_peer"] == p
+            assert not d["shutdown"]
+        assert afd.afd_window_poll(s.win, 0, TINY.num_peers) == [1, 1]
+        assert afd.afd_window_poll(s.win, 1, TINY.num_peers) == [0, 0]
+
+
+def test_return_header_and_flags():
+    s, inp = _session()
+    with s:
+        s.step(layer=2)
+        s.pack_all(layer=2)
+        s.run(layer=2)
+        s.ffn_stream.synchronize()
+        assert afd.afd_window_poll(s.win, 1, 2) == [2, 2]
+        for p in range(2):
+            hw, _ = _read_header(s, 1, p)
+            d = ref.decode_header(hw, TINY.num_experts)
+            assert d["echo_seq"] == 2 and d["seq"] == 2 and d["num_tokens"] == TINY.seq_lens[p]
+            assert d["layer_idx"] == 2 and d["src_peer"] == p
+            assert d["counts"].sum() == TINY.seq_lens[p] * TINY.top_k
+        s.unpack_all()
+        assert all(s.peer_status(p).status == 0 for p in range(2))
+
+
+def test_missing_peer_times_out_then_recovers(orc):
+    say("[protocol] timeout (20 ms bound), then recovery")
+    s, inp = _session(timeout_us=20_000)
+    with s:
+        s.pack(0)
+        s.peer_streams[0].synchronize()
+        s.run()
+        st = s.status()
+        assert st.status == afd.AFD_ERR_TIMEOUT and st.failed_peer == 1
+        assert afd.afd_window_poll(s.win, 1, 2) == [0, 0]  # nothing published
+        s.pack(1)
+        s.peer_streams[1].synchronize()
+        s.run()
+        assert s.status().status == 0  # peer 0's message was not consumed by the failed run
+        s.ffn_stream.synchronize()
+        s.unpack_all()
+        r = _oracle_out(orc, TINY, inp)
+        for p, o in enumerate(s.outputs_f32()):
+            assert row_rel_err(o, r["out_p"][p]) <= ROW_REL_TOL
+
+
+def test_stale_flag_is_not_consumed_twice():
+    s, inp = _session(timeout_us=20_000)
+    with s:
+        s.step()
+        # re-announce the old seq: the FFN mirror has already seen it
+        s.run()
+        st = s.status()
+        assert st.status == afd.AFD_ERR_TIMEOUT
+
+
+def test_shutdown_bit():
+    s, inp = _session()
+    with s:
+        s.pack(0, flags=afd.AFD_FLAG_SHUTDOWN)
+        s.pack(1)
+        for q in s.peer_streams:
+            q.synchronize()
+        s.run()
+        st = s.status()
+        assert st.status == afd.AFD_SHUTDOWN
+        assert afd.afd_window_poll(s.win, 1, 2) == [0, 0]
+
+
+@pytest.mark.parametrize("word,value", [(ref.WORD["magic"], 0x0BADF00D), (ref.WORD["version"], 9),
+                                        (ref.WORD["n_counts"], 3), (ref.WORD["layer_idx"], 77),
+                                        (ref.WORD["num_tokens"], 99), (ref.WORD["src_peer"], 0)])
+def test_corrupt_header_rejected_then_fixed(orc, word, value):
+    s, inp = _session()
+    with s:
+        s.pack_all()
+        hw, off = _read_header(s, 0, 1)
+        bad = hw.copy()
+        bad[word] = value
+        afd.afd_debug_write(s.win, off, bad.tobytes())
+        s.run()
+        st = s.status()
+        assert st.status == afd.AFD_ERR_HEADER and st.failed_peer == 1
+        assert afd.afd_window_poll(s.win, 1, 2) == [0, 0]
+        afd.afd_debug_write(s.win, off, hw.tobytes())
+        s.run()
+        assert s.status().status == 0
+        s.ffn_stream.synchronize()
+        s.unpack_all()
+        r = _oracle_out(orc, TINY, inp)
+        for p, o in enumerate(s.outputs_f32()):
+            assert row_rel_err(o, r["out_p"][p]) <= ROW_REL_TOL
+
+
+def test_echo_seq_mismatch_is_an_error():
+    s, inp = _session()
+    with s:
+        s.pack_all()
+        s.run()
+        s.ffn_stream.synchronize()
+        hw, off = _read_header(s, 1, 0)
+        bad = hw.copy()
+        bad[ref.WORD["echo_seq"]] += 5
+        afd.afd_debug_write(s.win, off, bad.tobytes())
+        s.out[0].fill_(7.0)
+        s.torch.cuda.synchronize()
+        s.unpack_all()
+        st = s.peer_status(0)
+        assert st.status == afd.AFD_ERR_SEQ and st.failed_peer == 0
+        assert (s.out[0].float() == 7.0).all().item()  # nothing copied
+        assert s.peer_status(1).status == 0
+
+
+def test_host_errors_capacity_ring_shape():
+    s, inp = _session()
+    with s:
+        with pytest.raises(afd.AfdError) as ei:
+            s.pack(0, seq_len=TINY.token_cap + 1)
+        assert ei.value.code == afd.AFD_ERR_CAPACITY
+        s.pack(0)
+        with pytest.raises(afd.AfdError) as ei:
+            s.pack(0)
+        assert ei.value.code == afd.AFD_ERR_RING
+        with pytest.raises(afd.AfdError) as ei:
+            afd.afd_slot_unpack(s.win, 0, 0, TINY.seq_lens[0] + 1, s.out[0].data_ptr(),
+                                s.peer_streams[0].cuda_stream)
+        assert ei.value.code == afd.AFD_ERR_SHAPE
+        with pytest.raises(afd.AfdError) as ei:
+            afd.afd_slot_pack(s.win, 5, 0, 0, 1, s.x[0].data_ptr(), s.l[0].data_ptr(), 0, 0)
+        assert ei.value.code == afd.AFD_ERR_INVALID
+        s.pack(1)
+        for q in s.peer_streams:
+            q.synchronize()
+        s.run()
+        s.ffn_stream.synchronize()
+        s.unpack_all()
+        assert s.status().status == 0
+
+
+def test_repeated_execution_and_ring_depth_two(orc):
+    wl = small_workload("ring2", seq_lens=(21, 0, 34), hidden=128, num_experts=8, top_k=2, intermediate=64,
+                        shared_intermediate=64, token_cap=40, ring_depth=2)
+    base = make_inputs(wl)
+    with FfnSession(wl, base, poll_timeout_us=200_000) as s:
+        for it in range(4):
+            stage = it % 2
+            wl_i = wl.with_(seed=100 + it)
+            inp = make_inputs(wl_i, with_weights=False)
+            inp.update({k: base[k] for k in ("W13", "W2", "Ws13", "Ws2")})
+            s.set_inputs(inp)
+            say(f"[protocol] repeated run {it} stage {stage}")
+            s.step(stage=stage, layer=it)
+            assert s.status(stage).status == 0
+            r = _oracle_out(orc, wl, inp)
+            for p, o in enumerate(s.outputs_f32()):
+                assert row_rel_err(o, r["out_p"][p]) <= ROW_REL_TOL, (it, p)
+
+
+def test_all_peers_empty():
+    wl = small_workload("empty", seq_lens=(0, 0), hidden=64, num_experts=8, top_k=2, intermediate=32,
+                        shared_intermediate=32, token_cap=8)
+    inp = make_inputs(wl)
+    with FfnSession(wl, inp, poll_timeout_us=200_000) as s:
+        s.step()
+        st = s.status()
+        assert st.status == 0 and st.total_tokens == 0
+        assert afd.afd_window_poll(s.win, 1, 2) == [0, 0]
