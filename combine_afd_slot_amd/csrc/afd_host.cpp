@@ -59,14 +59,24 @@ int32_t validate(const afd_window_config* c) {
     if (c->poll_timeout_us < 1) return fail(AFD_ERR_INVALID, "poll_timeout_us must be >= 1");
     if (!(c->routed_scaling_factor == c->routed_scaling_factor)) return fail(AFD_ERR_INVALID, "rsf is NaN");
     const int64_t tmax = (int64_t)c->num_peers * c->token_cap;
-    if (tmax * c->top_k > (int64_t)1 << 30) return fail(AFD_ERR_INVALID, "num_peers*token_cap*top_k too large");
+    if (tmax * c->top_k > (int64_t)1 << 28) return fail(AFD_ERR_INVALID, "num_peers*token_cap*top_k too large");
+    // the GEMM kernels address rows with 32-bit byte offsets from a base
+    const int64_t lim = (int64_t)1 << 32;
+    int64_t fb[AFD_NUM_FIELDS], slot = 0;
+    afd::slot_field_bytes(c->token_cap, c->hidden, c->num_experts, fb);
+    for (int i = 0; i < AFD_NUM_FIELDS; ++i) slot += afd::align_up(fb[i]);
+    const int64_t window = afd::align_up(4LL * c->num_peers * c->ring_depth) + slot * c->num_peers * c->ring_depth;
+    if (window >= lim || 2 * tmax * c->top_k * c->intermediate >= lim || 2 * tmax * c->shared_intermediate >= lim ||
+        4LL * c->intermediate * c->hidden >= lim || 4LL * c->shared_intermediate * c->hidden >= lim)
+        return fail(AFD_ERR_INVALID, "window, activation buffers and per-expert weights must each stay below 4 GiB");
     return AFD_OK;
 }
 
 // Workspace carve-up, in bytes from the workspace start.
 struct WsLayout {
     int64_t ctrl, peer_counts, blk_counts, blk_base, counts, eoff, grp_M, grp_row0, tstart1, tstart2;
-    int64_t ids, wts, perm, inv, tok_src, sh_src, sh_dst, h, hs, y, ys, bytes;
+    int64_t tinfo1, tinfo2, seg1, seg2, psrc, max_tiles1, max_tiles2;
+    int64_t ids, wts, perm, inv, tok_src, sh_src, h, hs, y, ys, zero, bytes;
     int64_t ctrl_ints;
     // control-word offsets inside ctrl (in ints)
     int64_t c_seen_in, c_ret_seq, c_seen_ret, c_cur_seq, c_off, c_T, c_done, c_run_status, c_peer_status;
@@ -76,7 +86,7 @@ WsLayout ws_layout(const afd_window_config& c) {
     WsLayout w{};
     const int64_t P = c.num_peers, R = c.ring_depth, E = c.num_experts, K = c.top_k;
     const int64_t tmax = P * c.token_cap, np = tmax * K;
-    const int64_t nb = (tmax + afd::kRouteChunk - 1) / afd::kRouteChunk;
+    const int64_t nb = (tmax + afd::kRouteChunk - 1) / afd::kRouteChunk + P;
     const int64_t G = E + (c.shared_intermediate > 0 ? 1 : 0);
     int64_t ci = 0;
     w.c_seen_in = ci; ci += P * R;
@@ -105,17 +115,33 @@ WsLayout ws_layout(const afd_window_config& c) {
     w.grp_row0 = take(4 * G);
     w.tstart1 = take(4 * (G + 1));
     w.tstart2 = take(4 * (G + 1));
+    {
+        // upper bounds of the tile counts: sum over groups of ceil(M/BM) <=
+        // (rows + groups*(BM-1)) / BM
+        const int64_t mt_r = (np + E * (afd::kBM - 1)) / afd::kBM;
+        const int64_t mt_s = c.shared_intermediate > 0 ? (tmax + afd::kBM - 1) / afd::kBM : 0;
+        const int64_t nt1_r = (c.intermediate + afd::kBN / 2 - 1) / (afd::kBN / 2);
+        const int64_t nt1_s = (c.shared_intermediate + afd::kBN / 2 - 1) / (afd::kBN / 2);
+        const int64_t nt2 = (c.hidden + afd::kBN - 1) / afd::kBN;
+        w.max_tiles1 = mt_r * nt1_r + mt_s * nt1_s;
+        w.max_tiles2 = (mt_r + mt_s) * nt2;
+    }
+    w.tinfo1 = take(8 * w.max_tiles1);
+    w.tinfo2 = take(8 * w.max_tiles2);
+    w.seg1 = take(4 * (afd::kXcds + 1));
+    w.seg2 = take(4 * (afd::kXcds + 1));
+    w.psrc = take(8 * np);
     w.ids = take(4 * np);
     w.wts = take(4 * np);
     w.perm = take(4 * np);
     w.inv = take(4 * np);
     w.tok_src = take(8 * tmax);
     w.sh_src = take(8 * tmax);
-    w.sh_dst = take(4 * tmax);
     w.h = take(2 * np * c.intermediate);
     w.hs = take(2 * tmax * (c.shared_intermediate > 0 ? c.shared_intermediate : 1));
     w.y = take(2 * np * c.hidden);
     w.ys = take(4 * tmax * c.hidden);
+    w.zero = take(256);
     w.bytes = cur;
     return w;
 }
@@ -186,18 +212,9 @@ void fill_ctx(afd_window* w) {
     d.has_shared = c.shared_intermediate > 0 ? 1 : 0;
     d.G = c.num_experts + d.has_shared;
     const int64_t tmax = (int64_t)c.num_peers * c.token_cap;
-    d.NB = (int)((tmax + afd::kRouteChunk - 1) / afd::kRouteChunk);
-    {
-        // sum over groups of ceil(M_g / BM) <= (pairs + E*(BM-1)) / BM, plus the shared group
-        const int64_t pairs = tmax * c.top_k;
-        const int64_t mt_r = (pairs + (int64_t)c.num_experts * (afd::kBM - 1)) / afd::kBM;
-        const int64_t mt_s = d.has_shared ? (tmax + afd::kBM - 1) / afd::kBM : 0;
-        const int64_t nt1_r = (c.intermediate + afd::kBN / 2 - 1) / (afd::kBN / 2);
-        const int64_t nt1_s = (c.shared_intermediate + afd::kBN / 2 - 1) / (afd::kBN / 2);
-        const int64_t nt2 = (c.hidden + afd::kBN - 1) / afd::kBN;
-        d.max_tiles1 = (int)(mt_r * nt1_r + mt_s * nt1_s);
-        d.max_tiles2 = (int)((mt_r + mt_s) * nt2);
-    }
+    d.NB = (int)((tmax + afd::kRouteChunk - 1) / afd::kRouteChunk) + c.num_peers;  // peer-aligned chunks
+    d.max_tiles1 = (int)L.max_tiles1;
+    d.max_tiles2 = (int)L.max_tiles2;
     d.slot_bytes = w->lay.slot_bytes;
     for (int i = 0; i < AFD_NUM_FIELDS; ++i) d.foff[i] = w->lay.field_off[i];
     d.in_win = w->base + w->lay.in_off;
@@ -211,7 +228,6 @@ void fill_ctx(afd_window* w) {
     d.cur_seq = ctrl + L.c_cur_seq;
     d.off = ctrl + L.c_off;
     d.Tptr = ctrl + L.c_T;
-    d.done_ctr = ctrl + L.c_done;
     d.run_status = ctrl + L.c_run_status;
     d.peer_status = ctrl + L.c_peer_status;
     d.peer_counts = (int*)(ws + L.peer_counts);
@@ -223,17 +239,22 @@ void fill_ctx(afd_window* w) {
     d.grp_row0 = (int*)(ws + L.grp_row0);
     d.tstart1 = (int*)(ws + L.tstart1);
     d.tstart2 = (int*)(ws + L.tstart2);
+    d.tinfo1 = (int2*)(ws + L.tinfo1);
+    d.tinfo2 = (int2*)(ws + L.tinfo2);
+    d.seg1 = (int*)(ws + L.seg1);
+    d.seg2 = (int*)(ws + L.seg2);
+    d.psrc = (uint64_t*)(ws + L.psrc);
     d.ids = (int*)(ws + L.ids);
     d.wts = (float*)(ws + L.wts);
     d.perm = (int*)(ws + L.perm);
     d.inv = (int*)(ws + L.inv);
     d.tok_src = (uint64_t*)(ws + L.tok_src);
     d.sh_src = (uint64_t*)(ws + L.sh_src);
-    d.sh_dst = (int*)(ws + L.sh_dst);
     d.h = (uint16_t*)(ws + L.h);
     d.hs = (uint16_t*)(ws + L.hs);
     d.y = (uint16_t*)(ws + L.y);
     d.ys = (float*)(ws + L.ys);
+    d.zero16 = (const uint16_t*)(ws + L.zero);
 }
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
@@ -326,6 +347,7 @@ int32_t afd_window_create(const afd_window_config* cfg, afd_window** out) {
     e = hipMemset(w->base + L.in_off, 0, (size_t)(L.in_slots_off - L.in_off));
     if (e == hipSuccess) e = hipMemset(w->base + L.ret_off, 0, (size_t)(L.ret_slots_off - L.ret_off));
     if (e == hipSuccess) e = hipMemset(w->base + L.workspace_off + w->wl.ctrl, 0, (size_t)(4 * w->wl.ctrl_ints));
+    if (e == hipSuccess) e = hipMemset(w->base + L.workspace_off + w->wl.zero, 0, 256);
     if (e == hipSuccess) e = hipDeviceSynchronize();
     if (e != hipSuccess) {
         (void)hipFree(w->base);

@@ -12,16 +12,25 @@ namespace afd {
 // Tokens handled by one routing / permutation workgroup.  The per-block
 // expert histograms of the routing kernel and the stable ranks of the
 // permutation kernel are both taken over these chunks, in token order.
-constexpr int kRouteChunk = 64;
+constexpr int kRouteChunk = 16;
 constexpr int kMaxTopK = 16;
 constexpr int kMaxPeers = 64;
 constexpr int kMaxExperts = 1024;
 
-// Grouped-GEMM macro tile (rows x columns x depth).  For the gate/up GEMM
-// the BN columns are BN/2 gate columns and the same BN/2 up columns.
-constexpr int kBM = 128;
+// Grouped-GEMM tile: kBM token rows (blocks of 32) of one group x kBN weight
+// rows, kBK deep per step, computed by kGemmThreads threads (16 waves: 4 per
+// SIMD, so that enough loads are in flight to feed the matrix cores).  A
+// group of at most kBM rows is one row tile, so each weight row is streamed
+// once per group.  For the gate/up GEMM the kBN weight rows are kBN/2 gate
+// rows and the same kBN/2 up rows.  kStages LDS buffers form a ring filled
+// kStages-1 steps ahead; a 64-deep step reads each operand row's 128 bytes,
+// one full L2 line.
+constexpr int kBM = 512;
 constexpr int kBN = 128;
 constexpr int kBK = 64;
+constexpr int kStages = 2;
+constexpr int kGemmThreads = 1024;
+constexpr int kXcds = 8;
 
 // Per-stage run status words: [status, failed_peer, seq of peer 0, T].
 constexpr int kStatusWords = 4;
@@ -48,31 +57,35 @@ struct DevCtx {
     int* cur_seq;      // [P]   inbound seq consumed by the current run
     int* off;          // [P+1] fan-in offsets
     int* Tptr;         // [1]   total tokens of the current run
-    int* done_ctr;     // [1]   combine completion counter
     int* run_status;   // [R][kStatusWords]
     int* peer_status;  // [P*R][kStatusWords]
     // routing / dispatch
     int* peer_counts;  // [P][E]
-    int* blk_counts;   // [NB][E]
-    int* blk_base;     // [NB][E]
+    int* blk_counts;   // [E][NB] per-chunk expert histograms
+    int* blk_base;     // [E][NB] stable base of each chunk inside its expert group
     int* counts;       // [E]
     int* eoff;         // [E+1]
     int* grp_M;        // [G]
     int* grp_row0;     // [G]
-    int* tstart1;      // [G+1] gate/up GEMM tile prefix
-    int* tstart2;      // [G+1] down GEMM tile prefix
+    int* tstart1;      // [G+1] gate/up GEMM tile prefix per group
+    int* tstart2;      // [G+1] down GEMM tile prefix per group
+    int2* tinfo1;      // [max_tiles1] (group, mt << 16 | nt) of each gate/up tile
+    int2* tinfo2;      // [max_tiles2]
+    int* seg1;         // [kXcds+1] cost-balanced tile segments of the gate/up GEMM
+    int* seg2;         // [kXcds+1]
+    uint64_t* psrc;    // [Tmax*K] address of the token row of each permuted pair
     int* ids;          // [Tmax*K]
     float* wts;        // [Tmax*K]
     int* perm;         // [Tmax*K]
     int* inv;          // [Tmax*K]
     uint64_t* tok_src; // [Tmax] address of token t's routed_x row
     uint64_t* sh_src;  // [Tmax] address of shared row t's shared_x row
-    int* sh_dst;       // [Tmax] fan-in token index of shared row t
     // expert activations
     uint16_t* h;       // [Tmax*K][I]  bf16 SwiGLU activations, permuted order
     uint16_t* hs;      // [Tmax][Is]   bf16 shared activations
     uint16_t* y;       // [Tmax*K][H]  bf16 routed expert outputs, permuted order
-    float* ys;         // [Tmax][H]    fp32 shared expert output, token order
+    float* ys;         // [Tmax][H]    fp32 shared expert output, token (= shared row) order
+    const uint16_t* zero16;  // 256 zero bytes: source of the K-tail chunks
 };
 
 struct Weights {
