@@ -86,6 +86,8 @@ def main():
     ap.add_argument("--workload", default="prefill")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-profile", action="store_true", help="no per-kernel events (pure step timing)")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="run only a plain 1 GiB device-to-device copy, 10 times (scale for HBM byte counters)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -94,6 +96,17 @@ def main():
         sys.exit(2)
 
     import torch
+    if args.calibrate_copy:
+        n = 1 << 30
+        src = torch.empty(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        src.fill_(1)
+        torch.cuda.synchronize()
+        for _ in range(10):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes_read": n, "calibrate_copy_bytes_written": n, "launches": 10}))
+        return
     from combine_afd_slot_amd import afd
     from combine_afd_slot_amd.driver import FfnSession
     from combine_afd_slot_amd.inputs import WORKLOADS, make_inputs
@@ -115,7 +128,9 @@ def main():
     log(f"[bench] warmup done ({args.warmup} steps); expert counts min/max {counts.min()}/{counts.max()}")
 
     if not args.no_profile:
-        afd.afd_profile_enable(sess.win, True)
+        # timed steps: events only around the two GEMM kernels, so the other
+        # kernels run back to back exactly as without profiling
+        afd.afd_profile_enable(sess.win, 2)
         afd.afd_profile_read(sess.win, reset=True)
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
@@ -135,11 +150,18 @@ def main():
     st = sess.status()
     if st.status != 0:
         raise RuntimeError(f"timed run failed: {afd.status_string(st.status)}")
-    kern = {}
+    kern, kern_all = {}, {}
     if not args.no_profile:
         tot, runs = afd.afd_profile_read(sess.win, reset=True)
-        afd.afd_profile_enable(sess.win, False)
-        kern = {k: v / max(runs, 1) for k, v in tot.items()}
+        kern = {k: v / max(runs, 1) for k, v in tot.items() if k.startswith("gemm")}
+        # an untimed pass with an event between every two kernels, for the
+        # per-kernel breakdown (the events add small gaps between launches)
+        afd.afd_profile_enable(sess.win, 1)
+        for i in range(min(args.steps, 10)):
+            sess.step()
+        tot, runs = afd.afd_profile_read(sess.win, reset=True)
+        afd.afd_profile_enable(sess.win, 0)
+        kern_all = {k: round(v / max(runs, 1), 4) for k, v in tot.items()}
     sess.close()
 
     ms = float(np.mean(step_ms))
@@ -171,6 +193,7 @@ def main():
     }
     if kern:
         line["kernel_ms"] = {k: round(v, 4) for k, v in kern.items()}
+        line["kernel_ms_all_separate_pass"] = kern_all
         dom = max(("gemm_gate_up_swiglu", "gemm_down"), key=lambda k: kern[k])
         # decode-shaped steps stream weights: bound by HBM; prefill steps by MFMA
         ai = alg[dom]["flops"] / alg[dom]["bytes"]

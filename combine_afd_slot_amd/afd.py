@@ -231,8 +231,9 @@ def afd_debug_write(win, offset, data: bytes) -> None:
     _check(lib().afd_debug_write(win, offset, len(data), buf))
 
 
-def afd_profile_enable(win, on=True) -> None:
-    _check(lib().afd_profile_enable(win, 1 if on else 0))
+def afd_profile_enable(win, mode=1) -> None:
+    """mode 0 off, 1 every kernel, 2 the two GEMM kernels only."""
+    _check(lib().afd_profile_enable(win, int(mode)))
 
 
 def afd_profile_read(win, reset=True):

@@ -36,6 +36,7 @@ const char* kProfileNames[AFD_PROFILE_SLOTS] = {"wait_fanin", "route_topk", "sca
                                                 "gemm_gate_up_swiglu", "gemm_down", "combine_split_publish",
                                                 "unused"};
 constexpr int kProfileUsed = 7;
+constexpr int kGemmFirst = 4;  // slots 4 and 5: the two GEMMs
 
 int32_t validate(const afd_window_config* c) {
     if (!c) return fail(AFD_ERR_INVALID, "config is NULL");
@@ -75,7 +76,7 @@ int32_t validate(const afd_window_config* c) {
 // Workspace carve-up, in bytes from the workspace start.
 struct WsLayout {
     int64_t ctrl, peer_counts, blk_counts, blk_base, counts, eoff, grp_M, grp_row0, tstart1, tstart2;
-    int64_t tinfo1, tinfo2, seg1, seg2, psrc, max_tiles1, max_tiles2;
+    int64_t tinfo1, tinfo2, seg1, seg2, tctr, psrc, max_tiles1, max_tiles2;
     int64_t ids, wts, perm, inv, tok_src, sh_src, h, hs, y, ys, zero, bytes;
     int64_t ctrl_ints;
     // control-word offsets inside ctrl (in ints)
@@ -130,6 +131,7 @@ WsLayout ws_layout(const afd_window_config& c) {
     w.tinfo2 = take(8 * w.max_tiles2);
     w.seg1 = take(4 * (afd::kXcds + 1));
     w.seg2 = take(4 * (afd::kXcds + 1));
+    w.tctr = take(4 * 2 * afd::kXcds);
     w.psrc = take(8 * np);
     w.ids = take(4 * np);
     w.wts = take(4 * np);
@@ -185,7 +187,7 @@ struct afd_window {
     std::vector<int32_t> pack_seq;    // [P*R] last seq sent by the peer (host side of the peer)
     std::vector<int32_t> packed_len;  // [P*R]
     std::vector<uint8_t> inflight;    // [P*R]
-    bool profile = false;
+    int profile = 0;  // 0 off, 1 every kernel, 2 the two GEMMs only
     hipEvent_t ev[AFD_PROFILE_SLOTS + 1] = {};
     bool ev_pending = false;
     double prof_ms[AFD_PROFILE_SLOTS] = {};
@@ -243,6 +245,7 @@ void fill_ctx(afd_window* w) {
     d.tinfo2 = (int2*)(ws + L.tinfo2);
     d.seg1 = (int*)(ws + L.seg1);
     d.seg2 = (int*)(ws + L.seg2);
+    d.tctr = (int*)(ws + L.tctr);
     d.psrc = (uint64_t*)(ws + L.psrc);
     d.ids = (int*)(ws + L.ids);
     d.wts = (float*)(ws + L.wts);
@@ -262,8 +265,9 @@ bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 // Fold the previous run's events into the accumulated times.
 void prof_collect(afd_window* w) {
     if (!w->ev_pending) return;
-    for (int i = 0; i <= kProfileUsed; ++i) (void)hipEventSynchronize(w->ev[i]);
-    for (int i = 0; i < kProfileUsed; ++i) {
+    const int lo = w->profile == 1 ? 0 : kGemmFirst, hi = w->profile == 1 ? kProfileUsed : kGemmFirst + 2;
+    for (int i = lo; i <= hi; ++i) (void)hipEventSynchronize(w->ev[i]);
+    for (int i = lo; i < hi; ++i) {
         float ms = 0.f;
         if (hipEventElapsedTime(&ms, w->ev[i], w->ev[i + 1]) == hipSuccess) w->prof_ms[i] += ms;
     }
@@ -429,11 +433,14 @@ int32_t afd_ffn_run(afd_window* w, int32_t stage, int32_t layer_idx, const afd_m
         return fail(AFD_ERR_INVALID, "weights must be 16-byte aligned");
     afd::Weights wt{(const uint16_t*)weights->w13, (const uint16_t*)weights->w2, (const uint16_t*)weights->ws13,
                     (const uint16_t*)weights->ws2};
+    hipEvent_t evs[AFD_PROFILE_SLOTS + 1] = {};
     hipEvent_t* ev = nullptr;
     if (w->profile) {
         std::lock_guard<std::mutex> g(w->prof_mu);
         prof_collect(w);
-        ev = w->ev;
+        for (int i = 0; i <= kProfileUsed; ++i)
+            if (w->profile == 1 || (i >= kGemmFirst && i <= kGemmFirst + 2)) evs[i] = w->ev[i];
+        ev = evs;
         w->ev_pending = true;
     }
     const long long timeout = (long long)c.poll_timeout_us * w->ticks_per_us;
@@ -545,9 +552,10 @@ int32_t afd_debug_write(afd_window* w, int64_t offset, int64_t bytes, const void
 
 int32_t afd_profile_enable(afd_window* w, int32_t on) {
     if (!w) return fail(AFD_ERR_INVALID, "window is NULL");
+    if (on < 0 || on > 2) return fail(AFD_ERR_INVALID, "profile mode must be 0, 1 or 2");
     std::lock_guard<std::mutex> g(w->prof_mu);
-    if (!on) prof_collect(w);
-    w->profile = on != 0;
+    prof_collect(w);
+    w->profile = on;
     return AFD_OK;
 }
 

@@ -73,6 +73,7 @@ struct DevCtx {
     int2* tinfo2;      // [max_tiles2]
     int* seg1;         // [kXcds+1] cost-balanced tile segments of the gate/up GEMM
     int* seg2;         // [kXcds+1]
+    int* tctr;         // [2][kXcds] tiles taken from each segment (zeroed by the planner)
     uint64_t* psrc;    // [Tmax*K] address of the token row of each permuted pair
     int* ids;          // [Tmax*K]
     float* wts;        // [Tmax*K]

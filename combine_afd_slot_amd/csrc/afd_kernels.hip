@@ -466,6 +466,7 @@ __device__ inline PlanGroup plan_group(const DevCtx& c, int T, const int* s_eoff
 }
 
 __device__ void plan_tiles(const DevCtx& c, int T, const int* s_eoff, int* sh) {
+    if (threadIdx.x < 2 * kXcds) c.tctr[threadIdx.x] = 0;
     __shared__ int s_t[2][kMaxExperts + 2];
     __shared__ long long s_c[2][kMaxExperts + 2];
     const int tid = threadIdx.x, G = c.G;
@@ -506,17 +507,16 @@ __device__ void plan_tiles(const DevCtx& c, int T, const int* s_eoff, int* sh) {
         const int maxt = mode == 1 ? c.max_tiles1 : c.max_tiles2;
         for (int j = tid; j <= G; j += 256) tstart[j] = s_t[mode - 1][j];
         const int total = s_t[mode - 1][G];
-        for (int t = tid; t < total && t < maxt; t += 256) {
-            int lo = 0, hi = G;
-            while (hi - lo > 1) {
-                const int mid = (lo + hi) >> 1;
-                if (s_t[mode - 1][mid] <= t) lo = mid;
-                else hi = mid;
+        // each group's tiles, column tile outer, row tile inner; the threads
+        // of a wave split one group's tiles between them
+        const int lane = tid & 63, wave = tid >> 6;
+        for (int j = wave; j < G; j += 4) {
+            const PlanGroup g = plan_group(c, T, s_eoff, j, mode);
+            const int n = g.mt * g.nt, t0 = s_t[mode - 1][j];
+            for (int i = lane; i < n; i += 64) {
+                const int nt = i / g.mt, mt = i - nt * g.mt;
+                if (t0 + i < maxt) tinfo[t0 + i] = make_int2(j, (mt << 16) | nt);
             }
-            const PlanGroup g = plan_group(c, T, s_eoff, lo, mode);
-            const int local = t - s_t[mode - 1][lo];
-            const int nt = local / g.mt, mt = local - nt * g.mt;
-            tinfo[t] = make_int2(lo, (mt << 16) | nt);
         }
         // segment x starts at the first tile whose cost prefix is >= x*C/kXcds
         int* seg = mode == 1 ? c.seg1 : c.seg2;
@@ -589,8 +589,10 @@ __global__ __launch_bounds__(256) void k_permute(DevCtx c, const int* status) {
         plan_tiles(c, T, s_eoff, sh);
         if (!have) return;
     }
+    __shared__ uint64_t ltok[kRouteChunk];
     const int np = (t1 - t0) * K;
     for (int i = tid; i < np; i += 256) lids[i] = c.ids[(int64_t)t0 * K + i];
+    if (tid < t1 - t0) ltok[tid] = c.tok_src[t0 + tid];
     __syncthreads();
     const int npairs = T * K;
     for (int e = tid; e < E; e += 256) {
@@ -600,7 +602,7 @@ __global__ __launch_bounds__(256) void k_permute(DevCtx c, const int* status) {
                 const int f = t0 * K + i;
                 if (pos < npairs) {
                     c.perm[pos] = f;
-                    c.psrc[pos] = c.tok_src[t0 + i / K];
+                    c.psrc[pos] = ltok[i / K];
                 }
                 c.inv[f] = pos;
                 ++pos;
@@ -700,14 +702,32 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(DevCtx c, const int* s
     const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wid >> 1, wn = wid & 1;
 
-    int seg_hi = total, step = gridDim.x, first = blockIdx.x;
-    if ((gridDim.x % kXcds) == 0) {
-        const int x = blockIdx.x % kXcds;
-        const int seg_lo = min(max(seg[x], 0), total);
-        seg_hi = min(max(seg[x + 1], seg_lo), total);
-        step = gridDim.x / kXcds;
-        first = seg_lo + blockIdx.x / kXcds;
+    // Tiles are taken dynamically: workgroup b starts on the segment of its
+    // XCD (b % kXcds) and, when that is drained, continues with the next
+    // segments.  Thread 0 owns the grabbing; each grab is issued a whole tile
+    // before it is needed and the index is broadcast through LDS at the tile
+    // boundary.
+    int* ctr = c.tctr + (MODE - 1) * kXcds;
+    int xi = (int)(blockIdx.x % kXcds), tries = 0, pend = 0;
+    auto grab_slow = [&]() -> int {  // thread 0 only: next tile, or -1 when all are taken
+        while (tries < kXcds) {
+            const int lo = min(max(seg[xi], 0), total), hi = min(max(seg[xi + 1], lo), total);
+            const int t = lo + atomicAdd(&ctr[xi], 1);
+            if (t < hi) return t;
+            xi = (xi + 1) % kXcds;
+            ++tries;
+        }
+        return -1;
+    };
+    int* bcast = (int*)smem;  // free at tile boundaries
+    if (tid == 0) {
+        const int t = grab_slow();
+        bcast[0] = t;
+        if (t >= 0) pend = atomicAdd(&ctr[xi], 1);  // the following tile, resolved a tile later
     }
+    __syncthreads();
+    int tile = bcast[0];
+    __syncthreads();
 
     const int lrow = lane >> 3;   // row inside a load instruction
     const int pc = lane & 7;      // LDS chunk of this lane
@@ -721,7 +741,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(DevCtx c, const int* s
         wrl[nb] = MODE == 1 ? nb * (kBN / 2) + wn * 32 + (lane & 31) : (wn * 2 + nb) * 32 + (lane & 31);
     const bool has_b = wid < kBTotal;  // every wave loads one weight-row instruction
 
-    for (int tile = first; tile < seg_hi; tile += step) {
+    while (tile >= 0) {
         const int2 ti = tinfo[tile];
         const int j = ti.x, mt = ti.y >> 16, nt = ti.y & 0xffff;
         const bool sh = c.has_shared && j == 0;
@@ -914,6 +934,24 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(DevCtx c, const int* s
                 }
             }
         }
+        // next tile: resolve the grab issued a tile ago, broadcast it
+        AFD_WAIT_VMCNT(0);
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+        __builtin_amdgcn_s_barrier();        // every wave is done with the LDS ring
+        if (tid == 0) {
+            const int lo = min(max(seg[xi], 0), total), hi = min(max(seg[xi + 1], lo), total);
+            int t = lo + pend;
+            if (t >= hi) {
+                xi = (xi + 1) % kXcds;
+                ++tries;
+                t = grab_slow();
+            }
+            bcast[0] = t;
+            if (t >= 0) pend = atomicAdd(&ctr[xi], 1);
+        }
+        __syncthreads();
+        tile = bcast[0];
+        __syncthreads();
     }
 }
 
@@ -969,7 +1007,7 @@ __global__ __launch_bounds__(256) void k_combine(DevCtx c, const int* status, in
 #pragma unroll
             for (int i = 0; i < 4; ++i)
                 out[i] = f2bf(c.rsf * acc[2 * i] + sv[2 * i]) | (f2bf(c.rsf * acc[2 * i + 1] + sv[2 * i + 1]) << 16);
-            dst[ch] = out;
+            __builtin_nontemporal_store(out, &dst[ch]);
         }
     }
 }
@@ -1010,9 +1048,12 @@ hipError_t launch_ffn(const DevCtx& c, int stage, int layer, const Weights& w, l
                       hipEvent_t* ev, hipStream_t st) {
     int* status = c.run_status + stage * kStatusWords;
     const int Tmax = c.P * c.token_cap;
+    // ev == nullptr: no events; otherwise ev[i] is recorded before kernel
+    // slot i (and ev[7] after the last) unless it is null (only the slots
+    // the caller asked for carry events)
     int slot = 0;
     auto mark = [&]() {
-        if (ev) (void)hipEventRecord(ev[slot], st);
+        if (ev && ev[slot]) (void)hipEventRecord(ev[slot], st);
         ++slot;
     };
     mark();

@@ -252,12 +252,15 @@ int32_t afd_debug_read(afd_window* w, int64_t offset, int64_t bytes, void* host_
 int32_t afd_debug_write(afd_window* w, int64_t offset, int64_t bytes, const void* host_src);
 
 /* Per-kernel timing of afd_ffn_run with HIP events recorded on ffn_stream
- * between its launches.  afd_profile_read returns the accumulated
- * milliseconds per kernel slot and the number of runs accumulated, then
- * (reset != 0) clears them; it synchronizes the pending events.  Kernel
- * slot names: afd_profile_kernel_name(i), i < AFD_PROFILE_SLOTS. */
+ * between its launches.  mode: 0 off, 1 an event between every two kernels,
+ * 2 events only around the two GEMM kernels (slots 4 and 5; the other
+ * kernels then run back to back as without profiling).  afd_profile_read
+ * returns the accumulated milliseconds per kernel slot and the number of
+ * runs accumulated, then (reset != 0) clears them; it synchronizes the
+ * pending events.  Kernel slot names: afd_profile_kernel_name(i),
+ * i < AFD_PROFILE_SLOTS. */
 #define AFD_PROFILE_SLOTS 8
-int32_t afd_profile_enable(afd_window* w, int32_t on);
+int32_t afd_profile_enable(afd_window* w, int32_t mode);
 int32_t afd_profile_read(afd_window* w, float* ms, int32_t n, int32_t* runs, int32_t reset);
 const char* afd_profile_kernel_name(int32_t i);
 
