@@ -77,7 +77,7 @@ int32_t validate(const afd_window_config* c) {
 struct WsLayout {
     int64_t ctrl, peer_counts, blk_counts, blk_base, counts, eoff, grp_M, grp_row0, tstart1, tstart2;
     int64_t tinfo1, tinfo2, seg1, seg2, tctr, psrc, max_tiles1, max_tiles2;
-    int64_t ids, wts, perm, inv, tok_src, sh_src, h, hs, y, ys, zero, bytes;
+    int64_t ids, wts, perm, inv, tok_src, sh_src, h, hs, y, ys, sink, bytes;
     int64_t ctrl_ints;
     // control-word offsets inside ctrl (in ints)
     int64_t c_seen_in, c_ret_seq, c_seen_ret, c_cur_seq, c_off, c_T, c_done, c_run_status, c_peer_status;
@@ -117,13 +117,14 @@ WsLayout ws_layout(const afd_window_config& c) {
     w.tstart1 = take(4 * (G + 1));
     w.tstart2 = take(4 * (G + 1));
     {
-        // upper bounds of the tile counts: sum over groups of ceil(M/BM) <=
-        // (rows + groups*(BM-1)) / BM
-        const int64_t mt_r = (np + E * (afd::kBM - 1)) / afd::kBM;
-        const int64_t mt_s = c.shared_intermediate > 0 ? (tmax + afd::kBM - 1) / afd::kBM : 0;
-        const int64_t nt1_r = (c.intermediate + afd::kBN / 2 - 1) / (afd::kBN / 2);
-        const int64_t nt1_s = (c.shared_intermediate + afd::kBN / 2 - 1) / (afd::kBN / 2);
-        const int64_t nt2 = (c.hidden + afd::kBN - 1) / afd::kBN;
+        // upper bounds of the tile counts: a group of M rows has
+        // ceil(ceil(M/32) / kTileBlocks) <= (M + kBX - 1) / kBX row tiles, so
+        // the sum over groups is <= (rows + groups*(kBX-1)) / kBX
+        const int64_t mt_r = (np + E * (afd::kBX - 1)) / afd::kBX;
+        const int64_t mt_s = c.shared_intermediate > 0 ? (tmax + afd::kBX - 1) / afd::kBX : 0;
+        const int64_t nt1_r = (c.intermediate + afd::kBW / 2 - 1) / (afd::kBW / 2);
+        const int64_t nt1_s = (c.shared_intermediate + afd::kBW / 2 - 1) / (afd::kBW / 2);
+        const int64_t nt2 = (c.hidden + afd::kBW - 1) / afd::kBW;
         w.max_tiles1 = mt_r * nt1_r + mt_s * nt1_s;
         w.max_tiles2 = (mt_r + mt_s) * nt2;
     }
@@ -143,7 +144,7 @@ WsLayout ws_layout(const afd_window_config& c) {
     w.hs = take(2 * tmax * (c.shared_intermediate > 0 ? c.shared_intermediate : 1));
     w.y = take(2 * np * c.hidden);
     w.ys = take(4 * tmax * c.hidden);
-    w.zero = take(256);
+    w.sink = take(afd::kSinkBytes);
     w.bytes = cur;
     return w;
 }
@@ -257,7 +258,7 @@ void fill_ctx(afd_window* w) {
     d.hs = (uint16_t*)(ws + L.hs);
     d.y = (uint16_t*)(ws + L.y);
     d.ys = (float*)(ws + L.ys);
-    d.zero16 = (const uint16_t*)(ws + L.zero);
+    d.sink = ws + L.sink;
 }
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
@@ -351,7 +352,6 @@ int32_t afd_window_create(const afd_window_config* cfg, afd_window** out) {
     e = hipMemset(w->base + L.in_off, 0, (size_t)(L.in_slots_off - L.in_off));
     if (e == hipSuccess) e = hipMemset(w->base + L.ret_off, 0, (size_t)(L.ret_slots_off - L.ret_off));
     if (e == hipSuccess) e = hipMemset(w->base + L.workspace_off + w->wl.ctrl, 0, (size_t)(4 * w->wl.ctrl_ints));
-    if (e == hipSuccess) e = hipMemset(w->base + L.workspace_off + w->wl.zero, 0, 256);
     if (e == hipSuccess) e = hipDeviceSynchronize();
     if (e != hipSuccess) {
         (void)hipFree(w->base);

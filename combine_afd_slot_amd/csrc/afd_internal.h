@@ -17,20 +17,26 @@ constexpr int kMaxTopK = 16;
 constexpr int kMaxPeers = 64;
 constexpr int kMaxExperts = 1024;
 
-// Grouped-GEMM tile: kBM token rows (blocks of 32) of one group x kBN weight
-// rows, kBK deep per step, computed by kGemmThreads threads (16 waves: 4 per
-// SIMD, so that enough loads are in flight to feed the matrix cores).  A
-// group of at most kBM rows is one row tile, so each weight row is streamed
-// once per group.  For the gate/up GEMM the kBN weight rows are kBN/2 gate
-// rows and the same kBN/2 up rows.  kStages LDS buffers form a ring filled
-// kStages-1 steps ahead; a 64-deep step reads each operand row's 128 bytes,
-// one full L2 line.
-constexpr int kBM = 512;
-constexpr int kBN = 128;
-constexpr int kBK = 64;
-constexpr int kStages = 2;
-constexpr int kGemmThreads = 1024;
+// Grouped-GEMM tile: up to kBX token rows (8 blocks of 32) of one group x kBW
+// weight rows, kBK deep per step, computed by kGemmThreads threads: 4 waves,
+// one per SIMD, each owning a 128 x 128 block of the tile (4 x 4 MFMA
+// outputs of 32 x 32), which keeps the LDS fragment traffic at half a KB per
+// MFMA.  A group's 32-row blocks are split evenly over ceil(blocks/8) row
+// tiles.  For the gate/up GEMM the kBW weight rows are kBW/2 gate rows and
+// the same kBW/2 up rows.  kStages LDS stages of 32 KB form a ring whose
+// loads run kStages-1 steps ahead of the MFMAs.
+constexpr int kBX = 256;
+constexpr int kBW = 256;
+constexpr int kBK = 32;
+constexpr int kStages = 4;
+constexpr int kGemmThreads = 256;
+constexpr int kTileBlocks = kBX / 32;
 constexpr int kXcds = 8;
+
+// Bytes of the store sink: GEMM epilogue lanes whose output row or column
+// lies past the tile's edge store there (lane l at 16 l) instead of
+// branching around the store.
+constexpr int kSinkBytes = 4096;
 
 // Per-stage run status words: [status, failed_peer, seq of peer 0, T].
 constexpr int kStatusWords = 4;
@@ -86,7 +92,7 @@ struct DevCtx {
     uint16_t* hs;      // [Tmax][Is]   bf16 shared activations
     uint16_t* y;       // [Tmax*K][H]  bf16 routed expert outputs, permuted order
     float* ys;         // [Tmax][H]    fp32 shared expert output, token (= shared row) order
-    const uint16_t* zero16;  // 256 zero bytes: source of the K-tail chunks
+    char* sink;        // [kSinkBytes] target of the GEMM epilogue stores of lanes past a tile edge
 };
 
 struct Weights {

@@ -32,12 +32,12 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 __device__ inline float bf2f(uint32_t b) { return __uint_as_float(b << 16); }
 
-// float -> bf16, round to nearest even (NaN stays NaN).
-__device__ inline uint32_t f2bf(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return u >> 16;
+// Two floats -> two bf16 (round to nearest even) packed in a word: one
+// v_cvt_pk_bf16_f32.
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ inline uint32_t pk_bf16(float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){a, b}, bf16x2_t));
 }
 
 __device__ inline char* slot_ptr(const DevCtx& c, char* win, int p, int s) {
@@ -441,12 +441,13 @@ __global__ __launch_bounds__(256) void k_scan(DevCtx c, const int* status) {
 // ---------------------------------------------------------------------------
 // GEMM tile plan (run by one workgroup of 256 threads).  Group j: 0 is the
 // shared expert over all T tokens, 1..E the routed experts.  A group of M
-// rows has ceil(M/kBM) row tiles and, for the gate/up GEMM, ceil(Ig/(kBN/2))
-// column tiles (kBN/2 gate + the same kBN/2 up rows of W13), for the down
-// GEMM ceil(H/kBN).  Tiles are numbered group-major, column tile next, row
-// tile fastest (row tiles of one column tile share their weight rows).  The
-// cost of a tile is (32-row blocks it holds) x (depth steps); the tile list
-// is cut into kXcds segments of equal cost, one per XCD.
+// rows has b = ceil(M/32) row blocks split evenly over ceil(b/kTileBlocks)
+// row tiles and, for the gate/up GEMM, ceil(Ig/(kBW/2)) column tiles (kBW/2
+// gate + the same kBW/2 up rows of W13), for the down GEMM ceil(H/kBW).
+// Tiles are numbered group-major, column tile next, row tile fastest (row
+// tiles of one column tile share their weight rows).  The cost of a tile is
+// (32-row blocks it holds) x (depth steps); the tile list is cut into kXcds
+// segments of equal cost, one per XCD.
 // ---------------------------------------------------------------------------
 struct PlanGroup {
     int M, mt, blocks, nt, nk;
@@ -458,9 +459,9 @@ __device__ inline PlanGroup plan_group(const DevCtx& c, int T, const int* s_eoff
     const int e = j - c.has_shared;
     const int Ig = shd ? c.Is : c.I;
     g.M = shd ? T : s_eoff[e + 1] - s_eoff[e];
-    g.mt = (g.M + kBM - 1) / kBM;
     g.blocks = (g.M + 31) / 32;
-    g.nt = mode == 1 ? (Ig + kBN / 2 - 1) / (kBN / 2) : (c.H + kBN - 1) / kBN;
+    g.mt = (g.blocks + kTileBlocks - 1) / kTileBlocks;
+    g.nt = mode == 1 ? (Ig + kBW / 2 - 1) / (kBW / 2) : (c.H + kBW - 1) / kBW;
     g.nk = mode == 1 ? (c.H + kBK - 1) / kBK : (Ig + kBK - 1) / kBK;
     return g;
 }
@@ -537,7 +538,8 @@ __device__ void plan_tiles(const DevCtx& c, int T, const int* s_eoff, int* sh) {
                 const long long u = (S - s_c[mode - 1][lo] + g.nk - 1) / g.nk;  // in 32-row blocks
                 int nt = (int)(u / g.blocks);
                 const int rem = (int)(u - (long long)nt * g.blocks);
-                int mt = (rem + kBM / 32 - 1) / (kBM / 32);
+                // first row tile that starts at or after block `rem`
+                int mt = (rem * g.mt + g.blocks - 1) / g.blocks;
                 if (mt >= g.mt) {
                     ++nt;
                     mt = 0;
@@ -614,47 +616,49 @@ __global__ __launch_bounds__(256) void k_permute(DevCtx c, const int* status) {
 // ---------------------------------------------------------------------------
 // a4/a5/a6: grouped GEMMs on MFMA (v_mfma_f32_32x32x16_bf16).
 //
-// A tile is up to 512 token rows of one group (16 blocks of 32) x 128
-// weight rows, 64 deep per step.  1024 threads = 16 waves in 8 (token) x 2
-// (weight) groups: wave (wm, wn) owns the token blocks wm and wm+8 (so a
-// partly filled tile keeps the waves balanced; blocks past the group's end
-// are skipped) and two 32-row weight blocks.  A group of at most 512 rows is
-// one row tile, so every weight row is streamed from HBM once per group; the
-// group's token rows are re-read from L2 by its column tiles.  Operands are K-contiguous rows
-// (token rows of X or h, weight rows of W13 / W2), so every MFMA fragment is
-// one 16-byte LDS read.  The weight fragment is the MFMA's first operand, so
-// a lane's accumulators hold one token row (lane % 32) and 4 runs of 4
-// consecutive output columns -- 8/16-byte stores in the epilogue.
+// A tile is up to 256 token rows of one group (8 blocks of 32) x 256 weight
+// rows, 64 deep per step.  256 threads = 4 waves, one per SIMD, placed 2
+// (token) x 2 (weight): wave (wx, ww) owns the token blocks wx, wx+2, wx+4,
+// wx+6 of the tile (so a partly filled tile keeps both token positions
+// equally loaded; blocks past the tile's end are skipped) and four 32-row
+// weight blocks: 16 accumulators of 32 x 32.  Per 16-deep slice a wave reads
+// 4 + 4 fragments of 1 KB from LDS and issues 16 MFMAs, half a KB of LDS
+// traffic per MFMA.  Operands are K-contiguous rows (token rows of X or h,
+// weight rows of W13 / W2), so every MFMA fragment is one 16-byte LDS read
+// per lane.  The weight fragment is the MFMA's first operand, so a lane's
+// accumulators hold one token row (lane % 32) and 4 runs of 4 consecutive
+// output columns -- 8/16-byte stores in the epilogue.
 //
-// Global -> LDS: direct-to-LDS loads (global_load_lds_dwordx4), so staging
-// costs no registers.  Two 80 KB stages (all 160 KB of LDS) are filled
-// alternately, one step ahead: a wave waits on its own vector-memory counter
-// for the stage it is about to read, then the workgroup barrier makes every
-// wave's loads of that stage visible and frees the other stage for the next
-// loads.  A 64-deep step covers each row's 128 bytes, one full L2 line.  One
-// load instruction of a wave fills 1 KB = 8 rows x 128 B; lane i fetches row
-// i/8, LDS chunk i%8 holding logical chunk (i%8) ^ swz(row), an XOR swizzle
-// that keeps the 16-byte fragment reads of 8 or 16 consecutive rows on
-// distinct banks.  Token-row load instructions whose 16 rows all lie past the group's
-// end are not issued.
+// Global -> LDS through registers: at the start of a depth step each wave
+// issues the 16-byte global loads of the next step (8 token-row and 8
+// weight-row loads of 1 KB per wave), reads and multiplies the current
+// stage, then writes the loaded data into the other of the two 64 KB LDS
+// stages; the barrier at the next step's start publishes it.  The loads
+// thus have a whole step of MFMA work to arrive, and no LDS read ever waits
+// on them.  (Direct-to-LDS loads would save the 64 staging registers, but
+// the compiler cannot tell the two stages apart and makes every LDS read
+// wait for all such loads in flight.)  One load instruction covers 1 KB =
+// 8 rows x 128 B; lane i fetches row i/8 and writes LDS chunk i%8, which
+// holds logical chunk (i%8) ^ swz(row), an XOR swizzle that keeps the
+// 16-byte fragment reads of 8 consecutive rows on distinct banks.
 //
 // MODE 1 (gate/up + SwiGLU): token rows are read straight from the inbound
 //   slots (routed rows through the per-pair row address, shared rows through
-//   the shared_x row address); the weight rows are 64 gate rows and the
-//   same 64 up rows of W13, and wave wn takes gate block wn and up block wn,
-//   so each lane holds gate and up of the same (row, column) and applies
-//   silu(g) * u in registers; h is stored bf16.
-// MODE 2 (down): token rows are the group's h rows, weight rows 128 rows of
+//   the shared_x row address); the weight rows are 128 gate rows and the
+//   same 128 up rows of W13, and wave ww takes gate blocks 2ww, 2ww+1 and
+//   the matching up blocks, so each lane holds gate and up of the same (row,
+//   column) and applies silu(g) * u in registers; h is stored bf16.
+// MODE 2 (down): token rows are the group's h rows, weight rows 256 rows of
 //   W2; routed output rows are stored bf16 in permuted order, shared rows
 //   fp32 in token order.
 //
 // Persistent: one workgroup per CU; the device-built tile list is cut into
 // 8 segments of equal cost, one per XCD (workgroups are dispatched to the
-// XCDs round-robin), whose workgroups take its tiles in turn.  Rows past the
-// group end and columns past the width load a valid row and are masked at
-// the store; depth past K loads zeros.
+// XCDs round-robin); a workgroup takes tiles from its XCD's segment and then
+// from the others.  Rows past the group end and columns past the width load
+// a valid row and are masked at the store; depth past K loads valid data
+// whose token-row copies are zeroed before they reach LDS.
 // ---------------------------------------------------------------------------
-__device__ inline int swz8(int r) { return (r ^ (r >> 3)) & 7; }
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -664,295 +668,480 @@ __device__ inline void dma16(const void* g, lds_ptr_t l) { __builtin_amdgcn_glob
 // s_waitcnt with only the vector-memory counter limited (gfx9 encoding).
 #define AFD_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(0x0F70 | ((n) & 15) | (((n) >> 4) << 14))
 
-__device__ inline void wait_vmcnt_upto(int n) {
-    // n is wave-uniform; the instruction needs an immediate
-    switch (n) {
-        case 0: AFD_WAIT_VMCNT(0); break;
-        case 1: AFD_WAIT_VMCNT(1); break;
-        case 2: AFD_WAIT_VMCNT(2); break;
-        case 3: AFD_WAIT_VMCNT(3); break;
-        case 4: AFD_WAIT_VMCNT(4); break;
-        case 5: AFD_WAIT_VMCNT(5); break;
-        case 6: AFD_WAIT_VMCNT(6); break;
-        case 7: AFD_WAIT_VMCNT(7); break;
-        case 8: AFD_WAIT_VMCNT(8); break;
-        default: AFD_WAIT_VMCNT(9); break;
+
+
+// Workgroup barrier that the compiler may not move memory accesses across
+// (a plain s_barrier: __syncthreads would also drain the load counters).
+#define AFD_BARRIER()                        \
+    do {                                     \
+        asm volatile("" ::: "memory");       \
+        __builtin_amdgcn_s_barrier();        \
+        asm volatile("" ::: "memory");       \
+    } while (0)
+
+constexpr int kRowBytes = kBK * 2;                      // 64: one row segment of a depth step
+constexpr int kChunks = kRowBytes / 16;                 // 4 16-byte chunks per row segment
+constexpr int kRowsPerLoad = 1024 / kRowBytes;          // 16 rows per 1 KB load instruction
+constexpr int kBlockBytes = 32 * kRowBytes;             // 2 KB per 32-row block
+constexpr int kXStageBytes = kBX * kRowBytes;           // 16 KB of token rows
+constexpr int kStageBytes = (kBX + kBW) * kRowBytes;    // 32 KB
+constexpr int kGemmWaves = kGemmThreads / 64;           // 4
+constexpr int kXInstr = kBX / kRowsPerLoad / kGemmWaves;  // 4 token-row loads per wave and step
+constexpr int kWInstr = kBW / kRowsPerLoad / kGemmWaves;  // 4 weight-row loads per wave and step
+constexpr int kLoadsPerStep = kXInstr + kWInstr;
+static_assert(kGemmWaves == 4 && kTileBlocks == 8 && kBK == 32 && kStages == 4,
+              "wave placement, swizzle and ring assume 4 waves, 8 token blocks, 32-deep steps, 4 stages");
+
+// LDS swizzle of 64-byte row segments: logical chunk c of row r sits at
+// chunk c ^ swz4(r).  The 16-byte fragment reads of 8 (or 16) consecutive
+// rows at one logical chunk then hit distinct banks.  swz4(r) depends on r
+// mod 8 only, so it is the same for every 32-row block and for every load
+// instruction (16 rows each).
+__device__ inline int swz4(int r) { return ((r >> 1) ^ (r >> 2)) & 3; }
+
+// What one wave needs to know about the current tile.
+struct GemmTile {
+    const char* abase;  // token-row base (inbound window, h or hs)
+    const char* bbase;  // weight-row base (this group's W13 / W2 slice)
+    // Load instruction i of the wave covers stage rows 16*(wid + 4i) .. +15;
+    // its lane offset (row offset + this lane's swizzled chunk) is fixed for
+    // the tile, the depth step moves the wave-uniform base.
+    uint32_t xo[kXInstr], wo[kWInstr];
+    uint32_t cx;           // this lane's logical chunk, as a byte offset
+    uint32_t tail_clamp;   // last 16-byte chunk of a row (K-tail loads)
+    int tb;                // 32-row token blocks of the tile, 1..8
+    int nk, kfull, Kdim;   // depth steps, steps fully inside K, K
+    int m0, rows, row0, Ig, nt;
+    bool sh;
+};
+
+// Direct-to-LDS loads of depth step kt into `stage` (lane l of instruction
+// i fills bytes 16 l of the instruction's 1 KB: row 16(wid + 4i) + l/4,
+// LDS chunk l % 4, which holds the swizzled logical chunk the lane
+// fetches).  All 4 token-row loads are issued (rows past the tile's blocks
+// are valid rows that land in LDS rows the MFMAs do not read).  A step past
+// the end of K (K not a multiple of 32) loads each row's last 16 bytes in
+// place of the missing chunks -- valid, finite data -- and the token-row
+// copies of those chunks are zeroed in LDS before the MFMAs.
+__device__ __forceinline__ void gemm_issue(const GemmTile& t, char* stage, int wid, int kt) {
+    const uint32_t kb = (uint32_t)kt * kRowBytes;
+    const char* ab = t.abase + kb;
+    const char* bb = t.bbase + kb;
+    const uint32_t fix = kb + t.cx > t.tail_clamp ? t.tail_clamp - kb - t.cx : 0u;
+#pragma unroll
+    for (int i = 0; i < kXInstr; ++i)
+        dma16(ab + (t.xo[i] + fix), (lds_ptr_t)(stage + (wid + kGemmWaves * i) * 1024));
+#pragma unroll
+    for (int i = 0; i < kWInstr; ++i)
+        dma16(bb + (t.wo[i] + fix), (lds_ptr_t)(stage + kXStageBytes + (wid + kGemmWaves * i) * 1024));
+}
+
+// Wait until at most n of this wave's load instructions are in flight.
+__device__ __forceinline__ void wait_loads(int n) {
+    if (n >= 2 * kLoadsPerStep) AFD_WAIT_VMCNT(2 * kLoadsPerStep);
+    else if (n >= kLoadsPerStep) AFD_WAIT_VMCNT(kLoadsPerStep);
+    else AFD_WAIT_VMCNT(0);
+}
+
+// Fragments of one 16-deep slice: 4 weight fragments and NV token fragments.
+template <int NV>
+struct GemmFrags {
+    bf16x8 w[4];
+    bf16x8 x[NV > 0 ? NV : 1];
+};
+
+// Reads slice kk (0 or 1) of the stage at `rd`.  The wave's weight fragment
+// jb sits at wl + (MODE 1) ((jb >> 1) * 4 + (jb & 1)) or (MODE 2) jb blocks
+// of 2 KB, its token fragment ib at tl + ib * 4 KB; slice kk flips address
+// bit 5 (the swizzled chunk).
+template <int MODE, int NV>
+__device__ __forceinline__ void gemm_frags(GemmFrags<NV>& f, const char* rd, int kk, uint32_t wl, uint32_t tl) {
+    const char* w = rd + (wl ^ (32u * kk));
+    const char* x = rd + (tl ^ (32u * kk));
+#pragma unroll
+    for (int jb = 0; jb < 4; ++jb)
+        f.w[jb] = __builtin_bit_cast(bf16x8, *(const u32x4*)(w + (MODE == 1 ? (jb >> 1) * 4 + (jb & 1) : jb) * kBlockBytes));
+#pragma unroll
+    for (int ib = 0; ib < NV; ++ib) f.x[ib] = __builtin_bit_cast(bf16x8, *(const u32x4*)(x + ib * 2 * kBlockBytes));
+}
+
+// In a step that reaches past K: token-fragment lanes whose chunk (8 depth
+// values at kt*32 + (2*kk + lane/32)*8) lies at or past K become zero, so
+// the (finite) clamped copies loaded there contribute nothing.  A select,
+// not a branch, so the step stays one basic block.
+template <int NV>
+__device__ __forceinline__ void gemm_tail(GemmFrags<NV>& f, const GemmTile& t, int kt, int kk, int lane) {
+    const bool past = kt * kBK + (2 * kk + (lane >> 5)) * 8 >= t.Kdim;
+#pragma unroll
+    for (int ib = 0; ib < NV; ++ib) {
+        u32x4 v = __builtin_bit_cast(u32x4, f.x[ib]);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) v[q] = past ? 0u : v[q];
+        f.x[ib] = __builtin_bit_cast(bf16x8, v);
     }
 }
 
-constexpr int kWaves = kGemmThreads / 64;                 // 16
-constexpr int kRowBytes = kBK * 2;                        // 128
-constexpr int kAStageBytes = kBM * kRowBytes;             // 64 KB
-constexpr int kStageBytes = (kBM + kBN) * kRowBytes;      // 80 KB
-constexpr int kRowsPerInstr = 1024 / kRowBytes;           // 8
-constexpr int kAInstr = kBM / kRowsPerInstr / kWaves;     // 4 token-row instructions per wave
-constexpr int kBTotal = kBN / kRowsPerInstr;              // 16 weight-row instructions per stage
-constexpr int kChunks = kRowBytes / 16;                   // 8
-constexpr int kWaveRows = kWaves / 2;                     // 8 token-block groups
+template <int NV>
+__device__ __forceinline__ void gemm_mfma(f32x16 (&acc)[NV > 0 ? NV : 1][4], const GemmFrags<NV>& f) {
+#pragma unroll
+    for (int ib = 0; ib < NV; ++ib)
+#pragma unroll
+        for (int jb = 0; jb < 4; ++jb)
+            acc[ib][jb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.w[jb], f.x[ib], acc[ib][jb], 0, 0, 0);
+}
+
+// Scheduling pattern: each MFMA of the group followed by one of the slice's
+// other memory instructions -- first its LDS reads, then its vector-memory
+// loads (the loads write LDS, so the scheduler keeps them after the reads)
+// -- so that the MFMA pipe stays fed while the wave issues them.
+template <int NMFMA, int NREAD, int NLOAD>
+__device__ __forceinline__ void gemm_interleave() {
+#pragma unroll
+    for (int i = 0; i < NMFMA; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (i < NREAD) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        else if (i - NREAD < NLOAD) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
+    }
+    if (NMFMA - NREAD < NLOAD) __builtin_amdgcn_sched_group_barrier(0x010, NLOAD - (NMFMA - NREAD), 0);
+}
+
+// One depth step kt of a wave with NV valid token blocks, software-
+// pipelined around a single barrier; TAIL: the step reaches past K.  On
+// entry `a` holds slice 0 of step kt.  (1) Slice 0's MFMAs, interleaved with
+// the reads of slice 1 into `b` and the loads of step kt+3 into the stage
+// step kt-1 used (every wave finished reading it before the previous step's
+// barrier).  (2) This wave's slice-1 reads done and its loads of step kt+1
+// landed (those of kt+2 and kt+3 may still fly), then the barrier: step
+// kt+1 is complete in LDS and every wave is done reading step kt.  (3) Slice
+// 1's MFMAs, interleaved with the reads of slice 0 of step kt+1 into `a`.
+// Each phase is one basic block: past the last step the loads reload the
+// last step into the idle stage and the reads read a stage nobody uses.
+template <int MODE, int NV, bool TAIL>
+__device__ __forceinline__ void gemm_step(f32x16 (&acc)[NV > 0 ? NV : 1][4], const GemmTile& t, char* smem,
+                                          int kt, int wid, int lane, uint32_t wl, uint32_t tl, GemmFrags<NV>& a,
+                                          GemmFrags<NV>& b) {
+    if (TAIL) gemm_tail(a, t, kt, 0, lane);
+    gemm_frags<MODE, NV>(b, smem + (kt & (kStages - 1)) * kStageBytes, 1, wl, tl);
+    gemm_issue(t, smem + ((kt + kStages - 1) & (kStages - 1)) * kStageBytes, wid, min(kt + kStages - 1, t.nk - 1));
+    gemm_mfma(acc, a);
+    gemm_interleave<4 * NV, 4 + NV, kLoadsPerStep>();
+    __builtin_amdgcn_sched_barrier(0);
+
+    __builtin_amdgcn_s_waitcnt(0xC07F);            // lgkmcnt(0)
+    AFD_WAIT_VMCNT(kLoadsPerStep * (kStages - 2));  // step kt+1 landed
+    AFD_BARRIER();
+
+    if (TAIL) gemm_tail(b, t, kt, 1, lane);
+    gemm_frags<MODE, NV>(a, smem + ((kt + 1) & (kStages - 1)) * kStageBytes, 0, wl, tl);
+    gemm_mfma(acc, b);
+    gemm_interleave<4 * NV, 4 + NV, 0>();
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+// Tile scheduler of a workgroup.  Tiles are taken dynamically: workgroup b
+// starts on the segment of its XCD (b % kXcds) and, when that is drained,
+// continues with the next segments.  Thread 0 owns the grabbing; each grab
+// is issued a whole tile before it is needed and resolved at the tile
+// boundary, then broadcast through LDS.
+struct GemmSched {
+    const int* seg;
+    int* ctr;
+    int total;
+    int xi, tries, pend;  // thread 0 only
+};
+
+__device__ __forceinline__ int sched_grab_slow(GemmSched& s) {  // next tile, or -1 when all are taken
+    while (s.tries < kXcds) {
+        const int lo = min(max(s.seg[s.xi], 0), s.total), hi = min(max(s.seg[s.xi + 1], lo), s.total);
+        const int t = lo + atomicAdd(&s.ctr[s.xi], 1);
+        if (t < hi) return t;
+        s.xi = (s.xi + 1) % kXcds;
+        ++s.tries;
+    }
+    return -1;
+}
+
+// Resolve the grab issued a tile ago and issue the following one.
+__device__ __forceinline__ int sched_next(GemmSched& s) {
+    const int lo = min(max(s.seg[s.xi], 0), s.total), hi = min(max(s.seg[s.xi + 1], lo), s.total);
+    int t = lo + s.pend;
+    if (t >= hi) {
+        s.xi = (s.xi + 1) % kXcds;
+        ++s.tries;
+        t = sched_grab_slow(s);
+    }
+    if (t >= 0) s.pend = atomicAdd(&s.ctr[s.xi], 1);
+    return t;
+}
+
+// Per-tile state of the wave: group, rows, depth, and the row offsets of its
+// load instructions.
+template <int MODE>
+__device__ __forceinline__ void gemm_setup(const DevCtx& c, const Weights& w, int tile, int wid, int lrow, uint32_t lcx,
+                                           GemmTile& t) {
+    // (every value here is wave-uniform: keep them in scalar registers)
+    const int2 ti = (MODE == 1 ? c.tinfo1 : c.tinfo2)[__builtin_amdgcn_readfirstlane(tile)];
+    const int j = __builtin_amdgcn_readfirstlane(ti.x), ty = __builtin_amdgcn_readfirstlane(ti.y);
+    const int mt = ty >> 16;
+    t.nt = ty & 0xffff;
+    t.sh = c.has_shared && j == 0;
+    const int e = j - c.has_shared;
+    const int M = __builtin_amdgcn_readfirstlane(c.grp_M[j]);
+    t.row0 = __builtin_amdgcn_readfirstlane(c.grp_row0[j]);
+    t.Ig = t.sh ? c.Is : c.I;
+    const int gb = (M + 31) >> 5;  // 32-row blocks of the group
+    const int ntm = (gb + kTileBlocks - 1) / kTileBlocks;
+    const int b0 = mt * gb / ntm, b1 = (mt + 1) * gb / ntm;
+    t.tb = b1 - b0;
+    t.m0 = b0 * 32;
+    t.rows = min(b1 * 32, M) - t.m0;  // valid token rows of the tile
+    t.Kdim = MODE == 1 ? c.H : t.Ig;
+    t.nk = (t.Kdim + kBK - 1) / kBK;
+    t.kfull = t.Kdim / kBK;
+    t.tail_clamp = (uint32_t)t.Kdim * 2 - 16;
+    // Row addresses as 32-bit byte offsets from a per-tile base (the window
+    // and every buffer stay below 4 GiB: checked at create).
+    if (MODE == 1) t.abase = c.in_win;
+    else t.abase = (const char*)(t.sh ? c.hs : c.h);
+    if (MODE == 1) t.bbase = (const char*)(t.sh ? w.ws13 : w.w13 + (int64_t)e * 2 * t.Ig * c.H);
+    else t.bbase = (const char*)(t.sh ? w.ws2 : w.w2 + (int64_t)e * c.H * t.Ig);
+    t.cx = lcx;
+#pragma unroll
+    for (int i = 0; i < kXInstr; ++i) {
+        const int r = (wid + kGemmWaves * i) * kRowsPerLoad + lrow;
+        int m = t.m0 + r;
+        if (m >= M) m = t.m0;
+        uint32_t o;
+        if (MODE == 1) o = (uint32_t)((t.sh ? c.sh_src[m] : c.psrc[t.row0 + m]) - (uint64_t)c.in_win);
+        else o = (uint32_t)(((int64_t)(t.sh ? m : t.row0 + m) * t.Ig) * 2);
+        t.xo[i] = o + lcx;
+    }
+#pragma unroll
+    for (int i = 0; i < kWInstr; ++i) {
+        const int r = (wid + kGemmWaves * i) * kRowsPerLoad + lrow;  // weight row of the stage
+        uint32_t o;
+        if (MODE == 1) {
+            int jj = t.nt * (kBW / 2) + (r & (kBW / 2 - 1));
+            if (jj >= t.Ig) jj = 0;
+            o = (uint32_t)((int64_t)((r / (kBW / 2)) * t.Ig + jj) * c.H * 2);
+        } else {
+            int n = t.nt * kBW + r;
+            if (n >= c.H) n = 0;
+            o = (uint32_t)((int64_t)n * t.Ig * 2);
+        }
+        t.wo[i] = o + lcx;
+    }
+}
+
+// The first kStages-1 steps of a tile into stages 0 .. (the ring must be
+// free; a tile shorter than the ring reloads its last step).
+__device__ __forceinline__ void gemm_prologue(const GemmTile& t, char* smem, int wid) {
+#pragma unroll
+    for (int p = 0; p < kStages - 1; ++p) gemm_issue(t, smem + p * kStageBytes, wid, min(p, t.nk - 1));
+}
+
+// Tile boundary, between the last depth step of the current tile and its
+// epilogue: once every wave is done with the ring, resolve the next tile,
+// set it up and start its loads, which then land while the epilogue runs.
+template <int MODE>
+__device__ __forceinline__ void gemm_boundary(const DevCtx& c, const Weights& w, GemmSched& sc, char* smem, int tid,
+                                              int wid, int lrow, uint32_t lcx, int& next, GemmTile& tn) {
+    int* slot = (int*)(smem + kStages * kStageBytes);
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS reads are done
+    AFD_BARRIER();
+    if (tid == 0) *slot = sched_next(sc);
+    __syncthreads();
+    next = __builtin_amdgcn_readfirstlane(*slot);
+    if (next >= 0) {
+        gemm_setup<MODE>(c, w, next, wid, lrow, lcx, tn);
+        gemm_prologue(tn, smem, wid);
+    }
+}
+
+// Epilogue of a tile.  In accumulator (ib, jb) a lane holds token row
+// (wx + 2*ib)*32 + (lane & 31) of the tile and, for a = 0..3, the 4 output
+// columns 32*(weight block) + a*8 + (lane >> 5)*4 + 0..3 in registers
+// 4a..4a+3.  Straight-line code: a lane whose row or columns lie past the
+// tile's edge stores into the sink instead (no divergent branches, which
+// would keep every accumulator live across them).
+// One accumulator element read out of its AGPR.  Reading the accumulators
+// one at a time keeps them in AGPRs until they are needed (the compiler
+// would otherwise copy all of them to VGPRs at the end of the depth loop and
+// run out of registers).  The caller leaves at least 18 wait states between
+// the last MFMA and the first read (the hardware does not interlock an MFMA
+// result read by a VALU instruction).
+__device__ __forceinline__ float agpr(float x) {
+    float r;
+    asm("v_accvgpr_read_b32 %0, %1" : "=v"(r) : "a"(x));
+    return r;
+}
+
+template <int MODE, int NV>
+__device__ __forceinline__ void gemm_epilogue(const f32x16 (&acc)[NV > 0 ? NV : 1][4], const DevCtx& c,
+                                              const GemmTile& t, int lane, int ww, int wx) {
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7");  // MFMA results settle (>= 18 wait states)
+    const int cq = (lane >> 5) * 4;
+    char* sink = c.sink + lane * 16;
+    if (MODE == 1) {
+        // h = silu(gate) * up, bf16; gate in weight blocks jb, up in jb + 2
+        uint16_t* base = t.sh ? c.hs : c.h + (int64_t)t.row0 * t.Ig;
+#pragma unroll
+        for (int ib = 0; ib < NV; ++ib) {
+            const int row = (wx + 2 * ib) * 32 + (lane & 31);
+            const bool rv = row < t.rows;
+            uint16_t* dst = base + (int64_t)(t.m0 + (rv ? row : 0)) * t.Ig;
+#pragma unroll
+            for (int jb = 0; jb < 2; ++jb) {
+#pragma unroll
+                for (int a = 0; a < 4; ++a) {
+                    const int jj = t.nt * (kBW / 2) + ww * 64 + jb * 32 + cq + a * 8;
+                    float hv[4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const float g = agpr(acc[ib][jb][4 * a + i]), u = agpr(acc[ib][jb + 2][4 * a + i]);
+                        hv[i] = g * __builtin_amdgcn_rcpf(1.f + __expf(-g)) * u;
+                    }
+                    u32x2* p = (rv && jj < t.Ig) ? (u32x2*)(dst + jj) : (u32x2*)sink;
+                    *p = (u32x2){pk_bf16(hv[0], hv[1]), pk_bf16(hv[2], hv[3])};
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+        }
+    } else if (t.sh) {
+        // shared expert rows: fp32, token order
+#pragma unroll
+        for (int ib = 0; ib < NV; ++ib) {
+            const int row = (wx + 2 * ib) * 32 + (lane & 31);
+            const bool rv = row < t.rows;
+            float* dst = c.ys + (int64_t)(t.m0 + (rv ? row : 0)) * c.H;
+#pragma unroll
+            for (int jb = 0; jb < 4; ++jb) {
+#pragma unroll
+                for (int a = 0; a < 4; ++a) {
+                    const int n = t.nt * kBW + (ww * 4 + jb) * 32 + cq + a * 8;
+                    f32x4* p = (rv && n < c.H) ? (f32x4*)(dst + n) : (f32x4*)sink;
+                    *p = (f32x4){agpr(acc[ib][jb][4 * a]), agpr(acc[ib][jb][4 * a + 1]), agpr(acc[ib][jb][4 * a + 2]),
+                                 agpr(acc[ib][jb][4 * a + 3])};
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+        }
+    } else {
+        // routed rows: bf16, permuted order
+#pragma unroll
+        for (int ib = 0; ib < NV; ++ib) {
+            const int row = (wx + 2 * ib) * 32 + (lane & 31);
+            const bool rv = row < t.rows;
+            uint16_t* dst = c.y + (int64_t)(t.row0 + t.m0 + (rv ? row : 0)) * c.H;
+#pragma unroll
+            for (int jb = 0; jb < 4; ++jb) {
+#pragma unroll
+                for (int a = 0; a < 4; ++a) {
+                    const int n = t.nt * kBW + (ww * 4 + jb) * 32 + cq + a * 8;
+                    u32x2* p = (rv && n < c.H) ? (u32x2*)(dst + n) : (u32x2*)sink;
+                    *p = (u32x2){pk_bf16(agpr(acc[ib][jb][4 * a]), agpr(acc[ib][jb][4 * a + 1])),
+                                 pk_bf16(agpr(acc[ib][jb][4 * a + 2]), agpr(acc[ib][jb][4 * a + 3]))};
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+        }
+    }
+}
+
+// The depth loop, the tile boundary and the epilogue of one tile for a wave
+// with NV valid token blocks (its blocks wx, wx+2, .. below tb).  Steps 0 ..
+// kStages-2 have been issued into stages 0 ...; on return `next` and `tn`
+// describe the next tile (next < 0: none), whose first steps are loading.
+template <int MODE, int NV>
+__device__ __forceinline__ void gemm_run(const DevCtx& c, const Weights& w, GemmSched& sc, const GemmTile& t,
+                                         char* smem, int tid, int wid, int lane, int ww, int wx, uint32_t wl,
+                                         uint32_t tl, int lrow, uint32_t lcx, int& next, GemmTile& tn) {
+    constexpr int NA = NV > 0 ? NV : 1;
+    f32x16 acc[NA][4];
+#pragma unroll
+    for (int a = 0; a < NA; ++a)
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[a][b][v] = 0.f;
+
+    // step 0 landed (this wave's loads, then everyone's), slice 0 read
+    AFD_WAIT_VMCNT(kLoadsPerStep * (kStages - 2));
+    AFD_BARRIER();
+    GemmFrags<NV> fa, fb;
+    gemm_frags<MODE, NV>(fa, smem, 0, wl, tl);
+    int kt = 0;
+    for (; kt < t.kfull; ++kt) gemm_step<MODE, NV, false>(acc, t, smem, kt, wid, lane, wl, tl, fa, fb);
+    for (; kt < t.nk; ++kt) gemm_step<MODE, NV, true>(acc, t, smem, kt, wid, lane, wl, tl, fa, fb);
+
+    gemm_boundary<MODE>(c, w, sc, smem, tid, wid, lrow, lcx, next, tn);
+
+    gemm_epilogue<MODE, NV>(acc, c, t, lane, ww, wx);
+}
 
 template <int MODE>
 __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(DevCtx c, const int* status, Weights w) {
     if (*status != AFD_OK) return;
-    __shared__ __attribute__((aligned(1024))) char smem[kStages * kStageBytes];
-    const int2* tinfo = MODE == 1 ? c.tinfo1 : c.tinfo2;
-    const int* seg = MODE == 1 ? c.seg1 : c.seg2;
-    const int total = (MODE == 1 ? c.tstart1 : c.tstart2)[c.G];
-    if (total <= 0 || total > (MODE == 1 ? c.max_tiles1 : c.max_tiles2)) return;  // nothing, or an insane plan
+    // One LDS array: the operand ring and, past it, the tile-index slot.
+    // (With a second __shared__ variable the compiler attaches alias scopes
+    // to LDS accesses and then makes every LDS read wait for the direct-to-
+    // LDS loads in flight; with one array it does not.)
+    __shared__ __attribute__((aligned(1024))) char smem[kStages * kStageBytes + 64];
+    int* slot = (int*)(smem + kStages * kStageBytes);
+    GemmSched sc;
+    sc.seg = MODE == 1 ? c.seg1 : c.seg2;
+    sc.ctr = c.tctr + (MODE - 1) * kXcds;
+    sc.total = (MODE == 1 ? c.tstart1 : c.tstart2)[c.G];
+    if (sc.total <= 0 || sc.total > (MODE == 1 ? c.max_tiles1 : c.max_tiles2)) return;  // nothing, or an insane plan
+    sc.xi = (int)(blockIdx.x % kXcds);
+    sc.tries = 0;
+    sc.pend = 0;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wid >> 1, wn = wid & 1;
+    const int wx = wid & 1, ww = wid >> 1;
 
-    // Tiles are taken dynamically: workgroup b starts on the segment of its
-    // XCD (b % kXcds) and, when that is drained, continues with the next
-    // segments.  Thread 0 owns the grabbing; each grab is issued a whole tile
-    // before it is needed and the index is broadcast through LDS at the tile
-    // boundary.
-    int* ctr = c.tctr + (MODE - 1) * kXcds;
-    int xi = (int)(blockIdx.x % kXcds), tries = 0, pend = 0;
-    auto grab_slow = [&]() -> int {  // thread 0 only: next tile, or -1 when all are taken
-        while (tries < kXcds) {
-            const int lo = min(max(seg[xi], 0), total), hi = min(max(seg[xi + 1], lo), total);
-            const int t = lo + atomicAdd(&ctr[xi], 1);
-            if (t < hi) return t;
-            xi = (xi + 1) % kXcds;
-            ++tries;
-        }
-        return -1;
-    };
-    int* bcast = (int*)smem;  // free at tile boundaries
+    const int lrow = lane >> 2;  // row inside a load instruction
+    // logical chunk fetched by this lane: (lane % 4) ^ swz4(16q + lrow) =
+    // (lane % 4) ^ swz4(lrow) for every load instruction q
+    const uint32_t lcx = (uint32_t)(((lane & 3) ^ swz4(lrow)) * 16);
+    // fragment byte offsets inside a stage: chunk ch = 2*kk + lane/32 of row
+    // r = 32*b + (lane & 31) sits at r*64 + (ch ^ swz4(r))*16 = b * 2 KB +
+    // fb ^ (32*kk) with fb = (lane & 31)*64 + ((lane/32) ^ swz4(lane))*16,
+    // the same lane part for every block.  The wave's weight blocks are
+    // (MODE 1) 2ww, 2ww+1, 4+2ww, 5+2ww and (MODE 2) 4ww .. 4ww+3, its token
+    // blocks wx, wx+2, wx+4, wx+6; the ww and wx terms go into the bases.
+    const uint32_t fb = (uint32_t)((lane & 31) * kRowBytes + (((lane >> 5) ^ swz4(lane & 31)) * 16));
+    const uint32_t wl = kXStageBytes + (uint32_t)ww * (MODE == 1 ? 2 : 4) * kBlockBytes + fb;
+    const uint32_t tl = (uint32_t)wx * kBlockBytes + fb;
+
+    // first tile
     if (tid == 0) {
-        const int t = grab_slow();
-        bcast[0] = t;
-        if (t >= 0) pend = atomicAdd(&ctr[xi], 1);  // the following tile, resolved a tile later
+        const int t = sched_grab_slow(sc);
+        *slot = t;
+        if (t >= 0) sc.pend = atomicAdd(&sc.ctr[sc.xi], 1);  // the following tile, resolved a tile later
     }
     __syncthreads();
-    int tile = bcast[0];
-    __syncthreads();
-
-    const int lrow = lane >> 3;   // row inside a load instruction
-    const int pc = lane & 7;      // LDS chunk of this lane
-    // chunk fetched by this lane: (i%8) ^ swz8(row) for row = 8*instr + lrow,
-    // which is (i%8) ^ lrow ^ (instr & 7)
-    const int s_lane = pc ^ lrow;
-    // weight fragment rows inside a stage (first MFMA operand)
-    int wrl[2];
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb)
-        wrl[nb] = MODE == 1 ? nb * (kBN / 2) + wn * 32 + (lane & 31) : (wn * 2 + nb) * 32 + (lane & 31);
-    const bool has_b = wid < kBTotal;  // every wave loads one weight-row instruction
-
+    int tile = __builtin_amdgcn_readfirstlane(*slot);
+    GemmTile t;
+    if (tile >= 0) {
+        gemm_setup<MODE>(c, w, tile, wid, lrow, lcx, t);
+        gemm_prologue(t, smem, wid);
+    }
     while (tile >= 0) {
-        const int2 ti = tinfo[tile];
-        const int j = ti.x, mt = ti.y >> 16, nt = ti.y & 0xffff;
-        const bool sh = c.has_shared && j == 0;
-        const int e = j - c.has_shared;
-        const int M = c.grp_M[j], row0 = c.grp_row0[j];
-        const int Ig = sh ? c.Is : c.I;
-        const int m0 = mt * kBM;
-        const int rows = min(kBM, M - m0);         // valid token rows of this tile (>= 1)
-        const int nblk = (rows + 31) >> 5;         // 32-row token blocks to compute
-        const int Kdim = MODE == 1 ? c.H : Ig;
-        const int nk = (Kdim + kBK - 1) / kBK;
-        // token-row load instructions of this wave: rows (wid*kAInstr + q)*16 ..
-        const int na = min(max((rows + kRowsPerInstr - 1) / kRowsPerInstr - wid * kAInstr, 0), kAInstr);
-        const int nw = na + (has_b ? 1 : 0);
-
-        // Row addresses as 32-bit byte offsets from a per-tile base (the
-        // window and every buffer stay below 4 GiB: checked at create).
-        const char* abase;
-        if (MODE == 1) abase = c.in_win;
-        else abase = (const char*)(sh ? c.hs : c.h);
-        const char* bbase;
-        if (MODE == 1) bbase = (const char*)(sh ? w.ws13 : w.w13 + (int64_t)e * 2 * Ig * c.H);
-        else bbase = (const char*)(sh ? w.ws2 : w.w2 + (int64_t)e * c.H * Ig);
-        uint32_t aoff[kAInstr], boff0 = 0;
-#pragma unroll
-        for (int q = 0; q < kAInstr; ++q) {
-            const int r = (wid * kAInstr + q) * kRowsPerInstr + lrow;
-            int m = m0 + r;
-            if (m >= M) m = m0;
-            if (MODE == 1) aoff[q] = (uint32_t)((sh ? c.sh_src[m] : c.psrc[row0 + m]) - (uint64_t)c.in_win);
-            else aoff[q] = (uint32_t)(((int64_t)(sh ? m : row0 + m) * Ig) * 2);
+        int next;
+        GemmTile tn;
+        switch ((t.tb - wx + 1) >> 1) {  // this wave's valid token blocks
+            case 4: gemm_run<MODE, 4>(c, w, sc, t, smem, tid, wid, lane, ww, wx, wl, tl, lrow, lcx, next, tn); break;
+            case 3: gemm_run<MODE, 3>(c, w, sc, t, smem, tid, wid, lane, ww, wx, wl, tl, lrow, lcx, next, tn); break;
+            case 2: gemm_run<MODE, 2>(c, w, sc, t, smem, tid, wid, lane, ww, wx, wl, tl, lrow, lcx, next, tn); break;
+            case 1: gemm_run<MODE, 1>(c, w, sc, t, smem, tid, wid, lane, ww, wx, wl, tl, lrow, lcx, next, tn); break;
+            default: gemm_run<MODE, 0>(c, w, sc, t, smem, tid, wid, lane, ww, wx, wl, tl, lrow, lcx, next, tn); break;
         }
-        {
-            const int r = wid * kRowsPerInstr + lrow;  // weight row of this wave's instruction
-            if (MODE == 1) {
-                int jj = nt * (kBN / 2) + (r & (kBN / 2 - 1));
-                if (jj >= Ig) jj = 0;
-                boff0 = (uint32_t)((int64_t)(((r & (kBN - 1)) / (kBN / 2)) * Ig + jj) * c.H * 2);
-            } else {
-                int n = nt * kBN + (r & (kBN - 1));
-                if (n >= c.H) n = 0;
-                boff0 = (uint32_t)((int64_t)n * Ig * 2);
-            }
-        }
-        const int kfull = Kdim / kBK;                // steps whose every chunk lies inside K
-        const uint32_t row_lim = (uint32_t)Kdim * 2;  // bytes of a row
-
-        // byte offset of this lane's chunk: (s_lane ^ (instr & 7)) * 16 =
-        // (16 * s_lane) ^ (16 * (instr & 7)), the second term wave-uniform
-        const uint32_t lco = (uint32_t)(s_lane * 16);
-
-        // A depth step past the end of K (K not a multiple of 64) loads each
-        // row's last 16 bytes in place of the missing chunks -- valid, finite
-        // data -- and the token fragments of those chunks are zeroed before
-        // the MFMA, so they contribute nothing.
-        const uint32_t tail_clamp = row_lim - 16;
-#define AFD_ISSUE(kt, st)                                                                            \
-    {                                                                                                \
-        char* sb_ = smem + (st) * kStageBytes;                                                       \
-        const uint32_t kb_ = (uint32_t)(kt) * (kBK * 2);                                             \
-        const bool full_ = (kt) < kfull;                                                             \
-        _Pragma("unroll") for (int q = 0; q < kAInstr; ++q) if (q < na) {                            \
-            uint32_t cc_ = kb_ + (lco ^ (uint32_t)(((wid * kAInstr + q) & 7) * 16));                 \
-            if (!full_) cc_ = min(cc_, tail_clamp);                                                  \
-            dma16(abase + (aoff[q] + cc_), (lds_ptr_t)(sb_ + (wid * kAInstr + q) * 1024));           \
-        }                                                                                            \
-        if (has_b) {                                                                                 \
-            uint32_t cc_ = kb_ + (lco ^ (uint32_t)((wid & 7) * 16));                                 \
-            if (!full_) cc_ = min(cc_, tail_clamp);                                                  \
-            dma16(bbase + (boff0 + cc_), (lds_ptr_t)(sb_ + kAStageBytes + wid * 1024));              \
-        }                                                                                            \
+        tile = next;
+        t = tn;
     }
-
-        f32x16 acc[2][2];
-#pragma unroll
-        for (int a = 0; a < 2; ++a)
-#pragma unroll
-            for (int b = 0; b < 2; ++b)
-#pragma unroll
-                for (int v = 0; v < 16; ++v) acc[a][b][v] = 0.f;
-
-        // every wave is done with the previous tile's LDS, and this wave's
-        // earlier memory operations have drained, before the ring is refilled
-        AFD_WAIT_VMCNT(0);
-        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-        __builtin_amdgcn_s_barrier();
-#pragma unroll
-        for (int p = 0; p < kStages - 1; ++p)
-            if (p < nk) AFD_ISSUE(p, p);
-
-        // this wave's valid token blocks: wm (if < nblk) and wm + 8 (if < nblk)
-        const int nv = (wm < nblk ? 1 : 0) + (wm + kWaveRows < nblk ? 1 : 0);
-        // fragment byte offsets inside a stage: chunk ch = 2*kk + lane/32 of
-        // row r sits at r*128 + (ch ^ swz8(r))*16 = fbase(r) ^ (32*kk) with
-        // fbase(r) = r*128 + ((lane/32) ^ swz8(r))*16
-        constexpr int kKK = kBK / 16;
-        uint32_t wfb[2], tfb[2];
-#pragma unroll
-        for (int nb = 0; nb < 2; ++nb)
-            wfb[nb] = kAStageBytes + wrl[nb] * kRowBytes + (((lane >> 5) ^ swz8(wrl[nb])) * 16);
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb) {
-            const int ar = (wm + kWaveRows * mb) * 32 + (lane & 31);
-            tfb[mb] = ar * kRowBytes + (((lane >> 5) ^ swz8(ar)) * 16);
-        }
-
-        // One depth step: all fragment reads of the stage first, then the
-        // MFMAs (NV = number of this wave's valid token blocks).
-#define AFD_STEP(NV)                                                                                 \
-    for (int kt = 0; kt < nk; ++kt) {                                                                \
-        const int st = kt % kStages;                                                                 \
-        const int later = min(nk - 1 - kt, kStages - 2);                                             \
-        wait_vmcnt_upto(later * nw);                                                                 \
-        __builtin_amdgcn_s_barrier();                                                                \
-        const char* sb = smem + st * kStageBytes;                                                    \
-        _Pragma("unroll") for (int kk = 0; kk < kKK; ++kk) {                                         \
-            bf16x8 wf[2], tf[2];                                                                     \
-            _Pragma("unroll") for (int nb = 0; nb < 2; ++nb)                                         \
-                wf[nb] = __builtin_bit_cast(bf16x8, *(const u32x4*)(sb + (wfb[nb] ^ (32u * kk))));   \
-            _Pragma("unroll") for (int mb = 0; mb < NV; ++mb)                                        \
-                tf[mb] = __builtin_bit_cast(bf16x8, *(const u32x4*)(sb + (tfb[mb] ^ (32u * kk))));   \
-            /* refill the other stage while this stage's first reads are in flight */               \
-            if (kk == 0 && kt + kStages - 1 < nk) AFD_ISSUE(kt + kStages - 1, (kt + kStages - 1) % kStages); \
-            if (kt >= kfull && kt * kBK + (2 * kk + (lane >> 5)) * 8 >= Kdim) {                      \
-                /* chunks at or past K contribute zero */                                            \
-                _Pragma("unroll") for (int mb = 0; mb < NV; ++mb)                                    \
-                    tf[mb] = __builtin_bit_cast(bf16x8, (u32x4){0u, 0u, 0u, 0u});                    \
-            }                                                                                        \
-            _Pragma("unroll") for (int mb = 0; mb < NV; ++mb)                                        \
-                _Pragma("unroll") for (int nb = 0; nb < 2; ++nb)                                     \
-                    acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[nb], tf[mb], acc[mb][nb], 0, 0, 0); \
-        }                                                                                            \
-    }
-        if (nv == 2) {
-            AFD_STEP(2)
-        } else if (nv == 1) {
-            AFD_STEP(1)
-        } else {
-            AFD_STEP(0)
-        }
-#undef AFD_STEP
-#undef AFD_ISSUE
-
-        // epilogue: in block (mb, nb) lane holds token row (wm + 8*mb)*32 +
-        // (lane & 31) and, for a = 0..3, the 4 output columns
-        // 32*(weight block) + a*8 + (lane >> 5)*4 + 0..3 in registers 4a..4a+3
-        const int cq = (lane >> 5) * 4;
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb) {
-            const int tb = wm + kWaveRows * mb;
-            if (tb >= nblk) continue;
-            const int row = tb * 32 + (lane & 31);
-            if (row >= rows) continue;
-            const int m = m0 + row;
-            if (MODE == 1) {
-                uint16_t* dst = sh ? c.hs + (int64_t)m * Ig : c.h + (int64_t)(row0 + m) * Ig;
-                const int jb = nt * (kBN / 2) + wn * 32 + cq;
-#pragma unroll
-                for (int a = 0; a < 4; ++a) {
-                    const int jj = jb + a * 8;
-                    if (jj < Ig) {
-                        uint32_t hv[4];
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) {
-                            const float g = acc[mb][0][4 * a + i], u = acc[mb][1][4 * a + i];
-                            hv[i] = f2bf(g * __builtin_amdgcn_rcpf(1.f + __expf(-g)) * u);
-                        }
-                        *(u32x2*)(dst + jj) = (u32x2){hv[0] | (hv[1] << 16), hv[2] | (hv[3] << 16)};
-                    }
-                }
-            } else {
-#pragma unroll
-                for (int nb = 0; nb < 2; ++nb) {
-                    const int nbase = nt * kBN + (wn * 2 + nb) * 32 + cq;
-#pragma unroll
-                    for (int a = 0; a < 4; ++a) {
-                        const int n = nbase + a * 8;
-                        if (n < c.H) {
-                            if (sh) {
-                                *(f32x4*)(c.ys + (int64_t)m * c.H + n) =
-                                    (f32x4){acc[mb][nb][4 * a], acc[mb][nb][4 * a + 1], acc[mb][nb][4 * a + 2],
-                                            acc[mb][nb][4 * a + 3]};
-                            } else {
-                                const uint32_t p0 = f2bf(acc[mb][nb][4 * a]) | (f2bf(acc[mb][nb][4 * a + 1]) << 16);
-                                const uint32_t p1 = f2bf(acc[mb][nb][4 * a + 2]) | (f2bf(acc[mb][nb][4 * a + 3]) << 16);
-                                *(u32x2*)(c.y + (int64_t)(row0 + m) * c.H + n) = (u32x2){p0, p1};
-                            }
-                        }
-                    }
-                }
-            }
-        }
-        // next tile: resolve the grab issued a tile ago, broadcast it
-        AFD_WAIT_VMCNT(0);
-        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-        __builtin_amdgcn_s_barrier();        // every wave is done with the LDS ring
-        if (tid == 0) {
-            const int lo = min(max(seg[xi], 0), total), hi = min(max(seg[xi + 1], lo), total);
-            int t = lo + pend;
-            if (t >= hi) {
-                xi = (xi + 1) % kXcds;
-                ++tries;
-                t = grab_slow();
-            }
-            bcast[0] = t;
-            if (t >= 0) pend = atomicAdd(&ctr[xi], 1);
-        }
-        __syncthreads();
-        tile = bcast[0];
-        __syncthreads();
-    }
+    // drain this wave's surplus loads before the workgroup ends
+    AFD_WAIT_VMCNT(0);
 }
 
 // ---------------------------------------------------------------------------
@@ -1006,7 +1195,7 @@ __global__ __launch_bounds__(256) void k_combine(DevCtx c, const int* status, in
             u32x4 out;
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                out[i] = f2bf(c.rsf * acc[2 * i] + sv[2 * i]) | (f2bf(c.rsf * acc[2 * i + 1] + sv[2 * i + 1]) << 16);
+                out[i] = pk_bf16(c.rsf * acc[2 * i] + sv[2 * i], c.rsf * acc[2 * i + 1] + sv[2 * i + 1]);
             __builtin_nontemporal_store(out, &dst[ch]);
         }
     }
