@@ -53,6 +53,24 @@ def algorithmic(wl, counts):
     }
 
 
+def measured_traffic(wl, kernel):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
+    summary, or None if it was measured on another workload or on a different
+    kernel source than the one built now."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "hbm_bytes_prefill_gemm.json")
+    src = os.path.join(ROOT, "combine_afd_slot_amd", "csrc", "afd_kernels.hip")
+    try:
+        side = json.load(open(path))
+        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    except OSError:
+        return None
+    if side.get("workload") != wl.name or side.get("kernel_source_sha256") != sha:
+        return None
+    b = side["bytes_per_launch"].get(kernel)
+    return None if b is None else int(b["read"] + b["written"])
+
+
 def cpu_baseline(wl, inp, target_s=15.0):
     """The oracle as it stands, timed on a bounded prefix sample of each peer."""
     from oracle import oracle
@@ -202,12 +220,12 @@ def main():
             ach = alg[dom]["flops"] / (kern[dom] * 1e-3) / 1e12
             line["roofline"] = {"kernel": dom, "bound": "mfma", "achieved": round(ach, 1),
                                 "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                                "frac": round(ach / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None}
+                                "frac": round(ach / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": measured_traffic(wl, dom)}
         else:
             ach = alg[dom]["bytes"] / (kern[dom] * 1e-3) / 1e9
             line["roofline"] = {"kernel": dom, "bound": "hbm", "achieved": round(ach, 1),
                                 "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None}
+                                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": measured_traffic(wl, dom)}
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a bounded sample")
         line["cpu_baseline"] = cpu_baseline(wl, inp)
