@@ -718,30 +718,26 @@ struct GemmTile {
 // Direct-to-LDS loads of depth step kt into `stage` (lane l of instruction
 // i fills bytes 16 l of the instruction's 1 KB: row 16(wid + 4i) + l/4,
 // LDS chunk l % 4, which holds the swizzled logical chunk the lane
-// fetches).  All 4 token-row loads are issued (rows past the tile's blocks
-// are valid rows that land in LDS rows the MFMAs do not read).  A step past
+// fetches).  NX of the 4 token-row loads are issued, enough for the tile's
+// blocks: NX = ceil(tb / 2) covers rows below 64 NX >= 32 tb (rows past the
+// tile's blocks are valid rows that land in LDS rows the MFMAs do not read).  A step past
 // the end of K (K not a multiple of 32) loads each row's last 16 bytes in
 // place of the missing chunks -- valid, finite data -- and the token-row
 // copies of those chunks are zeroed in LDS before the MFMAs.
+template <int NX>
 __device__ __forceinline__ void gemm_issue(const GemmTile& t, char* stage, int wid, int kt) {
     const uint32_t kb = (uint32_t)kt * kRowBytes;
     const char* ab = t.abase + kb;
     const char* bb = t.bbase + kb;
     const uint32_t fix = kb + t.cx > t.tail_clamp ? t.tail_clamp - kb - t.cx : 0u;
 #pragma unroll
-    for (int i = 0; i < kXInstr; ++i)
+    for (int i = 0; i < NX; ++i)
         dma16(ab + (t.xo[i] + fix), (lds_ptr_t)(stage + (wid + kGemmWaves * i) * 1024));
 #pragma unroll
     for (int i = 0; i < kWInstr; ++i)
         dma16(bb + (t.wo[i] + fix), (lds_ptr_t)(stage + kXStageBytes + (wid + kGemmWaves * i) * 1024));
 }
 
-// Wait until at most n of this wave's load instructions are in flight.
-__device__ __forceinline__ void wait_loads(int n) {
-    if (n >= 2 * kLoadsPerStep) AFD_WAIT_VMCNT(2 * kLoadsPerStep);
-    else if (n >= kLoadsPerStep) AFD_WAIT_VMCNT(kLoadsPerStep);
-    else AFD_WAIT_VMCNT(0);
-}
 
 // Fragments of one 16-deep slice: 4 weight fragments and NV token fragments.
 template <int NV>
@@ -816,19 +812,19 @@ __device__ __forceinline__ void gemm_interleave() {
 // 1's MFMAs, interleaved with the reads of slice 0 of step kt+1 into `a`.
 // Each phase is one basic block: past the last step the loads reload the
 // last step into the idle stage and the reads read a stage nobody uses.
-template <int MODE, int NV, bool TAIL>
+template <int MODE, int NV, int NX, bool TAIL>
 __device__ __forceinline__ void gemm_step(f32x16 (&acc)[NV > 0 ? NV : 1][4], const GemmTile& t, char* smem,
                                           int kt, int wid, int lane, uint32_t wl, uint32_t tl, GemmFrags<NV>& a,
                                           GemmFrags<NV>& b) {
     if (TAIL) gemm_tail(a, t, kt, 0, lane);
     gemm_frags<MODE, NV>(b, smem + (kt & (kStages - 1)) * kStageBytes, 1, wl, tl);
-    gemm_issue(t, smem + ((kt + kStages - 1) & (kStages - 1)) * kStageBytes, wid, min(kt + kStages - 1, t.nk - 1));
+    gemm_issue<NX>(t, smem + ((kt + kStages - 1) & (kStages - 1)) * kStageBytes, wid, min(kt + kStages - 1, t.nk - 1));
     gemm_mfma(acc, a);
-    gemm_interleave<4 * NV, 4 + NV, kLoadsPerStep>();
+    gemm_interleave<4 * NV, 4 + NV, NX + kWInstr>();
     __builtin_amdgcn_sched_barrier(0);
 
     __builtin_amdgcn_s_waitcnt(0xC07F);            // lgkmcnt(0)
-    AFD_WAIT_VMCNT(kLoadsPerStep * (kStages - 2));  // step kt+1 landed
+    AFD_WAIT_VMCNT((NX + kWInstr) * (kStages - 2));  // step kt+1 landed
     AFD_BARRIER();
 
     if (TAIL) gemm_tail(b, t, kt, 1, lane);
@@ -935,9 +931,18 @@ __device__ __forceinline__ void gemm_setup(const DevCtx& c, const Weights& w, in
 
 // The first kStages-1 steps of a tile into stages 0 .. (the ring must be
 // free; a tile shorter than the ring reloads its last step).
-__device__ __forceinline__ void gemm_prologue(const GemmTile& t, char* smem, int wid) {
+template <int NX>
+__device__ __forceinline__ void gemm_prologue_nx(const GemmTile& t, char* smem, int wid) {
 #pragma unroll
-    for (int p = 0; p < kStages - 1; ++p) gemm_issue(t, smem + p * kStageBytes, wid, min(p, t.nk - 1));
+    for (int p = 0; p < kStages - 1; ++p) gemm_issue<NX>(t, smem + p * kStageBytes, wid, min(p, t.nk - 1));
+}
+__device__ __forceinline__ void gemm_prologue(const GemmTile& t, char* smem, int wid) {
+    switch ((t.tb + 1) >> 1) {
+        case 1: gemm_prologue_nx<1>(t, smem, wid); break;
+        case 2: gemm_prologue_nx<2>(t, smem, wid); break;
+        case 3: gemm_prologue_nx<3>(t, smem, wid); break;
+        default: gemm_prologue_nx<4>(t, smem, wid); break;
+    }
 }
 
 // Tile boundary, between the last depth step of the current tile and its
@@ -1052,7 +1057,7 @@ __device__ __forceinline__ void gemm_epilogue(const f32x16 (&acc)[NV > 0 ? NV : 
 // with NV valid token blocks (its blocks wx, wx+2, .. below tb).  Steps 0 ..
 // kStages-2 have been issued into stages 0 ...; on return `next` and `tn`
 // describe the next tile (next < 0: none), whose first steps are loading.
-template <int MODE, int NV>
+template <int MODE, int NV, int NX>
 __device__ __forceinline__ void gemm_run(const DevCtx& c, const Weights& w, GemmSched& sc, const GemmTile& t,
                                          char* smem, int tid, int wid, int lane, int ww, int wx, uint32_t wl,
                                          uint32_t tl, int lrow, uint32_t lcx, int& next, GemmTile& tn) {
@@ -1066,13 +1071,13 @@ __device__ __forceinline__ void gemm_run(const DevCtx& c, const Weights& w, Gemm
             for (int v = 0; v < 16; ++v) acc[a][b][v] = 0.f;
 
     // step 0 landed (this wave's loads, then everyone's), slice 0 read
-    AFD_WAIT_VMCNT(kLoadsPerStep * (kStages - 2));
+    AFD_WAIT_VMCNT((NX + kWInstr) * (kStages - 2));
     AFD_BARRIER();
     GemmFrags<NV> fa, fb;
     gemm_frags<MODE, NV>(fa, smem, 0, wl, tl);
     int kt = 0;
-    for (; kt < t.kfull; ++kt) gemm_step<MODE, NV, false>(acc, t, smem, kt, wid, lane, wl, tl, fa, fb);
-    for (; kt < t.nk; ++kt) gemm_step<MODE, NV, true>(acc, t, smem, kt, wid, lane, wl, tl, fa, fb);
+    for (; kt < t.kfull; ++kt) gemm_step<MODE, NV, NX, false>(acc, t, smem, kt, wid, lane, wl, tl, fa, fb);
+    for (; kt < t.nk; ++kt) gemm_step<MODE, NV, NX, true>(acc, t, smem, kt, wid, lane, wl, tl, fa, fb);
 
     gemm_boundary<MODE>(c, w, sc, smem, tid, wid, lrow, lcx, next, tn);
 
@@ -1130,13 +1135,20 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(DevCtx c, const int* s
     while (tile >= 0) {
         int next;
         GemmTile tn;
-        switch ((t.tb - wx + 1) >> 1) {  // this wave's valid token blocks
-            case 4: gemm_run<MODE, 4>(c, w, sc, t, smem, tid, wid, lane, ww, wx, wl, tl, lrow, lcx, next, tn); break;
-            case 3: gemm_run<MODE, 3>(c, w, sc, t, smem, tid, wid, lane, ww, wx, wl, tl, lrow, lcx, next, tn); break;
-            case 2: gemm_run<MODE, 2>(c, w, sc, t, smem, tid, wid, lane, ww, wx, wl, tl, lrow, lcx, next, tn); break;
-            case 1: gemm_run<MODE, 1>(c, w, sc, t, smem, tid, wid, lane, ww, wx, wl, tl, lrow, lcx, next, tn); break;
-            default: gemm_run<MODE, 0>(c, w, sc, t, smem, tid, wid, lane, ww, wx, wl, tl, lrow, lcx, next, tn); break;
+        // this wave's valid token blocks NV = ceil((tb - wx) / 2) and the
+        // token-row loads per wave and step NX = ceil(tb / 2)
+#define AFD_RUN(NV, NX) gemm_run<MODE, NV, NX>(c, w, sc, t, smem, tid, wid, lane, ww, wx, wl, tl, lrow, lcx, next, tn)
+        switch (t.tb * 2 + wx) {  // key 2 tb + wx -> (NV, NX)
+            case 17: case 16: case 14: AFD_RUN(4, 4); break;  // tb 8, tb 7 wx 0
+            case 15: AFD_RUN(3, 4); break;                    // tb 7 wx 1
+            case 13: case 12: case 10: AFD_RUN(3, 3); break;  // tb 6, tb 5 wx 0
+            case 11: AFD_RUN(2, 3); break;                    // tb 5 wx 1
+            case 9: case 8: case 6: AFD_RUN(2, 2); break;     // tb 4, tb 3 wx 0
+            case 7: AFD_RUN(1, 2); break;                     // tb 3 wx 1
+            case 5: case 4: case 2: AFD_RUN(1, 1); break;     // tb 2, tb 1 wx 0
+            default: AFD_RUN(0, 1); break;                    // tb 1 wx 1
         }
+#undef AFD_RUN
         tile = next;
         t = tn;
     }
