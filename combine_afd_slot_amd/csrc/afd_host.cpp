@@ -75,9 +75,9 @@ int32_t validate(const afd_window_config* c) {
 
 // Workspace carve-up, in bytes from the workspace start.
 struct WsLayout {
-    int64_t ctrl, peer_counts, blk_counts, blk_base, counts, eoff, grp_M, grp_row0, tstart1, tstart2;
+    int64_t ctrl, peer_counts, blk_counts, blk_base, counts, eoff, tstart1, tstart2;
     int64_t tinfo1, tinfo2, seg1, seg2, tctr, psrc, max_tiles1, max_tiles2;
-    int64_t ids, wts, perm, inv, tok_src, sh_src, h, hs, y, ys, sink, bytes;
+    int64_t ids, wts, perm, inv, tok_src, sh_src, h, hs, y, ys, bytes;
     int64_t ctrl_ints;
     // control-word offsets inside ctrl (in ints)
     int64_t c_seen_in, c_ret_seq, c_seen_ret, c_cur_seq, c_off, c_T, c_done, c_run_status, c_peer_status;
@@ -112,8 +112,6 @@ WsLayout ws_layout(const afd_window_config& c) {
     w.blk_base = take(4 * nb * E);
     w.counts = take(4 * E);
     w.eoff = take(4 * (E + 1));
-    w.grp_M = take(4 * G);
-    w.grp_row0 = take(4 * G);
     w.tstart1 = take(4 * (G + 1));
     w.tstart2 = take(4 * (G + 1));
     {
@@ -128,11 +126,11 @@ WsLayout ws_layout(const afd_window_config& c) {
         w.max_tiles1 = mt_r * nt1_r + mt_s * nt1_s;
         w.max_tiles2 = (mt_r + mt_s) * nt2;
     }
-    w.tinfo1 = take(8 * w.max_tiles1);
-    w.tinfo2 = take(8 * w.max_tiles2);
-    w.seg1 = take(4 * (afd::kXcds + 1));
-    w.seg2 = take(4 * (afd::kXcds + 1));
-    w.tctr = take(4 * 2 * afd::kXcds);
+    w.tinfo1 = take(16 * w.max_tiles1);
+    w.tinfo2 = take(16 * w.max_tiles2);
+    w.seg1 = take(4 * (afd::kSegs + 1));
+    w.seg2 = take(4 * (afd::kSegs + 1));
+    w.tctr = take(4 * 2 * afd::kSegs);
     w.psrc = take(8 * np);
     w.ids = take(4 * np);
     w.wts = take(4 * np);
@@ -144,7 +142,6 @@ WsLayout ws_layout(const afd_window_config& c) {
     w.hs = take(2 * tmax * (c.shared_intermediate > 0 ? c.shared_intermediate : 1));
     w.y = take(2 * np * c.hidden);
     w.ys = take(4 * tmax * c.hidden);
-    w.sink = take(afd::kSinkBytes);
     w.bytes = cur;
     return w;
 }
@@ -238,12 +235,10 @@ void fill_ctx(afd_window* w) {
     d.blk_base = (int*)(ws + L.blk_base);
     d.counts = (int*)(ws + L.counts);
     d.eoff = (int*)(ws + L.eoff);
-    d.grp_M = (int*)(ws + L.grp_M);
-    d.grp_row0 = (int*)(ws + L.grp_row0);
     d.tstart1 = (int*)(ws + L.tstart1);
     d.tstart2 = (int*)(ws + L.tstart2);
-    d.tinfo1 = (int2*)(ws + L.tinfo1);
-    d.tinfo2 = (int2*)(ws + L.tinfo2);
+    d.tinfo1 = (int4*)(ws + L.tinfo1);
+    d.tinfo2 = (int4*)(ws + L.tinfo2);
     d.seg1 = (int*)(ws + L.seg1);
     d.seg2 = (int*)(ws + L.seg2);
     d.tctr = (int*)(ws + L.tctr);
@@ -258,7 +253,6 @@ void fill_ctx(afd_window* w) {
     d.hs = (uint16_t*)(ws + L.hs);
     d.y = (uint16_t*)(ws + L.y);
     d.ys = (float*)(ws + L.ys);
-    d.sink = ws + L.sink;
 }
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }

@@ -33,10 +33,10 @@ constexpr int kGemmThreads = 256;
 constexpr int kTileBlocks = kBX / 32;
 constexpr int kXcds = 8;
 
-// Bytes of the store sink: GEMM epilogue lanes whose output row or column
-// lies past the tile's edge store there (lane l at 16 l) instead of
-// branching around the store.
-constexpr int kSinkBytes = 4096;
+// Tile segments of a GEMM: the shared expert's tiles (the longest) cut into
+// kXcds cost-balanced segments, then the routed experts' tiles cut the same
+// way; segment s covers tiles [seg[s], seg[s+1]).
+constexpr int kSegs = 2 * kXcds;
 
 // Per-stage run status words: [status, failed_peer, seq of peer 0, T].
 constexpr int kStatusWords = 4;
@@ -71,15 +71,13 @@ struct DevCtx {
     int* blk_base;     // [E][NB] stable base of each chunk inside its expert group
     int* counts;       // [E]
     int* eoff;         // [E+1]
-    int* grp_M;        // [G]
-    int* grp_row0;     // [G]
     int* tstart1;      // [G+1] gate/up GEMM tile prefix per group
     int* tstart2;      // [G+1] down GEMM tile prefix per group
-    int2* tinfo1;      // [max_tiles1] (group, mt << 16 | nt) of each gate/up tile
-    int2* tinfo2;      // [max_tiles2]
-    int* seg1;         // [kXcds+1] cost-balanced tile segments of the gate/up GEMM
-    int* seg2;         // [kXcds+1]
-    int* tctr;         // [2][kXcds] tiles taken from each segment (zeroed by the planner)
+    int4* tinfo1;      // [max_tiles1] (group, nt | tb << 16, first row, rows) of each gate/up tile
+    int4* tinfo2;      // [max_tiles2]
+    int* seg1;         // [kSegs+1] tile segments of the gate/up GEMM
+    int* seg2;         // [kSegs+1]
+    int* tctr;         // [2][kSegs] tiles taken from each segment (zeroed by the planner)
     uint64_t* psrc;    // [Tmax*K] address of the token row of each permuted pair
     int* ids;          // [Tmax*K]
     float* wts;        // [Tmax*K]
@@ -92,7 +90,6 @@ struct DevCtx {
     uint16_t* hs;      // [Tmax][Is]   bf16 shared activations
     uint16_t* y;       // [Tmax*K][H]  bf16 routed expert outputs, permuted order
     float* ys;         // [Tmax][H]    fp32 shared expert output, token (= shared row) order
-    char* sink;        // [kSinkBytes] target of the GEMM epilogue stores of lanes past a tile edge
 };
 
 struct Weights {

@@ -446,8 +446,9 @@ __global__ __launch_bounds__(256) void k_scan(DevCtx c, const int* status) {
 // gate + the same kBW/2 up rows of W13), for the down GEMM ceil(H/kBW).
 // Tiles are numbered group-major, column tile next, row tile fastest (row
 // tiles of one column tile share their weight rows).  The cost of a tile is
-// (32-row blocks it holds) x (depth steps); the tile list is cut into kXcds
-// segments of equal cost, one per XCD.
+// (32-row blocks it holds) x (depth steps).  The shared group's tiles and
+// the routed groups' tiles are each cut into kXcds segments of equal cost,
+// one of each per XCD.
 // ---------------------------------------------------------------------------
 struct PlanGroup {
     int M, mt, blocks, nt, nk;
@@ -467,7 +468,7 @@ __device__ inline PlanGroup plan_group(const DevCtx& c, int T, const int* s_eoff
 }
 
 __device__ void plan_tiles(const DevCtx& c, int T, const int* s_eoff, int* sh) {
-    if (threadIdx.x < 2 * kXcds) c.tctr[threadIdx.x] = 0;
+    if (threadIdx.x < 2 * kSegs) c.tctr[threadIdx.x] = 0;
     __shared__ int s_t[2][kMaxExperts + 2];
     __shared__ long long s_c[2][kMaxExperts + 2];
     const int tid = threadIdx.x, G = c.G;
@@ -480,10 +481,6 @@ __device__ void plan_tiles(const DevCtx& c, int T, const int* s_eoff, int* sh) {
             const PlanGroup g = plan_group(c, T, s_eoff, j, mode);
             tiles += g.mt * g.nt;
             cost += (long long)g.nt * g.blocks * g.nk;
-            if (mode == 1) {
-                c.grp_M[j] = g.M;
-                c.grp_row0[j] = (c.has_shared && j == 0) ? 0 : s_eoff[j - c.has_shared];
-            }
         }
         // tile and cost prefixes over groups (costs fit in 31 bits for every
         // configuration the window accepts; scanned in two int halves anyway)
@@ -504,28 +501,42 @@ __device__ void plan_tiles(const DevCtx& c, int T, const int* s_eoff, int* sh) {
         }
         __syncthreads();
         int* tstart = mode == 1 ? c.tstart1 : c.tstart2;
-        int2* tinfo = mode == 1 ? c.tinfo1 : c.tinfo2;
+        int4* tinfo = mode == 1 ? c.tinfo1 : c.tinfo2;
         const int maxt = mode == 1 ? c.max_tiles1 : c.max_tiles2;
         for (int j = tid; j <= G; j += 256) tstart[j] = s_t[mode - 1][j];
         const int total = s_t[mode - 1][G];
         // each group's tiles, column tile outer, row tile inner; the threads
-        // of a wave split one group's tiles between them
+        // of a wave split one group's tiles between them.  Row tile mt holds
+        // the group's 32-row blocks [mt*b/mt_n, (mt+1)*b/mt_n).
         const int lane = tid & 63, wave = tid >> 6;
         for (int j = wave; j < G; j += 4) {
             const PlanGroup g = plan_group(c, T, s_eoff, j, mode);
             const int n = g.mt * g.nt, t0 = s_t[mode - 1][j];
+            const int row0 = (c.has_shared && j == 0) ? 0 : s_eoff[j - c.has_shared];
             for (int i = lane; i < n; i += 64) {
                 const int nt = i / g.mt, mt = i - nt * g.mt;
-                if (t0 + i < maxt) tinfo[t0 + i] = make_int2(j, (mt << 16) | nt);
+                const int b0 = mt * g.blocks / g.mt, b1 = (mt + 1) * g.blocks / g.mt;
+                const int m0 = b0 * 32, rows = min(b1 * 32, g.M) - m0;
+                if (t0 + i < maxt) tinfo[t0 + i] = make_int4(j, nt | ((b1 - b0) << 16), row0 + m0, rows);
             }
         }
-        // segment x starts at the first tile whose cost prefix is >= x*C/kXcds
+        // Segment boundaries.  Boundary b <= kXcds cuts the shared group
+        // (cost Ch, tiles [0, th)) at cost Ch*b/kXcds, boundary kXcds + b the
+        // routed groups at Ch + (C - Ch)*b/kXcds; each is the first tile
+        // whose cost prefix reaches the target.
         int* seg = mode == 1 ? c.seg1 : c.seg2;
-        if (tid <= kXcds) {
-            const long long C = s_c[mode - 1][G];
-            const long long S = C * tid / kXcds;
-            int res = total;
-            if (tid < kXcds && S < C) {
+        if (tid <= kSegs) {
+            const int hs = c.has_shared ? 1 : 0;
+            const long long C = s_c[mode - 1][G], Ch = s_c[mode - 1][hs];
+            const int th = s_t[mode - 1][hs];
+            const bool heavy = tid < kXcds;
+            const int lo_t = heavy ? 0 : th, hi_t = heavy ? th : total;
+            const long long S = heavy ? Ch * tid / kXcds : Ch + (C - Ch) * (tid - kXcds) / kXcds;
+            int res;
+            if (tid == 0) res = 0;
+            else if (tid == kXcds) res = th;
+            else if (tid == kSegs || S >= C) res = total;
+            else {
                 int lo = 0, hi = G;
                 while (hi - lo > 1) {
                     const int mid = (lo + hi) >> 1;
@@ -545,9 +556,8 @@ __device__ void plan_tiles(const DevCtx& c, int T, const int* s_eoff, int* sh) {
                     mt = 0;
                 }
                 res = s_t[mode - 1][lo] + nt * g.mt + mt;
-                if (res > total) res = total;
             }
-            seg[tid] = res;
+            seg[tid] = min(max(res, lo_t), hi_t);
         }
         __syncthreads();
     }
@@ -711,9 +721,11 @@ struct GemmTile {
     uint32_t tail_clamp;   // last 16-byte chunk of a row (K-tail loads)
     int tb;                // 32-row token blocks of the tile, 1..8
     int nk, kfull, Kdim;   // depth steps, steps fully inside K, K
-    int m0, rows, row0, Ig, nt;
+    int r0;                // first token row of the tile (h / y / ys row; fan-in token for shared rows)
+    int rows, Ig, nt;      // valid token rows, the group's intermediate width, column tile
     bool sh;
 };
+
 
 // Direct-to-LDS loads of depth step kt into `stage` (lane l of instruction
 // i fills bytes 16 l of the instruction's 1 KB: row 16(wid + 4i) + l/4,
@@ -783,7 +795,7 @@ __device__ __forceinline__ void gemm_mfma(f32x16 (&acc)[NV > 0 ? NV : 1][4], con
     for (int ib = 0; ib < NV; ++ib)
 #pragma unroll
         for (int jb = 0; jb < 4; ++jb)
-            acc[ib][jb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.w[jb], f.x[ib], acc[ib][jb], 0, 0, 0);
+            acc[ib][jb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.x[ib], f.w[jb], acc[ib][jb], 0, 0, 0);
 }
 
 // Scheduling pattern: each MFMA of the group followed by one of the slice's
@@ -834,40 +846,68 @@ __device__ __forceinline__ void gemm_step(f32x16 (&acc)[NV > 0 ? NV : 1][4], con
     __builtin_amdgcn_sched_barrier(0);
 }
 
-// Tile scheduler of a workgroup.  Tiles are taken dynamically: workgroup b
-// starts on the segment of its XCD (b % kXcds) and, when that is drained,
-// continues with the next segments.  Thread 0 owns the grabbing; each grab
-// is issued a whole tile before it is needed and resolved at the tile
-// boundary, then broadcast through LDS.
+// Tile scheduler of a workgroup.  Tiles are taken dynamically: a workgroup
+// on XCD x (x = b % kXcds: workgroups are dispatched to the XCDs round-
+// robin) takes tiles from the shared-expert segment x, then from the routed
+// segment x, then from the segments of XCD x+1, x+2, ...: every XCD starts
+// on its share of the longest tiles, and the tiles of one segment, which
+// share weight rows, stay in one XCD's L2 until other XCDs run dry.  Wave 0
+// owns the grabbing: the grab of the next tile is issued kGrabAhead depth
+// steps before the current tile ends (late enough that a workgroup does not
+// hold a tile that an idle one could run, early enough that the atomic has
+// returned when the tile ends), resolved at the tile boundary and broadcast
+// through LDS.  When the current segment is drained, one batch of loads
+// (a lane per segment) finds the next segment with tiles left.
+constexpr int kGrabAhead = 3;
+
 struct GemmSched {
     const int* seg;
     int* ctr;
-    int total;
-    int xi, tries, pend;  // thread 0 only
+    int x;                // this workgroup's XCD
+    int tries, si, pend;  // wave 0 only: position in the visiting order, its segment, the pending grab
 };
 
-__device__ __forceinline__ int sched_grab_slow(GemmSched& s) {  // next tile, or -1 when all are taken
-    while (s.tries < kXcds) {
-        const int lo = min(max(s.seg[s.xi], 0), s.total), hi = min(max(s.seg[s.xi + 1], lo), s.total);
-        const int t = lo + atomicAdd(&s.ctr[s.xi], 1);
-        if (t < hi) return t;
-        s.xi = (s.xi + 1) % kXcds;
-        ++s.tries;
+__device__ __forceinline__ int sched_seg(int x, int k) {  // k-th segment visited from XCD x
+    return (k & 1) * kXcds + (x + (k >> 1)) % kXcds;
+}
+
+// Next tile, or -1 when all are taken (wave 0, all lanes; uniform result).
+// Tile counters only grow, so a segment seen drained stays drained.
+__device__ __forceinline__ int sched_grab_slow(GemmSched& s, int lane) {
+    while (s.tries < kSegs) {
+        bool left = false;
+        if (lane >= s.tries && lane < kSegs) {
+            const int si = sched_seg(s.x, lane);
+            const int taken = __hip_atomic_load(&s.ctr[si], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            left = s.seg[si] + taken < s.seg[si + 1];
+        }
+        const uint64_t m = __ballot(left);
+        if (m == 0) {
+            s.tries = kSegs;
+            break;
+        }
+        s.tries = __builtin_ctzll(m);
+        s.si = sched_seg(s.x, s.tries);
+        int t = 0;
+        if (lane == 0) t = s.seg[s.si] + atomicAdd(&s.ctr[s.si], 1);
+        t = __builtin_amdgcn_readfirstlane(t);
+        if (t < __builtin_amdgcn_readfirstlane(s.seg[s.si + 1])) return t;
+        ++s.tries;  // lost the race for the segment's last tiles
     }
     return -1;
 }
 
-// Resolve the grab issued a tile ago and issue the following one.
-__device__ __forceinline__ int sched_next(GemmSched& s) {
-    const int lo = min(max(s.seg[s.xi], 0), s.total), hi = min(max(s.seg[s.xi + 1], lo), s.total);
-    int t = lo + s.pend;
-    if (t >= hi) {
-        s.xi = (s.xi + 1) % kXcds;
-        ++s.tries;
-        t = sched_grab_slow(s);
-    }
-    if (t >= 0) s.pend = atomicAdd(&s.ctr[s.xi], 1);
-    return t;
+__device__ __forceinline__ void sched_issue(GemmSched& s, int lane) {  // wave 0
+    if (s.tries < kSegs && lane == 0) s.pend = atomicAdd(&s.ctr[s.si], 1);
+}
+
+// Resolve the grab issued near the end of the current tile (wave 0).
+__device__ __forceinline__ int sched_next(GemmSched& s, int lane) {
+    if (s.tries >= kSegs) return -1;
+    const int t = __builtin_amdgcn_readfirstlane(s.seg[s.si] + s.pend);
+    if (t < __builtin_amdgcn_readfirstlane(s.seg[s.si + 1])) return t;
+    ++s.tries;
+    return sched_grab_slow(s, lane);
 }
 
 // Per-tile state of the wave: group, rows, depth, and the row offsets of its
@@ -876,21 +916,15 @@ template <int MODE>
 __device__ __forceinline__ void gemm_setup(const DevCtx& c, const Weights& w, int tile, int wid, int lrow, uint32_t lcx,
                                            GemmTile& t) {
     // (every value here is wave-uniform: keep them in scalar registers)
-    const int2 ti = (MODE == 1 ? c.tinfo1 : c.tinfo2)[__builtin_amdgcn_readfirstlane(tile)];
+    const int4 ti = (MODE == 1 ? c.tinfo1 : c.tinfo2)[__builtin_amdgcn_readfirstlane(tile)];
     const int j = __builtin_amdgcn_readfirstlane(ti.x), ty = __builtin_amdgcn_readfirstlane(ti.y);
-    const int mt = ty >> 16;
     t.nt = ty & 0xffff;
+    t.tb = ty >> 16;
+    t.r0 = __builtin_amdgcn_readfirstlane(ti.z);
+    t.rows = __builtin_amdgcn_readfirstlane(ti.w);
     t.sh = c.has_shared && j == 0;
     const int e = j - c.has_shared;
-    const int M = __builtin_amdgcn_readfirstlane(c.grp_M[j]);
-    t.row0 = __builtin_amdgcn_readfirstlane(c.grp_row0[j]);
     t.Ig = t.sh ? c.Is : c.I;
-    const int gb = (M + 31) >> 5;  // 32-row blocks of the group
-    const int ntm = (gb + kTileBlocks - 1) / kTileBlocks;
-    const int b0 = mt * gb / ntm, b1 = (mt + 1) * gb / ntm;
-    t.tb = b1 - b0;
-    t.m0 = b0 * 32;
-    t.rows = min(b1 * 32, M) - t.m0;  // valid token rows of the tile
     t.Kdim = MODE == 1 ? c.H : t.Ig;
     t.nk = (t.Kdim + kBK - 1) / kBK;
     t.kfull = t.Kdim / kBK;
@@ -905,11 +939,10 @@ __device__ __forceinline__ void gemm_setup(const DevCtx& c, const Weights& w, in
 #pragma unroll
     for (int i = 0; i < kXInstr; ++i) {
         const int r = (wid + kGemmWaves * i) * kRowsPerLoad + lrow;
-        int m = t.m0 + r;
-        if (m >= M) m = t.m0;
+        const int m = t.r0 + (r < t.rows ? r : 0);
         uint32_t o;
-        if (MODE == 1) o = (uint32_t)((t.sh ? c.sh_src[m] : c.psrc[t.row0 + m]) - (uint64_t)c.in_win);
-        else o = (uint32_t)(((int64_t)(t.sh ? m : t.row0 + m) * t.Ig) * 2);
+        if (MODE == 1) o = (uint32_t)((t.sh ? c.sh_src[m] : c.psrc[m]) - (uint64_t)c.in_win);
+        else o = (uint32_t)(((int64_t)m * t.Ig) * 2);
         t.xo[i] = o + lcx;
     }
 #pragma unroll
@@ -954,7 +987,10 @@ __device__ __forceinline__ void gemm_boundary(const DevCtx& c, const Weights& w,
     int* slot = (int*)(smem + kStages * kStageBytes);
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS reads are done
     AFD_BARRIER();
-    if (tid == 0) *slot = sched_next(sc);
+    if (wid == 0) {
+        const int t = sched_next(sc, tid);
+        if (tid == 0) *slot = t;
+    }
     __syncthreads();
     next = __builtin_amdgcn_readfirstlane(*slot);
     if (next >= 0) {
@@ -963,18 +999,36 @@ __device__ __forceinline__ void gemm_boundary(const DevCtx& c, const Weights& w,
     }
 }
 
-// Epilogue of a tile.  In accumulator (ib, jb) a lane holds token row
-// (wx + 2*ib)*32 + (lane & 31) of the tile and, for a = 0..3, the 4 output
-// columns 32*(weight block) + a*8 + (lane >> 5)*4 + 0..3 in registers
-// 4a..4a+3.  Straight-line code: a lane whose row or columns lie past the
-// tile's edge stores into the sink instead (no divergent branches, which
-// would keep every accumulator live across them).
+// Epilogue of a tile.  In accumulator (ib, jb) a lane holds output column
+// 32*(weight block) + (lane & 31) and, in register v = 0..15, token row
+// (wx + 2*ib)*32 + 8*(v/4) + 4*(lane/32) + v%4 of the tile.  One store
+// instruction thus writes 32 consecutive columns of each of two rows: whole
+// 64-byte segments.  The stores go through a buffer descriptor that spans
+// the tile's valid rows; lanes of a column past the output width add 2^31
+// to their offset.  The hardware drops out-of-range buffer stores, so the
+// code stays straight-line (a divergent branch would keep every
+// accumulator live across it).
 // One accumulator element read out of its AGPR.  Reading the accumulators
 // one at a time keeps them in AGPRs until they are needed (the compiler
 // would otherwise copy all of them to VGPRs at the end of the depth loop and
 // run out of registers).  The caller leaves at least 18 wait states between
 // the last MFMA and the first read (the hardware does not interlock an MFMA
 // result read by a VALU instruction).
+// Word 3 of a raw buffer descriptor on gfx9-family GPUs (32-bit data
+// format, stride 0: accesses are range-checked against the byte count).
+constexpr int kBufferFlags = 0x00020000;
+
+// Buffer descriptor over `bytes` bytes at `base` (wave-uniform values, made
+// explicitly scalar: a descriptor in vector registers would cost a
+// waterfall loop around every access).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t out_rsrc(const void* base, uint32_t bytes) {
+    const uint64_t a = (uint64_t)base;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+    return __builtin_amdgcn_make_buffer_rsrc((void*)(((uint64_t)hi << 32) | lo), 0,
+                                            (int)__builtin_amdgcn_readfirstlane(bytes), kBufferFlags);
+}
+
 __device__ __forceinline__ float agpr(float x) {
     float r;
     asm("v_accvgpr_read_b32 %0, %1" : "=v"(r) : "a"(x));
@@ -985,67 +1039,70 @@ template <int MODE, int NV>
 __device__ __forceinline__ void gemm_epilogue(const f32x16 (&acc)[NV > 0 ? NV : 1][4], const DevCtx& c,
                                               const GemmTile& t, int lane, int ww, int wx) {
     asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7");  // MFMA results settle (>= 18 wait states)
-    const int cq = (lane >> 5) * 4;
-    char* sink = c.sink + lane * 16;
+    const int lj = lane & 31;
+    const int rl = wx * 32 + 4 * (lane >> 5);  // this lane's first tile row in block ib = 0
     if (MODE == 1) {
         // h = silu(gate) * up, bf16; gate in weight blocks jb, up in jb + 2
-        uint16_t* base = t.sh ? c.hs : c.h + (int64_t)t.row0 * t.Ig;
+        const uint32_t ldb = (uint32_t)t.Ig * 2;
+        const __amdgpu_buffer_rsrc_t rs = out_rsrc((t.sh ? c.hs : c.h) + (int64_t)t.r0 * t.Ig, t.rows * ldb);
 #pragma unroll
-        for (int ib = 0; ib < NV; ++ib) {
-            const int row = (wx + 2 * ib) * 32 + (lane & 31);
-            const bool rv = row < t.rows;
-            uint16_t* dst = base + (int64_t)(t.m0 + (rv ? row : 0)) * t.Ig;
+        for (int jb = 0; jb < 2; ++jb) {
+            const int col = t.nt * (kBW / 2) + ww * 64 + jb * 32 + lj;
+            const uint32_t cb = (col < t.Ig ? 0u : 0x80000000u) + (uint32_t)col * 2 + (uint32_t)rl * ldb;
 #pragma unroll
-            for (int jb = 0; jb < 2; ++jb) {
+            for (int ib = 0; ib < NV; ++ib) {
 #pragma unroll
-                for (int a = 0; a < 4; ++a) {
-                    const int jj = t.nt * (kBW / 2) + ww * 64 + jb * 32 + cq + a * 8;
-                    float hv[4];
+                for (int v = 0; v < 16; v += 2) {
+                    float o[2];
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const float g = agpr(acc[ib][jb][4 * a + i]), u = agpr(acc[ib][jb + 2][4 * a + i]);
-                        hv[i] = g * __builtin_amdgcn_rcpf(1.f + __expf(-g)) * u;
+                    for (int q = 0; q < 2; ++q) {
+                        const float g = agpr(acc[ib][jb][v + q]), u = agpr(acc[ib][jb + 2][v + q]);
+                        o[q] = g * __builtin_amdgcn_rcpf(1.f + __expf(-g)) * u;
                     }
-                    u32x2* p = (rv && jj < t.Ig) ? (u32x2*)(dst + jj) : (u32x2*)sink;
-                    *p = (u32x2){pk_bf16(hv[0], hv[1]), pk_bf16(hv[2], hv[3])};
+                    const uint32_t pk = pk_bf16(o[0], o[1]);
+                    const uint32_t r = (uint32_t)(64 * ib + 8 * (v >> 2) + (v & 3));
+                    __builtin_amdgcn_raw_buffer_store_b16((uint16_t)pk, rs, (int)(cb + r * ldb), 0, 0);
+                    __builtin_amdgcn_raw_buffer_store_b16((uint16_t)(pk >> 16), rs, (int)(cb + (r + 1) * ldb), 0, 0);
                     __builtin_amdgcn_sched_barrier(0);
                 }
             }
         }
     } else if (t.sh) {
         // shared expert rows: fp32, token order
+        const uint32_t ldb = (uint32_t)c.H * 4;
+        const __amdgpu_buffer_rsrc_t rs = out_rsrc(c.ys + (int64_t)t.r0 * c.H, t.rows * ldb);
 #pragma unroll
-        for (int ib = 0; ib < NV; ++ib) {
-            const int row = (wx + 2 * ib) * 32 + (lane & 31);
-            const bool rv = row < t.rows;
-            float* dst = c.ys + (int64_t)(t.m0 + (rv ? row : 0)) * c.H;
+        for (int jb = 0; jb < 4; ++jb) {
+            const int col = t.nt * kBW + (ww * 4 + jb) * 32 + lj;
+            const uint32_t cb = (col < c.H ? 0u : 0x80000000u) + (uint32_t)col * 4 + (uint32_t)rl * ldb;
 #pragma unroll
-            for (int jb = 0; jb < 4; ++jb) {
+            for (int ib = 0; ib < NV; ++ib) {
 #pragma unroll
-                for (int a = 0; a < 4; ++a) {
-                    const int n = t.nt * kBW + (ww * 4 + jb) * 32 + cq + a * 8;
-                    f32x4* p = (rv && n < c.H) ? (f32x4*)(dst + n) : (f32x4*)sink;
-                    *p = (f32x4){agpr(acc[ib][jb][4 * a]), agpr(acc[ib][jb][4 * a + 1]), agpr(acc[ib][jb][4 * a + 2]),
-                                 agpr(acc[ib][jb][4 * a + 3])};
+                for (int v = 0; v < 16; v += 2) {
+                    const uint32_t r = (uint32_t)(64 * ib + 8 * (v >> 2) + (v & 3));
+                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(agpr(acc[ib][jb][v])), rs, (int)(cb + r * ldb), 0, 0);
+                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(agpr(acc[ib][jb][v + 1])), rs,
+                                                          (int)(cb + (r + 1) * ldb), 0, 0);
                     __builtin_amdgcn_sched_barrier(0);
                 }
             }
         }
     } else {
         // routed rows: bf16, permuted order
+        const uint32_t ldb = (uint32_t)c.H * 2;
+        const __amdgpu_buffer_rsrc_t rs = out_rsrc(c.y + (int64_t)t.r0 * c.H, t.rows * ldb);
 #pragma unroll
-        for (int ib = 0; ib < NV; ++ib) {
-            const int row = (wx + 2 * ib) * 32 + (lane & 31);
-            const bool rv = row < t.rows;
-            uint16_t* dst = c.y + (int64_t)(t.row0 + t.m0 + (rv ? row : 0)) * c.H;
+        for (int jb = 0; jb < 4; ++jb) {
+            const int col = t.nt * kBW + (ww * 4 + jb) * 32 + lj;
+            const uint32_t cb = (col < c.H ? 0u : 0x80000000u) + (uint32_t)col * 2 + (uint32_t)rl * ldb;
 #pragma unroll
-            for (int jb = 0; jb < 4; ++jb) {
+            for (int ib = 0; ib < NV; ++ib) {
 #pragma unroll
-                for (int a = 0; a < 4; ++a) {
-                    const int n = t.nt * kBW + (ww * 4 + jb) * 32 + cq + a * 8;
-                    u32x2* p = (rv && n < c.H) ? (u32x2*)(dst + n) : (u32x2*)sink;
-                    *p = (u32x2){pk_bf16(agpr(acc[ib][jb][4 * a]), agpr(acc[ib][jb][4 * a + 1])),
-                                 pk_bf16(agpr(acc[ib][jb][4 * a + 2]), agpr(acc[ib][jb][4 * a + 3]))};
+                for (int v = 0; v < 16; v += 2) {
+                    const uint32_t pk = pk_bf16(agpr(acc[ib][jb][v]), agpr(acc[ib][jb][v + 1]));
+                    const uint32_t r = (uint32_t)(64 * ib + 8 * (v >> 2) + (v & 3));
+                    __builtin_amdgcn_raw_buffer_store_b16((uint16_t)pk, rs, (int)(cb + r * ldb), 0, 0);
+                    __builtin_amdgcn_raw_buffer_store_b16((uint16_t)(pk >> 16), rs, (int)(cb + (r + 1) * ldb), 0, 0);
                     __builtin_amdgcn_sched_barrier(0);
                 }
             }
@@ -1076,6 +1133,9 @@ __device__ __forceinline__ void gemm_run(const DevCtx& c, const Weights& w, Gemm
     GemmFrags<NV> fa, fb;
     gemm_frags<MODE, NV>(fa, smem, 0, wl, tl);
     int kt = 0;
+    const int kg = min(t.kfull, max(t.nk - kGrabAhead, 0));
+    for (; kt < kg; ++kt) gemm_step<MODE, NV, NX, false>(acc, t, smem, kt, wid, lane, wl, tl, fa, fb);
+    if (wid == 0) sched_issue(sc, tid);  // the next tile
     for (; kt < t.kfull; ++kt) gemm_step<MODE, NV, NX, false>(acc, t, smem, kt, wid, lane, wl, tl, fa, fb);
     for (; kt < t.nk; ++kt) gemm_step<MODE, NV, NX, true>(acc, t, smem, kt, wid, lane, wl, tl, fa, fb);
 
@@ -1095,11 +1155,12 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(DevCtx c, const int* s
     int* slot = (int*)(smem + kStages * kStageBytes);
     GemmSched sc;
     sc.seg = MODE == 1 ? c.seg1 : c.seg2;
-    sc.ctr = c.tctr + (MODE - 1) * kXcds;
-    sc.total = (MODE == 1 ? c.tstart1 : c.tstart2)[c.G];
-    if (sc.total <= 0 || sc.total > (MODE == 1 ? c.max_tiles1 : c.max_tiles2)) return;  // nothing, or an insane plan
-    sc.xi = (int)(blockIdx.x % kXcds);
+    sc.ctr = c.tctr + (MODE - 1) * kSegs;
+    const int total = sc.seg[kSegs];
+    if (total <= 0 || total > (MODE == 1 ? c.max_tiles1 : c.max_tiles2)) return;  // nothing, or an insane plan
+    sc.x = (int)(blockIdx.x % kXcds);
     sc.tries = 0;
+    sc.si = 0;
     sc.pend = 0;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1120,10 +1181,9 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(DevCtx c, const int* s
     const uint32_t tl = (uint32_t)wx * kBlockBytes + fb;
 
     // first tile
-    if (tid == 0) {
-        const int t = sched_grab_slow(sc);
-        *slot = t;
-        if (t >= 0) sc.pend = atomicAdd(&sc.ctr[sc.xi], 1);  // the following tile, resolved a tile later
+    if (wid == 0) {
+        const int t0 = sched_grab_slow(sc, tid);
+        if (tid == 0) *slot = t0;
     }
     __syncthreads();
     int tile = __builtin_amdgcn_readfirstlane(*slot);
