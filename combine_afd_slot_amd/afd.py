@@ -36,7 +36,7 @@ HDR_WORDS = 12
 # Every symbol include/afd.h declares.
 EXPORTS = (
     "afd_layout_compute", "afd_window_create", "afd_window_destroy", "afd_window_layout",
-    "afd_slot_pack", "afd_ffn_run", "afd_slot_unpack", "afd_window_status", "afd_peer_status",
+    "afd_slot_pack", "afd_weights_pack", "afd_ffn_run", "afd_slot_unpack", "afd_window_status", "afd_peer_status",
     "afd_window_poll", "afd_debug_routing", "afd_debug_read", "afd_debug_write",
     "afd_profile_enable", "afd_profile_read", "afd_profile_kernel_name",
     "afd_header_encode", "afd_header_decode", "afd_last_error", "afd_status_string",
@@ -64,7 +64,7 @@ class Layout(ctypes.Structure):
                 ("slot_bytes", ctypes.c_int64), ("window_bytes", ctypes.c_int64), ("in_off", ctypes.c_int64),
                 ("in_slots_off", ctypes.c_int64), ("ret_off", ctypes.c_int64), ("ret_slots_off", ctypes.c_int64),
                 ("workspace_off", ctypes.c_int64), ("workspace_bytes", ctypes.c_int64),
-                ("total_bytes", ctypes.c_int64)]
+                ("total_bytes", ctypes.c_int64), ("packed_weight_bytes", ctypes.c_int64)]
 
 
 class RunInfo(ctypes.Structure):
@@ -100,7 +100,8 @@ def lib():
             "afd_window_destroy": [vp],
             "afd_window_layout": [vp, P(Layout)],
             "afd_slot_pack": [vp, i32, i32, i32, i32, vp, vp, u32, vp],
-            "afd_ffn_run": [vp, i32, i32, P(MoeWeights), vp],
+            "afd_weights_pack": [vp, P(MoeWeights), vp, i64, vp],
+            "afd_ffn_run": [vp, i32, i32, vp, vp],
             "afd_slot_unpack": [vp, i32, i32, i32, vp, vp],
             "afd_window_status": [vp, i32, vp, P(RunInfo)],
             "afd_peer_status": [vp, i32, i32, vp, P(RunInfo)],
@@ -179,9 +180,13 @@ def afd_slot_pack(win, peer, stage, layer_idx, seq_len, hidden_ptr, logits_ptr, 
                                       logits_ptr or None, flags, stream or None))
 
 
-def afd_ffn_run(win, stage, layer_idx, w13, w2, ws13=0, ws2=0, stream=0) -> int:
+def afd_weights_pack(win, w13, w2, ws13, ws2, dst, dst_bytes, stream=0) -> int:
     w = MoeWeights(w13, w2, ws13 or None, ws2 or None)
-    return _check(lib().afd_ffn_run(win, stage, layer_idx, ctypes.byref(w), stream or None))
+    return _check(lib().afd_weights_pack(win, ctypes.byref(w), dst or None, dst_bytes, stream or None))
+
+
+def afd_ffn_run(win, stage, layer_idx, packed_weights, stream=0) -> int:
+    return _check(lib().afd_ffn_run(win, stage, layer_idx, packed_weights or None, stream or None))
 
 
 def afd_slot_unpack(win, peer, stage, seq_len, out_ptr, stream=0) -> int:

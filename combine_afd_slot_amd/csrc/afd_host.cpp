@@ -138,8 +138,9 @@ WsLayout ws_layout(const afd_window_config& c) {
     w.inv = take(4 * np);
     w.tok_src = take(8 * tmax);
     w.sh_src = take(8 * tmax);
-    w.h = take(2 * np * c.intermediate);
-    w.hs = take(2 * tmax * (c.shared_intermediate > 0 ? c.shared_intermediate : 1));
+    // h and hs depth-block major: ceil(I/32) blocks of rows x 64 bytes
+    w.h = take(64 * np * ((c.intermediate + afd::kBK - 1) / afd::kBK));
+    w.hs = take(64 * tmax * (c.shared_intermediate > 0 ? (c.shared_intermediate + afd::kBK - 1) / afd::kBK : 1));
     w.y = take(2 * np * c.hidden);
     w.ys = take(4 * tmax * c.hidden);
     w.bytes = cur;
@@ -168,10 +169,31 @@ void layout_from(const afd_window_config& c, afd_layout* L, WsLayout* wl) {
     L->workspace_off = L->ret_off + afd::align_up(L->window_bytes);
     L->workspace_bytes = w.bytes;
     L->total_bytes = L->workspace_off + w.bytes;
+    int64_t off[4];
+    afd::packed_weight_layout(c, off, &L->packed_weight_bytes);
     if (wl) *wl = w;
 }
 
 }  // namespace
+
+namespace afd {
+void packed_weight_layout(const afd_window_config& c, int64_t off[4], int64_t* total) {
+    const int64_t E = c.num_experts, H = c.hidden, I = c.intermediate, Is = c.shared_intermediate;
+    const int64_t nk1 = (H + kBK - 1) / kBK, nt2 = (H + kBW - 1) / kBW;
+    const int64_t nt1 = (I + kBW / 2 - 1) / (kBW / 2), nk2 = (I + kBK - 1) / kBK;
+    const int64_t nt1s = (Is + kBW / 2 - 1) / (kBW / 2), nk2s = (Is + kBK - 1) / kBK;
+    int64_t cur = 0;
+    off[0] = cur;  // w13
+    cur += E * nt1 * nk1 * kWTileBytes;
+    off[1] = cur;  // ws13
+    cur += nt1s * nk1 * kWTileBytes;
+    off[2] = cur;  // w2
+    cur += E * nt2 * nk2 * kWTileBytes;
+    off[3] = cur;  // ws2
+    cur += nt2 * nk2s * kWTileBytes;
+    *total = cur;
+}
+}  // namespace afd
 
 struct afd_window {
     afd_window_config cfg;
@@ -215,6 +237,10 @@ void fill_ctx(afd_window* w) {
     d.NB = (int)((tmax + afd::kRouteChunk - 1) / afd::kRouteChunk) + c.num_peers;  // peer-aligned chunks
     d.max_tiles1 = (int)L.max_tiles1;
     d.max_tiles2 = (int)L.max_tiles2;
+    d.hrows = (int)(tmax * c.top_k);
+    d.hsrows = (int)tmax;
+    d.nt1 = (c.intermediate + afd::kBW / 2 - 1) / (afd::kBW / 2);
+    d.nt2 = (c.hidden + afd::kBW - 1) / afd::kBW;
     d.slot_bytes = w->lay.slot_bytes;
     for (int i = 0; i < AFD_NUM_FIELDS; ++i) d.foff[i] = w->lay.field_off[i];
     d.in_win = w->base + w->lay.in_off;
@@ -414,19 +440,36 @@ int32_t afd_slot_pack(afd_window* w, int32_t peer, int32_t stage, int32_t layer_
     return AFD_OK;
 }
 
-int32_t afd_ffn_run(afd_window* w, int32_t stage, int32_t layer_idx, const afd_moe_weights* weights,
+int32_t afd_weights_pack(afd_window* w, const afd_moe_weights* src, void* dst, int64_t dst_bytes, void* stream) {
+    if (!w || !src || !dst) return fail(AFD_ERR_INVALID, "NULL argument");
+    const afd_window_config& c = w->cfg;
+    if (!src->w13 || !src->w2) return fail(AFD_ERR_INVALID, "routed weights are NULL");
+    if (c.shared_intermediate > 0 && (!src->ws13 || !src->ws2))
+        return fail(AFD_ERR_INVALID, "shared weights are NULL");
+    if (!aligned(src->w13, 16) || !aligned(src->w2, 16) ||
+        (c.shared_intermediate > 0 && (!aligned(src->ws13, 16) || !aligned(src->ws2, 16))))
+        return fail(AFD_ERR_INVALID, "weights must be 16-byte aligned");
+    if (!aligned(dst, 256)) return fail(AFD_ERR_INVALID, "packed weights must be 256-byte aligned");
+    int64_t off[4], total = 0;
+    afd::packed_weight_layout(c, off, &total);
+    if (dst_bytes < total)
+        return fail(AFD_ERR_INVALID, "packed weights need %lld bytes, got %lld", (long long)total, (long long)dst_bytes);
+    hipError_t e = afd::launch_pack_weights(w->ctx, *src, (char*)dst, off, total, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "weight pack launch");
+    return AFD_OK;
+}
+
+int32_t afd_ffn_run(afd_window* w, int32_t stage, int32_t layer_idx, const void* packed_weights,
                     void* ffn_stream) {
-    if (!w || !weights) return fail(AFD_ERR_INVALID, "NULL argument");
+    if (!w || !packed_weights) return fail(AFD_ERR_INVALID, "NULL argument");
     const afd_window_config& c = w->cfg;
     if (stage < 0 || stage >= c.ring_depth) return fail(AFD_ERR_INVALID, "stage %d out of range", stage);
-    if (!weights->w13 || !weights->w2) return fail(AFD_ERR_INVALID, "routed weights are NULL");
-    if (c.shared_intermediate > 0 && (!weights->ws13 || !weights->ws2))
-        return fail(AFD_ERR_INVALID, "shared weights are NULL");
-    if (!aligned(weights->w13, 16) || !aligned(weights->w2, 16) ||
-        (c.shared_intermediate > 0 && (!aligned(weights->ws13, 16) || !aligned(weights->ws2, 16))))
-        return fail(AFD_ERR_INVALID, "weights must be 16-byte aligned");
-    afd::Weights wt{(const uint16_t*)weights->w13, (const uint16_t*)weights->w2, (const uint16_t*)weights->ws13,
-                    (const uint16_t*)weights->ws2};
+    if (!aligned(packed_weights, 256)) return fail(AFD_ERR_INVALID, "packed weights must be 256-byte aligned");
+    int64_t off[4], total = 0;
+    afd::packed_weight_layout(c, off, &total);
+    const char* pw = (const char*)packed_weights;
+    afd::Weights wt{pw + off[0], pw + off[2], c.shared_intermediate > 0 ? pw + off[1] : nullptr,
+                    c.shared_intermediate > 0 ? pw + off[3] : nullptr};
     hipEvent_t evs[AFD_PROFILE_SLOTS + 1] = {};
     hipEvent_t* ev = nullptr;
     if (w->profile) {

@@ -50,6 +50,8 @@ struct DevCtx {
     int G;           // GEMM groups: shared first (when present), then experts
     int NB;          // routing chunks for P*token_cap tokens
     int max_tiles1, max_tiles2;  // upper bounds of the GEMM tile counts (sanity limits)
+    int hrows, hsrows;           // row capacity of h (Tmax*K) and hs (Tmax)
+    int nt1, nt2;                // column tiles of a routed expert: gate/up ceil(I/128), down ceil(H/256)
     int64_t slot_bytes;
     int64_t foff[AFD_NUM_FIELDS];
     // windows (flags at offset 0 of each window)
@@ -86,20 +88,39 @@ struct DevCtx {
     uint64_t* tok_src; // [Tmax] address of token t's routed_x row
     uint64_t* sh_src;  // [Tmax] address of shared row t's shared_x row
     // expert activations
-    uint16_t* h;       // [Tmax*K][I]  bf16 SwiGLU activations, permuted order
-    uint16_t* hs;      // [Tmax][Is]   bf16 shared activations
+    // h and hs are stored depth-block major: element (row, j) at
+    // ((j / 32) * rows + row) * 32 + j % 32, so the rows of one 32-deep
+    // step of a down-GEMM tile are one contiguous run.
+    uint16_t* h;       // [ceil(I/32)][Tmax*K][32]  bf16 SwiGLU activations, permuted order
+    uint16_t* hs;      // [ceil(Is/32)][Tmax][32]   bf16 shared activations
     uint16_t* y;       // [Tmax*K][H]  bf16 routed expert outputs, permuted order
     float* ys;         // [Tmax][H]    fp32 shared expert output, token (= shared row) order
 };
 
+// One layer's packed weights (written by k_pack_weights): tiles of 256
+// weight rows x 32 depth values, 16 KB each, a row's 64 bytes with chunk c
+// of the row stored at chunk position c ^ swz4(row) (the LDS order of the
+// GEMM stages).  Tile (column tile nt, depth step kt) of
+//   w13  [E][nt1][nk1]: rows 0..127 gate rows nt*128 + r, rows 128..255 the
+//        same up rows (rows past I zero); nk1 = ceil(H/32)
+//   ws13 [ceil(Is/128)][nk1]: the same for the shared expert
+//   w2   [E][nt2][nk2]: rows nt*256 + r of W2 (rows past H zero); nk2 = ceil(I/32)
+//   ws2  [nt2][ceil(Is/32)]
+// Depth past K is zero.
+constexpr int kWTileBytes = kBW * kBK * 2;  // 16 KB
 struct Weights {
-    const uint16_t* w13;
-    const uint16_t* w2;
-    const uint16_t* ws13;
-    const uint16_t* ws2;
+    const char* w13;
+    const char* w2;
+    const char* ws13;
+    const char* ws2;
 };
 
+// Byte offsets of the four packed regions and the total (host).
+void packed_weight_layout(const afd_window_config& c, int64_t off[4], int64_t* total);
+
 // Launchers (afd_kernels.hip).  All return the launch's hipError_t.
+hipError_t launch_pack_weights(const DevCtx& c, const afd_moe_weights& src, char* dst, const int64_t off[4],
+                               int64_t total, hipStream_t st);
 hipError_t launch_pack(const DevCtx& c, int peer, int stage, int layer, int seq_len, const void* hidden,
                        const float* logits, uint32_t flags, int seq, hipStream_t st);
 hipError_t launch_unpack(const DevCtx& c, int peer, int stage, int seq_len, int expect_echo, void* out,

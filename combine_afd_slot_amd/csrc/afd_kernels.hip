@@ -709,6 +709,58 @@ static_assert(kGemmWaves == 4 && kTileBlocks == 8 && kBK == 32 && kStages == 4,
 // instruction (16 rows each).
 __device__ inline int swz4(int r) { return ((r >> 1) ^ (r >> 2)) & 3; }
 
+// ---------------------------------------------------------------------------
+// Weight packing (one-time per layer): one thread per 16-byte chunk of the
+// packed tiles (the layout next to struct Weights).  Chunk position p of
+// row r of a tile holds depth values kt*32 + 8*(p ^ swz4(r)) .. +7 of the
+// tile's weight row r, or zeros past the matrix.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_pack_weights(DevCtx c, afd_moe_weights src, char* dst, int64_t off1,
+                                                      int64_t off2, int64_t off3, int64_t total) {
+    const int64_t H = c.H, I = c.I, Is = c.Is;
+    const int64_t nk1 = (H + kBK - 1) / kBK, nk2 = (I + kBK - 1) / kBK, nk2s = (Is + kBK - 1) / kBK;
+    const int64_t nt1 = c.nt1, nt1s = (Is + kBW / 2 - 1) / (kBW / 2), nt2 = c.nt2;
+    const int64_t nchunks = total / 16;
+    for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < nchunks; q += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t byte = q * 16;
+        const int region = byte < off1 ? 0 : byte < off2 ? 1 : byte < off3 ? 2 : 3;
+        const int64_t local = byte - (region == 0 ? 0 : region == 1 ? off1 : region == 2 ? off2 : off3);
+        const int64_t tile = local / kWTileBytes;
+        const int within = (int)(local % kWTileBytes);
+        const int r = within / kRowBytes, p = (within % kRowBytes) / 16;
+        const int64_t k0 = (int64_t)(tile % (region < 2 ? nk1 : region == 2 ? nk2 : nk2s)) * kBK + 8 * (p ^ swz4(r));
+        const int64_t tt = tile / (region < 2 ? nk1 : region == 2 ? nk2 : nk2s);  // column tile (and expert)
+        const uint16_t* row = nullptr;
+        if (region == 0 || region == 1) {
+            const int64_t Ig = region == 0 ? I : Is, nt = region == 0 ? tt % nt1 : tt % nt1s;
+            const int64_t jj = nt * (kBW / 2) + (r & (kBW / 2 - 1));
+            if (jj < Ig && k0 < H) {
+                const int64_t srow = (r < kBW / 2 ? 0 : Ig) + jj;
+                row = region == 0 ? (const uint16_t*)src.w13 + ((tt / nt1) * 2 * I + srow) * H
+                                  : (const uint16_t*)src.ws13 + srow * H;
+            }
+        } else {
+            const int64_t Ig = region == 2 ? I : Is, nt = tt % nt2;
+            const int64_t n = nt * kBW + r;
+            if (n < H && k0 < Ig)
+                row = region == 2 ? (const uint16_t*)src.w2 + ((tt / nt2) * H + n) * I : (const uint16_t*)src.ws2 + n * Is;
+        }
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (row) v = *(const u32x4*)(row + k0);
+        *(u32x4*)(dst + byte) = v;
+    }
+}
+
+hipError_t launch_pack_weights(const DevCtx& c, const afd_moe_weights& src, char* dst, const int64_t off[4],
+                               int64_t total, hipStream_t st) {
+    const int64_t nchunks = total / 16;
+    const int64_t blocks = std::min<int64_t>((nchunks + 255) / 256, 65536);
+    if (blocks <= 0) return hipSuccess;
+    hipLaunchKernelGGL(k_pack_weights, dim3((unsigned)blocks), dim3(256), 0, st, c, src, dst, off[1], off[2], off[3],
+                       total);
+    return hipGetLastError();
+}
+
 // What one wave needs to know about the current tile.
 struct GemmTile {
     const char* abase;  // token-row base (inbound window, h or hs)
@@ -716,9 +768,11 @@ struct GemmTile {
     // Load instruction i of the wave covers stage rows 16*(wid + 4i) .. +15;
     // its lane offset (row offset + this lane's swizzled chunk) is fixed for
     // the tile, the depth step moves the wave-uniform base.
-    uint32_t xo[kXInstr], wo[kWInstr];
+    uint32_t xo[kXInstr];
+    uint32_t astep;        // token-side bytes per depth step (64 in slot rows, rows*64 in h / hs)
+    uint32_t wlane;        // this lane's byte in a packed weight tile's first KB of the wave
     uint32_t cx;           // this lane's logical chunk, as a byte offset
-    uint32_t tail_clamp;   // last 16-byte chunk of a row (K-tail loads)
+    uint32_t tail_clamp;   // last 16-byte chunk of a slot row (K-tail loads of the gate/up GEMM)
     int tb;                // 32-row token blocks of the tile, 1..8
     int nk, kfull, Kdim;   // depth steps, steps fully inside K, K
     int r0;                // first token row of the tile (h / y / ys row; fan-in token for shared rows)
@@ -732,22 +786,28 @@ struct GemmTile {
 // LDS chunk l % 4, which holds the swizzled logical chunk the lane
 // fetches).  NX of the 4 token-row loads are issued, enough for the tile's
 // blocks: NX = ceil(tb / 2) covers rows below 64 NX >= 32 tb (rows past the
-// tile's blocks are valid rows that land in LDS rows the MFMAs do not read).  A step past
-// the end of K (K not a multiple of 32) loads each row's last 16 bytes in
-// place of the missing chunks -- valid, finite data -- and the token-row
-// copies of those chunks are zeroed in LDS before the MFMAs.
-template <int NX>
+// tile's blocks are valid rows that land in LDS rows the MFMAs do not read).
+// The weight rows come from the packed tile of the step, already in LDS
+// order: each instruction copies one contiguous KB.  In the gate/up GEMM a
+// step past the end of K (K not a multiple of 32) loads each token row's
+// last 16 bytes in place of the missing chunks -- valid, finite data -- and
+// the token-row copies of those chunks are zeroed in LDS before the MFMAs;
+// h and hs rows are stored in whole 32-deep blocks.
+template <int MODE, int NX>
 __device__ __forceinline__ void gemm_issue(const GemmTile& t, char* stage, int wid, int kt) {
-    const uint32_t kb = (uint32_t)kt * kRowBytes;
-    const char* ab = t.abase + kb;
-    const char* bb = t.bbase + kb;
-    const uint32_t fix = kb + t.cx > t.tail_clamp ? t.tail_clamp - kb - t.cx : 0u;
+    const char* ab = t.abase + (int64_t)kt * t.astep;
+    const char* bb = t.bbase + (int64_t)kt * kWTileBytes;
+    uint32_t fix = 0u;
+    if (MODE == 1) {
+        const uint32_t kb = (uint32_t)kt * kRowBytes;
+        fix = kb + t.cx > t.tail_clamp ? t.tail_clamp - kb - t.cx : 0u;
+    }
 #pragma unroll
     for (int i = 0; i < NX; ++i)
         dma16(ab + (t.xo[i] + fix), (lds_ptr_t)(stage + (wid + kGemmWaves * i) * 1024));
 #pragma unroll
     for (int i = 0; i < kWInstr; ++i)
-        dma16(bb + (t.wo[i] + fix), (lds_ptr_t)(stage + kXStageBytes + (wid + kGemmWaves * i) * 1024));
+        dma16(bb + (t.wlane + i * kGemmWaves * 1024), (lds_ptr_t)(stage + kXStageBytes + (wid + kGemmWaves * i) * 1024));
 }
 
 
@@ -830,7 +890,7 @@ __device__ __forceinline__ void gemm_step(f32x16 (&acc)[NV > 0 ? NV : 1][4], con
                                           GemmFrags<NV>& b) {
     if (TAIL) gemm_tail(a, t, kt, 0, lane);
     gemm_frags<MODE, NV>(b, smem + (kt & (kStages - 1)) * kStageBytes, 1, wl, tl);
-    gemm_issue<NX>(t, smem + ((kt + kStages - 1) & (kStages - 1)) * kStageBytes, wid, min(kt + kStages - 1, t.nk - 1));
+    gemm_issue<MODE, NX>(t, smem + ((kt + kStages - 1) & (kStages - 1)) * kStageBytes, wid, min(kt + kStages - 1, t.nk - 1));
     gemm_mfma(acc, a);
     gemm_interleave<4 * NV, 4 + NV, NX + kWInstr>();
     __builtin_amdgcn_sched_barrier(0);
@@ -929,12 +989,22 @@ __device__ __forceinline__ void gemm_setup(const DevCtx& c, const Weights& w, in
     t.nk = (t.Kdim + kBK - 1) / kBK;
     t.kfull = t.Kdim / kBK;
     t.tail_clamp = (uint32_t)t.Kdim * 2 - 16;
-    // Row addresses as 32-bit byte offsets from a per-tile base (the window
-    // and every buffer stay below 4 GiB: checked at create).
-    if (MODE == 1) t.abase = c.in_win;
-    else t.abase = (const char*)(t.sh ? c.hs : c.h);
-    if (MODE == 1) t.bbase = (const char*)(t.sh ? w.ws13 : w.w13 + (int64_t)e * 2 * t.Ig * c.H);
-    else t.bbase = (const char*)(t.sh ? w.ws2 : w.w2 + (int64_t)e * c.H * t.Ig);
+    // Token rows: slot rows through their row addresses (gate/up; 32-bit
+    // byte offsets from the window, which stays below 4 GiB: checked at
+    // create) or rows of the depth-block-major h / hs (down).
+    if (MODE == 1) {
+        t.abase = c.in_win;
+        t.astep = kRowBytes;
+    } else {
+        t.abase = (const char*)(t.sh ? c.hs : c.h);
+        t.astep = (uint32_t)(t.sh ? c.hsrows : c.hrows) * kRowBytes;
+    }
+    // this group's packed weight tiles of column tile nt: nk consecutive tiles
+    if (MODE == 1) t.bbase = t.sh ? w.ws13 + (int64_t)t.nt * t.nk * kWTileBytes
+                                  : w.w13 + ((int64_t)e * c.nt1 + t.nt) * t.nk * kWTileBytes;
+    else t.bbase = t.sh ? w.ws2 + (int64_t)t.nt * t.nk * kWTileBytes
+                        : w.w2 + ((int64_t)e * c.nt2 + t.nt) * t.nk * kWTileBytes;
+    t.wlane = (uint32_t)wid * 1024u + (uint32_t)(threadIdx.x & 63) * 16u;
     t.cx = lcx;
 #pragma unroll
     for (int i = 0; i < kXInstr; ++i) {
@@ -942,39 +1012,25 @@ __device__ __forceinline__ void gemm_setup(const DevCtx& c, const Weights& w, in
         const int m = t.r0 + (r < t.rows ? r : 0);
         uint32_t o;
         if (MODE == 1) o = (uint32_t)((t.sh ? c.sh_src[m] : c.psrc[m]) - (uint64_t)c.in_win);
-        else o = (uint32_t)(((int64_t)m * t.Ig) * 2);
+        else o = (uint32_t)m * kRowBytes;
         t.xo[i] = o + lcx;
-    }
-#pragma unroll
-    for (int i = 0; i < kWInstr; ++i) {
-        const int r = (wid + kGemmWaves * i) * kRowsPerLoad + lrow;  // weight row of the stage
-        uint32_t o;
-        if (MODE == 1) {
-            int jj = t.nt * (kBW / 2) + (r & (kBW / 2 - 1));
-            if (jj >= t.Ig) jj = 0;
-            o = (uint32_t)((int64_t)((r / (kBW / 2)) * t.Ig + jj) * c.H * 2);
-        } else {
-            int n = t.nt * kBW + r;
-            if (n >= c.H) n = 0;
-            o = (uint32_t)((int64_t)n * t.Ig * 2);
-        }
-        t.wo[i] = o + lcx;
     }
 }
 
 // The first kStages-1 steps of a tile into stages 0 .. (the ring must be
 // free; a tile shorter than the ring reloads its last step).
-template <int NX>
+template <int MODE, int NX>
 __device__ __forceinline__ void gemm_prologue_nx(const GemmTile& t, char* smem, int wid) {
 #pragma unroll
-    for (int p = 0; p < kStages - 1; ++p) gemm_issue<NX>(t, smem + p * kStageBytes, wid, min(p, t.nk - 1));
+    for (int p = 0; p < kStages - 1; ++p) gemm_issue<MODE, NX>(t, smem + p * kStageBytes, wid, min(p, t.nk - 1));
 }
+template <int MODE>
 __device__ __forceinline__ void gemm_prologue(const GemmTile& t, char* smem, int wid) {
     switch ((t.tb + 1) >> 1) {
-        case 1: gemm_prologue_nx<1>(t, smem, wid); break;
-        case 2: gemm_prologue_nx<2>(t, smem, wid); break;
-        case 3: gemm_prologue_nx<3>(t, smem, wid); break;
-        default: gemm_prologue_nx<4>(t, smem, wid); break;
+        case 1: gemm_prologue_nx<MODE, 1>(t, smem, wid); break;
+        case 2: gemm_prologue_nx<MODE, 2>(t, smem, wid); break;
+        case 3: gemm_prologue_nx<MODE, 3>(t, smem, wid); break;
+        default: gemm_prologue_nx<MODE, 4>(t, smem, wid); break;
     }
 }
 
@@ -995,7 +1051,7 @@ __device__ __forceinline__ void gemm_boundary(const DevCtx& c, const Weights& w,
     next = __builtin_amdgcn_readfirstlane(*slot);
     if (next >= 0) {
         gemm_setup<MODE>(c, w, next, wid, lrow, lcx, tn);
-        gemm_prologue(tn, smem, wid);
+        gemm_prologue<MODE>(tn, smem, wid);
     }
 }
 
@@ -1042,13 +1098,16 @@ __device__ __forceinline__ void gemm_epilogue(const f32x16 (&acc)[NV > 0 ? NV : 
     const int lj = lane & 31;
     const int rl = wx * 32 + 4 * (lane >> 5);  // this lane's first tile row in block ib = 0
     if (MODE == 1) {
-        // h = silu(gate) * up, bf16; gate in weight blocks jb, up in jb + 2
-        const uint32_t ldb = (uint32_t)t.Ig * 2;
-        const __amdgpu_buffer_rsrc_t rs = out_rsrc((t.sh ? c.hs : c.h) + (int64_t)t.r0 * t.Ig, t.rows * ldb);
+        // h = silu(gate) * up, bf16; gate in weight blocks jb, up in jb + 2.
+        // Column block jb is one 32-deep block of h: rows of 64 bytes.
+        const int64_t hrows = t.sh ? c.hsrows : c.hrows;
+        char* hb = (char*)(t.sh ? c.hs : c.h);
 #pragma unroll
         for (int jb = 0; jb < 2; ++jb) {
-            const int col = t.nt * (kBW / 2) + ww * 64 + jb * 32 + lj;
-            const uint32_t cb = (col < t.Ig ? 0u : 0x80000000u) + (uint32_t)col * 2 + (uint32_t)rl * ldb;
+            const int col0 = t.nt * (kBW / 2) + ww * 64 + jb * 32;
+            const __amdgpu_buffer_rsrc_t rs =
+                out_rsrc(hb + ((int64_t)(col0 >> 5) * hrows + t.r0) * kRowBytes, (uint32_t)t.rows * kRowBytes);
+            const uint32_t cb = (col0 + lj < t.Ig ? 0u : 0x80000000u) + (uint32_t)lj * 2 + (uint32_t)rl * kRowBytes;
 #pragma unroll
             for (int ib = 0; ib < NV; ++ib) {
 #pragma unroll
@@ -1061,8 +1120,8 @@ __device__ __forceinline__ void gemm_epilogue(const f32x16 (&acc)[NV > 0 ? NV : 
                     }
                     const uint32_t pk = pk_bf16(o[0], o[1]);
                     const uint32_t r = (uint32_t)(64 * ib + 8 * (v >> 2) + (v & 3));
-                    __builtin_amdgcn_raw_buffer_store_b16((uint16_t)pk, rs, (int)(cb + r * ldb), 0, 0);
-                    __builtin_amdgcn_raw_buffer_store_b16((uint16_t)(pk >> 16), rs, (int)(cb + (r + 1) * ldb), 0, 0);
+                    __builtin_amdgcn_raw_buffer_store_b16((uint16_t)pk, rs, (int)(cb + r * kRowBytes), 0, 0);
+                    __builtin_amdgcn_raw_buffer_store_b16((uint16_t)(pk >> 16), rs, (int)(cb + (r + 1) * kRowBytes), 0, 0);
                     __builtin_amdgcn_sched_barrier(0);
                 }
             }
@@ -1190,7 +1249,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(DevCtx c, const int* s
     GemmTile t;
     if (tile >= 0) {
         gemm_setup<MODE>(c, w, tile, wid, lrow, lcx, t);
-        gemm_prologue(t, smem, wid);
+        gemm_prologue<MODE>(t, smem, wid);
     }
     while (tile >= 0) {
         int next;

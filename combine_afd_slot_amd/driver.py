@@ -57,7 +57,15 @@ class FfnSession:
             self.ws2 = _dev_bf16(torch, inputs["Ws2"], self.dev)
         else:
             self.ws13 = self.ws2 = None
+        # the layer's weights in GEMM tile order (what afd_ffn_run reads)
+        nbytes = self.layout.packed_weight_bytes
+        self.packed = torch.empty(nbytes, dtype=torch.uint8, device=self.dev)
         torch.cuda.synchronize(self.dev)
+        afd.afd_weights_pack(self.win, self.w13.data_ptr(), self.w2.data_ptr(),
+                             self.ws13.data_ptr() if self.ws13 is not None else 0,
+                             self.ws2.data_ptr() if self.ws2 is not None else 0,
+                             self.packed.data_ptr(), nbytes, self.ffn_stream.cuda_stream)
+        self.ffn_stream.synchronize()
 
     # ---------------------------------------------------------------- steps
     def pack(self, peer, stage=0, layer=0, flags=0, seq_len=None):
@@ -74,10 +82,7 @@ class FfnSession:
                 s.synchronize()
 
     def run(self, stage=0, layer=0):
-        return afd.afd_ffn_run(self.win, stage, layer, self.w13.data_ptr(), self.w2.data_ptr(),
-                               self.ws13.data_ptr() if self.ws13 is not None else 0,
-                               self.ws2.data_ptr() if self.ws2 is not None else 0,
-                               self.ffn_stream.cuda_stream)
+        return afd.afd_ffn_run(self.win, stage, layer, self.packed.data_ptr(), self.ffn_stream.cuda_stream)
 
     def unpack(self, peer, stage=0):
         n = self.wl.seq_lens[peer]

@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define AFD_ABI_VERSION 1
+#define AFD_ABI_VERSION 2
 
 /* Header flags bit 1: shutdown sentinel ("Window and slot layout"). */
 #define AFD_FLAG_SHUTDOWN 0x2u
@@ -143,6 +143,7 @@ typedef struct afd_layout {
     int64_t workspace_off;               /* FFN workspace                            */
     int64_t workspace_bytes;
     int64_t total_bytes;                 /* the whole allocation                     */
+    int64_t packed_weight_bytes;         /* one layer's weights in GEMM tile order   */
 } afd_layout;
 
 /* Status of the last device-side operation of a stage (afd_window_status) or
@@ -164,6 +165,19 @@ typedef struct afd_moe_weights {
     const void* ws13;
     const void* ws2;
 } afd_moe_weights;
+
+/* Repack one layer's expert weights (the row-major afd_moe_weights layout
+ * above) into the order the grouped GEMMs stream them, on `stream`.  A
+ * one-time step when a layer's weights are loaded; afd_ffn_run reads only
+ * the packed copy ("Attention gate and FFN expert compute": the expert FFN
+ * weights of a layer stay resident on the FFN rank).  The packed format is
+ * internal to this library version (it holds every weight once, padded to
+ * whole GEMM tiles with zeros): dst must hold layout.packed_weight_bytes
+ * bytes, 256-byte aligned, caller-owned, and must not overlap src.
+ * Errors: AFD_ERR_INVALID (NULL or misaligned pointers, dst_bytes too small,
+ * shared weights missing when shared_intermediate > 0). */
+int32_t afd_weights_pack(afd_window* w, const afd_moe_weights* src, void* dst, int64_t dst_bytes,
+                         void* stream);
 
 /* Header fields for the host codec (tests; the device uses the same code). */
 typedef struct afd_header_fields {
@@ -211,8 +225,12 @@ int32_t afd_slot_pack(afd_window* w, int32_t peer, int32_t stage, int32_t layer_
  * and group sizes stay on the device.  Device-side failures land in the
  * stage's status word (afd_window_status).  Peers must have enqueued their
  * packs on other streams before this call can complete; keep the number of
- * concurrently waiting streams within the device's hardware queues. */
-int32_t afd_ffn_run(afd_window* w, int32_t stage, int32_t layer_idx, const afd_moe_weights* weights,
+ * concurrently waiting streams within the device's hardware queues.
+ * packed_weights: the layer's weights as written by afd_weights_pack for
+ * this window's configuration (borrowed; 256-byte aligned).
+ * Errors: AFD_ERR_INVALID (NULL window or weights, misaligned weights, stage
+ * out of range). */
+int32_t afd_ffn_run(afd_window* w, int32_t stage, int32_t layer_idx, const void* packed_weights,
                     void* ffn_stream);
 
 /* Attention side, peer `peer`: wait (bounded, on the device) for the return

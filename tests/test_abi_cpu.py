@@ -28,7 +28,7 @@ def test_library_exports_every_declared_symbol():
     missing = [s for s in declared if not hasattr(L, s)]
     assert not missing, missing
     assert sorted(afd.EXPORTS) == declared
-    assert afd.afd_abi_version() == 1
+    assert afd.afd_abi_version() == 2
 
 
 CFGS = [
@@ -63,6 +63,22 @@ def test_layout_matches_reference(kw):
     assert L.total_bytes == L.workspace_off + L.workspace_bytes
     for off in (L.in_off, L.in_slots_off, L.ret_off, L.ret_slots_off, L.workspace_off):
         assert off % 256 == 0
+
+
+@pytest.mark.parametrize("kw", CFGS)
+def test_packed_weight_bytes(kw):
+    # every weight once, in whole tiles of 256 rows x 32 depth values (16 KB):
+    # gate/up tiles of 128 gate + 128 up rows, down tiles of 256 output rows
+    cfg = afd.make_config(**kw)
+    L = afd.afd_layout_compute(cfg)
+    E, H, I, Is = kw["num_experts"], kw["hidden"], kw["intermediate"], kw["shared_intermediate"]
+    cdiv = lambda a, b: -(-a // b)
+    tiles = (E * cdiv(I, 128) * cdiv(H, 32) + cdiv(Is, 128) * cdiv(H, 32)
+             + E * cdiv(H, 256) * cdiv(I, 32) + cdiv(H, 256) * cdiv(Is, 32))
+    assert L.packed_weight_bytes == tiles * 16384
+    # no padding when the widths are whole tiles
+    if I % 128 == 0 and Is % 128 == 0 and H % 256 == 0:
+        assert L.packed_weight_bytes == 2 * (E * 3 * I * H + 3 * Is * H)
 
 
 @pytest.mark.parametrize("kw", CFGS)

@@ -55,6 +55,10 @@ SMALL = [
     # many peers, E=256 (four logits per lane), K=8
     small_workload("e256", seq_lens=(5, 17, 0, 29, 3, 64, 1, 40), hidden=256, num_experts=256, top_k=8,
                    intermediate=128, shared_intermediate=128, token_cap=64),
+    # depth tails in both GEMMs (hidden, intermediate and the shared width not
+    # multiples of the 32-deep step; the shared width below one step)
+    small_workload("depth_tails", seq_lens=(45, 20), hidden=72, num_experts=7, top_k=3, intermediate=40,
+                   shared_intermediate=24, token_cap=48),
 ]
 
 

@@ -204,6 +204,28 @@ def test_host_errors_capacity_ring_shape():
         assert s.status().status == 0
 
 
+def test_weight_pack_and_run_argument_errors():
+    s, inp = _session()
+    with s:
+        n = s.layout.packed_weight_bytes
+        ws = (s.w13.data_ptr(), s.w2.data_ptr(), s.ws13.data_ptr(), s.ws2.data_ptr())
+        for args in [(*ws, 0, n),                              # no destination
+                     (*ws, s.packed.data_ptr(), n - 16),        # too small
+                     (*ws, s.packed.data_ptr() + 16, n),        # not 256-byte aligned
+                     (0, *ws[1:], s.packed.data_ptr(), n),      # no routed gate/up weights
+                     (*ws[:2], 0, ws[3], s.packed.data_ptr(), n)]:  # shared weights missing
+            with pytest.raises(afd.AfdError) as ei:
+                afd.afd_weights_pack(s.win, *args, s.ffn_stream.cuda_stream)
+            assert ei.value.code == afd.AFD_ERR_INVALID
+        for pw in (0, s.packed.data_ptr() + 16):
+            with pytest.raises(afd.AfdError) as ei:
+                afd.afd_ffn_run(s.win, 0, 0, pw, s.ffn_stream.cuda_stream)
+            assert ei.value.code == afd.AFD_ERR_INVALID
+        # the rejected calls left the window usable
+        s.step()
+        assert s.status().status == 0
+
+
 def test_repeated_execution_and_ring_depth_two(orc):
     wl = small_workload("ring2", seq_lens=(21, 0, 34), hidden=128, num_experts=8, top_k=2, intermediate=64,
                         shared_intermediate=64, token_cap=40, ring_depth=2)
