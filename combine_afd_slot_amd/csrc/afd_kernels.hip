@@ -439,16 +439,15 @@ __global__ __launch_bounds__(256) void k_scan(DevCtx c, const int* status) {
 }
 
 // ---------------------------------------------------------------------------
-// GEMM tile plan (run by one workgroup of 256 threads).  Group j: 0 is the
-// shared expert over all T tokens, 1..E the routed experts.  A group of M
-// rows has b = ceil(M/32) row blocks split evenly over ceil(b/kTileBlocks)
-// row tiles and, for the gate/up GEMM, ceil(Ig/(kBW/2)) column tiles (kBW/2
-// gate + the same kBW/2 up rows of W13), for the down GEMM ceil(H/kBW).
-// Tiles are numbered group-major, column tile next, row tile fastest (row
-// tiles of one column tile share their weight rows).  The cost of a tile is
-// (32-row blocks it holds) x (depth steps).  The shared group's tiles and
-// the routed groups' tiles are each cut into kXcds segments of equal cost,
-// one of each per XCD.
+// GEMM tile plan.  Group j: 0 is the shared expert over all T tokens (when
+// present), then the routed experts.  A group of M rows has b = ceil(M/32)
+// row blocks split evenly over ceil(b/kTileBlocks) row tiles and, for the
+// gate/up GEMM, ceil(Ig/(kBW/2)) column tiles (kBW/2 gate + the same kBW/2
+// up rows of W13), for the down GEMM ceil(H/kBW).  Tiles are numbered
+// group-major, column tile next, row tile fastest (row tiles of one column
+// tile share their weight rows).  The cost of a tile is (32-row blocks it
+// holds) x (depth steps).  The shared group's tiles and the routed groups'
+// tiles are each cut into kXcds segments of equal cost, one of each per XCD.
 // ---------------------------------------------------------------------------
 struct PlanGroup {
     int M, mt, blocks, nt, nk;
@@ -467,68 +466,89 @@ __device__ inline PlanGroup plan_group(const DevCtx& c, int T, const int* s_eoff
     return g;
 }
 
-__device__ void plan_tiles(const DevCtx& c, int T, const int* s_eoff, int* sh) {
-    if (threadIdx.x < 2 * kSegs) c.tctr[threadIdx.x] = 0;
-    __shared__ int s_t[2][kMaxExperts + 2];
-    __shared__ long long s_c[2][kMaxExperts + 2];
+// Block-wide exclusive prefix sums of four int64 values per thread.  `sh`
+// holds 16 values.
+__device__ void block_excl_scan4(long long (&v)[4], long long* sh) {
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    long long x[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) x[q] = v[q];
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const long long y = __shfl_up(x[q], o);
+            if (lane >= o) x[q] += y;
+        }
+    }
+    if (lane == 63)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) sh[wid * 4 + q] = x[q];
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        long long base = 0;
+        for (int w = 0; w < wid; ++w) base += sh[w * 4 + q];
+        v[q] = x[q] - v[q] + base;
+    }
+    __syncthreads();
+}
+
+// Tile and cost prefixes over the groups of both GEMMs into LDS:
+// s_t[m][j] / s_c[m][j] = tiles / cost of GEMM m+1 before group j (j = G:
+// the totals).
+__device__ void plan_prefix(const DevCtx& c, int T, const int* s_eoff, int (*s_t)[kMaxExperts + 2],
+                            long long (*s_c)[kMaxExperts + 2], long long* sh) {
     const int tid = threadIdx.x, G = c.G;
     const int per = (G + 255) / 256;
     const int j0 = tid * per, j1 = min(G, j0 + per);
-    for (int mode = 1; mode <= 2; ++mode) {
-        int tiles = 0;
-        long long cost = 0;
-        for (int j = j0; j < j1; ++j) {
-            const PlanGroup g = plan_group(c, T, s_eoff, j, mode);
-            tiles += g.mt * g.nt;
-            cost += (long long)g.nt * g.blocks * g.nk;
+    long long v[4] = {0, 0, 0, 0};  // tiles of GEMM 1, 2; cost of GEMM 1, 2
+    for (int j = j0; j < j1; ++j) {
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+            const PlanGroup g = plan_group(c, T, s_eoff, j, m + 1);
+            v[m] += g.mt * g.nt;
+            v[2 + m] += (long long)g.nt * g.blocks * g.nk;
         }
-        // tile and cost prefixes over groups (costs fit in 31 bits for every
-        // configuration the window accepts; scanned in two int halves anyway)
-        int rt = block_excl_scan(tiles, sh);
-        int rc_lo = block_excl_scan((int)(cost & 0xffff), sh);
-        int rc_hi = block_excl_scan((int)(cost >> 16), sh);
-        long long rc = ((long long)rc_hi << 16) + rc_lo;
-        for (int j = j0; j < j1; ++j) {
-            const PlanGroup g = plan_group(c, T, s_eoff, j, mode);
-            s_t[mode - 1][j] = rt;
-            s_c[mode - 1][j] = rc;
-            rt += g.mt * g.nt;
-            rc += (long long)g.nt * g.blocks * g.nk;
+    }
+    block_excl_scan4(v, sh);
+    for (int j = j0; j < j1; ++j) {
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+            const PlanGroup g = plan_group(c, T, s_eoff, j, m + 1);
+            s_t[m][j] = (int)v[m];
+            s_c[m][j] = v[2 + m];
+            v[m] += g.mt * g.nt;
+            v[2 + m] += (long long)g.nt * g.blocks * g.nk;
         }
-        if (tid == 255) {
-            s_t[mode - 1][G] = rt;
-            s_c[mode - 1][G] = rc;
+    }
+    if (tid == 255)
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+            s_t[m][G] = (int)v[m];
+            s_c[m][G] = v[2 + m];
         }
-        __syncthreads();
-        int* tstart = mode == 1 ? c.tstart1 : c.tstart2;
-        int4* tinfo = mode == 1 ? c.tinfo1 : c.tinfo2;
-        const int maxt = mode == 1 ? c.max_tiles1 : c.max_tiles2;
-        for (int j = tid; j <= G; j += 256) tstart[j] = s_t[mode - 1][j];
-        const int total = s_t[mode - 1][G];
-        // each group's tiles, column tile outer, row tile inner; the threads
-        // of a wave split one group's tiles between them.  Row tile mt holds
-        // the group's 32-row blocks [mt*b/mt_n, (mt+1)*b/mt_n).
-        const int lane = tid & 63, wave = tid >> 6;
-        for (int j = wave; j < G; j += 4) {
-            const PlanGroup g = plan_group(c, T, s_eoff, j, mode);
-            const int n = g.mt * g.nt, t0 = s_t[mode - 1][j];
-            const int row0 = (c.has_shared && j == 0) ? 0 : s_eoff[j - c.has_shared];
-            for (int i = lane; i < n; i += 64) {
-                const int nt = i / g.mt, mt = i - nt * g.mt;
-                const int b0 = mt * g.blocks / g.mt, b1 = (mt + 1) * g.blocks / g.mt;
-                const int m0 = b0 * 32, rows = min(b1 * 32, g.M) - m0;
-                if (t0 + i < maxt) tinfo[t0 + i] = make_int4(j, nt | ((b1 - b0) << 16), row0 + m0, rows);
-            }
-        }
-        // Segment boundaries.  Boundary b <= kXcds cuts the shared group
-        // (cost Ch, tiles [0, th)) at cost Ch*b/kXcds, boundary kXcds + b the
-        // routed groups at Ch + (C - Ch)*b/kXcds; each is the first tile
-        // whose cost prefix reaches the target.
-        int* seg = mode == 1 ? c.seg1 : c.seg2;
+    __syncthreads();
+}
+
+// The plan's global tables (one workgroup): tile prefixes, the zeroed tile
+// counters and the segment boundaries.  Boundary b <= kXcds cuts the shared
+// group (cost Ch, tiles [0, th)) at cost Ch*b/kXcds, boundary kXcds + b the
+// routed groups at Ch + (C - Ch)*b/kXcds; each is the first tile whose cost
+// prefix reaches the target.
+__device__ void plan_publish(const DevCtx& c, int T, const int* s_eoff, int (*s_t)[kMaxExperts + 2],
+                             long long (*s_c)[kMaxExperts + 2]) {
+    const int tid = threadIdx.x, G = c.G;
+    if (tid < 2 * kSegs) c.tctr[tid] = 0;
+    for (int m = 0; m < 2; ++m) {
+        int* tstart = m == 0 ? c.tstart1 : c.tstart2;
+        for (int j = tid; j <= G; j += 256) tstart[j] = s_t[m][j];
+        int* seg = m == 0 ? c.seg1 : c.seg2;
         if (tid <= kSegs) {
             const int hs = c.has_shared ? 1 : 0;
-            const long long C = s_c[mode - 1][G], Ch = s_c[mode - 1][hs];
-            const int th = s_t[mode - 1][hs];
+            const int total = s_t[m][G];
+            const long long C = s_c[m][G], Ch = s_c[m][hs];
+            const int th = s_t[m][hs];
             const bool heavy = tid < kXcds;
             const int lo_t = heavy ? 0 : th, hi_t = heavy ? th : total;
             const long long S = heavy ? Ch * tid / kXcds : Ch + (C - Ch) * (tid - kXcds) / kXcds;
@@ -540,13 +560,13 @@ __device__ void plan_tiles(const DevCtx& c, int T, const int* s_eoff, int* sh) {
                 int lo = 0, hi = G;
                 while (hi - lo > 1) {
                     const int mid = (lo + hi) >> 1;
-                    if (s_c[mode - 1][mid] <= S) lo = mid;
+                    if (s_c[m][mid] <= S) lo = mid;
                     else hi = mid;
                 }
                 // skip groups with no tiles that share the same cost start
-                while (lo + 1 < G && s_c[mode - 1][lo + 1] <= S) ++lo;
-                const PlanGroup g = plan_group(c, T, s_eoff, lo, mode);
-                const long long u = (S - s_c[mode - 1][lo] + g.nk - 1) / g.nk;  // in 32-row blocks
+                while (lo + 1 < G && s_c[m][lo + 1] <= S) ++lo;
+                const PlanGroup g = plan_group(c, T, s_eoff, lo, m + 1);
+                const long long u = (S - s_c[m][lo] + g.nk - 1) / g.nk;  // in 32-row blocks
                 int nt = (int)(u / g.blocks);
                 const int rem = (int)(u - (long long)nt * g.blocks);
                 // first row tile that starts at or after block `rem`
@@ -555,33 +575,67 @@ __device__ void plan_tiles(const DevCtx& c, int T, const int* s_eoff, int* sh) {
                     ++nt;
                     mt = 0;
                 }
-                res = s_t[mode - 1][lo] + nt * g.mt + mt;
+                res = s_t[m][lo] + nt * g.mt + mt;
             }
             seg[tid] = min(max(res, lo_t), hi_t);
         }
-        __syncthreads();
+    }
+}
+
+// This workgroup's share of the tile descriptors of both GEMMs (the tile
+// list is split evenly over the grid): tile i belongs to the group whose
+// tile range holds i; row tile mt of a group holds its 32-row blocks
+// [mt*b/mt_n, (mt+1)*b/mt_n).
+__device__ void plan_fill(const DevCtx& c, int T, const int* s_eoff, int (*s_t)[kMaxExperts + 2]) {
+    const int G = c.G;
+    for (int m = 0; m < 2; ++m) {
+        int4* tinfo = m == 0 ? c.tinfo1 : c.tinfo2;
+        const int maxt = m == 0 ? c.max_tiles1 : c.max_tiles2;
+        const int total = min(s_t[m][G], maxt);
+        const int per = (total + (int)gridDim.x - 1) / (int)gridDim.x;
+        const int i1 = min(total, ((int)blockIdx.x + 1) * per);
+        for (int i = (int)blockIdx.x * per + threadIdx.x; i < i1; i += blockDim.x) {
+            int lo = 0, hi = G;  // s_t[m][lo] <= i < s_t[m][hi]
+            while (hi - lo > 1) {
+                const int mid = (lo + hi) >> 1;
+                if (s_t[m][mid] <= i) lo = mid;
+                else hi = mid;
+            }
+            const PlanGroup g = plan_group(c, T, s_eoff, lo, m + 1);
+            const int local = i - s_t[m][lo];
+            const int nt = local / g.mt, mt = local - nt * g.mt;
+            const int b0 = mt * g.blocks / g.mt, b1 = (mt + 1) * g.blocks / g.mt;
+            const int row0 = (c.has_shared && lo == 0) ? 0 : s_eoff[lo - c.has_shared];
+            tinfo[i] = make_int4(lo, nt | ((b1 - b0) << 16), row0 + b0 * 32, min(b1 * 32, g.M) - b0 * 32);
+        }
     }
 }
 
 // ---------------------------------------------------------------------------
 // a3 (second half): the stable dispatch permutation ("[RFC]: Async GPU
 // Connector", "Data flow": argsort(stable=True) over the flattened ids,
-// bincount, cumsum).  Each workgroup scans the expert counts into the expert
-// offsets (workgroup 0 also publishes them, with the GEMM group table: group
-// 0 is the shared expert over all T tokens, groups 1..E the routed experts,
-// and the tile prefixes of both GEMMs).  Pair f = t*K + k goes to
-// eoff[e] + #{f' < f : ids_f' = e}: the chunk's base per expert from k_scan,
-// then, inside the chunk, one thread per expert walks the pairs in flat order.
+// bincount, cumsum).  Every workgroup scans the expert counts into the
+// expert offsets and the GEMM plan prefixes and writes its share of the
+// tile descriptors (workgroup 0 also publishes the offsets, the tile
+// prefixes and the segments).  Pair f = t*K + k goes to eoff[e] + #{f' < f :
+// ids_f' = e}: the chunk's base per expert from k_scan plus the number of
+// earlier tokens of the chunk that chose e (a token's K experts are
+// distinct, so that is the pair's rank inside the chunk): a bit mask of the
+// chunk's tokens per expert and a population count.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_permute(DevCtx c, const int* status) {
     if (*status != AFD_OK) return;
+    static_assert(kRouteChunk <= 32 && kRouteChunk * kMaxTopK <= 256, "chunk masks and one pair per thread");
     const int T = *c.Tptr;
     int t0 = 0, t1 = 0, p = 0;
     const bool have = chunk_range(c, blockIdx.x, t0, t1, p);
-    if (blockIdx.x != 0 && !have) return;
     __shared__ int sh[16];
+    __shared__ long long sh4[16];
     __shared__ int s_eoff[kMaxExperts + 1];
-    __shared__ int lids[kRouteChunk * kMaxTopK];
+    __shared__ int s_t[2][kMaxExperts + 2];
+    __shared__ long long s_c[2][kMaxExperts + 2];
+    __shared__ uint32_t emask[kMaxExperts];
+    __shared__ uint64_t ltok[kRouteChunk];
     const int E = c.E, K = c.K, tid = threadIdx.x;
     {
         const int per = (E + 255) / 256;
@@ -595,31 +649,32 @@ __global__ __launch_bounds__(256) void k_permute(DevCtx c, const int* status) {
         }
         if (tid == 255) s_eoff[E] = run;
     }
+    for (int e = tid; e < E; e += 256) emask[e] = 0u;
     __syncthreads();
+    plan_prefix(c, T, s_eoff, s_t, s_c, sh4);
     if (blockIdx.x == 0) {
         for (int e = tid; e <= E; e += 256) c.eoff[e] = s_eoff[e];
-        plan_tiles(c, T, s_eoff, sh);
-        if (!have) return;
+        plan_publish(c, T, s_eoff, s_t, s_c);
     }
-    __shared__ uint64_t ltok[kRouteChunk];
+    plan_fill(c, T, s_eoff, s_t);
+    if (!have) return;
     const int np = (t1 - t0) * K;
-    for (int i = tid; i < np; i += 256) lids[i] = c.ids[(int64_t)t0 * K + i];
     if (tid < t1 - t0) ltok[tid] = c.tok_src[t0 + tid];
+    int e = 0;
+    if (tid < np) {
+        e = c.ids[(int64_t)t0 * K + tid];
+        atomicOr(&emask[e], 1u << (tid / K));
+    }
     __syncthreads();
-    const int npairs = T * K;
-    for (int e = tid; e < E; e += 256) {
-        int pos = s_eoff[e] + c.blk_base[(int64_t)e * c.NB + blockIdx.x];
-        for (int i = 0; i < np; ++i) {
-            if (lids[i] == e) {
-                const int f = t0 * K + i;
-                if (pos < npairs) {
-                    c.perm[pos] = f;
-                    c.psrc[pos] = ltok[i / K];
-                }
-                c.inv[f] = pos;
-                ++pos;
-            }
+    if (tid < np) {
+        const int tl = tid / K;
+        const int pos = s_eoff[e] + c.blk_base[(int64_t)e * c.NB + blockIdx.x] + __popc(emask[e] & ((1u << tl) - 1u));
+        const int f = t0 * K + tid;
+        if (pos < T * K) {
+            c.perm[pos] = f;
+            c.psrc[pos] = ltok[tl];
         }
+        c.inv[f] = pos;
     }
 }
 
