@@ -208,8 +208,13 @@ __global__ __launch_bounds__(64) void k_wait(DevCtx c, int s, int layer, long lo
         }
         if (err == AFD_OK) {
             afd_header_fields h;
-            const int32_t* hw = (const int32_t*)(slot_ptr(c, c.in_win, p, s) + c.foff[AFD_FIELD_HEADER]);
-            err = header_decode(hw, c.E, &h);
+            // the fixed words in one batch of loads (the header is 256-byte aligned)
+            static_assert(AFD_HDR_WORDS == 12, "three 16-byte loads");
+            const u32x4* hq = (const u32x4*)(slot_ptr(c, c.in_win, p, s) + c.foff[AFD_FIELD_HEADER]);
+            u32x4 hv[3];
+#pragma unroll
+            for (int i = 0; i < 3; ++i) hv[i] = hq[i];
+            err = header_decode((const int32_t*)hv, c.E, &h);
             if (err == AFD_OK) err = inbound_check(h, p, s, layer, c.token_cap, f);
             if (err == AFD_OK) {
                 ntok = h.num_tokens;
@@ -238,9 +243,9 @@ __global__ __launch_bounds__(64) void k_wait(DevCtx c, int s, int layer, long lo
             for (int q = 0; q < c.P; ++q) {
                 c.seen_in[q * c.R + s] = s_flag[q];
                 c.cur_seq[q] = s_flag[q];
-                c.off[q + 1] = c.off[q] + s_ntok[q];
+                T += s_ntok[q];
+                c.off[q + 1] = T;
             }
-            T = c.off[c.P];
         }
         *c.Tptr = status == AFD_OK ? T : 0;
         st[0] = status;
@@ -275,34 +280,59 @@ __device__ int block_excl_scan(int v, int* sh) {
 // chunk may be shorter).  Chunks are numbered in fan-in token order, so the
 // flat pair order f = t*K + k runs through the chunks in order.
 // ---------------------------------------------------------------------------
-__device__ inline int num_chunks(const DevCtx& c) {
-    int n = 0;
-    for (int q = 0; q < c.P; ++q) n += (c.off[q + 1] - c.off[q] + kRouteChunk - 1) / kRouteChunk;
-    return n;
+// Peer q's chunk count and the inclusive prefix over peers 0..q, in lane q
+// of the calling wavefront (all 64 lanes active; P <= 64): one round of
+// loads and a wave prefix sum.
+__device__ inline void peer_chunks(const DevCtx& c, int& lo, int& n, int& nc, int& inc) {
+    const int lane = threadIdx.x & 63;
+    lo = 0;
+    n = 0;
+    if (lane < c.P) {
+        lo = c.off[lane];
+        n = c.off[lane + 1] - lo;
+    }
+    nc = (n + kRouteChunk - 1) / kRouteChunk;
+    inc = nc;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(inc, o);
+        if (lane >= o) inc += y;
+    }
 }
 
+// Chunk b's token range [t0, t1) and its peer p (false: no such chunk).
 __device__ inline bool chunk_range(const DevCtx& c, int b, int& t0, int& t1, int& p) {
-    int cum = 0;
-    for (int q = 0; q < c.P; ++q) {
-        const int n = c.off[q + 1] - c.off[q];
-        const int nc = (n + kRouteChunk - 1) / kRouteChunk;
-        if (b < cum + nc) {
-            p = q;
-            t0 = c.off[q] + (b - cum) * kRouteChunk;
-            t1 = min(c.off[q + 1], t0 + kRouteChunk);
-            return true;
-        }
-        cum += nc;
-    }
-    return false;
+    int lo, n, nc, inc;
+    peer_chunks(c, lo, n, nc, inc);
+    const uint64_t m = __ballot((int)(threadIdx.x & 63) < c.P && b >= inc - nc && b < inc);
+    if (m == 0) return false;
+    p = __builtin_ctzll(m);
+    const int base = __shfl(lo, p), first = __shfl(inc - nc, p), np = __shfl(n, p);
+    t0 = base + (b - first) * kRouteChunk;
+    t1 = min(base + np, t0 + kRouteChunk);
+    return true;
+}
+
+// Sum over the 64 lanes of a wavefront with DPP moves (no LDS): butterflies
+// inside each row of 16 lanes, then the row sums carried across rows with
+// the row broadcasts; lane 63 ends up with the total.
+__device__ inline float wave_sum(float x) {
+    x += __builtin_amdgcn_update_dpp(0.f, x, 0xB1, 0xF, 0xF, false);   // quad_perm [1,0,3,2]
+    x += __builtin_amdgcn_update_dpp(0.f, x, 0x4E, 0xF, 0xF, false);   // quad_perm [2,3,0,1]
+    x += __builtin_amdgcn_update_dpp(0.f, x, 0x141, 0xF, 0xF, false);  // row_half_mirror
+    x += __builtin_amdgcn_update_dpp(0.f, x, 0x140, 0xF, 0xF, false);  // row_mirror
+    x += __builtin_amdgcn_update_dpp(0.f, x, 0x142, 0xA, 0xF, false);  // row_bcast:15 into rows 1, 3
+    x += __builtin_amdgcn_update_dpp(0.f, x, 0x143, 0xC, 0xF, false);  // row_bcast:31 into rows 2, 3
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 63));
 }
 
 // ---------------------------------------------------------------------------
-// a2: routing.  One wavefront per token; each workgroup takes one chunk.
-// The order is (larger logit first, equal logits: lower expert index first;
-// -0.0 equals +0.0 under float compare).  The wave stages the token's E
-// logits in LDS and every lane ranks its own logits against all E of them;
-// the K experts of rank < K are the top-K, and rank k is the k-th selected.
+// a2: routing.  One workgroup per chunk, one wavefront per token.  The
+// order is (larger logit first, equal logits: lower expert index first;
+// -0.0 equals +0.0 under float compare).  Every lane ranks its own logits
+// against all E of the token's logits, broadcast one at a time from the
+// lane that holds them (a scalar read of a lane: no memory round trip); the
+// K experts of rank < K are the top-K, and rank k is the k-th selected.
 // Weights: w_k = exp(L_k - L_max) / sum over the selected of exp(L - L_max)
 // (the softmax restricted to the top-K and renormalised); without
 // renormalisation the denominator runs over all E experts.  ("[RFC]: Async
@@ -310,69 +340,76 @@ __device__ inline bool chunk_range(const DevCtx& c, int b, int& t0, int& t1, int
 // a single group.)  The chunk's expert histogram goes to blk_counts[e][b].
 // ---------------------------------------------------------------------------
 template <int EPL>
-__global__ __launch_bounds__(256) void k_route(DevCtx c, int* status, int s) {
+__global__ __launch_bounds__(64 * kRouteChunk) void k_route(DevCtx c, int* status, int s) {
     if (*status != AFD_OK) return;
     int t_begin, t_end, p;
     if (!chunk_range(c, blockIdx.x, t_begin, t_end, p)) return;
-    constexpr int TPW = kRouteChunk / 4;
     __shared__ int hist[kMaxExperts];
-    __shared__ float lv[4][kMaxExperts];
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
     const int E = c.E, K = c.K;
     for (int e = threadIdx.x; e < E; e += blockDim.x) hist[e] = 0;
     const char* slot = slot_ptr(c, c.in_win, p, s);
-    float v[TPW][EPL];
-#pragma unroll
-    for (int i = 0; i < TPW; ++i) {
-        const int t = t_begin + wave * TPW + i;
-        const float* lg = (const float*)(slot + c.foff[AFD_FIELD_ROUTE_TABLE]) +
-                          (int64_t)(min(t, t_end - 1) - c.off[p]) * E;
+    const int t = t_begin + (int)(threadIdx.x >> 6);
+    const bool live = t < t_end;
+    const int r = min(t, t_end - 1) - c.off[p];  // row of the token in its peer's slot
+    float v[EPL];
+    {
+        const float* lg = (const float*)(slot + c.foff[AFD_FIELD_ROUTE_TABLE]) + (int64_t)r * E;
 #pragma unroll
         for (int j = 0; j < EPL; ++j) {
             const int e = lane + 64 * j;
             const float x = e < E ? lg[e] : -INFINITY;
-            v[i][j] = x == x ? x : -INFINITY;  // NaN logits are out of contract; keep the order total
+            v[j] = x == x ? x : -INFINITY;  // NaN logits are out of contract; keep the order total
         }
     }
+    // the token's row addresses and the check of its shared row (one FFN
+    // replica owns every shared row: shared_idx must be 0..n_p-1)
+    bool si_bad = false;
+    if (live && lane == 0) {
+        c.tok_src[t] = (uint64_t)(slot + c.foff[AFD_FIELD_ROUTED_X] + (int64_t)r * c.H * 2);
+        c.sh_src[t] = (uint64_t)(slot + c.foff[AFD_FIELD_SHARED_X] + (int64_t)r * c.H * 2);
+        si_bad = ((const int*)(slot + c.foff[AFD_FIELD_SHARED_IDX]))[r] != r;
+    }
     __syncthreads();  // hist zeroed
-    float* L = lv[wave];
-#pragma unroll
-    for (int i = 0; i < TPW; ++i) {
-        const int t = t_begin + wave * TPW + i;
-        if (t >= t_end) break;
-#pragma unroll
-        for (int j = 0; j < EPL; ++j)
-            if (lane + 64 * j < E) L[lane + 64 * j] = v[i][j];
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    if (live) {
+        // Logits past E are -inf and have indices past every valid one, so
+        // they never raise a valid logit's rank.
         int rank[EPL];
 #pragma unroll
         for (int j = 0; j < EPL; ++j) rank[j] = 0;
-        for (int q = 0; q < E; ++q) {
-            const float x = L[q];
 #pragma unroll
-            for (int j = 0; j < EPL; ++j) {
-                const int e = lane + 64 * j;
-                rank[j] += (x > v[i][j] || (x == v[i][j] && q < e)) ? 1 : 0;
+        for (int jj = 0; jj < EPL; ++jj) {
+            if (64 * jj >= E) break;
+#pragma unroll 8
+            for (int sl = 0; sl < 64; ++sl) {
+                const float x = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v[jj]), sl));
+                const int q = sl + 64 * jj;
+#pragma unroll
+                for (int j = 0; j < EPL; ++j) {
+                    const int e = lane + 64 * j;
+                    rank[j] += (x > v[j] || (x == v[j] && q < e)) ? 1 : 0;
+                }
             }
         }
-        // the maximum is the value of rank 0
-        float m = -INFINITY;
+        // the maximum is the logit of rank 0 (exactly one lane holds it)
+        float top = -INFINITY;
+        bool has_top = false;
 #pragma unroll
-        for (int j = 0; j < EPL; ++j) m = fmaxf(m, (lane + 64 * j < E) ? v[i][j] : -INFINITY);
-#pragma unroll
-        for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+        for (int j = 0; j < EPL; ++j)
+            if (lane + 64 * j < E && rank[j] == 0) {
+                top = v[j];
+                has_top = true;
+            }
+        const float m = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(top), __builtin_ctzll(__ballot(has_top))));
         float ex[EPL], part = 0.f;
 #pragma unroll
         for (int j = 0; j < EPL; ++j) {
             const int e = lane + 64 * j;
             const bool sel = e < E && rank[j] < K;
-            ex[j] = (e < E) ? expf(v[i][j] - m) : 0.f;
+            ex[j] = (e < E) ? expf(v[j] - m) : 0.f;
             if (c.renorm ? sel : (e < E)) part += ex[j];
         }
-#pragma unroll
-        for (int o = 32; o >= 1; o >>= 1) part += __shfl_xor(part, o);
+        part = wave_sum(part);
 #pragma unroll
         for (int j = 0; j < EPL; ++j) {
             const int e = lane + 64 * j;
@@ -382,16 +419,8 @@ __global__ __launch_bounds__(256) void k_route(DevCtx c, int* status, int s) {
                 atomicAdd(&hist[e], 1);
             }
         }
-        if (lane == 0) {
-            const int r = t - c.off[p];
-            c.tok_src[t] = (uint64_t)(slot + c.foff[AFD_FIELD_ROUTED_X] + (int64_t)r * c.H * 2);
-            c.sh_src[t] = (uint64_t)(slot + c.foff[AFD_FIELD_SHARED_X] + (int64_t)r * c.H * 2);
-            // one FFN replica owns every shared row: shared_idx must be 0..n_p-1
-            const int si = ((const int*)(slot + c.foff[AFD_FIELD_SHARED_IDX]))[r];
-            if (si != r) atomicCAS(status, AFD_OK, AFD_ERR_HEADER);
-        }
-        __builtin_amdgcn_wave_barrier();  // L is rewritten by the next token
     }
+    if (si_bad) atomicCAS(status, AFD_OK, AFD_ERR_HEADER);
     __syncthreads();
     for (int e = threadIdx.x; e < E; e += blockDim.x) c.blk_counts[(int64_t)e * c.NB + blockIdx.x] = hist[e];
 }
@@ -410,10 +439,11 @@ __global__ __launch_bounds__(256) void k_scan(DevCtx c, const int* status) {
     __shared__ int pc[kMaxPeers];
     __shared__ int pchunk[kMaxPeers + 1];
     const int e = blockIdx.x;
-    if (threadIdx.x == 0) {
-        pchunk[0] = 0;
-        for (int q = 0; q < c.P; ++q)
-            pchunk[q + 1] = pchunk[q] + (c.off[q + 1] - c.off[q] + kRouteChunk - 1) / kRouteChunk;
+    if (threadIdx.x < 64) {
+        int lo, n, nc, inc;
+        peer_chunks(c, lo, n, nc, inc);
+        if (threadIdx.x == 0) pchunk[0] = 0;
+        if ((int)threadIdx.x < c.P) pchunk[threadIdx.x + 1] = inc;
     }
     if (threadIdx.x < kMaxPeers) pc[threadIdx.x] = 0;
     __syncthreads();
@@ -1395,27 +1425,30 @@ __global__ __launch_bounds__(256) void k_combine(DevCtx c, const int* status, in
 // no reply and so creates no wait.
 __global__ __launch_bounds__(64) void k_publish(DevCtx c, const int* status, int s, int layer) {
     if (*status != AFD_OK) return;
-    const int p = threadIdx.x;
-    if (p >= c.P) return;
+    const int p = blockIdx.x, lane = threadIdx.x;  // one wavefront per peer
     const int n_p = c.off[p + 1] - c.off[p];
     if (n_p == 0) return;
     const int idx = p * c.R + s;
+    int32_t* w = (int32_t*)(slot_ptr(c, c.ret_win, p, s) + c.foff[AFD_FIELD_HEADER]);
     const int rs = c.ret_seq[idx] + 1;
-    c.ret_seq[idx] = rs;
-    afd_header_fields f;
-    f.flags = 0;
-    f.seq = rs;
-    f.echo_seq = c.cur_seq[p];
-    f.layer_idx = layer;
-    f.stage_idx = s;
-    f.num_tokens = n_p;
-    f.routed_tokens = n_p;
-    f.shared_tokens = n_p;
-    f.src_peer = p;
-    f.n_counts = c.E;
-    header_encode(f, c.peer_counts + p * c.E, (int32_t*)(slot_ptr(c, c.ret_win, p, s) + c.foff[AFD_FIELD_HEADER]));
-    __threadfence();
-    st_release((int*)c.ret_win + idx, rs);
+    for (int e = lane; e < c.E; e += 64) w[AFD_HDR_WORDS + e] = c.peer_counts[p * c.E + e];
+    if (lane == 0) {
+        c.ret_seq[idx] = rs;
+        afd_header_fields f;
+        f.flags = 0;
+        f.seq = rs;
+        f.echo_seq = c.cur_seq[p];
+        f.layer_idx = layer;
+        f.stage_idx = s;
+        f.num_tokens = n_p;
+        f.routed_tokens = n_p;
+        f.shared_tokens = n_p;
+        f.src_peer = p;
+        f.n_counts = c.E;
+        header_encode_fixed(f, w);
+    }
+    __threadfence();  // the wave's header stores (every lane) before the flag
+    if (lane == 0) st_release((int*)c.ret_win + idx, rs);
 }
 
 // ---------------------------------------------------------------------------
@@ -1434,11 +1467,11 @@ hipError_t launch_ffn(const DevCtx& c, int stage, int layer, const Weights& w, l
     mark();
     k_wait<<<1, 64, 0, st>>>(c, stage, layer, timeout_ticks);
     mark();
-    if (c.E <= 64) k_route<1><<<c.NB, 256, 0, st>>>(c, status, stage);
-    else if (c.E <= 128) k_route<2><<<c.NB, 256, 0, st>>>(c, status, stage);
-    else if (c.E <= 256) k_route<4><<<c.NB, 256, 0, st>>>(c, status, stage);
-    else if (c.E <= 512) k_route<8><<<c.NB, 256, 0, st>>>(c, status, stage);
-    else k_route<16><<<c.NB, 256, 0, st>>>(c, status, stage);
+    if (c.E <= 64) k_route<1><<<c.NB, 64 * kRouteChunk, 0, st>>>(c, status, stage);
+    else if (c.E <= 128) k_route<2><<<c.NB, 64 * kRouteChunk, 0, st>>>(c, status, stage);
+    else if (c.E <= 256) k_route<4><<<c.NB, 64 * kRouteChunk, 0, st>>>(c, status, stage);
+    else if (c.E <= 512) k_route<8><<<c.NB, 64 * kRouteChunk, 0, st>>>(c, status, stage);
+    else k_route<16><<<c.NB, 64 * kRouteChunk, 0, st>>>(c, status, stage);
     mark();
     k_scan<<<c.E, 256, 0, st>>>(c, status);
     mark();
@@ -1460,7 +1493,7 @@ hipError_t launch_ffn(const DevCtx& c, int stage, int layer, const Weights& w, l
 #undef AFD_COMBINE_CASE
         default: return hipErrorInvalidValue;
     }
-    k_publish<<<1, 64, 0, st>>>(c, status, stage, layer);
+    k_publish<<<c.P, 64, 0, st>>>(c, status, stage, layer);
     mark();
     return hipGetLastError();
 }

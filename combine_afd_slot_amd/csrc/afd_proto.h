@@ -39,7 +39,8 @@ AFD_HD void slot_field_bytes(int64_t token_cap, int64_t hidden, int64_t experts,
 }
 
 // Header: encode into `w` (12 + n_counts words).
-AFD_HD void header_encode(const afd_header_fields& f, const int32_t* counts, int32_t* w) {
+// The fixed words of a header (everything but the per-expert counts).
+AFD_HD void header_encode_fixed(const afd_header_fields& f, int32_t* w) {
     w[AFD_HDR_MAGIC] = AFD_HDR_MAGIC_VALUE;
     w[AFD_HDR_VERSION] = AFD_HDR_VERSION_VALUE;
     w[AFD_HDR_FLAGS] = f.flags;
@@ -52,6 +53,10 @@ AFD_HD void header_encode(const afd_header_fields& f, const int32_t* counts, int
     w[AFD_HDR_SHARED_TOKENS] = f.shared_tokens;
     w[AFD_HDR_SRC_PEER] = f.src_peer;
     w[AFD_HDR_N_COUNTS] = f.n_counts;
+}
+
+AFD_HD void header_encode(const afd_header_fields& f, const int32_t* counts, int32_t* w) {
+    header_encode_fixed(f, w);
     for (int32_t i = 0; i < f.n_counts; ++i) w[AFD_HDR_WORDS + i] = counts ? counts[i] : 0;
 }
 
