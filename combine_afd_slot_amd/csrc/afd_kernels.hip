@@ -879,9 +879,8 @@ struct GemmTile {
 // the token-row copies of those chunks are zeroed in LDS before the MFMAs;
 // h and hs rows are stored in whole 32-deep blocks.
 template <int MODE, int NX>
-__device__ __forceinline__ void gemm_issue(const GemmTile& t, char* stage, int wid, int kt) {
+__device__ __forceinline__ void gemm_issue_x(const GemmTile& t, char* stage, int wid, int kt) {
     const char* ab = t.abase + (int64_t)kt * t.astep;
-    const char* bb = t.bbase + (int64_t)kt * kWTileBytes;
     uint32_t fix = 0u;
     if (MODE == 1) {
         const uint32_t kb = (uint32_t)kt * kRowBytes;
@@ -890,9 +889,18 @@ __device__ __forceinline__ void gemm_issue(const GemmTile& t, char* stage, int w
 #pragma unroll
     for (int i = 0; i < NX; ++i)
         dma16(ab + (t.xo[i] + fix), (lds_ptr_t)(stage + (wid + kGemmWaves * i) * 1024));
+}
+__device__ __forceinline__ void gemm_issue_w(const GemmTile& t, char* stage, int wid, int kt) {
+    const char* bb = t.bbase + (int64_t)kt * kWTileBytes;
 #pragma unroll
     for (int i = 0; i < kWInstr; ++i)
         dma16(bb + (t.wlane + i * kGemmWaves * 1024), (lds_ptr_t)(stage + kXStageBytes + (wid + kGemmWaves * i) * 1024));
+}
+// Both halves of a step, weight rows first (the order every step keeps).
+template <int MODE, int NX>
+__device__ __forceinline__ void gemm_issue(const GemmTile& t, char* stage, int wid, int kt) {
+    gemm_issue_w(t, stage, wid, kt);
+    gemm_issue_x<MODE, NX>(t, stage, wid, kt);
 }
 
 
@@ -961,33 +969,41 @@ __device__ __forceinline__ void gemm_interleave() {
 // One depth step kt of a wave with NV valid token blocks, software-
 // pipelined around a single barrier; TAIL: the step reaches past K.  On
 // entry `a` holds slice 0 of step kt.  (1) Slice 0's MFMAs, interleaved with
-// the reads of slice 1 into `b` and the loads of step kt+3 into the stage
-// step kt-1 used (every wave finished reading it before the previous step's
-// barrier).  (2) This wave's slice-1 reads done and its loads of step kt+1
-// landed (those of kt+2 and kt+3 may still fly), then the barrier: step
-// kt+1 is complete in LDS and every wave is done reading step kt.  (3) Slice
-// 1's MFMAs, interleaved with the reads of slice 0 of step kt+1 into `a`.
-// Each phase is one basic block: past the last step the loads reload the
-// last step into the idle stage and the reads read a stage nobody uses.
+// the reads of slice 1 into `b` and the weight-row loads of step kt+3 into
+// the stage step kt-1 used (every wave finished reading it before the
+// previous step's barrier).  (2) This wave's slice-1 reads done and its
+// loads of step kt+1 landed, then the barrier: step kt+1 is complete in LDS
+// and every wave is done reading step kt.  (3) Slice 1's MFMAs, interleaved
+// with the reads of slice 0 of step kt+1 into `a` and the token-row loads
+// of step kt+3.  Splitting a step's loads over both phases spreads the
+// global-to-LDS traffic, which all four waves issue in the same phases,
+// over the whole step.  Each phase is one basic block: past the last step
+// the loads reload the last step into the idle stage and the reads read a
+// stage nobody uses.
 template <int MODE, int NV, int NX, bool TAIL>
 __device__ __forceinline__ void gemm_step(f32x16 (&acc)[NV > 0 ? NV : 1][4], const GemmTile& t, char* smem,
                                           int kt, int wid, int lane, uint32_t wl, uint32_t tl, GemmFrags<NV>& a,
                                           GemmFrags<NV>& b) {
+    char* const ld = smem + ((kt + kStages - 1) & (kStages - 1)) * kStageBytes;
+    const int kl = min(kt + kStages - 1, t.nk - 1);
     if (TAIL) gemm_tail(a, t, kt, 0, lane);
     gemm_frags<MODE, NV>(b, smem + (kt & (kStages - 1)) * kStageBytes, 1, wl, tl);
-    gemm_issue<MODE, NX>(t, smem + ((kt + kStages - 1) & (kStages - 1)) * kStageBytes, wid, min(kt + kStages - 1, t.nk - 1));
+    gemm_issue_w(t, ld, wid, kl);
     gemm_mfma(acc, a);
-    gemm_interleave<4 * NV, 4 + NV, NX + kWInstr>();
+    gemm_interleave<4 * NV, 4 + NV, kWInstr>();
     __builtin_amdgcn_sched_barrier(0);
 
-    __builtin_amdgcn_s_waitcnt(0xC07F);            // lgkmcnt(0)
-    AFD_WAIT_VMCNT((NX + kWInstr) * (kStages - 2));  // step kt+1 landed
+    // step kt+1 landed: in flight may be only the loads of step kt+2 and the
+    // weight-row loads of step kt+3 just issued
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    AFD_WAIT_VMCNT(NX + 2 * kWInstr);
     AFD_BARRIER();
 
     if (TAIL) gemm_tail(b, t, kt, 1, lane);
     gemm_frags<MODE, NV>(a, smem + ((kt + 1) & (kStages - 1)) * kStageBytes, 0, wl, tl);
+    gemm_issue_x<MODE, NX>(t, ld, wid, kl);
     gemm_mfma(acc, b);
-    gemm_interleave<4 * NV, 4 + NV, 0>();
+    gemm_interleave<4 * NV, 4 + NV, NX>();
     __builtin_amdgcn_sched_barrier(0);
 }
 
