@@ -142,7 +142,7 @@ WsLayout ws_layout(const afd_window_config& c) {
     w.h = take(64 * np * ((c.intermediate + afd::kBK - 1) / afd::kBK));
     w.hs = take(64 * tmax * (c.shared_intermediate > 0 ? (c.shared_intermediate + afd::kBK - 1) / afd::kBK : 1));
     w.y = take(2 * np * c.hidden);
-    w.ys = take(4 * tmax * c.hidden);
+    w.ys = take(2 * tmax * c.hidden);
     w.bytes = cur;
     return w;
 }
@@ -278,7 +278,7 @@ void fill_ctx(afd_window* w) {
     d.h = (uint16_t*)(ws + L.h);
     d.hs = (uint16_t*)(ws + L.hs);
     d.y = (uint16_t*)(ws + L.y);
-    d.ys = (float*)(ws + L.ys);
+    d.ys = (uint16_t*)(ws + L.ys);
 }
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }

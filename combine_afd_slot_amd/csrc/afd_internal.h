@@ -94,7 +94,7 @@ struct DevCtx {
     uint16_t* h;       // [ceil(I/32)][Tmax*K][32]  bf16 SwiGLU activations, permuted order
     uint16_t* hs;      // [ceil(Is/32)][Tmax][32]   bf16 shared activations
     uint16_t* y;       // [Tmax*K][H]  bf16 routed expert outputs, permuted order
-    float* ys;         // [Tmax][H]    fp32 shared expert output, token (= shared row) order
+    uint16_t* ys;      // [Tmax][H]    bf16 shared expert output, token (= shared row) order
 };
 
 // One layer's packed weights (written by k_pack_weights): tiles of 256

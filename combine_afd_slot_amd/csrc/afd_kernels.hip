@@ -1,17 +1,20 @@
 // afd_kernels.hip -- gfx950 kernels of the AFD FFN-rank hot path.
 //
-// One FFN run (afd_ffn_run) is seven launches on the FFN stream:
+// One FFN run (afd_ffn_run) is eight launches on the FFN stream:
 //   k_wait     bounded acquire-spin on the P inbound flags, header checks,
 //              fan-in offsets (the fan-in itself is virtual: no copy)
 //   k_route    one wavefront per token: top-k over the fp32 logits, weights,
-//              per-chunk expert histogram, per-peer expert counts
-//   k_scan     per-expert counts and offsets, stable per-chunk bases, the
-//              GEMM group table and tile prefixes (all on the device)
-//   k_permute  stable dispatch order: perm / inv
+//              per-chunk expert histogram
+//   k_scan     per-expert counts, stable per-chunk bases, per-peer counts
+//   k_permute  expert offsets, the GEMM tile plan, stable dispatch order
+//              (perm / inv / token-row addresses)
 //   k_gemm<1>  grouped gate/up GEMM (MFMA bf16) with the SwiGLU epilogue
-//   k_gemm<2>  grouped down GEMM (MFMA bf16)
+//   k_gemm<2>  grouped down GEMM (MFMA bf16), routed and shared experts
 //   k_combine  weighted combine + shared branch, bf16 rows written straight
-//              into each peer's return slot, then the return flags
+//              into each peer's return slot
+//   k_publish  return headers and flags, one wavefront per peer
+// Weights are read from the tile-ordered copy written once per layer by
+// k_pack_weights.
 //
 // Sources: "[RFC]: Async GPU Connector" (sections "Window and slot layout",
 // "Data flow", "Attention gate and FFN expert compute"), "Data on the wire:
@@ -712,47 +715,42 @@ __global__ __launch_bounds__(256) void k_permute(DevCtx c, const int* status) {
 // a4/a5/a6: grouped GEMMs on MFMA (v_mfma_f32_32x32x16_bf16).
 //
 // A tile is up to 256 token rows of one group (8 blocks of 32) x 256 weight
-// rows, 64 deep per step.  256 threads = 4 waves, one per SIMD, placed 2
+// rows, 32 deep per step.  256 threads = 4 waves, one per SIMD, placed 2
 // (token) x 2 (weight): wave (wx, ww) owns the token blocks wx, wx+2, wx+4,
-// wx+6 of the tile (so a partly filled tile keeps both token positions
-// equally loaded; blocks past the tile's end are skipped) and four 32-row
-// weight blocks: 16 accumulators of 32 x 32.  Per 16-deep slice a wave reads
-// 4 + 4 fragments of 1 KB from LDS and issues 16 MFMAs, half a KB of LDS
-// traffic per MFMA.  Operands are K-contiguous rows (token rows of X or h,
-// weight rows of W13 / W2), so every MFMA fragment is one 16-byte LDS read
-// per lane.  The weight fragment is the MFMA's first operand, so a lane's
-// accumulators hold one token row (lane % 32) and 4 runs of 4 consecutive
-// output columns -- 8/16-byte stores in the epilogue.
+// wx+6 of the tile (a partly filled tile keeps both token positions equally
+// loaded; blocks past the tile's end are skipped) and four 32-row weight
+// blocks: up to 16 accumulators of 32 x 32 in AGPRs.  Per 16-deep slice a
+// wave reads 4 + 4 fragments of 1 KB from LDS and issues 16 MFMAs.  Operands
+// are K-contiguous rows, so every fragment is one 16-byte LDS read per lane.
+// The token fragment is the MFMA's first operand: a lane's accumulator holds
+// one output column (lane % 32) of 16 token rows, and one store instruction
+// writes 32 consecutive columns of two rows.
 //
-// Global -> LDS through registers: at the start of a depth step each wave
-// issues the 16-byte global loads of the next step (8 token-row and 8
-// weight-row loads of 1 KB per wave), reads and multiplies the current
-// stage, then writes the loaded data into the other of the two 64 KB LDS
-// stages; the barrier at the next step's start publishes it.  The loads
-// thus have a whole step of MFMA work to arrive, and no LDS read ever waits
-// on them.  (Direct-to-LDS loads would save the 64 staging registers, but
-// the compiler cannot tell the two stages apart and makes every LDS read
-// wait for all such loads in flight.)  One load instruction covers 1 KB =
-// 8 rows x 128 B; lane i fetches row i/8 and writes LDS chunk i%8, which
-// holds logical chunk (i%8) ^ swz(row), an XOR swizzle that keeps the
-// 16-byte fragment reads of 8 consecutive rows on distinct banks.
+// Global -> LDS: direct-to-LDS 16-byte loads into a ring of 4 stages of
+// 32 KB (16 KB token rows, 16 KB weight rows), issued 3 steps ahead; LDS
+// rows of 64 bytes hold their four 16-byte chunks XOR-swizzled (swz4), which
+// keeps the fragment reads of consecutive rows on distinct banks.  The
+// weight rows come from the packed weight copy, already in that order: each
+// load instruction copies one contiguous KB.  All LDS lives in one array
+// (with a second __shared__ variable the compiler attaches alias scopes and
+// makes every LDS read wait for the direct-to-LDS loads in flight).
 //
 // MODE 1 (gate/up + SwiGLU): token rows are read straight from the inbound
-//   slots (routed rows through the per-pair row address, shared rows through
-//   the shared_x row address); the weight rows are 128 gate rows and the
-//   same 128 up rows of W13, and wave ww takes gate blocks 2ww, 2ww+1 and
-//   the matching up blocks, so each lane holds gate and up of the same (row,
-//   column) and applies silu(g) * u in registers; h is stored bf16.
+//   slots through the per-pair row address (shared rows through the
+//   shared_x row address); the weight rows are 128 gate rows and the same
+//   128 up rows of W13, and wave ww takes gate blocks 2ww, 2ww+1 and the
+//   matching up blocks, so each lane holds gate and up of the same (row,
+//   column) and applies silu(g) * u in registers; h is stored bf16,
+//   depth-block major.
 // MODE 2 (down): token rows are the group's h rows, weight rows 256 rows of
-//   W2; routed output rows are stored bf16 in permuted order, shared rows
-//   fp32 in token order.
+//   W2; output rows are stored bf16, routed rows in permuted order (y),
+//   shared rows in token order (ys).
 //
-// Persistent: one workgroup per CU; the device-built tile list is cut into
-// 8 segments of equal cost, one per XCD (workgroups are dispatched to the
-// XCDs round-robin); a workgroup takes tiles from its XCD's segment and then
-// from the others.  Rows past the group end and columns past the width load
-// a valid row and are masked at the store; depth past K loads valid data
-// whose token-row copies are zeroed before they reach LDS.
+// Persistent: one workgroup per CU takes tiles from per-XCD segments of the
+// device-built tile list (see the scheduler below).  Rows past the group end
+// and columns past the width load valid rows and are dropped at the store;
+// depth past K loads valid data whose token-row copies are zeroed before the
+// MFMAs.
 // ---------------------------------------------------------------------------
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
@@ -1227,30 +1225,12 @@ __device__ __forceinline__ void gemm_epilogue(const f32x16 (&acc)[NV > 0 ? NV : 
                 }
             }
         }
-    } else if (t.sh) {
-        // shared expert rows: fp32, token order
-        const uint32_t ldb = (uint32_t)c.H * 4;
-        const __amdgpu_buffer_rsrc_t rs = out_rsrc(c.ys + (int64_t)t.r0 * c.H, t.rows * ldb);
-#pragma unroll
-        for (int jb = 0; jb < 4; ++jb) {
-            const int col = t.nt * kBW + (ww * 4 + jb) * 32 + lj;
-            const uint32_t cb = (col < c.H ? 0u : 0x80000000u) + (uint32_t)col * 4 + (uint32_t)rl * ldb;
-#pragma unroll
-            for (int ib = 0; ib < NV; ++ib) {
-#pragma unroll
-                for (int v = 0; v < 16; v += 2) {
-                    const uint32_t r = (uint32_t)(64 * ib + 8 * (v >> 2) + (v & 3));
-                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(agpr(acc[ib][jb][v])), rs, (int)(cb + r * ldb), 0, 0);
-                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(agpr(acc[ib][jb][v + 1])), rs,
-                                                          (int)(cb + (r + 1) * ldb), 0, 0);
-                    __builtin_amdgcn_sched_barrier(0);
-                }
-            }
-        }
     } else {
-        // routed rows: bf16, permuted order
+        // bf16 rows: routed rows into y (permuted order), shared rows into ys
+        // (token order); one code path for both, so the accumulators never
+        // have to live across a branch
         const uint32_t ldb = (uint32_t)c.H * 2;
-        const __amdgpu_buffer_rsrc_t rs = out_rsrc(c.y + (int64_t)t.r0 * c.H, t.rows * ldb);
+        const __amdgpu_buffer_rsrc_t rs = out_rsrc((t.sh ? c.ys : c.y) + (int64_t)t.r0 * c.H, t.rows * ldb);
 #pragma unroll
         for (int jb = 0; jb < 4; ++jb) {
             const int col = t.nt * kBW + (ww * 4 + jb) * 32 + lj;
@@ -1378,7 +1358,8 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(DevCtx c, const int* s
 
 // ---------------------------------------------------------------------------
 // a7: combine + split + publish.  out[t] = rsf * sum_k w[t,k] * y[inv[t*K+k]]
-// + S[t] in fp32 (k in order), rounded to bf16 and written into row t - off[p]
+// + S[t] in fp32 (k in order; S the bf16 shared-expert row), rounded to bf16
+// and written into row t - off[p]
 // of peer p's return slot ("Data flow": weighted index_add_ combine with the
 // shared branch added; "Data on the wire", Step 4: split back by seq_lens).
 // ---------------------------------------------------------------------------
@@ -1405,10 +1386,12 @@ __global__ __launch_bounds__(256) void k_combine(DevCtx c, const int* status, in
             for (int k = 0; k < KK; ++k) yv[k] = *(const u32x4*)(c.y + (int64_t)pos[k] * H + ch * 8);
             float sv[8];
             if (c.has_shared) {
-                const float4* sp = (const float4*)(c.ys + (int64_t)t * H + ch * 8);
-                const float4 s0 = sp[0], s1 = sp[1];
-                sv[0] = s0.x; sv[1] = s0.y; sv[2] = s0.z; sv[3] = s0.w;
-                sv[4] = s1.x; sv[5] = s1.y; sv[6] = s1.z; sv[7] = s1.w;
+                const u32x4 sq = *(const u32x4*)(c.ys + (int64_t)t * H + ch * 8);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    sv[2 * i] = bf2f(sq[i] & 0xffffu);
+                    sv[2 * i + 1] = bf2f(sq[i] >> 16);
+                }
             } else {
 #pragma unroll
                 for (int i = 0; i < 8; ++i) sv[i] = 0.f;
