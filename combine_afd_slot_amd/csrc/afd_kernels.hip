@@ -1116,26 +1116,27 @@ __device__ __forceinline__ void gemm_setup(const DevCtx& c, const Weights& w, in
     }
 }
 
-// The first kStages-1 steps of a tile into stages 0 .. (the ring must be
-// free; a tile shorter than the ring reloads its last step).
-template <int MODE, int NX>
-__device__ __forceinline__ void gemm_prologue_nx(const GemmTile& t, char* smem, int wid) {
-#pragma unroll
-    for (int p = 0; p < kStages - 1; ++p) gemm_issue<MODE, NX>(t, smem + p * kStageBytes, wid, min(p, t.nk - 1));
+// The first kStages-1 steps of a tile go into stages 0 .. (the ring must be
+// free; a tile shorter than the ring reloads its last step), one step per
+// call so that the tile boundary can spread them over the epilogue of the
+// previous tile.  All four token-row loads are issued whatever the tile's
+// height (the extra ones load valid rows into LDS rows the MFMAs do not
+// read): the first waits of the tile, sized for its own NX, then wait for at
+// least as many loads as they need, and there is no branch on the tile's
+// height among the loads.
+template <int MODE>
+__device__ __forceinline__ void gemm_prologue_step(const GemmTile& t, char* smem, int wid, int p) {
+    gemm_issue<MODE, kXInstr>(t, smem + p * kStageBytes, wid, min(p, t.nk - 1));
 }
 template <int MODE>
 __device__ __forceinline__ void gemm_prologue(const GemmTile& t, char* smem, int wid) {
-    switch ((t.tb + 1) >> 1) {
-        case 1: gemm_prologue_nx<MODE, 1>(t, smem, wid); break;
-        case 2: gemm_prologue_nx<MODE, 2>(t, smem, wid); break;
-        case 3: gemm_prologue_nx<MODE, 3>(t, smem, wid); break;
-        default: gemm_prologue_nx<MODE, 4>(t, smem, wid); break;
-    }
+#pragma unroll
+    for (int p = 0; p < kStages - 1; ++p) gemm_prologue_step<MODE>(t, smem, wid, p);
 }
 
 // Tile boundary, between the last depth step of the current tile and its
-// epilogue: once every wave is done with the ring, resolve the next tile,
-// set it up and start its loads, which then land while the epilogue runs.
+// epilogue: once every wave is done with the ring, resolve the next tile and
+// set it up (its first loads are issued during the epilogue).
 template <int MODE>
 __device__ __forceinline__ void gemm_boundary(const DevCtx& c, const Weights& w, GemmSched& sc, char* smem, int tid,
                                               int wid, int lrow, uint32_t lcx, int& next, GemmTile& tn) {
@@ -1148,27 +1149,9 @@ __device__ __forceinline__ void gemm_boundary(const DevCtx& c, const Weights& w,
     }
     __syncthreads();
     next = __builtin_amdgcn_readfirstlane(*slot);
-    if (next >= 0) {
-        gemm_setup<MODE>(c, w, next, wid, lrow, lcx, tn);
-        gemm_prologue<MODE>(tn, smem, wid);
-    }
+    if (next >= 0) gemm_setup<MODE>(c, w, next, wid, lrow, lcx, tn);
 }
 
-// Epilogue of a tile.  In accumulator (ib, jb) a lane holds output column
-// 32*(weight block) + (lane & 31) and, in register v = 0..15, token row
-// (wx + 2*ib)*32 + 8*(v/4) + 4*(lane/32) + v%4 of the tile.  One store
-// instruction thus writes 32 consecutive columns of each of two rows: whole
-// 64-byte segments.  The stores go through a buffer descriptor that spans
-// the tile's valid rows; lanes of a column past the output width add 2^31
-// to their offset.  The hardware drops out-of-range buffer stores, so the
-// code stays straight-line (a divergent branch would keep every
-// accumulator live across it).
-// One accumulator element read out of its AGPR.  Reading the accumulators
-// one at a time keeps them in AGPRs until they are needed (the compiler
-// would otherwise copy all of them to VGPRs at the end of the depth loop and
-// run out of registers).  The caller leaves at least 18 wait states between
-// the last MFMA and the first read (the hardware does not interlock an MFMA
-// result read by a VALU instruction).
 // Word 3 of a raw buffer descriptor on gfx9-family GPUs (32-bit data
 // format, stride 0: accesses are range-checked against the byte count).
 constexpr int kBufferFlags = 0x00020000;
@@ -1184,18 +1167,33 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t out_rsrc(const void* base, uin
                                             (int)__builtin_amdgcn_readfirstlane(bytes), kBufferFlags);
 }
 
+// One accumulator element read out of its AGPR.  Reading the accumulators
+// one at a time keeps them in AGPRs until they are needed (the compiler
+// would otherwise copy all of them to VGPRs at the end of the depth loop and
+// run out of registers).  The caller leaves at least 18 wait states between
+// the last MFMA and the first read (the hardware does not interlock an MFMA
+// result read by a VALU instruction).
 __device__ __forceinline__ float agpr(float x) {
     float r;
     asm("v_accvgpr_read_b32 %0, %1" : "=v"(r) : "a"(x));
     return r;
 }
 
+// Epilogue of token block ib of a tile.  In accumulator (ib, jb) a lane
+// holds output column 32*(weight block) + (lane & 31) and, in register v =
+// 0..15, token row (wx + 2*ib)*32 + 8*(v/4) + 4*(lane/32) + v%4 of the
+// tile.  One store instruction thus writes 32 consecutive columns of each of
+// two rows: whole 64-byte segments.  The stores go through a buffer
+// descriptor that spans the tile's valid rows; lanes of a column past the
+// output width add 2^31 to their offset.  The hardware drops out-of-range
+// buffer stores, so the code stays straight-line (a divergent branch would
+// keep every accumulator live across it).  The caller pads the wait states
+// between the last MFMA and the first accumulator read.
 template <int MODE, int NV>
-__device__ __forceinline__ void gemm_epilogue(const f32x16 (&acc)[NV > 0 ? NV : 1][4], const DevCtx& c,
-                                              const GemmTile& t, int lane, int ww, int wx) {
-    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7");  // MFMA results settle (>= 18 wait states)
+__device__ __forceinline__ void gemm_epilogue_ib(const f32x16 (&acc)[NV > 0 ? NV : 1][4], const DevCtx& c,
+                                                 const GemmTile& t, int lane, int ww, int wx, int ib) {
     const int lj = lane & 31;
-    const int rl = wx * 32 + 4 * (lane >> 5);  // this lane's first tile row in block ib = 0
+    const uint32_t rb = (uint32_t)((wx + 2 * ib) * 32 + 4 * (lane >> 5));  // this lane's first row of the block
     if (MODE == 1) {
         // h = silu(gate) * up, bf16; gate in weight blocks jb, up in jb + 2.
         // Column block jb is one 32-deep block of h: rows of 64 bytes.
@@ -1206,23 +1204,20 @@ __device__ __forceinline__ void gemm_epilogue(const f32x16 (&acc)[NV > 0 ? NV : 
             const int col0 = t.nt * (kBW / 2) + ww * 64 + jb * 32;
             const __amdgpu_buffer_rsrc_t rs =
                 out_rsrc(hb + ((int64_t)(col0 >> 5) * hrows + t.r0) * kRowBytes, (uint32_t)t.rows * kRowBytes);
-            const uint32_t cb = (col0 + lj < t.Ig ? 0u : 0x80000000u) + (uint32_t)lj * 2 + (uint32_t)rl * kRowBytes;
+            const uint32_t cb = (col0 + lj < t.Ig ? 0u : 0x80000000u) + (uint32_t)lj * 2 + rb * kRowBytes;
 #pragma unroll
-            for (int ib = 0; ib < NV; ++ib) {
+            for (int v = 0; v < 16; v += 2) {
+                float o[2];
 #pragma unroll
-                for (int v = 0; v < 16; v += 2) {
-                    float o[2];
-#pragma unroll
-                    for (int q = 0; q < 2; ++q) {
-                        const float g = agpr(acc[ib][jb][v + q]), u = agpr(acc[ib][jb + 2][v + q]);
-                        o[q] = g * __builtin_amdgcn_rcpf(1.f + __expf(-g)) * u;
-                    }
-                    const uint32_t pk = pk_bf16(o[0], o[1]);
-                    const uint32_t r = (uint32_t)(64 * ib + 8 * (v >> 2) + (v & 3));
-                    __builtin_amdgcn_raw_buffer_store_b16((uint16_t)pk, rs, (int)(cb + r * kRowBytes), 0, 0);
-                    __builtin_amdgcn_raw_buffer_store_b16((uint16_t)(pk >> 16), rs, (int)(cb + (r + 1) * kRowBytes), 0, 0);
-                    __builtin_amdgcn_sched_barrier(0);
+                for (int q = 0; q < 2; ++q) {
+                    const float g = agpr(acc[ib][jb][v + q]), u = agpr(acc[ib][jb + 2][v + q]);
+                    o[q] = g * __builtin_amdgcn_rcpf(1.f + __expf(-g)) * u;
                 }
+                const uint32_t pk = pk_bf16(o[0], o[1]);
+                const uint32_t r = (uint32_t)(8 * (v >> 2) + (v & 3));
+                __builtin_amdgcn_raw_buffer_store_b16((uint16_t)pk, rs, (int)(cb + r * kRowBytes), 0, 0);
+                __builtin_amdgcn_raw_buffer_store_b16((uint16_t)(pk >> 16), rs, (int)(cb + (r + 1) * kRowBytes), 0, 0);
+                __builtin_amdgcn_sched_barrier(0);
             }
         }
     } else {
@@ -1234,17 +1229,14 @@ __device__ __forceinline__ void gemm_epilogue(const f32x16 (&acc)[NV > 0 ? NV : 
 #pragma unroll
         for (int jb = 0; jb < 4; ++jb) {
             const int col = t.nt * kBW + (ww * 4 + jb) * 32 + lj;
-            const uint32_t cb = (col < c.H ? 0u : 0x80000000u) + (uint32_t)col * 2 + (uint32_t)rl * ldb;
+            const uint32_t cb = (col < c.H ? 0u : 0x80000000u) + (uint32_t)col * 2 + rb * ldb;
 #pragma unroll
-            for (int ib = 0; ib < NV; ++ib) {
-#pragma unroll
-                for (int v = 0; v < 16; v += 2) {
-                    const uint32_t pk = pk_bf16(agpr(acc[ib][jb][v]), agpr(acc[ib][jb][v + 1]));
-                    const uint32_t r = (uint32_t)(64 * ib + 8 * (v >> 2) + (v & 3));
-                    __builtin_amdgcn_raw_buffer_store_b16((uint16_t)pk, rs, (int)(cb + r * ldb), 0, 0);
-                    __builtin_amdgcn_raw_buffer_store_b16((uint16_t)(pk >> 16), rs, (int)(cb + (r + 1) * ldb), 0, 0);
-                    __builtin_amdgcn_sched_barrier(0);
-                }
+            for (int v = 0; v < 16; v += 2) {
+                const uint32_t pk = pk_bf16(agpr(acc[ib][jb][v]), agpr(acc[ib][jb][v + 1]));
+                const uint32_t r = (uint32_t)(8 * (v >> 2) + (v & 3));
+                __builtin_amdgcn_raw_buffer_store_b16((uint16_t)pk, rs, (int)(cb + r * ldb), 0, 0);
+                __builtin_amdgcn_raw_buffer_store_b16((uint16_t)(pk >> 16), rs, (int)(cb + (r + 1) * ldb), 0, 0);
+                __builtin_amdgcn_sched_barrier(0);
             }
         }
     }
@@ -1281,7 +1273,16 @@ __device__ __forceinline__ void gemm_run(const DevCtx& c, const Weights& w, Gemm
 
     gemm_boundary<MODE>(c, w, sc, smem, tid, wid, lrow, lcx, next, tn);
 
-    gemm_epilogue<MODE, NV>(acc, c, t, lane, ww, wx);
+    // Epilogue, token block by token block, with the next tile's first
+    // steps issued in between: the global-to-LDS traffic of those loads
+    // (which the CU moves at a fixed rate) overlaps the epilogue instead of
+    // stalling the wave in one burst.
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7");  // MFMA results settle (>= 18 wait states)
+#pragma unroll
+    for (int ib = 0; ib < (NV > kStages - 1 ? NV : kStages - 1); ++ib) {
+        if (ib < kStages - 1 && next >= 0) gemm_prologue_step<MODE>(tn, smem, wid, ib);
+        if (ib < NV) gemm_epilogue_ib<MODE, NV>(acc, c, t, lane, ww, wx, ib);
+    }
 }
 
 template <int MODE>
