@@ -924,6 +924,28 @@ __device__ __forceinline__ void gemm_frags(GemmFrags<NV>& f, const char* rd, int
     for (int ib = 0; ib < NV; ++ib) f.x[ib] = __builtin_bit_cast(bf16x8, *(const u32x4*)(x + ib * 2 * kBlockBytes));
 }
 
+// The fragment reads of slice kk alternating, in program order, with NL
+// loads issued by `load(i)`: read 0, load 0, read 1, load 1, ... (then the
+// remaining reads).  With the matching scheduling pattern each wave spreads
+// its global-to-LDS loads over the whole phase instead of issuing them in
+// one burst that the CU's load path (which moves about 64 bytes per clock)
+// can only drain while the wave stalls.
+template <int MODE, int NV, int NL, typename Load>
+__device__ __forceinline__ void gemm_frags_loads(GemmFrags<NV>& f, const char* rd, int kk, uint32_t wl, uint32_t tl,
+                                                 Load load) {
+    const char* w = rd + (wl ^ (32u * kk));
+    const char* x = rd + (tl ^ (32u * kk));
+    constexpr int NR = 4 + NV;
+#pragma unroll
+    for (int i = 0; i < (NR > NL ? NR : NL); ++i) {
+        if (i < 4)
+            f.w[i] = __builtin_bit_cast(bf16x8, *(const u32x4*)(w + (MODE == 1 ? (i >> 1) * 4 + (i & 1) : i) * kBlockBytes));
+        else if (i < NR)
+            f.x[i - 4] = __builtin_bit_cast(bf16x8, *(const u32x4*)(x + (i - 4) * 2 * kBlockBytes));
+        if (i < NL) load(i);
+    }
+}
+
 // In a step that reaches past K: token-fragment lanes whose chunk (8 depth
 // values at kt*32 + (2*kk + lane/32)*8) lies at or past K become zero, so
 // the (finite) clamped copies loaded there contribute nothing.  A select,
@@ -947,6 +969,30 @@ __device__ __forceinline__ void gemm_mfma(f32x16 (&acc)[NV > 0 ? NV : 1][4], con
 #pragma unroll
         for (int jb = 0; jb < 4; ++jb)
             acc[ib][jb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.x[ib], f.w[jb], acc[ib][jb], 0, 0, 0);
+}
+
+// Scheduling pattern matching gemm_frags_loads: each MFMA followed by the
+// next memory instruction in program order (reads and loads alternate while
+// both remain).
+template <int NMFMA, int NREAD, int NLOAD>
+__device__ __forceinline__ void gemm_interleave_alt() {
+    constexpr int NPAIR = NREAD < NLOAD ? NREAD : NLOAD;
+    constexpr int NOPS = NREAD + NLOAD;
+#pragma unroll
+    for (int i = 0; i < NMFMA; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (i < NOPS) {
+            const bool rd = i < 2 * NPAIR ? (i % 2 == 0) : (NREAD > NLOAD);
+            if (rd) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            else __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
+        }
+    }
+#pragma unroll
+    for (int i = NMFMA; i < NOPS; ++i) {
+        const bool rd = i < 2 * NPAIR ? (i % 2 == 0) : (NREAD > NLOAD);
+        if (rd) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        else __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
+    }
 }
 
 // Scheduling pattern: each MFMA of the group followed by one of the slice's
@@ -985,10 +1031,14 @@ __device__ __forceinline__ void gemm_step(f32x16 (&acc)[NV > 0 ? NV : 1][4], con
     char* const ld = smem + ((kt + kStages - 1) & (kStages - 1)) * kStageBytes;
     const int kl = min(kt + kStages - 1, t.nk - 1);
     if (TAIL) gemm_tail(a, t, kt, 0, lane);
-    gemm_frags<MODE, NV>(b, smem + (kt & (kStages - 1)) * kStageBytes, 1, wl, tl);
-    gemm_issue_w(t, ld, wid, kl);
+    {
+        const char* bb = t.bbase + (int64_t)kl * kWTileBytes;
+        gemm_frags_loads<MODE, NV, kWInstr>(b, smem + (kt & (kStages - 1)) * kStageBytes, 1, wl, tl, [&](int i) {
+            dma16(bb + (t.wlane + i * kGemmWaves * 1024), (lds_ptr_t)(ld + kXStageBytes + (wid + kGemmWaves * i) * 1024));
+        });
+    }
     gemm_mfma(acc, a);
-    gemm_interleave<4 * NV, 4 + NV, kWInstr>();
+    gemm_interleave_alt<4 * NV, 4 + NV, kWInstr>();
     __builtin_amdgcn_sched_barrier(0);
 
     // step kt+1 landed: in flight may be only the loads of step kt+2 and the
@@ -998,10 +1048,19 @@ __device__ __forceinline__ void gemm_step(f32x16 (&acc)[NV > 0 ? NV : 1][4], con
     AFD_BARRIER();
 
     if (TAIL) gemm_tail(b, t, kt, 1, lane);
-    gemm_frags<MODE, NV>(a, smem + ((kt + 1) & (kStages - 1)) * kStageBytes, 0, wl, tl);
-    gemm_issue_x<MODE, NX>(t, ld, wid, kl);
+    {
+        const char* ab = t.abase + (int64_t)kl * t.astep;
+        uint32_t fix = 0u;
+        if (MODE == 1) {
+            const uint32_t kb = (uint32_t)kl * kRowBytes;
+            fix = kb + t.cx > t.tail_clamp ? t.tail_clamp - kb - t.cx : 0u;
+        }
+        gemm_frags_loads<MODE, NV, NX>(a, smem + ((kt + 1) & (kStages - 1)) * kStageBytes, 0, wl, tl, [&](int i) {
+            dma16(ab + (t.xo[i] + fix), (lds_ptr_t)(ld + (wid + kGemmWaves * i) * 1024));
+        });
+    }
     gemm_mfma(acc, b);
-    gemm_interleave<4 * NV, 4 + NV, NX>();
+    gemm_interleave_alt<4 * NV, 4 + NV, NX>();
     __builtin_amdgcn_sched_barrier(0);
 }
 
