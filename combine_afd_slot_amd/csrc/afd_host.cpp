@@ -207,7 +207,7 @@ struct afd_window {
     std::vector<int32_t> pack_seq;    // [P*R] last seq sent by the peer (host side of the peer)
     std::vector<int32_t> packed_len;  // [P*R]
     std::vector<uint8_t> inflight;    // [P*R]
-    int profile = 0;  // 0 off, 1 every kernel, 2 the two GEMMs only
+    int profile = 0;  // 0 off, 1 every kernel, 2 the two GEMMs, 3 the gate/up GEMM
     hipEvent_t ev[AFD_PROFILE_SLOTS + 1] = {};
     bool ev_pending = false;
     double prof_ms[AFD_PROFILE_SLOTS] = {};
@@ -286,7 +286,8 @@ bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 // Fold the previous run's events into the accumulated times.
 void prof_collect(afd_window* w) {
     if (!w->ev_pending) return;
-    const int lo = w->profile == 1 ? 0 : kGemmFirst, hi = w->profile == 1 ? kProfileUsed : kGemmFirst + 2;
+    const int lo = w->profile == 1 ? 0 : kGemmFirst;
+    const int hi = w->profile == 1 ? kProfileUsed : w->profile == 2 ? kGemmFirst + 2 : kGemmFirst + 1;
     for (int i = lo; i <= hi; ++i) (void)hipEventSynchronize(w->ev[i]);
     for (int i = lo; i < hi; ++i) {
         float ms = 0.f;
@@ -476,7 +477,7 @@ int32_t afd_ffn_run(afd_window* w, int32_t stage, int32_t layer_idx, const void*
         std::lock_guard<std::mutex> g(w->prof_mu);
         prof_collect(w);
         for (int i = 0; i <= kProfileUsed; ++i)
-            if (w->profile == 1 || (i >= kGemmFirst && i <= kGemmFirst + 2)) evs[i] = w->ev[i];
+            if (w->profile == 1 || (i >= kGemmFirst && i <= kGemmFirst + (w->profile == 2 ? 2 : 1))) evs[i] = w->ev[i];
         ev = evs;
         w->ev_pending = true;
     }
@@ -589,7 +590,7 @@ int32_t afd_debug_write(afd_window* w, int64_t offset, int64_t bytes, const void
 
 int32_t afd_profile_enable(afd_window* w, int32_t on) {
     if (!w) return fail(AFD_ERR_INVALID, "window is NULL");
-    if (on < 0 || on > 2) return fail(AFD_ERR_INVALID, "profile mode must be 0, 1 or 2");
+    if (on < 0 || on > 3) return fail(AFD_ERR_INVALID, "profile mode must be 0, 1, 2 or 3");
     std::lock_guard<std::mutex> g(w->prof_mu);
     prof_collect(w);
     w->profile = on;

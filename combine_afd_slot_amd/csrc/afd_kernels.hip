@@ -773,7 +773,6 @@ __device__ inline void dma16(const void* g, lds_ptr_t l) { __builtin_amdgcn_glob
     } while (0)
 
 constexpr int kRowBytes = kBK * 2;                      // 64: one row segment of a depth step
-constexpr int kChunks = kRowBytes / 16;                 // 4 16-byte chunks per row segment
 constexpr int kRowsPerLoad = 1024 / kRowBytes;          // 16 rows per 1 KB load instruction
 constexpr int kBlockBytes = 32 * kRowBytes;             // 2 KB per 32-row block
 constexpr int kXStageBytes = kBX * kRowBytes;           // 16 KB of token rows
@@ -781,7 +780,6 @@ constexpr int kStageBytes = (kBX + kBW) * kRowBytes;    // 32 KB
 constexpr int kGemmWaves = kGemmThreads / 64;           // 4
 constexpr int kXInstr = kBX / kRowsPerLoad / kGemmWaves;  // 4 token-row loads per wave and step
 constexpr int kWInstr = kBW / kRowsPerLoad / kGemmWaves;  // 4 weight-row loads per wave and step
-constexpr int kLoadsPerStep = kXInstr + kWInstr;
 static_assert(kGemmWaves == 4 && kTileBlocks == 8 && kBK == 32 && kStages == 4,
               "wave placement, swizzle and ring assume 4 waves, 8 token blocks, 32-deep steps, 4 stages");
 

@@ -271,8 +271,10 @@ int32_t afd_debug_write(afd_window* w, int64_t offset, int64_t bytes, const void
 
 /* Per-kernel timing of afd_ffn_run with HIP events recorded on ffn_stream
  * between its launches.  mode: 0 off, 1 an event between every two kernels,
- * 2 events only around the two GEMM kernels (slots 4 and 5; the other
- * kernels then run back to back as without profiling).  afd_profile_read
+ * 2 events only around the two GEMM kernels (slots 4 and 5), 3 events only
+ * around the gate/up GEMM (slot 4).  Each event record costs a few
+ * microseconds between two launches; in modes 2 and 3 the other kernels run
+ * back to back as without profiling.  afd_profile_read
  * returns the accumulated milliseconds per kernel slot and the number of
  * runs accumulated, then (reset != 0) clears them; it synchronizes the
  * pending events.  Kernel slot names: afd_profile_kernel_name(i),

@@ -226,6 +226,32 @@ def test_weight_pack_and_run_argument_errors():
         assert s.status().status == 0
 
 
+def test_profile_modes():
+    """Per-kernel event timing: mode 1 times every kernel, mode 2 the two
+    GEMMs, mode 3 the gate/up GEMM only; other modes are rejected."""
+    s, _ = _session()
+    with s:
+        names = [afd.lib().afd_profile_kernel_name(i).decode() for i in range(afd.AFD_PROFILE_SLOTS)]
+        used = [n for n in names if n != "unused"]
+        for mode, timed in ((1, set(used)), (2, {"gemm_gate_up_swiglu", "gemm_down"}), (3, {"gemm_gate_up_swiglu"})):
+            afd.afd_profile_enable(s.win, mode)
+            afd.afd_profile_read(s.win, reset=True)
+            for _ in range(3):
+                s.step()
+            tot, runs = afd.afd_profile_read(s.win, reset=True)
+            say(f"[protocol] profile mode {mode}: runs {runs} {tot}")
+            assert runs >= 2
+            for n in used:
+                assert (tot[n] > 0.0) == (n in timed), (mode, n, tot[n])
+        afd.afd_profile_enable(s.win, 0)
+        for bad in (-1, 4):
+            with pytest.raises(afd.AfdError) as ei:
+                afd.afd_profile_enable(s.win, bad)
+            assert ei.value.code == afd.AFD_ERR_INVALID
+        s.step()
+        assert s.status().status == 0
+
+
 def test_repeated_execution_and_ring_depth_two(orc):
     wl = small_workload("ring2", seq_lens=(21, 0, 34), hidden=128, num_experts=8, top_k=2, intermediate=64,
                         shared_intermediate=64, token_cap=40, ring_depth=2)
