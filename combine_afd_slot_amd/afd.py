@@ -36,7 +36,9 @@ HDR_WORDS = 12
 # Every symbol include/afd.h declares.
 EXPORTS = (
     "afd_layout_compute", "afd_window_create", "afd_window_destroy", "afd_window_layout",
-    "afd_slot_pack", "afd_weights_pack", "afd_ffn_run", "afd_slot_unpack", "afd_window_status", "afd_peer_status",
+    "afd_slot_pack", "afd_weights_pack", "afd_ffn_run", "afd_layer_table_set", "afd_ffn_run_table",
+    "afd_ffn_loop_create", "afd_ffn_loop_launch", "afd_ffn_loop_destroy",
+    "afd_slot_unpack", "afd_window_status", "afd_peer_status",
     "afd_window_poll", "afd_debug_routing", "afd_debug_read", "afd_debug_write",
     "afd_profile_enable", "afd_profile_read", "afd_profile_kernel_name",
     "afd_header_encode", "afd_header_decode", "afd_last_error", "afd_status_string",
@@ -102,6 +104,11 @@ def lib():
             "afd_slot_pack": [vp, i32, i32, i32, i32, vp, vp, u32, vp],
             "afd_weights_pack": [vp, P(MoeWeights), vp, i64, vp],
             "afd_ffn_run": [vp, i32, i32, vp, vp],
+            "afd_layer_table_set": [vp, i32, P(vp), vp],
+            "afd_ffn_run_table": [vp, i32, vp],
+            "afd_ffn_loop_create": [vp, i32, i32, vp, P(vp)],
+            "afd_ffn_loop_launch": [vp, vp],
+            "afd_ffn_loop_destroy": [vp],
             "afd_slot_unpack": [vp, i32, i32, i32, vp, vp],
             "afd_window_status": [vp, i32, vp, P(RunInfo)],
             "afd_peer_status": [vp, i32, i32, vp, P(RunInfo)],
@@ -187,6 +194,30 @@ def afd_weights_pack(win, w13, w2, ws13, ws2, dst, dst_bytes, stream=0) -> int:
 
 def afd_ffn_run(win, stage, layer_idx, packed_weights, stream=0) -> int:
     return _check(lib().afd_ffn_run(win, stage, layer_idx, packed_weights or None, stream or None))
+
+
+def afd_layer_table_set(win, packed_ptrs, stream=0) -> int:
+    """packed_ptrs: device pointers of each layer's packed weights (entry i = layer i)."""
+    arr = (ctypes.c_void_p * len(packed_ptrs))(*[p or None for p in packed_ptrs])
+    return _check(lib().afd_layer_table_set(win, len(packed_ptrs), arr, stream or None))
+
+
+def afd_ffn_run_table(win, stage, stream=0) -> int:
+    return _check(lib().afd_ffn_run_table(win, stage, stream or None))
+
+
+def afd_ffn_loop_create(win, n_runs, first_stage, stream):
+    h = ctypes.c_void_p()
+    _check(lib().afd_ffn_loop_create(win, n_runs, first_stage, stream or None, ctypes.byref(h)))
+    return h.value
+
+
+def afd_ffn_loop_launch(loop, stream=0) -> int:
+    return _check(lib().afd_ffn_loop_launch(loop, stream or None))
+
+
+def afd_ffn_loop_destroy(loop) -> int:
+    return _check(lib().afd_ffn_loop_destroy(loop or None))
 
 
 def afd_slot_unpack(win, peer, stage, seq_len, out_ptr, stream=0) -> int:

@@ -9,6 +9,7 @@
 #include <cstdlib>
 #include <cstring>
 #include <mutex>
+#include <new>
 #include <string>
 #include <vector>
 
@@ -77,10 +78,11 @@ int32_t validate(const afd_window_config* c) {
 struct WsLayout {
     int64_t ctrl, peer_counts, blk_counts, blk_base, counts, eoff, tstart1, tstart2;
     int64_t tinfo1, tinfo2, seg1, seg2, tctr, psrc, max_tiles1, max_tiles2;
-    int64_t ids, wts, perm, inv, tok_src, sh_src, h, hs, y, ys, bytes;
+    int64_t ids, wts, perm, inv, tok_src, sh_src, h, hs, y, ys, wtable, bytes;
     int64_t ctrl_ints;
     // control-word offsets inside ctrl (in ints)
     int64_t c_seen_in, c_ret_seq, c_seen_ret, c_cur_seq, c_off, c_T, c_done, c_run_status, c_peer_status;
+    int64_t c_layer_cur, c_nlayers;
 };
 
 WsLayout ws_layout(const afd_window_config& c) {
@@ -99,6 +101,8 @@ WsLayout ws_layout(const afd_window_config& c) {
     w.c_done = ci; ci += 1;
     w.c_run_status = ci; ci += R * afd::kStatusWords;
     w.c_peer_status = ci; ci += P * R * afd::kStatusWords;
+    w.c_layer_cur = ci; ci += 1;
+    w.c_nlayers = ci; ci += 1;
     w.ctrl_ints = ci;
     int64_t cur = 0;
     auto take = [&](int64_t bytes) {
@@ -143,6 +147,7 @@ WsLayout ws_layout(const afd_window_config& c) {
     w.hs = take(64 * tmax * (c.shared_intermediate > 0 ? (c.shared_intermediate + afd::kBK - 1) / afd::kBK : 1));
     w.y = take(2 * np * c.hidden);
     w.ys = take(2 * tmax * c.hidden);
+    w.wtable = take((int64_t)sizeof(afd::Weights) * afd::kMaxLayers);
     w.bytes = cur;
     return w;
 }
@@ -213,6 +218,15 @@ struct afd_window {
     double prof_ms[AFD_PROFILE_SLOTS] = {};
     int prof_runs = 0;
     std::mutex prof_mu;
+    int n_layers = 0;  // entries of the device layer table
+};
+
+// A captured sequence of layer-table runs (afd_ffn_loop_create).
+struct afd_ffn_loop {
+    afd_window* w = nullptr;
+    hipGraph_t graph = nullptr;
+    hipGraphExec_t exec = nullptr;
+    int n_runs = 0;
 };
 
 namespace {
@@ -255,6 +269,9 @@ void fill_ctx(afd_window* w) {
     d.off = ctrl + L.c_off;
     d.Tptr = ctrl + L.c_T;
     d.run_status = ctrl + L.c_run_status;
+    d.layer_cur = ctrl + L.c_layer_cur;
+    d.nlayers = ctrl + L.c_nlayers;
+    d.wtable = (const afd::Weights*)(ws + L.wtable);
     d.peer_status = ctrl + L.c_peer_status;
     d.peer_counts = (int*)(ws + L.peer_counts);
     d.blk_counts = (int*)(ws + L.blk_counts);
@@ -295,6 +312,28 @@ void prof_collect(afd_window* w) {
     }
     w->prof_runs += 1;
     w->ev_pending = false;
+}
+
+// The events a run records for the current profile mode (nullptr: none).
+hipEvent_t* profile_events(afd_window* w, hipEvent_t (&evs)[AFD_PROFILE_SLOTS + 1]) {
+    if (!w->profile) return nullptr;
+    std::lock_guard<std::mutex> g(w->prof_mu);
+    prof_collect(w);
+    for (int i = 0; i <= kProfileUsed; ++i)
+        if (w->profile == 1 || (i >= kGemmFirst && i <= kGemmFirst + (w->profile == 2 ? 2 : 1))) evs[i] = w->ev[i];
+    w->ev_pending = true;
+    return evs;
+}
+
+long long poll_ticks(const afd_window* w) { return (long long)w->cfg.poll_timeout_us * w->ticks_per_us; }
+
+// The four packed regions of one layer's weights (afd_weights_pack layout).
+afd::Weights packed_weights_of(const afd_window_config& c, const void* packed) {
+    int64_t off[4], total = 0;
+    afd::packed_weight_layout(c, off, &total);
+    const char* pw = (const char*)packed;
+    return afd::Weights{pw + off[0], pw + off[2], c.shared_intermediate > 0 ? pw + off[1] : nullptr,
+                        c.shared_intermediate > 0 ? pw + off[3] : nullptr};
 }
 
 }  // namespace
@@ -466,24 +505,102 @@ int32_t afd_ffn_run(afd_window* w, int32_t stage, int32_t layer_idx, const void*
     const afd_window_config& c = w->cfg;
     if (stage < 0 || stage >= c.ring_depth) return fail(AFD_ERR_INVALID, "stage %d out of range", stage);
     if (!aligned(packed_weights, 256)) return fail(AFD_ERR_INVALID, "packed weights must be 256-byte aligned");
-    int64_t off[4], total = 0;
-    afd::packed_weight_layout(c, off, &total);
-    const char* pw = (const char*)packed_weights;
-    afd::Weights wt{pw + off[0], pw + off[2], c.shared_intermediate > 0 ? pw + off[1] : nullptr,
-                    c.shared_intermediate > 0 ? pw + off[3] : nullptr};
+    const afd::Weights wt = packed_weights_of(c, packed_weights);
     hipEvent_t evs[AFD_PROFILE_SLOTS + 1] = {};
-    hipEvent_t* ev = nullptr;
-    if (w->profile) {
-        std::lock_guard<std::mutex> g(w->prof_mu);
-        prof_collect(w);
-        for (int i = 0; i <= kProfileUsed; ++i)
-            if (w->profile == 1 || (i >= kGemmFirst && i <= kGemmFirst + (w->profile == 2 ? 2 : 1))) evs[i] = w->ev[i];
-        ev = evs;
-        w->ev_pending = true;
-    }
-    const long long timeout = (long long)c.poll_timeout_us * w->ticks_per_us;
-    hipError_t e = afd::launch_ffn(w->ctx, stage, layer_idx, wt, timeout, w->num_cu, ev, (hipStream_t)ffn_stream);
+    hipError_t e = afd::launch_ffn(w->ctx, stage, layer_idx, wt, poll_ticks(w), w->num_cu, profile_events(w, evs),
+                                   (hipStream_t)ffn_stream);
     if (e != hipSuccess) return hip_fail(e, "ffn launch");
+    return AFD_OK;
+}
+
+int32_t afd_layer_table_set(afd_window* w, int32_t n_layers, const void* const* packed_weights, void* stream) {
+    if (!w || !packed_weights) return fail(AFD_ERR_INVALID, "NULL argument");
+    if (n_layers < 1 || n_layers > afd::kMaxLayers)
+        return fail(AFD_ERR_INVALID, "n_layers %d outside 1..%d", n_layers, afd::kMaxLayers);
+    std::vector<afd::Weights> tab((size_t)n_layers);
+    for (int i = 0; i < n_layers; ++i) {
+        if (!packed_weights[i] || !aligned(packed_weights[i], 256))
+            return fail(AFD_ERR_INVALID, "layer %d: packed weights NULL or not 256-byte aligned", i);
+        tab[(size_t)i] = packed_weights_of(w->cfg, packed_weights[i]);
+    }
+    hipStream_t st = (hipStream_t)stream;
+    const int32_t n = n_layers;
+    hipError_t e = hipMemcpyAsync((void*)w->ctx.wtable, tab.data(), tab.size() * sizeof(afd::Weights),
+                                  hipMemcpyHostToDevice, st);
+    if (e == hipSuccess) e = hipMemcpyAsync(w->ctx.nlayers, &n, sizeof n, hipMemcpyHostToDevice, st);
+    if (e == hipSuccess) e = hipStreamSynchronize(st);  // the host copies are temporaries
+    if (e != hipSuccess) return hip_fail(e, "layer table copy");
+    w->n_layers = n_layers;
+    return AFD_OK;
+}
+
+int32_t afd_ffn_run_table(afd_window* w, int32_t stage, void* ffn_stream) {
+    if (!w) return fail(AFD_ERR_INVALID, "window is NULL");
+    if (stage < 0 || stage >= w->cfg.ring_depth) return fail(AFD_ERR_INVALID, "stage %d out of range", stage);
+    if (w->n_layers < 1) return fail(AFD_ERR_INVALID, "no layer table set (afd_layer_table_set)");
+    hipEvent_t evs[AFD_PROFILE_SLOTS + 1] = {};
+    hipError_t e = afd::launch_ffn(w->ctx, stage, -1, afd::Weights{}, poll_ticks(w), w->num_cu,
+                                   profile_events(w, evs), (hipStream_t)ffn_stream);
+    if (e != hipSuccess) return hip_fail(e, "ffn launch");
+    return AFD_OK;
+}
+
+int32_t afd_ffn_loop_create(afd_window* w, int32_t n_runs, int32_t first_stage, void* stream, afd_ffn_loop** out) {
+    if (!w || !out) return fail(AFD_ERR_INVALID, "NULL argument");
+    *out = nullptr;
+    const afd_window_config& c = w->cfg;
+    if (n_runs < 1) return fail(AFD_ERR_INVALID, "n_runs %d < 1", n_runs);
+    if (first_stage < 0 || first_stage >= c.ring_depth)
+        return fail(AFD_ERR_INVALID, "first_stage %d out of range", first_stage);
+    if (w->n_layers < 1) return fail(AFD_ERR_INVALID, "no layer table set (afd_layer_table_set)");
+    if (w->profile) return fail(AFD_ERR_INVALID, "per-kernel profiling must be off while capturing");
+    if (!stream) return fail(AFD_ERR_INVALID, "capture needs a created stream, not the null stream");
+    hipStream_t st = (hipStream_t)stream;
+    hipError_t e = hipStreamBeginCapture(st, hipStreamCaptureModeThreadLocal);
+    if (e != hipSuccess) return hip_fail(e, "begin capture");
+    for (int i = 0; i < n_runs && e == hipSuccess; ++i)
+        e = afd::launch_ffn(w->ctx, (first_stage + i) % c.ring_depth, -1, afd::Weights{}, poll_ticks(w), w->num_cu,
+                            nullptr, st);
+    hipGraph_t g = nullptr;
+    const hipError_t e2 = hipStreamEndCapture(st, &g);
+    if (e == hipSuccess) e = e2;
+    hipGraphExec_t x = nullptr;
+    if (e == hipSuccess) e = hipGraphInstantiate(&x, g, nullptr, nullptr, 0);
+    if (e != hipSuccess) {
+        if (g) (void)hipGraphDestroy(g);
+        return hip_fail(e, "capture of the FFN loop");
+    }
+    afd_ffn_loop* l = new (std::nothrow) afd_ffn_loop;
+    if (!l) {
+        (void)hipGraphExecDestroy(x);
+        (void)hipGraphDestroy(g);
+        return fail(AFD_ERR_DEVICE, "out of host memory");
+    }
+    l->w = w;
+    l->graph = g;
+    l->exec = x;
+    l->n_runs = n_runs;
+    *out = l;
+    return AFD_OK;
+}
+
+int32_t afd_ffn_loop_launch(afd_ffn_loop* l, void* stream) {
+    if (!l) return fail(AFD_ERR_INVALID, "loop is NULL");
+    hipError_t e = hipGraphLaunch(l->exec, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "loop launch");
+    return AFD_OK;
+}
+
+int32_t afd_ffn_loop_destroy(afd_ffn_loop* l) {
+    if (!l) return AFD_OK;
+    hipError_t e = hipSuccess;
+    if (l->exec) e = hipGraphExecDestroy(l->exec);
+    if (l->graph) {
+        const hipError_t e2 = hipGraphDestroy(l->graph);
+        if (e == hipSuccess) e = e2;
+    }
+    delete l;
+    if (e != hipSuccess) return hip_fail(e, "loop destroy");
     return AFD_OK;
 }
 

@@ -15,6 +15,7 @@ namespace afd {
 constexpr int kRouteChunk = 16;
 constexpr int kMaxTopK = 16;
 constexpr int kMaxPeers = 64;
+constexpr int kMaxLayers = 1024;  // entries of the device layer table
 constexpr int kMaxExperts = 1024;
 
 // Grouped-GEMM tile: up to kBX token rows (8 blocks of 32) of one group x kBW
@@ -41,6 +42,8 @@ constexpr int kSegs = 2 * kXcds;
 // Per-stage run status words: [status, failed_peer, seq of peer 0, T].
 constexpr int kStatusWords = 4;
 
+struct Weights;
+
 // Everything a kernel needs, passed by value.
 struct DevCtx {
     // configuration
@@ -66,6 +69,9 @@ struct DevCtx {
     int* off;          // [P+1] fan-in offsets
     int* Tptr;         // [1]   total tokens of the current run
     int* run_status;   // [R][kStatusWords]
+    int* layer_cur;    // [1]   layer of the current run (from the headers in layer-table runs)
+    int* nlayers;      // [1]   entries of the layer table (0: none set)
+    const Weights* wtable;  // [kMaxLayers] packed weights of each layer (layer-table runs)
     int* peer_status;  // [P*R][kStatusWords]
     // routing / dispatch
     int* peer_counts;  // [P][E]

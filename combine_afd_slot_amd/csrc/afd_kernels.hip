@@ -190,8 +190,10 @@ hipError_t launch_unpack(const DevCtx& c, int peer, int stage, int seq_len, int 
 // peers' num_tokens ("Data on the wire", Steps 2-3).  Nothing is consumed
 // unless every peer arrived with a valid header (or shutdown).
 // ---------------------------------------------------------------------------
+// layer < 0: a layer-table run; the layer is the one every peer's header
+// carries, and it must have an entry in the table.
 __global__ __launch_bounds__(64) void k_wait(DevCtx c, int s, int layer, long long timeout) {
-    __shared__ int s_flag[kMaxPeers], s_err[kMaxPeers], s_ntok[kMaxPeers], s_shut[kMaxPeers];
+    __shared__ int s_flag[kMaxPeers], s_err[kMaxPeers], s_ntok[kMaxPeers], s_shut[kMaxPeers], s_layer[kMaxPeers];
     const int p = threadIdx.x;
     int* st = c.run_status + s * kStatusWords;
     if (p < c.P) {
@@ -199,7 +201,7 @@ __global__ __launch_bounds__(64) void k_wait(DevCtx c, int s, int layer, long lo
         int* flag = (int*)c.in_win + idx;
         const int seen = c.seen_in[idx];
         const long long t0 = wall_clock64();
-        int f = seen, err = AFD_OK, ntok = 0, shut = 0;
+        int f = seen, err = AFD_OK, ntok = 0, shut = 0, hl = -1;
         for (;;) {
             f = ld_acquire(flag);
             if (f != seen) break;
@@ -218,7 +220,10 @@ __global__ __launch_bounds__(64) void k_wait(DevCtx c, int s, int layer, long lo
 #pragma unroll
             for (int i = 0; i < 3; ++i) hv[i] = hq[i];
             err = header_decode((const int32_t*)hv, c.E, &h);
-            if (err == AFD_OK) err = inbound_check(h, p, s, layer, c.token_cap, f);
+            if (err == AFD_OK) {
+                hl = h.layer_idx;
+                err = inbound_check(h, p, s, layer < 0 ? hl : layer, c.token_cap, f);
+            }
             if (err == AFD_OK) {
                 ntok = h.num_tokens;
                 shut = (h.flags & (int)AFD_FLAG_SHUTDOWN) != 0;
@@ -228,6 +233,7 @@ __global__ __launch_bounds__(64) void k_wait(DevCtx c, int s, int layer, long lo
         s_err[p] = err;
         s_ntok[p] = ntok;
         s_shut[p] = shut;
+        s_layer[p] = hl;
     }
     __syncthreads();
     if (threadIdx.x == 0) {
@@ -240,6 +246,20 @@ __global__ __launch_bounds__(64) void k_wait(DevCtx c, int s, int layer, long lo
             shut |= s_shut[q];
         }
         if (status == AFD_OK && shut) status = AFD_SHUTDOWN;
+        int L = layer;
+        if (layer < 0 && status == AFD_OK) {
+            L = s_layer[0];
+            for (int q = 1; q < c.P && status == AFD_OK; ++q)
+                if (s_layer[q] != L) {
+                    status = AFD_ERR_HEADER;
+                    failed = q;
+                }
+            if (status == AFD_OK && (L < 0 || L >= *c.nlayers)) {
+                status = AFD_ERR_HEADER;
+                failed = 0;
+            }
+        }
+        *c.layer_cur = L;
         int T = 0;
         if (status == AFD_OK || status == AFD_SHUTDOWN) {
             c.off[0] = 0;
@@ -1343,8 +1363,10 @@ __device__ __forceinline__ void gemm_run(const DevCtx& c, const Weights& w, Gemm
 }
 
 template <int MODE>
-__global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(DevCtx c, const int* status, Weights w) {
+__global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(DevCtx c, const int* status, Weights w_arg, int layer) {
     if (*status != AFD_OK) return;
+    // layer < 0: the layer-table entry of the run's layer (checked by k_wait)
+    const Weights w = layer < 0 ? c.wtable[*c.layer_cur] : w_arg;
     // One LDS array: the operand ring and, past it, the tile-index slot.
     // (With a second __shared__ variable the compiler attaches alias scopes
     // to LDS accesses and then makes every LDS read wait for the direct-to-
@@ -1495,7 +1517,7 @@ __global__ __launch_bounds__(64) void k_publish(DevCtx c, const int* status, int
         f.flags = 0;
         f.seq = rs;
         f.echo_seq = c.cur_seq[p];
-        f.layer_idx = layer;
+        f.layer_idx = layer < 0 ? *c.layer_cur : layer;
         f.stage_idx = s;
         f.num_tokens = n_p;
         f.routed_tokens = n_p;
@@ -1509,6 +1531,8 @@ __global__ __launch_bounds__(64) void k_publish(DevCtx c, const int* status, int
 }
 
 // ---------------------------------------------------------------------------
+// layer < 0: a layer-table run (the layer from the headers, the weights from
+// the device table; `w` is unused).
 hipError_t launch_ffn(const DevCtx& c, int stage, int layer, const Weights& w, long long timeout_ticks, int num_cu,
                       hipEvent_t* ev, hipStream_t st) {
     int* status = c.run_status + stage * kStatusWords;
@@ -1534,9 +1558,9 @@ hipError_t launch_ffn(const DevCtx& c, int stage, int layer, const Weights& w, l
     mark();
     k_permute<<<c.NB, 256, 0, st>>>(c, status);
     mark();
-    k_gemm<1><<<num_cu, kGemmThreads, 0, st>>>(c, status, w);
+    k_gemm<1><<<num_cu, kGemmThreads, 0, st>>>(c, status, w, layer);
     mark();
-    k_gemm<2><<<num_cu, kGemmThreads, 0, st>>>(c, status, w);
+    k_gemm<2><<<num_cu, kGemmThreads, 0, st>>>(c, status, w, layer);
     mark();
     int cgrid = Tmax < num_cu * 8 ? Tmax : num_cu * 8;
     if (cgrid < 1) cgrid = 1;

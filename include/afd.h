@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define AFD_ABI_VERSION 2
+#define AFD_ABI_VERSION 3
 
 /* Header flags bit 1: shutdown sentinel ("Window and slot layout"). */
 #define AFD_FLAG_SHUTDOWN 0x2u
@@ -232,6 +232,55 @@ int32_t afd_slot_pack(afd_window* w, int32_t peer, int32_t stage, int32_t layer_
  * out of range). */
 int32_t afd_ffn_run(afd_window* w, int32_t stage, int32_t layer_idx, const void* packed_weights,
                     void* ffn_stream);
+
+/* Layer-select weights ("[RFC]: Async AFD for Prefill on Ascend NPU",
+ * "Architecture": layer-select operators take the address table of every
+ * layer's weights and a layer index held on the device; "FFN execution
+ * modes").  Copies a table of n_layers packed weight copies (each written by
+ * afd_weights_pack for this window's configuration, 256-byte aligned,
+ * borrowed: they must stay valid while runs that may select them are in
+ * flight) into the window's device table; entry i serves layer_idx i.
+ * packed_weights is a host array of n_layers device pointers.  Synchronizes
+ * `stream` (the host array may be freed on return).  A later call replaces
+ * the table; runs captured earlier read the new entries (the table and its
+ * size live on the device).  Errors: AFD_ERR_INVALID (NULL arguments,
+ * n_layers outside 1..1024, a NULL or misaligned entry), AFD_ERR_DEVICE. */
+int32_t afd_layer_table_set(afd_window* w, int32_t n_layers, const void* const* packed_weights, void* stream);
+
+/* afd_ffn_run with the layer identity kept on the device ("[RFC]: Async AFD
+ * for Prefill on Ascend NPU", "FFN execution modes", eager mode): the layer is
+ * the layer_idx that every peer's inbound header of the stage carries, and
+ * the weights are that entry of the layer table.  Headers that disagree, or
+ * a layer outside the table, fail the run with AFD_ERR_HEADER in the stage's
+ * status word (nothing is consumed or published, as for any header error).
+ * The return headers carry the selected layer.  The call reads nothing back
+ * and allocates nothing, so it can be captured into a HIP graph.
+ * Errors: AFD_ERR_INVALID (NULL window, stage out of range, no layer table
+ * set). */
+int32_t afd_ffn_run_table(afd_window* w, int32_t stage, void* ffn_stream);
+
+/* A fixed-length FFN loop captured once and replayed ("[RFC]: Async AFD for
+ * Prefill on Ascend NPU", "FFN execution modes", graph mode: fixed-shape
+ * buffers, a fixed number of iterations, receive steps that spin on the
+ * device).  afd_ffn_loop_create captures n_runs consecutive
+ * afd_ffn_run_table runs on stages first_stage, first_stage+1, ... (mod
+ * ring_depth) from `stream` (a created stream, not the null stream) into a
+ * HIP graph and instantiates it; nothing runs yet.  afd_ffn_loop_launch
+ * enqueues one replay of all n_runs runs on `stream`: each run waits on the
+ * device for its stage's inbound messages (peers pack on their own streams,
+ * and may enqueue the packs of later runs once the return of the run that
+ * last used the stage is unpacked on their stream), and takes its layer and
+ * weights from the headers and the layer table at run time.  Sequence
+ * numbers and mirrors live on the device, so replays continue where the
+ * last run stopped.  The loop borrows the window: destroy the loop first.
+ * Errors: AFD_ERR_INVALID (NULL arguments, n_runs < 1, first_stage out of
+ * range, no layer table, per-kernel profiling on, null stream),
+ * AFD_ERR_DEVICE (capture, instantiation or launch failed). */
+typedef struct afd_ffn_loop afd_ffn_loop; /* opaque, library-owned */
+int32_t afd_ffn_loop_create(afd_window* w, int32_t n_runs, int32_t first_stage, void* stream, afd_ffn_loop** out);
+int32_t afd_ffn_loop_launch(afd_ffn_loop* loop, void* stream);
+/* Frees the loop's graph; NULL is accepted. */
+int32_t afd_ffn_loop_destroy(afd_ffn_loop* loop);
 
 /* Attention side, peer `peer`: wait (bounded, on the device) for the return
  * flag of (peer, stage), check its header (echo_seq must be the seq this

@@ -23,7 +23,7 @@ import pytest
 
 from combine_afd_slot_amd import build
 
-KERNELS = ["_ZN3afd6k_gemmILi1EEEvNS_6DevCtxEPKiNS_7WeightsE", "_ZN3afd6k_gemmILi2EEEvNS_6DevCtxEPKiNS_7WeightsE"]
+KERNELS = ["_ZN3afd6k_gemmILi1EEEvNS_6DevCtxEPKiNS_7WeightsEi", "_ZN3afd6k_gemmILi2EEEvNS_6DevCtxEPKiNS_7WeightsEi"]
 MIN_MFMA_TO_READ = 18
 
 
