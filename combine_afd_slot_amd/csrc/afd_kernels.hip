@@ -364,9 +364,10 @@ __device__ inline float wave_sum(float x) {
 // ---------------------------------------------------------------------------
 template <int EPL>
 __global__ __launch_bounds__(64 * kRouteChunk) void k_route(DevCtx c, int* status, int s) {
-    if (*status != AFD_OK) return;
+    const int st = *status;  // loaded together with the peer offsets of chunk_range
     int t_begin, t_end, p;
-    if (!chunk_range(c, blockIdx.x, t_begin, t_end, p)) return;
+    const bool have = chunk_range(c, blockIdx.x, t_begin, t_end, p);
+    if (st != AFD_OK || !have) return;
     __shared__ int hist[kMaxExperts];
     const int lane = threadIdx.x & 63;
     const int E = c.E, K = c.K;
@@ -677,11 +678,8 @@ __device__ void plan_fill(const DevCtx& c, int T, const int* s_eoff, int (*s_t)[
 // chunk's tokens per expert and a population count.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_permute(DevCtx c, const int* status) {
-    if (*status != AFD_OK) return;
     static_assert(kRouteChunk <= 32 && kRouteChunk * kMaxTopK <= 256, "chunk masks and one pair per thread");
-    const int T = *c.Tptr;
-    int t0 = 0, t1 = 0, p = 0;
-    const bool have = chunk_range(c, blockIdx.x, t0, t1, p);
+    static_assert(kMaxExperts <= 4 * 256, "at most four expert counts per thread");
     __shared__ int sh[16];
     __shared__ long long sh4[16];
     __shared__ int s_eoff[kMaxExperts + 1];
@@ -690,19 +688,40 @@ __global__ __launch_bounds__(256) void k_permute(DevCtx c, const int* status) {
     __shared__ uint32_t emask[kMaxExperts];
     __shared__ uint64_t ltok[kRouteChunk];
     const int E = c.E, K = c.K, tid = threadIdx.x;
+    // Loads that do not depend on each other are issued together, so their
+    // latencies overlap: the status word, the token count and the peer
+    // offsets (chunk_range); then this chunk's expert ids and token-row
+    // addresses with the expert counts; then the chunk's base in each of its
+    // pairs' expert groups, which arrives while the plan is computed.
+    const int st = *status;
+    const int T = *c.Tptr;
+    int t0 = 0, t1 = 0, p = 0;
+    const bool have = chunk_range(c, blockIdx.x, t0, t1, p);
+    if (st != AFD_OK) return;
+    const int nt = have ? t1 - t0 : 0, np = nt * K;
+    int e = 0;
+    uint64_t trow = 0;
+    if (tid < np) e = c.ids[(int64_t)t0 * K + tid];
+    if (tid < nt) trow = c.tok_src[t0 + tid];
+    const int per = (E + 255) / 256;
+    const int e0 = tid * per, e1 = min(E, e0 + per);
+    int cnt[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) cnt[j] = e0 + j < e1 ? c.counts[e0 + j] : 0;
+    int base = 0;
+    if (tid < np) base = c.blk_base[(int64_t)e * c.NB + blockIdx.x];
     {
-        const int per = (E + 255) / 256;
-        const int e0 = tid * per, e1 = min(E, e0 + per);
-        int sum = 0;
-        for (int e = e0; e < e1; ++e) sum += c.counts[e];
-        int run = block_excl_scan(sum, sh);
-        for (int e = e0; e < e1; ++e) {
-            s_eoff[e] = run;
-            run += c.counts[e];
-        }
+        int run = block_excl_scan(cnt[0] + cnt[1] + cnt[2] + cnt[3], sh);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            if (e0 + j < e1) {
+                s_eoff[e0 + j] = run;
+                run += cnt[j];
+            }
         if (tid == 255) s_eoff[E] = run;
     }
-    for (int e = tid; e < E; e += 256) emask[e] = 0u;
+    for (int q = tid; q < E; q += 256) emask[q] = 0u;
+    if (tid < nt) ltok[tid] = trow;
     __syncthreads();
     plan_prefix(c, T, s_eoff, s_t, s_c, sh4);
     if (blockIdx.x == 0) {
@@ -711,17 +730,11 @@ __global__ __launch_bounds__(256) void k_permute(DevCtx c, const int* status) {
     }
     plan_fill(c, T, s_eoff, s_t);
     if (!have) return;
-    const int np = (t1 - t0) * K;
-    if (tid < t1 - t0) ltok[tid] = c.tok_src[t0 + tid];
-    int e = 0;
-    if (tid < np) {
-        e = c.ids[(int64_t)t0 * K + tid];
-        atomicOr(&emask[e], 1u << (tid / K));
-    }
+    if (tid < np) atomicOr(&emask[e], 1u << (tid / K));
     __syncthreads();
     if (tid < np) {
         const int tl = tid / K;
-        const int pos = s_eoff[e] + c.blk_base[(int64_t)e * c.NB + blockIdx.x] + __popc(emask[e] & ((1u << tl) - 1u));
+        const int pos = s_eoff[e] + base + __popc(emask[e] & ((1u << tl) - 1u));
         const int f = t0 * K + tid;
         if (pos < T * K) {
             c.perm[pos] = f;
@@ -1445,8 +1458,9 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(DevCtx c, const int* s
 // ---------------------------------------------------------------------------
 template <int KK>
 __global__ __launch_bounds__(256) void k_combine(DevCtx c, const int* status, int s, int layer) {
-    if (*status != AFD_OK) return;
+    const int st = *status;  // loaded together with the token count
     const int T = *c.Tptr;
+    if (st != AFD_OK) return;
     const int H = c.H, H8 = c.H / 8;
     const int npairs = T * KK;
     for (int t = blockIdx.x; t < T; t += gridDim.x) {
