@@ -65,7 +65,7 @@ int32_t validate(const afd_window_config* c) {
     // the GEMM kernels address rows with 32-bit byte offsets from a base
     const int64_t lim = (int64_t)1 << 32;
     int64_t fb[AFD_NUM_FIELDS], slot = 0;
-    afd::slot_field_bytes(c->token_cap, c->hidden, c->num_experts, fb);
+    afd::slot_field_bytes(c->token_cap, c->hidden, c->num_experts, c->shared_intermediate > 0, fb);
     for (int i = 0; i < AFD_NUM_FIELDS; ++i) slot += afd::align_up(fb[i]);
     const int64_t window = afd::align_up(4LL * c->num_peers * c->ring_depth) + slot * c->num_peers * c->ring_depth;
     if (window >= lim || 2 * tmax * c->top_k * c->intermediate >= lim || 2 * tmax * c->shared_intermediate >= lim ||
@@ -155,7 +155,7 @@ WsLayout ws_layout(const afd_window_config& c) {
 void layout_from(const afd_window_config& c, afd_layout* L, WsLayout* wl) {
     std::memset(L, 0, sizeof *L);
     int64_t fb[AFD_NUM_FIELDS];
-    afd::slot_field_bytes(c.token_cap, c.hidden, c.num_experts, fb);
+    afd::slot_field_bytes(c.token_cap, c.hidden, c.num_experts, c.shared_intermediate > 0, fb);
     int64_t cur = 0;
     for (int i = 0; i < AFD_NUM_FIELDS; ++i) {
         L->field_off[i] = cur;

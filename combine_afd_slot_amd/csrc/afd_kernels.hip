@@ -67,9 +67,11 @@ __device__ inline void st_release(int* p, int v) {
 // header and a release store of the flag ("Window and slot layout": payload
 // and flag ordered on one stream; the flag value is the sender's seq).
 // ---------------------------------------------------------------------------
+// shared: the window carries shared rows (shared_x, shared_idx); a routed-
+// only window does not.
 __global__ __launch_bounds__(256) void k_pack_payload(char* slot, int64_t o_rt, int64_t o_rx, int64_t o_si,
                                                       int64_t o_sx, const uint4* hidden, const float* logits,
-                                                      int n, int H, int E) {
+                                                      int n, int H, int E, int shared) {
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
     const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const int64_t nch = (int64_t)n * H / 8;
@@ -78,13 +80,15 @@ __global__ __launch_bounds__(256) void k_pack_payload(char* slot, int64_t o_rt, 
     for (int64_t i = gid; i < nch; i += stride) {
         uint4 v = hidden[i];
         rx[i] = v;
-        sx[i] = v;
+        if (shared) sx[i] = v;
     }
     float* rt = (float*)(slot + o_rt);
     const int64_t nl = (int64_t)n * E;
     for (int64_t i = gid; i < nl; i += stride) rt[i] = logits[i];
-    int* si = (int*)(slot + o_si);
-    for (int64_t i = gid; i < n; i += stride) si[i] = (int)i;
+    if (shared) {
+        int* si = (int*)(slot + o_si);
+        for (int64_t i = gid; i < n; i += stride) si[i] = (int)i;
+    }
 }
 
 __global__ void k_pack_publish(char* slot, int* flag, afd_header_fields f) {
@@ -107,7 +111,7 @@ hipError_t launch_pack(const DevCtx& c, int peer, int stage, int layer, int seq_
         if (grid < 1) grid = 1;
         k_pack_payload<<<grid, 256, 0, st>>>(slot, c.foff[AFD_FIELD_ROUTE_TABLE], c.foff[AFD_FIELD_ROUTED_X],
                                              c.foff[AFD_FIELD_SHARED_IDX], c.foff[AFD_FIELD_SHARED_X],
-                                             (const uint4*)hidden, logits, seq_len, c.H, c.E);
+                                             (const uint4*)hidden, logits, seq_len, c.H, c.E, c.has_shared);
     }
     afd_header_fields f;
     f.flags = (int32_t)flags;
@@ -117,7 +121,7 @@ hipError_t launch_pack(const DevCtx& c, int peer, int stage, int layer, int seq_
     f.stage_idx = stage;
     f.num_tokens = seq_len;
     f.routed_tokens = seq_len;
-    f.shared_tokens = seq_len;
+    f.shared_tokens = c.has_shared ? seq_len : 0;
     f.src_peer = peer;
     f.n_counts = c.E;
     k_pack_publish<<<1, 64, 0, st>>>(slot + c.foff[AFD_FIELD_HEADER], (int*)c.in_win + peer * c.R + stage, f);
@@ -222,7 +226,7 @@ __global__ __launch_bounds__(64) void k_wait(DevCtx c, int s, int layer, long lo
             err = header_decode((const int32_t*)hv, c.E, &h);
             if (err == AFD_OK) {
                 hl = h.layer_idx;
-                err = inbound_check(h, p, s, layer < 0 ? hl : layer, c.token_cap, f);
+                err = inbound_check(h, p, s, layer < 0 ? hl : layer, c.token_cap, f, c.has_shared);
             }
             if (err == AFD_OK) {
                 ntok = h.num_tokens;
@@ -391,8 +395,10 @@ __global__ __launch_bounds__(64 * kRouteChunk) void k_route(DevCtx c, int* statu
     bool si_bad = false;
     if (live && lane == 0) {
         c.tok_src[t] = (uint64_t)(slot + c.foff[AFD_FIELD_ROUTED_X] + (int64_t)r * c.H * 2);
-        c.sh_src[t] = (uint64_t)(slot + c.foff[AFD_FIELD_SHARED_X] + (int64_t)r * c.H * 2);
-        si_bad = ((const int*)(slot + c.foff[AFD_FIELD_SHARED_IDX]))[r] != r;
+        if (c.has_shared) {  // (a routed-only window carries no shared rows)
+            c.sh_src[t] = (uint64_t)(slot + c.foff[AFD_FIELD_SHARED_X] + (int64_t)r * c.H * 2);
+            si_bad = ((const int*)(slot + c.foff[AFD_FIELD_SHARED_IDX]))[r] != r;
+        }
     }
     __syncthreads();  // hist zeroed
     if (live) {
@@ -1535,7 +1541,7 @@ __global__ __launch_bounds__(64) void k_publish(DevCtx c, const int* status, int
         f.stage_idx = s;
         f.num_tokens = n_p;
         f.routed_tokens = n_p;
-        f.shared_tokens = n_p;
+        f.shared_tokens = c.has_shared ? n_p : 0;
         f.src_peer = p;
         f.n_counts = c.E;
         header_encode_fixed(f, w);

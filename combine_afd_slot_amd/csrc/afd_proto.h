@@ -29,13 +29,17 @@ constexpr int64_t kAlign = 256;
 
 AFD_HD int64_t align_up(int64_t n, int64_t a = kAlign) { return (n + a - 1) / a * a; }
 
-// Per-slot field sizes (unaligned bytes).
-AFD_HD void slot_field_bytes(int64_t token_cap, int64_t hidden, int64_t experts, int64_t out[AFD_NUM_FIELDS]) {
+// Per-slot field sizes (unaligned bytes).  Without a shared expert on the
+// FFN side the protocol is routed-only ("[RFC]: Async AFD for Prefill on
+// Ascend NPU", "Shared-expert ownership": no shared-expert data crosses the
+// data plane), so shared_idx and shared_x take no space.
+AFD_HD void slot_field_bytes(int64_t token_cap, int64_t hidden, int64_t experts, bool shared,
+                             int64_t out[AFD_NUM_FIELDS]) {
     out[AFD_FIELD_HEADER] = 4 * (AFD_HDR_WORDS + experts);
     out[AFD_FIELD_ROUTE_TABLE] = 4 * token_cap * experts;
     out[AFD_FIELD_ROUTED_X] = 2 * token_cap * hidden;
-    out[AFD_FIELD_SHARED_IDX] = 4 * token_cap;
-    out[AFD_FIELD_SHARED_X] = 2 * token_cap * hidden;
+    out[AFD_FIELD_SHARED_IDX] = shared ? 4 * token_cap : 0;
+    out[AFD_FIELD_SHARED_X] = shared ? 2 * token_cap * hidden : 0;
 }
 
 // Header: encode into `w` (12 + n_counts words).
@@ -83,11 +87,13 @@ AFD_HD int32_t header_decode(const int32_t* w, int32_t expect_counts, afd_header
 // message must belong to this (peer, stage, layer), fit the slot, carry the
 // seq of the flag that announced it, and (one FFN replica) route and share
 // every token.
+// shared: the window carries shared rows (every token has one); routed-only
+// messages carry none (shared_tokens 0).
 AFD_HD int32_t inbound_check(const afd_header_fields& f, int32_t peer, int32_t stage, int32_t layer,
-                             int32_t token_cap, int32_t flag_seq) {
+                             int32_t token_cap, int32_t flag_seq, bool shared) {
     if (f.src_peer != peer || f.stage_idx != stage || f.layer_idx != layer) return AFD_ERR_HEADER;
     if (f.num_tokens < 0 || f.num_tokens > token_cap) return AFD_ERR_HEADER;
-    if (f.routed_tokens != f.num_tokens || f.shared_tokens != f.num_tokens) return AFD_ERR_HEADER;
+    if (f.routed_tokens != f.num_tokens || f.shared_tokens != (shared ? f.num_tokens : 0)) return AFD_ERR_HEADER;
     if (f.seq != flag_seq) return AFD_ERR_HEADER;
     return AFD_OK;
 }

@@ -108,7 +108,12 @@ typedef struct afd_window afd_window; /* opaque, library-owned */
  * Limits: 1 <= num_peers <= 64; 1 <= ring_depth <= 4; token_cap >= 1;
  * hidden, intermediate, shared_intermediate multiples of 8 (16-byte rows);
  * 1 <= top_k <= min(num_experts, 16); 1 <= num_experts <= 1024;
- * shared_intermediate 0 = no shared expert; renormalize 0 or 1;
+ * shared_intermediate 0 = no shared expert on the FFN side: the routed-only
+ * protocol ("[RFC]: Async AFD for Prefill on Ascend NPU", "Shared-expert
+ * ownership"), where the slots have no shared_idx / shared_x space (both
+ * fields 0 bytes), nothing is copied into them, and headers carry
+ * shared_tokens = 0 (the attention side adds its own shared branch to the
+ * returned routed output); renormalize 0 or 1;
  * poll_timeout_us >= 1. */
 typedef struct afd_window_config {
     uint32_t struct_size;

@@ -14,6 +14,11 @@ Readings where the page is silent (also listed in the design notes):
     tokens in every field: route_table fp32 [token_cap][E] (router logits),
     routed_x bf16 [token_cap][H], shared_idx int32 [token_cap],
     shared_x bf16 [token_cap][H];
+  * a window without a shared expert on the FFN side follows the
+    routed-only protocol of "[RFC]: Async AFD for Prefill on Ascend NPU",
+    section "Shared-expert ownership" (no shared-expert data on the data
+    plane): shared_idx and shared_x are 0 bytes and headers carry
+    shared_tokens = 0;
   * flags are int32; the flag array also starts 256-byte aligned (offset 0)
     and the first slot starts at the next 256-byte boundary after it;
   * header word order: magic, version, flags, seq, echo_seq, layer_idx,
@@ -42,21 +47,21 @@ def align_up(n: int, a: int = ALIGN) -> int:
     return (n + a - 1) // a * a
 
 
-def slot_fields(token_cap: int, hidden: int, num_experts: int) -> dict:
-    """Byte size of each slot field before alignment."""
+def slot_fields(token_cap: int, hidden: int, num_experts: int, shared: bool = True) -> dict:
+    """Byte size of each slot field before alignment (shared=False: routed-only)."""
     return {
         "header": 4 * (HEADER_WORDS + num_experts),
         "route_table": 4 * token_cap * num_experts,
         "routed_x": 2 * token_cap * hidden,
-        "shared_idx": 4 * token_cap,
-        "shared_x": 2 * token_cap * hidden,
+        "shared_idx": 4 * token_cap if shared else 0,
+        "shared_x": 2 * token_cap * hidden if shared else 0,
     }
 
 
 def window_layout(num_peers: int, ring_depth: int, token_cap: int, hidden: int,
-                  num_experts: int) -> dict:
+                  num_experts: int, shared: bool = True) -> dict:
     """Offsets of one window (flags, then slots), relative to its start."""
-    sizes = slot_fields(token_cap, hidden, num_experts)
+    sizes = slot_fields(token_cap, hidden, num_experts, shared)
     off, cur = {}, 0
     for name in FIELDS:
         off[name] = cur

@@ -50,7 +50,8 @@ def test_layout_matches_reference(kw):
     cfg = afd.make_config(**kw)
     L = afd.afd_layout_compute(cfg)
     R = kw.get("ring_depth", 1)
-    r = ref.window_layout(kw["num_peers"], R, kw["token_cap"], kw["hidden"], kw["num_experts"])
+    r = ref.window_layout(kw["num_peers"], R, kw["token_cap"], kw["hidden"], kw["num_experts"],
+                          shared=kw["shared_intermediate"] > 0)
     for i, name in enumerate(ref.FIELDS):
         assert L.field_off[i] == r["field_off"][name], name
         assert L.field_bytes[i] == r["field_bytes"][name], name

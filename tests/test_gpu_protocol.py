@@ -90,6 +90,53 @@ def test_return_header_and_flags():
         assert all(s.peer_status(p).status == 0 for p in range(2))
 
 
+def test_routed_only_window(orc):
+    """No shared expert on the FFN side: the routed-only protocol ("[RFC]:
+    Async AFD for Prefill on Ascend NPU", "Shared-expert ownership").  The
+    slots have no shared fields, messages and replies carry shared_tokens =
+    0, the output is the routed branch alone, and a message that claims
+    shared rows is a header error."""
+    wl = small_workload("routed_only", seq_lens=(19, 0, 30), hidden=64, num_experts=8, top_k=2,
+                        intermediate=48, shared_intermediate=0, token_cap=32)
+    inp = make_inputs(wl)
+    with FfnSession(wl, inp, poll_timeout_us=200_000) as s:
+        L = s.layout
+        assert L.field_bytes[3] == 0 and L.field_bytes[4] == 0
+        assert L.slot_bytes == sum(ref.align_up(L.field_bytes[i]) for i in range(3))
+        s.pack_all(layer=1)
+        for p, n in enumerate(wl.seq_lens):
+            so = _slot_off(s, L.in_off, p, 0)
+            rx = np.frombuffer(afd.afd_debug_read(s.win, so + L.field_off[2], 2 * n * wl.hidden), np.uint16)
+            np.testing.assert_array_equal(rx.reshape(n, wl.hidden), inp["x"][p])
+            d = ref.decode_header(_read_header(s, 0, p)[0], wl.num_experts)
+            assert d["num_tokens"] == n and d["routed_tokens"] == n and d["shared_tokens"] == 0
+        s.run(layer=1)
+        s.ffn_stream.synchronize()
+        assert s.status().status == 0
+        for p, n in enumerate(wl.seq_lens):
+            if n:
+                d = ref.decode_header(_read_header(s, 1, p)[0], wl.num_experts)
+                assert d["num_tokens"] == n and d["shared_tokens"] == 0
+        s.unpack_all()
+        r = orc.ffn(inp["x"], inp["l"], inp["W13"], inp["W2"], None, None, K=wl.top_k)
+        for p, o in enumerate(s.outputs_f32()):
+            assert row_rel_err(o, r["out_p"][p]) <= ROW_REL_TOL
+        # a message with shared rows on a routed-only window
+        s.pack_all(layer=1)
+        hw, off = _read_header(s, 0, 2)
+        bad = hw.copy()
+        bad[ref.WORD["shared_tokens"]] = wl.seq_lens[2]
+        afd.afd_debug_write(s.win, off, bad.tobytes())
+        s.run(layer=1)
+        st = s.status()
+        assert st.status == afd.AFD_ERR_HEADER and st.failed_peer == 2
+        afd.afd_debug_write(s.win, off, hw.tobytes())
+        s.run(layer=1)
+        s.ffn_stream.synchronize()
+        assert s.status().status == 0
+        s.unpack_all()
+
+
 def test_missing_peer_times_out_then_recovers(orc):
     say("[protocol] timeout (20 ms bound), then recovery")
     s, inp = _session(timeout_us=20_000)
