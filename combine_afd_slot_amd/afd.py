@@ -36,7 +36,7 @@ HDR_WORDS = 12
 # Every symbol include/afd.h declares.
 EXPORTS = (
     "afd_layout_compute", "afd_window_create", "afd_window_destroy", "afd_window_layout",
-    "afd_slot_pack", "afd_weights_pack", "afd_ffn_run", "afd_layer_table_set", "afd_ffn_run_table",
+    "afd_slot_pack", "afd_weights_pack", "afd_ffn_run", "afd_ffn_run_ready", "afd_layer_table_set", "afd_ffn_run_table",
     "afd_ffn_loop_create", "afd_ffn_loop_launch", "afd_ffn_loop_destroy",
     "afd_slot_unpack", "afd_window_status", "afd_peer_status",
     "afd_window_poll", "afd_debug_routing", "afd_debug_read", "afd_debug_write",
@@ -71,7 +71,7 @@ class Layout(ctypes.Structure):
 
 class RunInfo(ctypes.Structure):
     _fields_ = [("status", ctypes.c_int32), ("failed_peer", ctypes.c_int32), ("last_seq", ctypes.c_int32),
-                ("total_tokens", ctypes.c_int32)]
+                ("total_tokens", ctypes.c_int32), ("served_mask", ctypes.c_uint64)]
 
 
 class MoeWeights(ctypes.Structure):
@@ -104,6 +104,7 @@ def lib():
             "afd_slot_pack": [vp, i32, i32, i32, i32, vp, vp, u32, vp],
             "afd_weights_pack": [vp, P(MoeWeights), vp, i64, vp],
             "afd_ffn_run": [vp, i32, i32, vp, vp],
+            "afd_ffn_run_ready": [vp, i32, i32, vp, i32, i32, vp],
             "afd_layer_table_set": [vp, i32, P(vp), vp],
             "afd_ffn_run_table": [vp, i32, vp],
             "afd_ffn_loop_create": [vp, i32, i32, vp, P(vp)],
@@ -194,6 +195,12 @@ def afd_weights_pack(win, w13, w2, ws13, ws2, dst, dst_bytes, stream=0) -> int:
 
 def afd_ffn_run(win, stage, layer_idx, packed_weights, stream=0) -> int:
     return _check(lib().afd_ffn_run(win, stage, layer_idx, packed_weights or None, stream or None))
+
+
+def afd_ffn_run_ready(win, stage, layer_idx, packed_weights, max_peers, gather_us=0, stream=0) -> int:
+    """layer_idx < 0: layer from the headers, weights from the layer table."""
+    return _check(lib().afd_ffn_run_ready(win, stage, layer_idx, packed_weights or None, max_peers, gather_us,
+                                          stream or None))
 
 
 def afd_layer_table_set(win, packed_ptrs, stream=0) -> int:

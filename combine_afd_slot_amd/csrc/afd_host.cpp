@@ -82,7 +82,7 @@ struct WsLayout {
     int64_t ctrl_ints;
     // control-word offsets inside ctrl (in ints)
     int64_t c_seen_in, c_ret_seq, c_seen_ret, c_cur_seq, c_off, c_T, c_done, c_run_status, c_peer_status;
-    int64_t c_layer_cur, c_nlayers;
+    int64_t c_layer_cur, c_nlayers, c_rr;
 };
 
 WsLayout ws_layout(const afd_window_config& c) {
@@ -103,6 +103,7 @@ WsLayout ws_layout(const afd_window_config& c) {
     w.c_peer_status = ci; ci += P * R * afd::kStatusWords;
     w.c_layer_cur = ci; ci += 1;
     w.c_nlayers = ci; ci += 1;
+    w.c_rr = ci; ci += R;
     w.ctrl_ints = ci;
     int64_t cur = 0;
     auto take = [&](int64_t bytes) {
@@ -271,6 +272,7 @@ void fill_ctx(afd_window* w) {
     d.run_status = ctrl + L.c_run_status;
     d.layer_cur = ctrl + L.c_layer_cur;
     d.nlayers = ctrl + L.c_nlayers;
+    d.rr = ctrl + L.c_rr;
     d.wtable = (const afd::Weights*)(ws + L.wtable);
     d.peer_status = ctrl + L.c_peer_status;
     d.peer_counts = (int*)(ws + L.peer_counts);
@@ -534,6 +536,30 @@ int32_t afd_layer_table_set(afd_window* w, int32_t n_layers, const void* const* 
     return AFD_OK;
 }
 
+int32_t afd_ffn_run_ready(afd_window* w, int32_t stage, int32_t layer_idx, const void* packed_weights,
+                          int32_t max_peers, int32_t gather_us, void* ffn_stream) {
+    if (!w) return fail(AFD_ERR_INVALID, "window is NULL");
+    const afd_window_config& c = w->cfg;
+    if (stage < 0 || stage >= c.ring_depth) return fail(AFD_ERR_INVALID, "stage %d out of range", stage);
+    if (max_peers < 1 || max_peers > c.num_peers)
+        return fail(AFD_ERR_INVALID, "max_peers %d outside 1..%d", max_peers, c.num_peers);
+    if (gather_us < 0 || gather_us > c.poll_timeout_us)
+        return fail(AFD_ERR_INVALID, "gather_us %d outside 0..poll_timeout_us", gather_us);
+    afd::Weights wt{};
+    if (layer_idx < 0) {
+        if (w->n_layers < 1) return fail(AFD_ERR_INVALID, "no layer table set (afd_layer_table_set)");
+    } else {
+        if (!packed_weights || !aligned(packed_weights, 256))
+            return fail(AFD_ERR_INVALID, "packed weights NULL or not 256-byte aligned");
+        wt = packed_weights_of(c, packed_weights);
+    }
+    hipEvent_t evs[AFD_PROFILE_SLOTS + 1] = {};
+    hipError_t e = afd::launch_ffn(w->ctx, stage, layer_idx, wt, poll_ticks(w), w->num_cu, profile_events(w, evs),
+                                   (hipStream_t)ffn_stream, max_peers, (long long)gather_us * w->ticks_per_us);
+    if (e != hipSuccess) return hip_fail(e, "ffn launch");
+    return AFD_OK;
+}
+
 int32_t afd_ffn_run_table(afd_window* w, int32_t stage, void* ffn_stream) {
     if (!w) return fail(AFD_ERR_INVALID, "window is NULL");
     if (stage < 0 || stage >= w->cfg.ring_depth) return fail(AFD_ERR_INVALID, "stage %d out of range", stage);
@@ -638,6 +664,7 @@ static int32_t read_status(afd_window* w, const int* dev_words, void* stream, af
     info->failed_peer = words[1];
     info->last_seq = words[2];
     info->total_tokens = words[3];
+    info->served_mask = (uint64_t)(uint32_t)words[4] | ((uint64_t)(uint32_t)words[5] << 32);
     (void)w;
     return AFD_OK;
 }

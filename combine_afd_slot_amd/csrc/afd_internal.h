@@ -40,7 +40,9 @@ constexpr int kXcds = 8;
 constexpr int kSegs = 2 * kXcds;
 
 // Per-stage run status words: [status, failed_peer, seq of peer 0, T].
-constexpr int kStatusWords = 4;
+// Run status words: [status, failed_peer, seq of peer 0, T, served peers
+// (bits 0..31), served peers (bits 32..63)].
+constexpr int kStatusWords = 6;
 
 struct Weights;
 
@@ -69,6 +71,7 @@ struct DevCtx {
     int* off;          // [P+1] fan-in offsets
     int* Tptr;         // [1]   total tokens of the current run
     int* run_status;   // [R][kStatusWords]
+    int* rr;           // [R]   first peer an any-ready run of the stage scans (rotates for fairness)
     int* layer_cur;    // [1]   layer of the current run (from the headers in layer-table runs)
     int* nlayers;      // [1]   entries of the layer table (0: none set)
     const Weights* wtable;  // [kMaxLayers] packed weights of each layer (layer-table runs)
@@ -132,8 +135,10 @@ hipError_t launch_pack(const DevCtx& c, int peer, int stage, int layer, int seq_
 hipError_t launch_unpack(const DevCtx& c, int peer, int stage, int seq_len, int expect_echo, void* out,
                          long long timeout_ticks, hipStream_t st);
 // One FFN run; `ev` (may be null) holds kProfileSlots+1 events recorded
-// between the launches.
+// between the launches.  max_take = 0: the work item is every peer of the
+// stage; max_take > 0: at most max_take of the peers that are ready (an
+// any-ready run), after waiting gather_ticks past the first one for more.
 hipError_t launch_ffn(const DevCtx& c, int stage, int layer, const Weights& w, long long timeout_ticks,
-                      int num_cu, hipEvent_t* ev, hipStream_t st);
+                      int num_cu, hipEvent_t* ev, hipStream_t st, int max_take = 0, long long gather_ticks = 0);
 
 }  // namespace afd

@@ -193,29 +193,77 @@ hipError_t launch_unpack(const DevCtx& c, int peer, int stage, int seq_len, int 
 // headers are checked; the fan-in offsets are the exclusive scan of the
 // peers' num_tokens ("Data on the wire", Steps 2-3).  Nothing is consumed
 // unless every peer arrived with a valid header (or shutdown).
-// ---------------------------------------------------------------------------
+//
 // layer < 0: a layer-table run; the layer is the one every peer's header
 // carries, and it must have an entry in the table.
-__global__ __launch_bounds__(64) void k_wait(DevCtx c, int s, int layer, long long timeout) {
+//
+// max_take > 0: an any-ready run ("Asynchronous work-item contract", item
+// 3; "Risks and alternatives": a device-side wait on the flag array with a
+// rotating scan start).  The wavefront polls all P flags together until one
+// has changed (bounded), then up to `gather` ticks more for others, and
+// takes at most max_take of the changed ones, scanning from the stage's
+// rotating start; only those are checked and consumed, the rest stay
+// pending with no tokens in this run, and the start moves past the last one
+// taken.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(64) void k_wait(DevCtx c, int s, int layer, long long timeout, int max_take,
+                                             long long gather) {
     __shared__ int s_flag[kMaxPeers], s_err[kMaxPeers], s_ntok[kMaxPeers], s_shut[kMaxPeers], s_layer[kMaxPeers];
     const int p = threadIdx.x;
     int* st = c.run_status + s * kStatusWords;
-    if (p < c.P) {
-        const int idx = p * c.R + s;
-        int* flag = (int*)c.in_win + idx;
-        const int seen = c.seen_in[idx];
+    const bool in = p < c.P;
+    const int idx = p * c.R + s;
+    const int* flag = (const int*)c.in_win + idx;
+    const int seen = in ? c.seen_in[idx] : 0;
+    int f = seen, err = AFD_OK;
+    uint64_t taken = c.P == 64 ? ~0ull : (1ull << c.P) - 1;  // peers of this work item
+    int last = c.P - 1;                                     // the last one in scan order
+    if (max_take == 0) {
+        if (in) {
+            const long long t0 = wall_clock64();
+            for (;;) {
+                f = ld_acquire((int*)flag);
+                if (f != seen) break;
+                if (wall_clock64() - t0 > timeout) {
+                    err = AFD_ERR_TIMEOUT;
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(2);
+            }
+        }
+    } else {
+        // every decision below is wave-uniform (scalar clock, ballot)
         const long long t0 = wall_clock64();
-        int f = seen, err = AFD_OK, ntok = 0, shut = 0, hl = -1;
+        long long t1 = -1;
+        uint64_t ready = 0;
         for (;;) {
-            f = ld_acquire(flag);
-            if (f != seen) break;
-            if (wall_clock64() - t0 > timeout) {
-                err = AFD_ERR_TIMEOUT;
+            if (in) f = ld_acquire((int*)flag);
+            ready = __ballot(in && f != seen);
+            const long long now = wall_clock64();
+            if (ready) {
+                if (t1 < 0) t1 = now;
+                if (__popcll(ready) == (unsigned)c.P || now - t1 >= gather) break;
+            } else if (now - t0 > timeout) {
                 break;
             }
             __builtin_amdgcn_s_sleep(2);
         }
-        if (err == AFD_OK) {
+        const int r0 = c.rr[s];
+        taken = 0;
+        for (int q = 0, n = 0; q < c.P && n < max_take; ++q) {
+            const int pq = (r0 + q) % c.P;
+            if ((ready >> pq) & 1) {
+                taken |= 1ull << pq;
+                last = pq;
+                ++n;
+            }
+        }
+        if (!((taken >> p) & 1)) f = seen;  // left pending for a later run
+    }
+    const bool take = in && ((taken >> p) & 1);
+    if (in) {
+        int ntok = 0, shut = 0, hl = -1;
+        if (take && err == AFD_OK) {
             afd_header_fields h;
             // the fixed words in one batch of loads (the header is 256-byte aligned)
             static_assert(AFD_HDR_WORDS == 12, "three 16-byte loads");
@@ -241,7 +289,7 @@ __global__ __launch_bounds__(64) void k_wait(DevCtx c, int s, int layer, long lo
     }
     __syncthreads();
     if (threadIdx.x == 0) {
-        int status = AFD_OK, failed = -1, shut = 0;
+        int status = taken ? AFD_OK : AFD_ERR_TIMEOUT, failed = -1, shut = 0;
         for (int q = 0; q < c.P; ++q) {
             if (s_err[q] != AFD_OK && status == AFD_OK) {
                 status = s_err[q];
@@ -252,33 +300,39 @@ __global__ __launch_bounds__(64) void k_wait(DevCtx c, int s, int layer, long lo
         if (status == AFD_OK && shut) status = AFD_SHUTDOWN;
         int L = layer;
         if (layer < 0 && status == AFD_OK) {
-            L = s_layer[0];
-            for (int q = 1; q < c.P && status == AFD_OK; ++q)
-                if (s_layer[q] != L) {
+            const int q0 = __builtin_ctzll(taken);
+            L = s_layer[q0];
+            for (int q = q0 + 1; q < c.P && status == AFD_OK; ++q)
+                if (((taken >> q) & 1) && s_layer[q] != L) {
                     status = AFD_ERR_HEADER;
                     failed = q;
                 }
             if (status == AFD_OK && (L < 0 || L >= *c.nlayers)) {
                 status = AFD_ERR_HEADER;
-                failed = 0;
+                failed = q0;
             }
         }
         *c.layer_cur = L;
         int T = 0;
-        if (status == AFD_OK || status == AFD_SHUTDOWN) {
+        const bool consume = status == AFD_OK || status == AFD_SHUTDOWN;
+        if (consume) {
             c.off[0] = 0;
             for (int q = 0; q < c.P; ++q) {
-                c.seen_in[q * c.R + s] = s_flag[q];
+                c.seen_in[q * c.R + s] = s_flag[q];  // (unchanged for a peer not taken)
                 c.cur_seq[q] = s_flag[q];
                 T += s_ntok[q];
                 c.off[q + 1] = T;
             }
+            if (max_take) c.rr[s] = (last + 1) % c.P;
         }
+        const uint64_t served = consume ? taken : 0;
         *c.Tptr = status == AFD_OK ? T : 0;
         st[0] = status;
         st[1] = failed;
         st[2] = s_flag[0];
         st[3] = status == AFD_OK ? T : 0;
+        st[4] = (int)(uint32_t)served;
+        st[5] = (int)(uint32_t)(served >> 32);
     }
 }
 
@@ -1554,7 +1608,7 @@ __global__ __launch_bounds__(64) void k_publish(DevCtx c, const int* status, int
 // layer < 0: a layer-table run (the layer from the headers, the weights from
 // the device table; `w` is unused).
 hipError_t launch_ffn(const DevCtx& c, int stage, int layer, const Weights& w, long long timeout_ticks, int num_cu,
-                      hipEvent_t* ev, hipStream_t st) {
+                      hipEvent_t* ev, hipStream_t st, int max_take, long long gather_ticks) {
     int* status = c.run_status + stage * kStatusWords;
     const int Tmax = c.P * c.token_cap;
     // ev == nullptr: no events; otherwise ev[i] is recorded before kernel
@@ -1566,7 +1620,7 @@ hipError_t launch_ffn(const DevCtx& c, int stage, int layer, const Weights& w, l
         ++slot;
     };
     mark();
-    k_wait<<<1, 64, 0, st>>>(c, stage, layer, timeout_ticks);
+    k_wait<<<1, 64, 0, st>>>(c, stage, layer, timeout_ticks, max_take, gather_ticks);
     mark();
     if (c.E <= 64) k_route<1><<<c.NB, 64 * kRouteChunk, 0, st>>>(c, status, stage);
     else if (c.E <= 128) k_route<2><<<c.NB, 64 * kRouteChunk, 0, st>>>(c, status, stage);

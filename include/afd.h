@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define AFD_ABI_VERSION 3
+#define AFD_ABI_VERSION 4
 
 /* Header flags bit 1: shutdown sentinel ("Window and slot layout"). */
 #define AFD_FLAG_SHUTDOWN 0x2u
@@ -158,6 +158,8 @@ typedef struct afd_run_info {
     int32_t failed_peer;  /* first peer that failed, -1 if none                */
     int32_t last_seq;     /* FFN run: seq consumed from peer 0; unpack: return seq */
     int32_t total_tokens; /* FFN run: T = sum of the peers' num_tokens         */
+    uint64_t served_mask; /* FFN run: bit p set = peer p's message was consumed (and answered
+                             when non-empty); 0 when the run failed; unpack: 0          */
 } afd_run_info;
 
 /* Expert weights of one layer (device pointers, bf16, borrowed).
@@ -263,6 +265,28 @@ int32_t afd_layer_table_set(afd_window* w, int32_t n_layers, const void* const* 
  * Errors: AFD_ERR_INVALID (NULL window, stage out of range, no layer table
  * set). */
 int32_t afd_ffn_run_table(afd_window* w, int32_t stage, void* ffn_stream);
+
+/* Any-ready consumption ("[RFC]: Async AFD for Prefill on Ascend NPU",
+ * "Asynchronous work-item contract": the FFN side may take any ready
+ * replica without waiting for the others, and must not starve one;
+ * "[RFC]: Async GPU Connector", "Risks and alternatives": a device-side wait
+ * on the flag array, with a rotating scan start against starvation).  Like
+ * afd_ffn_run, but the work item is not every peer of the stage: the device
+ * waits (bounded by poll_timeout_us) until at least one peer's message of
+ * the stage has arrived, then up to gather_us more microseconds for others
+ * (0: none), and takes at most max_peers of the peers that are ready then,
+ * scanning from a per-stage start that moves past the last peer taken
+ * (round robin).  Only the taken peers are consumed and answered; the others
+ * stay pending for a later run.  Each taken peer's rows are computed exactly
+ * as in a run over all peers.  afd_window_status reports the taken peers in
+ * served_mask.  layer_idx < 0 selects the layer from the headers and the
+ * weights from the layer table (as afd_ffn_run_table; packed_weights is
+ * ignored).  Nothing ready within the bound is AFD_ERR_TIMEOUT.  Errors:
+ * AFD_ERR_INVALID (NULL window, stage out of range, max_peers outside
+ * 1..num_peers, gather_us outside 0..poll_timeout_us, missing or misaligned
+ * weights, layer_idx < 0 without a layer table). */
+int32_t afd_ffn_run_ready(afd_window* w, int32_t stage, int32_t layer_idx, const void* packed_weights,
+                          int32_t max_peers, int32_t gather_us, void* ffn_stream);
 
 /* A fixed-length FFN loop captured once and replayed ("[RFC]: Async AFD for
  * Prefill on Ascend NPU", "FFN execution modes", graph mode: fixed-shape
