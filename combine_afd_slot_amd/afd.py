@@ -58,7 +58,8 @@ class WindowConfig(ctypes.Structure):
                 ("hidden", ctypes.c_int32), ("num_experts", ctypes.c_int32), ("top_k", ctypes.c_int32),
                 ("intermediate", ctypes.c_int32), ("shared_intermediate", ctypes.c_int32),
                 ("routed_scaling_factor", ctypes.c_float), ("renormalize", ctypes.c_int32),
-                ("poll_timeout_us", ctypes.c_int32), ("reserved", ctypes.c_int32 * 4)]
+                ("poll_timeout_us", ctypes.c_int32), ("attention_routes", ctypes.c_int32),
+                ("reserved", ctypes.c_int32 * 3)]
 
 
 class Layout(ctypes.Structure):
@@ -151,13 +152,15 @@ def _check(rc: int) -> int:
 
 
 def make_config(num_peers, token_cap, hidden, num_experts, top_k, intermediate, shared_intermediate,
-                ring_depth=1, routed_scaling_factor=1.0, renormalize=1, poll_timeout_us=2_000_000) -> WindowConfig:
+                ring_depth=1, routed_scaling_factor=1.0, renormalize=1, poll_timeout_us=2_000_000,
+                attention_routes=0) -> WindowConfig:
     c = WindowConfig()
     c.struct_size = ctypes.sizeof(WindowConfig)
     c.num_peers, c.ring_depth, c.token_cap = num_peers, ring_depth, token_cap
     c.hidden, c.num_experts, c.top_k = hidden, num_experts, top_k
     c.intermediate, c.shared_intermediate = intermediate, shared_intermediate
     c.routed_scaling_factor, c.renormalize, c.poll_timeout_us = routed_scaling_factor, renormalize, poll_timeout_us
+    c.attention_routes = attention_routes
     return c
 
 

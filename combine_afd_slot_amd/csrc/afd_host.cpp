@@ -43,8 +43,10 @@ int32_t validate(const afd_window_config* c) {
     if (!c) return fail(AFD_ERR_INVALID, "config is NULL");
     if (c->struct_size != sizeof(afd_window_config))
         return fail(AFD_ERR_INVALID, "struct_size %u != %zu", c->struct_size, sizeof(afd_window_config));
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 3; ++i)
         if (c->reserved[i] != 0) return fail(AFD_ERR_INVALID, "reserved[%d] must be 0", i);
+    if (c->attention_routes != 0 && c->attention_routes != 1)
+        return fail(AFD_ERR_INVALID, "attention_routes must be 0 or 1");
     if (c->num_peers < 1 || c->num_peers > afd::kMaxPeers) return fail(AFD_ERR_INVALID, "num_peers out of [1,64]");
     if (c->ring_depth < 1 || c->ring_depth > 4) return fail(AFD_ERR_INVALID, "ring_depth out of [1,4]");
     if (c->token_cap < 1) return fail(AFD_ERR_INVALID, "token_cap must be >= 1");
@@ -65,7 +67,8 @@ int32_t validate(const afd_window_config* c) {
     // the GEMM kernels address rows with 32-bit byte offsets from a base
     const int64_t lim = (int64_t)1 << 32;
     int64_t fb[AFD_NUM_FIELDS], slot = 0;
-    afd::slot_field_bytes(c->token_cap, c->hidden, c->num_experts, c->shared_intermediate > 0, fb);
+    afd::slot_field_bytes(c->token_cap, c->hidden, c->num_experts, c->top_k, c->shared_intermediate > 0,
+                          c->attention_routes != 0, fb);
     for (int i = 0; i < AFD_NUM_FIELDS; ++i) slot += afd::align_up(fb[i]);
     const int64_t window = afd::align_up(4LL * c->num_peers * c->ring_depth) + slot * c->num_peers * c->ring_depth;
     if (window >= lim || 2 * tmax * c->top_k * c->intermediate >= lim || 2 * tmax * c->shared_intermediate >= lim ||
@@ -78,7 +81,7 @@ int32_t validate(const afd_window_config* c) {
 struct WsLayout {
     int64_t ctrl, peer_counts, blk_counts, blk_base, counts, eoff, tstart1, tstart2;
     int64_t tinfo1, tinfo2, seg1, seg2, tctr, psrc, max_tiles1, max_tiles2;
-    int64_t ids, wts, perm, inv, tok_src, sh_src, h, hs, y, ys, wtable, bytes;
+    int64_t ids, wts, perm, inv, tok_src, sh_src, h, hs, y, ys, wtable, pid, pwt, ppos, pblk, pbase, pcnt, retmap, bytes;
     int64_t ctrl_ints;
     // control-word offsets inside ctrl (in ints)
     int64_t c_seen_in, c_ret_seq, c_seen_ret, c_cur_seq, c_off, c_T, c_done, c_run_status, c_peer_status;
@@ -149,6 +152,19 @@ WsLayout ws_layout(const afd_window_config& c) {
     w.y = take(2 * np * c.hidden);
     w.ys = take(2 * tmax * c.hidden);
     w.wtable = take((int64_t)sizeof(afd::Weights) * afd::kMaxLayers);
+    {
+        // attention-side routing: per (peer, stage) message state on the peer side
+        const int64_t ar = c.attention_routes ? 1 : 0;
+        const int64_t msgs = P * R, pairs = (int64_t)c.token_cap * K;
+        const int64_t nbp = (c.token_cap + afd::kRouteChunk - 1) / afd::kRouteChunk;
+        w.pid = take(ar * 4 * msgs * pairs);
+        w.pwt = take(ar * 4 * msgs * pairs);
+        w.ppos = take(ar * 4 * msgs * pairs);
+        w.pblk = take(ar * 4 * msgs * E * nbp);
+        w.pbase = take(ar * 4 * msgs * E * nbp);
+        w.pcnt = take(ar * 4 * msgs * E);
+        w.retmap = take(ar * 4 * np);
+    }
     w.bytes = cur;
     return w;
 }
@@ -156,7 +172,8 @@ WsLayout ws_layout(const afd_window_config& c) {
 void layout_from(const afd_window_config& c, afd_layout* L, WsLayout* wl) {
     std::memset(L, 0, sizeof *L);
     int64_t fb[AFD_NUM_FIELDS];
-    afd::slot_field_bytes(c.token_cap, c.hidden, c.num_experts, c.shared_intermediate > 0, fb);
+    afd::slot_field_bytes(c.token_cap, c.hidden, c.num_experts, c.top_k, c.shared_intermediate > 0,
+                          c.attention_routes != 0, fb);
     int64_t cur = 0;
     for (int i = 0; i < AFD_NUM_FIELDS; ++i) {
         L->field_off[i] = cur;
@@ -273,6 +290,15 @@ void fill_ctx(afd_window* w) {
     d.layer_cur = ctrl + L.c_layer_cur;
     d.nlayers = ctrl + L.c_nlayers;
     d.rr = ctrl + L.c_rr;
+    d.attn_routes = c.attention_routes;
+    d.NBp = (c.token_cap + afd::kRouteChunk - 1) / afd::kRouteChunk;
+    d.pid = (int*)(ws + L.pid);
+    d.pwt = (float*)(ws + L.pwt);
+    d.ppos = (int*)(ws + L.ppos);
+    d.pblk = (int*)(ws + L.pblk);
+    d.pbase = (int*)(ws + L.pbase);
+    d.pcnt = (int*)(ws + L.pcnt);
+    d.retmap = (int*)(ws + L.retmap);
     d.wtable = (const afd::Weights*)(ws + L.wtable);
     d.peer_status = ctrl + L.c_peer_status;
     d.peer_counts = (int*)(ws + L.peer_counts);

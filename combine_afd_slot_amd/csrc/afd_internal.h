@@ -73,13 +73,26 @@ struct DevCtx {
     int* run_status;   // [R][kStatusWords]
     int* rr;           // [R]   first peer an any-ready run of the stage scans (rotates for fairness)
     int* layer_cur;    // [1]   layer of the current run (from the headers in layer-table runs)
+    // attention-side routing (attn_routes): the routed rows arrive grouped by
+    // expert, the peer keeps the top-k weights and combines on return
+    int attn_routes;
+    int NBp;           // routing chunks of one message: ceil(token_cap / kRouteChunk)
+    int* pid;          // [P*R][token_cap*K] expert of pair (t, k) of the (peer, stage) message
+    float* pwt;        // [P*R][token_cap*K] its weight
+    int* ppos;         // [P*R][token_cap*K] its row among the message's grouped rows
+    int* pblk;         // [P*R][E][NBp] chunk histograms of the message's pairs
+    int* pbase;        // [P*R][E][NBp] pairs of the expert in earlier chunks
+    int* pcnt;         // [P*R][E] the message's group list (pairs per expert)
+    int* retmap;       // [Tmax*K] peer * token_cap*K + row in the peer's slot, of each grouped row
     int* nlayers;      // [1]   entries of the layer table (0: none set)
     const Weights* wtable;  // [kMaxLayers] packed weights of each layer (layer-table runs)
     int* peer_status;  // [P*R][kStatusWords]
     // routing / dispatch
     int* peer_counts;  // [P][E]
-    int* blk_counts;   // [E][NB] per-chunk expert histograms
-    int* blk_base;     // [E][NB] stable base of each chunk inside its expert group
+    int* blk_counts;   // [E][NB] per-chunk expert histograms (attention-routed runs, with NB >= P:
+                       //   [P][E] first row of each group in the peer's slot)
+    int* blk_base;     // [E][NB] stable base of each chunk inside its expert group (attention-
+                       //   routed runs: [P][E] first row of the peer's share of each group)
     int* counts;       // [E]
     int* eoff;         // [E+1]
     int* tstart1;      // [G+1] gate/up GEMM tile prefix per group

@@ -62,16 +62,98 @@ __device__ inline void st_release(int* p, int v) {
 }
 
 // ---------------------------------------------------------------------------
+// Block-wide exclusive prefix sum of one int per thread (blockDim a multiple
+// of 64, at most 1024).  `sh` holds 16 ints.
+// ---------------------------------------------------------------------------
+__device__ int block_excl_scan(int v, int* sh) {
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    int x = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(x, o);
+        if (lane >= o) x += y;
+    }
+    if (lane == 63) sh[wid] = x;
+    __syncthreads();
+    int wbase = 0;
+    for (int w = 0; w < wid; ++w) wbase += sh[w];
+    __syncthreads();
+    return x + wbase - v;
+}
+
+// Sum over the 64 lanes of a wavefront with DPP moves (no LDS): butterflies
+// inside each row of 16 lanes, then the row sums carried across rows with
+// the row broadcasts; lane 63 ends up with the total.
+__device__ inline float wave_sum(float x) {
+    x += __builtin_amdgcn_update_dpp(0.f, x, 0xB1, 0xF, 0xF, false);   // quad_perm [1,0,3,2]
+    x += __builtin_amdgcn_update_dpp(0.f, x, 0x4E, 0xF, 0xF, false);   // quad_perm [2,3,0,1]
+    x += __builtin_amdgcn_update_dpp(0.f, x, 0x141, 0xF, 0xF, false);  // row_half_mirror
+    x += __builtin_amdgcn_update_dpp(0.f, x, 0x140, 0xF, 0xF, false);  // row_mirror
+    x += __builtin_amdgcn_update_dpp(0.f, x, 0x142, 0xA, 0xF, false);  // row_bcast:15 into rows 1, 3
+    x += __builtin_amdgcn_update_dpp(0.f, x, 0x143, 0xC, 0xF, false);  // row_bcast:31 into rows 2, 3
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 63));
+}
+
+// One token's top-K by a wavefront: lane l holds logits l, l+64, ... in v
+// (-inf past E).  On return rank[j] is the rank of logit l + 64 j (rank < K:
+// selected, rank k the k-th) and wt[j] its weight.  Shared by the FFN-side
+// routing and the attention-side pack, so both select and weigh alike.
+template <int EPL>
+__device__ __forceinline__ void route_token(const float (&v)[EPL], int E, int K, int renorm, int lane,
+                                            int (&rank)[EPL], float (&wt)[EPL]) {
+    // Logits past E are -inf and have indices past every valid one, so
+    // they never raise a valid logit's rank.
+#pragma unroll
+    for (int j = 0; j < EPL; ++j) rank[j] = 0;
+#pragma unroll
+    for (int jj = 0; jj < EPL; ++jj) {
+        if (64 * jj >= E) break;
+#pragma unroll 8
+        for (int sl = 0; sl < 64; ++sl) {
+            const float x = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v[jj]), sl));
+            const int q = sl + 64 * jj;
+#pragma unroll
+            for (int j = 0; j < EPL; ++j) {
+                const int e = lane + 64 * j;
+                rank[j] += (x > v[j] || (x == v[j] && q < e)) ? 1 : 0;
+            }
+        }
+    }
+    // the maximum is the logit of rank 0 (exactly one lane holds it)
+    float top = -INFINITY;
+    bool has_top = false;
+#pragma unroll
+    for (int j = 0; j < EPL; ++j)
+        if (lane + 64 * j < E && rank[j] == 0) {
+            top = v[j];
+            has_top = true;
+        }
+    const float m = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(top), __builtin_ctzll(__ballot(has_top))));
+    float ex[EPL], part = 0.f;
+#pragma unroll
+    for (int j = 0; j < EPL; ++j) {
+        const int e = lane + 64 * j;
+        const bool sel = e < E && rank[j] < K;
+        ex[j] = (e < E) ? expf(v[j] - m) : 0.f;
+        if (renorm ? sel : (e < E)) part += ex[j];
+    }
+    part = wave_sum(part);
+#pragma unroll
+    for (int j = 0; j < EPL; ++j) wt[j] = ex[j] / part;
+}
+
+// ---------------------------------------------------------------------------
 // Pack (attention side).  Payload first, then -- in a second launch on the
 // same stream, so the whole payload is complete and written back -- the
 // header and a release store of the flag ("Window and slot layout": payload
 // and flag ordered on one stream; the flag value is the sender's seq).
 // ---------------------------------------------------------------------------
 // shared: the window carries shared rows (shared_x, shared_idx); a routed-
-// only window does not.
+// only window does not.  grouped: the attention side routes, so no logits
+// travel and the routed rows are written grouped by expert (k_pscatter).
 __global__ __launch_bounds__(256) void k_pack_payload(char* slot, int64_t o_rt, int64_t o_rx, int64_t o_si,
                                                       int64_t o_sx, const uint4* hidden, const float* logits,
-                                                      int n, int H, int E, int shared) {
+                                                      int n, int H, int E, int shared, int grouped) {
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
     const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const int64_t nch = (int64_t)n * H / 8;
@@ -79,11 +161,11 @@ __global__ __launch_bounds__(256) void k_pack_payload(char* slot, int64_t o_rt, 
     uint4* sx = (uint4*)(slot + o_sx);
     for (int64_t i = gid; i < nch; i += stride) {
         uint4 v = hidden[i];
-        rx[i] = v;
+        if (!grouped) rx[i] = v;
         if (shared) sx[i] = v;
     }
     float* rt = (float*)(slot + o_rt);
-    const int64_t nl = (int64_t)n * E;
+    const int64_t nl = grouped ? 0 : (int64_t)n * E;
     for (int64_t i = gid; i < nl; i += stride) rt[i] = logits[i];
     if (shared) {
         int* si = (int*)(slot + o_si);
@@ -91,11 +173,121 @@ __global__ __launch_bounds__(256) void k_pack_payload(char* slot, int64_t o_rt, 
     }
 }
 
-__global__ void k_pack_publish(char* slot, int* flag, afd_header_fields f) {
+__global__ void k_pack_publish(char* slot, int* flag, afd_header_fields f, const int* counts) {
     if (threadIdx.x == 0) {
-        header_encode(f, nullptr, (int32_t*)slot);
+        header_encode(f, counts, (int32_t*)slot);
         __threadfence();
         st_release(flag, f.seq);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Attention-side routing of one message (attention-routed windows; "[RFC]:
+// Async GPU Connector", "Data flow", step 1: the sender routes, flattens its
+// top-k ids and sorts them stably, which groups the routed rows by expert;
+// the counts are the group list; step 4: the top-k weights stay with the
+// sender).  Message idx = peer * R + stage, its n tokens in chunks of
+// kRouteChunk.  k_proute: one wavefront per token, the same top-K code as
+// the FFN side (route_token); chunk histograms.  k_pscan: one workgroup per
+// expert scans its column of chunk histograms.  k_pscatter: the row of pair
+// f = t*K + k among the grouped rows is goff[e] + (pairs of e in earlier
+// chunks) + (earlier tokens of the chunk that chose e), and token t's hidden
+// row is copied there, once per k.
+// ---------------------------------------------------------------------------
+template <int EPL>
+__global__ __launch_bounds__(64 * kRouteChunk) void k_proute(DevCtx c, int idx, const float* logits, int n) {
+    __shared__ int hist[kMaxExperts];
+    const int lane = threadIdx.x & 63;
+    const int E = c.E, K = c.K;
+    for (int e = threadIdx.x; e < E; e += blockDim.x) hist[e] = 0;
+    const int t = (int)blockIdx.x * kRouteChunk + (int)(threadIdx.x >> 6);
+    const bool live = t < n;
+    const int r = min(t, n - 1);
+    float v[EPL];
+#pragma unroll
+    for (int j = 0; j < EPL; ++j) {
+        const int e = lane + 64 * j;
+        const float x = e < E ? logits[(int64_t)r * E + e] : -INFINITY;
+        v[j] = x == x ? x : -INFINITY;  // (the same rule as the FFN side)
+    }
+    __syncthreads();  // hist zeroed
+    if (live) {
+        int rank[EPL];
+        float wt[EPL];
+        route_token<EPL>(v, E, K, c.renorm, lane, rank, wt);
+        const int64_t base = (int64_t)idx * c.token_cap * K + (int64_t)t * K;
+#pragma unroll
+        for (int j = 0; j < EPL; ++j) {
+            const int e = lane + 64 * j;
+            if (e < E && rank[j] < K) {
+                c.pid[base + rank[j]] = e;
+                c.pwt[base + rank[j]] = wt[j];
+                atomicAdd(&hist[e], 1);
+            }
+        }
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < E; e += blockDim.x) c.pblk[((int64_t)idx * E + e) * c.NBp + blockIdx.x] = hist[e];
+}
+
+__global__ __launch_bounds__(256) void k_pscan(DevCtx c, int idx, int nb) {
+    __shared__ int sh[16];
+    const int e = blockIdx.x;
+    const int* col = c.pblk + ((int64_t)idx * c.E + e) * c.NBp;
+    int* base = c.pbase + ((int64_t)idx * c.E + e) * c.NBp;
+    const int per = (nb + 255) / 256;
+    const int b0 = threadIdx.x * per, b1 = min(nb, b0 + per);
+    int sum = 0;
+    for (int b = b0; b < b1; ++b) sum += col[b];
+    int run = block_excl_scan(sum, sh);
+    for (int b = b0; b < b1; ++b) {
+        base[b] = run;
+        run += col[b];
+    }
+    if (threadIdx.x == 255) c.pcnt[(int64_t)idx * c.E + e] = run;
+}
+
+__global__ __launch_bounds__(256) void k_pscatter(DevCtx c, int idx, char* slot, const uint4* hidden, int n) {
+    static_assert(kRouteChunk <= 32 && kRouteChunk * kMaxTopK <= 256, "chunk masks and one pair per thread");
+    __shared__ int sh[16];
+    __shared__ int s_goff[kMaxExperts];
+    __shared__ uint32_t emask[kMaxExperts];
+    __shared__ int s_pos[kRouteChunk * kMaxTopK];
+    const int E = c.E, K = c.K, tid = threadIdx.x;
+    const int b = blockIdx.x, t0 = b * kRouteChunk, nt = min(kRouteChunk, n - t0), np = nt * K;
+    const int64_t pbase = (int64_t)idx * c.token_cap * K;
+    int e = 0;
+    if (tid < np) e = c.pid[pbase + (int64_t)t0 * K + tid];
+    {
+        const int per = (E + 255) / 256;
+        const int e0 = tid * per, e1 = min(E, e0 + per);
+        int cnt[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) cnt[j] = e0 + j < e1 ? c.pcnt[(int64_t)idx * E + e0 + j] : 0;
+        int run = block_excl_scan(cnt[0] + cnt[1] + cnt[2] + cnt[3], sh);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            if (e0 + j < e1) {
+                s_goff[e0 + j] = run;
+                run += cnt[j];
+            }
+    }
+    for (int q = tid; q < E; q += 256) emask[q] = 0u;
+    __syncthreads();
+    if (tid < np) atomicOr(&emask[e], 1u << (tid / K));
+    __syncthreads();
+    if (tid < np) {
+        const int tl = tid / K;
+        const int pos = s_goff[e] + c.pbase[((int64_t)idx * E + e) * c.NBp + b] + __popc(emask[e] & ((1u << tl) - 1u));
+        c.ppos[pbase + (int64_t)t0 * K + tid] = pos;
+        s_pos[tid] = pos;
+    }
+    __syncthreads();
+    const int H8 = c.H / 8;
+    uint4* rx = (uint4*)(slot + c.foff[AFD_FIELD_ROUTED_X]);
+    for (int i = tid; i < np * H8; i += 256) {
+        const int j = i / H8, ch = i - j * H8;
+        rx[(int64_t)s_pos[j] * H8 + ch] = hidden[(int64_t)(t0 + j / K) * H8 + ch];
     }
 }
 
@@ -111,7 +303,19 @@ hipError_t launch_pack(const DevCtx& c, int peer, int stage, int layer, int seq_
         if (grid < 1) grid = 1;
         k_pack_payload<<<grid, 256, 0, st>>>(slot, c.foff[AFD_FIELD_ROUTE_TABLE], c.foff[AFD_FIELD_ROUTED_X],
                                              c.foff[AFD_FIELD_SHARED_IDX], c.foff[AFD_FIELD_SHARED_X],
-                                             (const uint4*)hidden, logits, seq_len, c.H, c.E, c.has_shared);
+                                             (const uint4*)hidden, logits, seq_len, c.H, c.E, c.has_shared,
+                                             c.attn_routes);
+        if (c.attn_routes && seq_len > 0) {
+            const int idx = peer * c.R + stage;
+            const int nb = (seq_len + kRouteChunk - 1) / kRouteChunk;
+            if (c.E <= 64) k_proute<1><<<nb, 64 * kRouteChunk, 0, st>>>(c, idx, logits, seq_len);
+            else if (c.E <= 128) k_proute<2><<<nb, 64 * kRouteChunk, 0, st>>>(c, idx, logits, seq_len);
+            else if (c.E <= 256) k_proute<4><<<nb, 64 * kRouteChunk, 0, st>>>(c, idx, logits, seq_len);
+            else if (c.E <= 512) k_proute<8><<<nb, 64 * kRouteChunk, 0, st>>>(c, idx, logits, seq_len);
+            else k_proute<16><<<nb, 64 * kRouteChunk, 0, st>>>(c, idx, logits, seq_len);
+            k_pscan<<<c.E, 256, 0, st>>>(c, idx, nb);
+            k_pscatter<<<nb, 256, 0, st>>>(c, idx, slot, (const uint4*)hidden, seq_len);
+        }
     }
     afd_header_fields f;
     f.flags = (int32_t)flags;
@@ -120,11 +324,13 @@ hipError_t launch_pack(const DevCtx& c, int peer, int stage, int layer, int seq_
     f.layer_idx = layer;
     f.stage_idx = stage;
     f.num_tokens = seq_len;
-    f.routed_tokens = seq_len;
+    f.routed_tokens = seq_len * (c.attn_routes ? c.K : 1);
     f.shared_tokens = c.has_shared ? seq_len : 0;
     f.src_peer = peer;
     f.n_counts = c.E;
-    k_pack_publish<<<1, 64, 0, st>>>(slot + c.foff[AFD_FIELD_HEADER], (int*)c.in_win + peer * c.R + stage, f);
+    // attention-routed: the header carries the group list
+    const int* counts = c.attn_routes && seq_len > 0 ? c.pcnt + (int64_t)(peer * c.R + stage) * c.E : nullptr;
+    k_pack_publish<<<1, 64, 0, st>>>(slot + c.foff[AFD_FIELD_HEADER], (int*)c.in_win + peer * c.R + stage, f, counts);
     return hipGetLastError();
 }
 
@@ -171,11 +377,61 @@ __global__ __launch_bounds__(256) void k_unpack_copy(const int* st, const uint4*
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < nch; i += stride) out[i] = src[i];
 }
 
+template <int KK>
+__device__ __forceinline__ u32x4 combine_chunk(const u32x4 (&yv)[KK], const float (&wk)[KK], u32x4 sq, bool shared,
+                                               float rsf);
+
+// Attention-routed messages: the sender combines ("[RFC]: Async GPU
+// Connector", "Data flow", step 4): out[t] = rsf * sum over k, in k order,
+// of w[t,k] * (returned row ppos[t,k]) + the returned shared row t, with
+// the weights and rows kept from the pack -- the arithmetic of k_combine.
+template <int KK>
+__global__ __launch_bounds__(256) void k_pcombine(DevCtx c, int idx, const int* st, const char* slot, u32x4* out,
+                                                  int n) {
+    if (*st != AFD_OK) return;
+    const int H8 = c.H / 8;
+    const int64_t pb = (int64_t)idx * c.token_cap * KK;
+    const u32x4* rx = (const u32x4*)(slot + c.foff[AFD_FIELD_ROUTED_X]);
+    const u32x4* sx = (const u32x4*)(slot + c.foff[AFD_FIELD_SHARED_X]);
+    for (int t = blockIdx.x; t < n; t += gridDim.x) {
+        int pos[KK];
+        float wk[KK];
+#pragma unroll
+        for (int k = 0; k < KK; ++k) {
+            pos[k] = min(max(c.ppos[pb + (int64_t)t * KK + k], 0), n * KK - 1);
+            wk[k] = c.pwt[pb + (int64_t)t * KK + k];
+        }
+        for (int ch = threadIdx.x; ch < H8; ch += blockDim.x) {
+            u32x4 yv[KK];
+#pragma unroll
+            for (int k = 0; k < KK; ++k) yv[k] = rx[(int64_t)pos[k] * H8 + ch];
+            const u32x4 sq = c.has_shared ? sx[(int64_t)t * H8 + ch] : (u32x4)0u;
+            out[(int64_t)t * H8 + ch] = combine_chunk<KK>(yv, wk, sq, c.has_shared, c.rsf);
+        }
+    }
+}
+
 hipError_t launch_unpack(const DevCtx& c, int peer, int stage, int seq_len, int expect_echo, void* out,
                          long long timeout_ticks, hipStream_t st) {
     k_unpack_wait<<<1, 64, 0, st>>>(c, peer, stage, expect_echo, seq_len, timeout_ticks);
     const int idx = peer * c.R + stage;
     const char* slot = c.ret_win + c.slots_off + (int64_t)idx * c.slot_bytes;
+    if (c.attn_routes) {
+        int grid = seq_len < 2048 ? seq_len : 2048;
+        if (grid < 1) grid = 1;
+        const int* sw = c.peer_status + idx * kStatusWords;
+        switch (c.K) {
+#define AFD_PCOMBINE_CASE(k) \
+    case k: k_pcombine<k><<<grid, 256, 0, st>>>(c, idx, sw, slot, (u32x4*)out, seq_len); break;
+            AFD_PCOMBINE_CASE(1) AFD_PCOMBINE_CASE(2) AFD_PCOMBINE_CASE(3) AFD_PCOMBINE_CASE(4)
+            AFD_PCOMBINE_CASE(5) AFD_PCOMBINE_CASE(6) AFD_PCOMBINE_CASE(7) AFD_PCOMBINE_CASE(8)
+            AFD_PCOMBINE_CASE(9) AFD_PCOMBINE_CASE(10) AFD_PCOMBINE_CASE(11) AFD_PCOMBINE_CASE(12)
+            AFD_PCOMBINE_CASE(13) AFD_PCOMBINE_CASE(14) AFD_PCOMBINE_CASE(15) AFD_PCOMBINE_CASE(16)
+#undef AFD_PCOMBINE_CASE
+            default: return hipErrorInvalidValue;
+        }
+        return hipGetLastError();
+    }
     int64_t nch = (int64_t)seq_len * c.H / 8;
     int grid = (int)((nch + 255) / 256);
     if (grid > 2048) grid = 2048;
@@ -274,7 +530,20 @@ __global__ __launch_bounds__(64) void k_wait(DevCtx c, int s, int layer, long lo
             err = header_decode((const int32_t*)hv, c.E, &h);
             if (err == AFD_OK) {
                 hl = h.layer_idx;
-                err = inbound_check(h, p, s, layer < 0 ? hl : layer, c.token_cap, f, c.has_shared);
+                err = inbound_check(h, p, s, layer < 0 ? hl : layer, c.token_cap, f, c.has_shared,
+                                    c.attn_routes ? c.K : 1);
+            }
+            if (err == AFD_OK && c.attn_routes) {
+                // the group list: non-negative, and it covers every routed row
+                const int* cnt = (const int*)hq + AFD_HDR_WORDS;
+                long long sum = 0;
+                bool neg = false;
+                for (int e = 0; e < c.E; ++e) {
+                    const int v = cnt[e];
+                    neg |= v < 0;
+                    sum += v;
+                }
+                if (neg || sum != h.routed_tokens) err = AFD_ERR_HEADER;
             }
             if (err == AFD_OK) {
                 ntok = h.num_tokens;
@@ -337,26 +606,6 @@ __global__ __launch_bounds__(64) void k_wait(DevCtx c, int s, int layer, long lo
 }
 
 // ---------------------------------------------------------------------------
-// Block-wide exclusive prefix sum of one int per thread (blockDim a multiple
-// of 64, at most 1024).  `sh` holds 16 ints.
-// ---------------------------------------------------------------------------
-__device__ int block_excl_scan(int v, int* sh) {
-    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-    int x = v;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const int y = __shfl_up(x, o);
-        if (lane >= o) x += y;
-    }
-    if (lane == 63) sh[wid] = x;
-    __syncthreads();
-    int wbase = 0;
-    for (int w = 0; w < wid; ++w) wbase += sh[w];
-    __syncthreads();
-    return x + wbase - v;
-}
-
-// ---------------------------------------------------------------------------
 // Routing chunks: kRouteChunk consecutive tokens of one peer (a peer's last
 // chunk may be shorter).  Chunks are numbered in fan-in token order, so the
 // flat pair order f = t*K + k runs through the chunks in order.
@@ -392,19 +641,6 @@ __device__ inline bool chunk_range(const DevCtx& c, int b, int& t0, int& t1, int
     t0 = base + (b - first) * kRouteChunk;
     t1 = min(base + np, t0 + kRouteChunk);
     return true;
-}
-
-// Sum over the 64 lanes of a wavefront with DPP moves (no LDS): butterflies
-// inside each row of 16 lanes, then the row sums carried across rows with
-// the row broadcasts; lane 63 ends up with the total.
-__device__ inline float wave_sum(float x) {
-    x += __builtin_amdgcn_update_dpp(0.f, x, 0xB1, 0xF, 0xF, false);   // quad_perm [1,0,3,2]
-    x += __builtin_amdgcn_update_dpp(0.f, x, 0x4E, 0xF, 0xF, false);   // quad_perm [2,3,0,1]
-    x += __builtin_amdgcn_update_dpp(0.f, x, 0x141, 0xF, 0xF, false);  // row_half_mirror
-    x += __builtin_amdgcn_update_dpp(0.f, x, 0x140, 0xF, 0xF, false);  // row_mirror
-    x += __builtin_amdgcn_update_dpp(0.f, x, 0x142, 0xA, 0xF, false);  // row_bcast:15 into rows 1, 3
-    x += __builtin_amdgcn_update_dpp(0.f, x, 0x143, 0xC, 0xF, false);  // row_bcast:31 into rows 2, 3
-    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 63));
 }
 
 // ---------------------------------------------------------------------------
@@ -456,50 +692,15 @@ __global__ __launch_bounds__(64 * kRouteChunk) void k_route(DevCtx c, int* statu
     }
     __syncthreads();  // hist zeroed
     if (live) {
-        // Logits past E are -inf and have indices past every valid one, so
-        // they never raise a valid logit's rank.
         int rank[EPL];
-#pragma unroll
-        for (int j = 0; j < EPL; ++j) rank[j] = 0;
-#pragma unroll
-        for (int jj = 0; jj < EPL; ++jj) {
-            if (64 * jj >= E) break;
-#pragma unroll 8
-            for (int sl = 0; sl < 64; ++sl) {
-                const float x = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v[jj]), sl));
-                const int q = sl + 64 * jj;
-#pragma unroll
-                for (int j = 0; j < EPL; ++j) {
-                    const int e = lane + 64 * j;
-                    rank[j] += (x > v[j] || (x == v[j] && q < e)) ? 1 : 0;
-                }
-            }
-        }
-        // the maximum is the logit of rank 0 (exactly one lane holds it)
-        float top = -INFINITY;
-        bool has_top = false;
-#pragma unroll
-        for (int j = 0; j < EPL; ++j)
-            if (lane + 64 * j < E && rank[j] == 0) {
-                top = v[j];
-                has_top = true;
-            }
-        const float m = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(top), __builtin_ctzll(__ballot(has_top))));
-        float ex[EPL], part = 0.f;
-#pragma unroll
-        for (int j = 0; j < EPL; ++j) {
-            const int e = lane + 64 * j;
-            const bool sel = e < E && rank[j] < K;
-            ex[j] = (e < E) ? expf(v[j] - m) : 0.f;
-            if (c.renorm ? sel : (e < E)) part += ex[j];
-        }
-        part = wave_sum(part);
+        float wt[EPL];
+        route_token<EPL>(v, E, K, c.renorm, lane, rank, wt);
 #pragma unroll
         for (int j = 0; j < EPL; ++j) {
             const int e = lane + 64 * j;
             if (e < E && rank[j] < K) {
                 c.ids[(int64_t)t * K + rank[j]] = e;
-                c.wts[(int64_t)t * K + rank[j]] = ex[j] / part;
+                c.wts[(int64_t)t * K + rank[j]] = wt[j];
                 atomicAdd(&hist[e], 1);
             }
         }
@@ -801,6 +1002,124 @@ __global__ __launch_bounds__(256) void k_permute(DevCtx c, const int* status) {
             c.psrc[pos] = ltok[tl];
         }
         c.inv[f] = pos;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Attention-routed runs, FFN side.  Each message's routed rows arrive
+// grouped by expert, with the group list (rows per expert) in its header
+// ("[RFC]: Async GPU Connector", "Data flow", steps 2-3), so the FFN side
+// routes nothing and merges the P group lists.  The grouped GEMM takes its
+// rows expert-major, then peer, then the peer's own order: the order the
+// stable sort of an FFN-routed run gives, so in both modes every GEMM row
+// has the same place and the tile plan is the same.
+// k_gscan: workgroup p < P scans peer p's group list over the experts (the
+// first row of each group in the peer's slot, kept in blk_counts[p][e])
+// and keeps the list for the return header; every other workgroup takes
+// one expert per thread and scans the lists over the peers (the peer's
+// first row inside the expert's group, blk_base[p][e]) and sums them.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_gscan(DevCtx c, const int* status, int s) {
+    if (*status != AFD_OK) return;
+    __shared__ int sh[16];
+    const int E = c.E, P = c.P, b = blockIdx.x, tid = threadIdx.x;
+    if (b < P) {
+        const bool live = c.off[b + 1] > c.off[b];  // (a peer not served has no tokens)
+        const int* cnt = (const int*)(slot_ptr(c, c.in_win, b, s) + c.foff[AFD_FIELD_HEADER]) + AFD_HDR_WORDS;
+        const int per = (E + 255) / 256;
+        const int e0 = tid * per, e1 = min(E, e0 + per);
+        int v[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) v[j] = live && e0 + j < e1 ? cnt[e0 + j] : 0;
+        int run = block_excl_scan(v[0] + v[1] + v[2] + v[3], sh);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            if (e0 + j < e1) {
+                c.blk_counts[b * E + e0 + j] = run;
+                c.peer_counts[b * E + e0 + j] = v[j];
+                run += v[j];
+            }
+        return;
+    }
+    const int e = (b - P) * 256 + tid;
+    if (e >= E) return;
+    int run = 0;
+    for (int q = 0; q < P; ++q) {
+        const int* cnt = (const int*)(slot_ptr(c, c.in_win, q, s) + c.foff[AFD_FIELD_HEADER]) + AFD_HDR_WORDS;
+        const int v = c.off[q + 1] > c.off[q] ? cnt[e] : 0;
+        c.blk_base[q * E + e] = run;
+        run += v;
+    }
+    c.counts[e] = run;
+}
+
+// k_gdispatch: the expert offsets and the GEMM plan as in k_permute, then
+// for every GEMM row pos its expert (the group holding pos), its peer (the
+// share holding it) and its row in that peer's slot: the token-row address
+// for the gate/up GEMM and the return row (peer * token_cap*K + row) for
+// k_retcopy.  Shared rows: addresses and the shared_idx check as in k_route.
+__global__ __launch_bounds__(256) void k_gdispatch(DevCtx c, int* status, int s) {
+    __shared__ int sh[16];
+    __shared__ long long sh4[16];
+    __shared__ int s_eoff[kMaxExperts + 1];
+    __shared__ int s_t[2][kMaxExperts + 2];
+    __shared__ long long s_c[2][kMaxExperts + 2];
+    const int st = *status;
+    const int T = *c.Tptr;
+    if (st != AFD_OK) return;
+    const int E = c.E, K = c.K, P = c.P, tid = threadIdx.x;
+    {
+        const int per = (E + 255) / 256;
+        const int e0 = tid * per, e1 = min(E, e0 + per);
+        int cnt[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) cnt[j] = e0 + j < e1 ? c.counts[e0 + j] : 0;
+        int run = block_excl_scan(cnt[0] + cnt[1] + cnt[2] + cnt[3], sh);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            if (e0 + j < e1) {
+                s_eoff[e0 + j] = run;
+                run += cnt[j];
+            }
+        if (tid == 255) s_eoff[E] = run;
+    }
+    __syncthreads();
+    plan_prefix(c, T, s_eoff, s_t, s_c, sh4);
+    if (blockIdx.x == 0) {
+        for (int e = tid; e <= E; e += 256) c.eoff[e] = s_eoff[e];
+        plan_publish(c, T, s_eoff, s_t, s_c);
+    }
+    plan_fill(c, T, s_eoff, s_t);
+    const int n = min(T * K, s_eoff[E]);  // (equal: k_wait checked every group list)
+    const int capK = c.token_cap * K;
+    const int stride = (int)gridDim.x * 256;
+    for (int pos = (int)blockIdx.x * 256 + tid; pos < n; pos += stride) {
+        int lo = 0, hi = E;  // s_eoff[lo] <= pos < s_eoff[hi]
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (s_eoff[mid] <= pos) lo = mid;
+            else hi = mid;
+        }
+        const int q = pos - s_eoff[lo];
+        int pl = 0, ph = P;  // base(pl) <= q < base(ph), base(P) = the group's size
+        while (ph - pl > 1) {
+            const int mid = (pl + ph) >> 1;
+            if (c.blk_base[mid * E + lo] <= q) pl = mid;
+            else ph = mid;
+        }
+        const int local = c.blk_counts[pl * E + lo] + q - c.blk_base[pl * E + lo];
+        c.psrc[pos] = (uint64_t)(slot_ptr(c, c.in_win, pl, s) + c.foff[AFD_FIELD_ROUTED_X] + (int64_t)local * c.H * 2);
+        c.retmap[pos] = pl * capK + local;
+    }
+    if (c.has_shared) {
+        bool bad = false;
+        for (int t = (int)blockIdx.x * 256 + tid; t < T; t += stride) {
+            const int p = peer_of(c, t), r = t - c.off[p];
+            const char* slot = slot_ptr(c, c.in_win, p, s);
+            c.sh_src[t] = (uint64_t)(slot + c.foff[AFD_FIELD_SHARED_X] + (int64_t)r * c.H * 2);
+            bad |= ((const int*)(slot + c.foff[AFD_FIELD_SHARED_IDX]))[r] != r;
+        }
+        if (bad) atomicCAS(status, AFD_OK, AFD_ERR_HEADER);
     }
 }
 
@@ -1516,6 +1835,36 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(DevCtx c, const int* s
 // of peer p's return slot ("Data flow": weighted index_add_ combine with the
 // shared branch added; "Data on the wire", Step 4: split back by seq_lens).
 // ---------------------------------------------------------------------------
+// One 16-byte chunk (8 columns) of an output row: rsf * (sum over k, in k
+// order, of w[k] * y_k) + the shared row, from bf16 rows, summed in fp32,
+// rounded to bf16 (RNE).  The FFN-side combine and the attention-side
+// combine of attention-routed messages both use it.
+template <int KK>
+__device__ __forceinline__ u32x4 combine_chunk(const u32x4 (&yv)[KK], const float (&wk)[KK], u32x4 sq, bool shared,
+                                               float rsf) {
+    float sv[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        sv[2 * i] = shared ? bf2f(sq[i] & 0xffffu) : 0.f;
+        sv[2 * i + 1] = shared ? bf2f(sq[i] >> 16) : 0.f;
+    }
+    float acc[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+#pragma unroll
+    for (int k = 0; k < KK; ++k) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            acc[2 * i] += wk[k] * bf2f(yv[k][i] & 0xffffu);
+            acc[2 * i + 1] += wk[k] * bf2f(yv[k][i] >> 16);
+        }
+    }
+    u32x4 out;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) out[i] = pk_bf16(rsf * acc[2 * i] + sv[2 * i], rsf * acc[2 * i + 1] + sv[2 * i + 1]);
+    return out;
+}
+
 template <int KK>
 __global__ __launch_bounds__(256) void k_combine(DevCtx c, const int* status, int s, int layer) {
     const int st = *status;  // loaded together with the token count
@@ -1538,35 +1887,36 @@ __global__ __launch_bounds__(256) void k_combine(DevCtx c, const int* status, in
             u32x4 yv[KK];
 #pragma unroll
             for (int k = 0; k < KK; ++k) yv[k] = *(const u32x4*)(c.y + (int64_t)pos[k] * H + ch * 8);
-            float sv[8];
-            if (c.has_shared) {
-                const u32x4 sq = *(const u32x4*)(c.ys + (int64_t)t * H + ch * 8);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    sv[2 * i] = bf2f(sq[i] & 0xffffu);
-                    sv[2 * i + 1] = bf2f(sq[i] >> 16);
-                }
-            } else {
-#pragma unroll
-                for (int i = 0; i < 8; ++i) sv[i] = 0.f;
-            }
-            float acc[8];
-#pragma unroll
-            for (int i = 0; i < 8; ++i) acc[i] = 0.f;
-#pragma unroll
-            for (int k = 0; k < KK; ++k) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    acc[2 * i] += wk[k] * bf2f(yv[k][i] & 0xffffu);
-                    acc[2 * i + 1] += wk[k] * bf2f(yv[k][i] >> 16);
-                }
-            }
-            u32x4 out;
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                out[i] = pk_bf16(c.rsf * acc[2 * i] + sv[2 * i], c.rsf * acc[2 * i + 1] + sv[2 * i + 1]);
-            __builtin_nontemporal_store(out, &dst[ch]);
+            const u32x4 sq = c.has_shared ? *(const u32x4*)(c.ys + (int64_t)t * H + ch * 8) : (u32x4)0u;
+            __builtin_nontemporal_store(combine_chunk<KK>(yv, wk, sq, c.has_shared, c.rsf), &dst[ch]);
         }
+    }
+}
+
+// Attention-routed runs: no combine on the FFN side ("[RFC]: Async GPU
+// Connector", "Data flow", step 4: the expert outputs go back in the order
+// they came, the sender combines).  GEMM row pos goes to row retmap[pos] of
+// its peer's return routed_x, shared row t to row t - off[p] of its peer's
+// return shared_x.  One workgroup per row.
+__global__ __launch_bounds__(256) void k_retcopy(DevCtx c, const int* status, int s) {
+    const int st = *status;
+    const int T = *c.Tptr;
+    if (st != AFD_OK) return;
+    const int H8 = c.H / 8, capK = c.token_cap * c.K;
+    const int nr = T * c.K, rows = nr + (c.has_shared ? T : 0);
+    for (int row = blockIdx.x; row < rows; row += gridDim.x) {
+        const u32x4* src;
+        u32x4* dst;
+        if (row < nr) {
+            const int m = c.retmap[row], p = m / capK, r = m - p * capK;
+            src = (const u32x4*)(c.y + (int64_t)row * c.H);
+            dst = (u32x4*)(slot_ptr(c, c.ret_win, p, s) + c.foff[AFD_FIELD_ROUTED_X] + (int64_t)r * c.H * 2);
+        } else {
+            const int t = row - nr, p = peer_of(c, t), r = t - c.off[p];
+            src = (const u32x4*)(c.ys + (int64_t)t * c.H);
+            dst = (u32x4*)(slot_ptr(c, c.ret_win, p, s) + c.foff[AFD_FIELD_SHARED_X] + (int64_t)r * c.H * 2);
+        }
+        for (int ch = threadIdx.x; ch < H8; ch += blockDim.x) __builtin_nontemporal_store(src[ch], &dst[ch]);
     }
 }
 
@@ -1594,7 +1944,7 @@ __global__ __launch_bounds__(64) void k_publish(DevCtx c, const int* status, int
         f.layer_idx = layer < 0 ? *c.layer_cur : layer;
         f.stage_idx = s;
         f.num_tokens = n_p;
-        f.routed_tokens = n_p;
+        f.routed_tokens = n_p * (c.attn_routes ? c.K : 1);
         f.shared_tokens = c.has_shared ? n_p : 0;
         f.src_peer = p;
         f.n_counts = c.E;
@@ -1622,15 +1972,23 @@ hipError_t launch_ffn(const DevCtx& c, int stage, int layer, const Weights& w, l
     mark();
     k_wait<<<1, 64, 0, st>>>(c, stage, layer, timeout_ticks, max_take, gather_ticks);
     mark();
-    if (c.E <= 64) k_route<1><<<c.NB, 64 * kRouteChunk, 0, st>>>(c, status, stage);
-    else if (c.E <= 128) k_route<2><<<c.NB, 64 * kRouteChunk, 0, st>>>(c, status, stage);
-    else if (c.E <= 256) k_route<4><<<c.NB, 64 * kRouteChunk, 0, st>>>(c, status, stage);
-    else if (c.E <= 512) k_route<8><<<c.NB, 64 * kRouteChunk, 0, st>>>(c, status, stage);
-    else k_route<16><<<c.NB, 64 * kRouteChunk, 0, st>>>(c, status, stage);
-    mark();
-    k_scan<<<c.E, 256, 0, st>>>(c, status);
-    mark();
-    k_permute<<<c.NB, 256, 0, st>>>(c, status);
+    if (c.attn_routes) {
+        // (the routing slots: the merge of the group lists, then the dispatch)
+        k_gscan<<<c.P + (c.E + 255) / 256, 256, 0, st>>>(c, status, stage);
+        mark();
+        mark();
+        k_gdispatch<<<c.NB, 256, 0, st>>>(c, status, stage);
+    } else {
+        if (c.E <= 64) k_route<1><<<c.NB, 64 * kRouteChunk, 0, st>>>(c, status, stage);
+        else if (c.E <= 128) k_route<2><<<c.NB, 64 * kRouteChunk, 0, st>>>(c, status, stage);
+        else if (c.E <= 256) k_route<4><<<c.NB, 64 * kRouteChunk, 0, st>>>(c, status, stage);
+        else if (c.E <= 512) k_route<8><<<c.NB, 64 * kRouteChunk, 0, st>>>(c, status, stage);
+        else k_route<16><<<c.NB, 64 * kRouteChunk, 0, st>>>(c, status, stage);
+        mark();
+        k_scan<<<c.E, 256, 0, st>>>(c, status);
+        mark();
+        k_permute<<<c.NB, 256, 0, st>>>(c, status);
+    }
     mark();
     k_gemm<1><<<num_cu, kGemmThreads, 0, st>>>(c, status, w, layer);
     mark();
@@ -1638,6 +1996,12 @@ hipError_t launch_ffn(const DevCtx& c, int stage, int layer, const Weights& w, l
     mark();
     int cgrid = Tmax < num_cu * 8 ? Tmax : num_cu * 8;
     if (cgrid < 1) cgrid = 1;
+    if (c.attn_routes) {
+        k_retcopy<<<num_cu * 8, 256, 0, st>>>(c, status, stage);
+        k_publish<<<c.P, 64, 0, st>>>(c, status, stage, layer);
+        mark();
+        return hipGetLastError();
+    }
     switch (c.K) {
 #define AFD_COMBINE_CASE(k) \
     case k: k_combine<k><<<cgrid, 256, 0, st>>>(c, status, stage, layer); break;

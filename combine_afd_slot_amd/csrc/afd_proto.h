@@ -33,11 +33,16 @@ AFD_HD int64_t align_up(int64_t n, int64_t a = kAlign) { return (n + a - 1) / a 
 // FFN side the protocol is routed-only ("[RFC]: Async AFD for Prefill on
 // Ascend NPU", "Shared-expert ownership": no shared-expert data crosses the
 // data plane), so shared_idx and shared_x take no space.
-AFD_HD void slot_field_bytes(int64_t token_cap, int64_t hidden, int64_t experts, bool shared,
-                             int64_t out[AFD_NUM_FIELDS]) {
+// When the attention side routes ("[RFC]: Async GPU Connector", "Data flow":
+// the sender sorts its (token, expert) pairs and sends the routed rows
+// grouped by expert with the group list in the header; "Capacity and ring
+// depth": routed_cap = token_cap * topk / ffn_size, here one FFN rank), no
+// logits travel and routed_x holds token_cap * top_k rows.
+AFD_HD void slot_field_bytes(int64_t token_cap, int64_t hidden, int64_t experts, int64_t top_k, bool shared,
+                             bool attn_routes, int64_t out[AFD_NUM_FIELDS]) {
     out[AFD_FIELD_HEADER] = 4 * (AFD_HDR_WORDS + experts);
-    out[AFD_FIELD_ROUTE_TABLE] = 4 * token_cap * experts;
-    out[AFD_FIELD_ROUTED_X] = 2 * token_cap * hidden;
+    out[AFD_FIELD_ROUTE_TABLE] = attn_routes ? 0 : 4 * token_cap * experts;
+    out[AFD_FIELD_ROUTED_X] = 2 * token_cap * (attn_routes ? top_k : 1) * hidden;
     out[AFD_FIELD_SHARED_IDX] = shared ? 4 * token_cap : 0;
     out[AFD_FIELD_SHARED_X] = shared ? 2 * token_cap * hidden : 0;
 }
@@ -88,12 +93,14 @@ AFD_HD int32_t header_decode(const int32_t* w, int32_t expect_counts, afd_header
 // seq of the flag that announced it, and (one FFN replica) route and share
 // every token.
 // shared: the window carries shared rows (every token has one); routed-only
-// messages carry none (shared_tokens 0).
+// messages carry none (shared_tokens 0).  kmul: routed rows per token (1
+// when the FFN routes, top_k when the attention side sends its routed rows).
 AFD_HD int32_t inbound_check(const afd_header_fields& f, int32_t peer, int32_t stage, int32_t layer,
-                             int32_t token_cap, int32_t flag_seq, bool shared) {
+                             int32_t token_cap, int32_t flag_seq, bool shared, int32_t kmul) {
     if (f.src_peer != peer || f.stage_idx != stage || f.layer_idx != layer) return AFD_ERR_HEADER;
     if (f.num_tokens < 0 || f.num_tokens > token_cap) return AFD_ERR_HEADER;
-    if (f.routed_tokens != f.num_tokens || f.shared_tokens != (shared ? f.num_tokens : 0)) return AFD_ERR_HEADER;
+    if (f.routed_tokens != f.num_tokens * kmul || f.shared_tokens != (shared ? f.num_tokens : 0))
+        return AFD_ERR_HEADER;
     if (f.seq != flag_seq) return AFD_ERR_HEADER;
     return AFD_OK;
 }

@@ -59,6 +59,7 @@ class Workload:
     recipe: str = "chunked"
     seed: int = 0
     ring_depth: int = 1
+    attention_routes: int = 0       # 1: the attention side routes (grouped routed rows, sender combines)
     notes: str = field(default="", compare=False)
 
     @property

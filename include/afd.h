@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define AFD_ABI_VERSION 4
+#define AFD_ABI_VERSION 5
 
 /* Header flags bit 1: shutdown sentinel ("Window and slot layout"). */
 #define AFD_FLAG_SHUTDOWN 0x2u
@@ -128,7 +128,9 @@ typedef struct afd_window_config {
     float routed_scaling_factor; /* scales the routed branch (1.0 = none)                    */
     int32_t renormalize;         /* 1: top-k weights renormalised to sum to 1                */
     int32_t poll_timeout_us;     /* bound of every device-side flag wait                     */
-    int32_t reserved[4];         /* must be 0                                                */
+    int32_t attention_routes;    /* 0: the FFN routes (logits travel); 1: the attention side
+                                    routes and sends rows grouped by expert (see below)      */
+    int32_t reserved[3];         /* must be 0                                                */
 } afd_window_config;
 
 /* Byte layout of the library's single device allocation.  The inbound

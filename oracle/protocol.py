@@ -19,6 +19,13 @@ Readings where the page is silent (also listed in the design notes):
     section "Shared-expert ownership" (no shared-expert data on the data
     plane): shared_idx and shared_x are 0 bytes and headers carry
     shared_tokens = 0;
+  * when the attention side routes (the arrangement of section "Data flow":
+    the sender sorts its flattened (token, expert) pairs stably and sends the
+    routed rows grouped by expert, the group list in the header's
+    expert_counts), no logits travel, so route_table is 0 bytes, and
+    routed_x holds token_cap * top_k rows (section "Capacity and ring
+    depth": routed_cap = token_cap * topk / ffn_size, with one FFN rank);
+    routed_tokens is num_tokens * top_k;
   * flags are int32; the flag array also starts 256-byte aligned (offset 0)
     and the first slot starts at the next 256-byte boundary after it;
   * header word order: magic, version, flags, seq, echo_seq, layer_idx,
@@ -47,21 +54,24 @@ def align_up(n: int, a: int = ALIGN) -> int:
     return (n + a - 1) // a * a
 
 
-def slot_fields(token_cap: int, hidden: int, num_experts: int, shared: bool = True) -> dict:
-    """Byte size of each slot field before alignment (shared=False: routed-only)."""
+def slot_fields(token_cap: int, hidden: int, num_experts: int, shared: bool = True,
+                top_k: int = 0) -> dict:
+    """Byte size of each slot field before alignment (shared=False: routed-only;
+    top_k > 0: the attention side routes and sends top_k rows per token)."""
     return {
         "header": 4 * (HEADER_WORDS + num_experts),
-        "route_table": 4 * token_cap * num_experts,
-        "routed_x": 2 * token_cap * hidden,
+        "route_table": 0 if top_k else 4 * token_cap * num_experts,
+        "routed_x": 2 * token_cap * (top_k or 1) * hidden,
         "shared_idx": 4 * token_cap if shared else 0,
         "shared_x": 2 * token_cap * hidden if shared else 0,
     }
 
 
 def window_layout(num_peers: int, ring_depth: int, token_cap: int, hidden: int,
-                  num_experts: int, shared: bool = True) -> dict:
-    """Offsets of one window (flags, then slots), relative to its start."""
-    sizes = slot_fields(token_cap, hidden, num_experts, shared)
+                  num_experts: int, shared: bool = True, top_k: int = 0) -> dict:
+    """Offsets of one window (flags, then slots), relative to its start
+    (top_k > 0: an attention-routed window)."""
+    sizes = slot_fields(token_cap, hidden, num_experts, shared, top_k)
     off, cur = {}, 0
     for name in FIELDS:
         off[name] = cur

@@ -28,7 +28,7 @@ def test_library_exports_every_declared_symbol():
     missing = [s for s in declared if not hasattr(L, s)]
     assert not missing, missing
     assert sorted(afd.EXPORTS) == declared
-    assert afd.afd_abi_version() == 4
+    assert afd.afd_abi_version() == 5
 
 
 CFGS = [
@@ -42,6 +42,10 @@ CFGS = [
     dict(num_peers=8, token_cap=16, hidden=2048, num_experts=64, top_k=6, intermediate=1408,
          shared_intermediate=2816),
     dict(num_peers=3, token_cap=37, hidden=40, num_experts=5, top_k=5, intermediate=8, shared_intermediate=0),
+    dict(num_peers=2, token_cap=16, hidden=64, num_experts=8, top_k=2, intermediate=32, shared_intermediate=32,
+         attention_routes=1),
+    dict(num_peers=4, token_cap=4096, hidden=2048, num_experts=64, top_k=6, intermediate=1408,
+         shared_intermediate=0, attention_routes=1, ring_depth=2),
 ]
 
 
@@ -51,7 +55,8 @@ def test_layout_matches_reference(kw):
     L = afd.afd_layout_compute(cfg)
     R = kw.get("ring_depth", 1)
     r = ref.window_layout(kw["num_peers"], R, kw["token_cap"], kw["hidden"], kw["num_experts"],
-                          shared=kw["shared_intermediate"] > 0)
+                          shared=kw["shared_intermediate"] > 0,
+                          top_k=kw["top_k"] if kw.get("attention_routes") else 0)
     for i, name in enumerate(ref.FIELDS):
         assert L.field_off[i] == r["field_off"][name], name
         assert L.field_bytes[i] == r["field_bytes"][name], name
@@ -103,7 +108,7 @@ def test_slot_fields_disjoint_aligned_viewable(kw):
     dict(struct_size=3), dict(reserved=1), dict(num_peers=0), dict(num_peers=65), dict(ring_depth=0),
     dict(ring_depth=5), dict(token_cap=0), dict(hidden=60), dict(num_experts=0), dict(top_k=0),
     dict(top_k=9), dict(intermediate=12), dict(shared_intermediate=-8), dict(renormalize=2),
-    dict(poll_timeout_us=0),
+    dict(poll_timeout_us=0), dict(attention_routes=2), dict(attention_routes=-1),
 ])
 def test_config_rejected(bad):
     kw = dict(CFGS[0])

@@ -1,0 +1,191 @@
+"""GPU: attention-routed windows (attention_routes = 1).
+
+"[RFC]: Async GPU Connector", "Data flow": the sender routes its tokens,
+sorts the flattened (token, expert) pairs stably, sends the routed rows
+grouped by expert with the group list in the header, keeps the top-k
+weights, and combines the expert outputs that come back in the same order;
+"Capacity and ring depth": routed_x holds token_cap * top_k rows (one FFN
+rank).
+
+Checks:
+  * the inbound slot a pack writes against the oracle's routing and stable
+    dispatch of that message alone: the group list bit for bit, each grouped
+    row the bytes of its token's hidden row;
+  * the return slot: the header's group list, every returned routed row
+    against the oracle's expert output for that row, the shared rows against
+    the oracle's shared expert;
+  * the outputs bit for bit against an FFN-routed window on the same inputs
+    (same top-k code, same GEMM row order and plan, same combine
+    arithmetic), and against the oracle within the row tolerance;
+  * a group list that does not cover the routed rows is a header error and
+    consumes nothing; any-ready runs serve a subset with the same bits.
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+
+from combine_afd_slot_amd import afd
+from combine_afd_slot_amd.driver import FfnSession
+from combine_afd_slot_amd.inputs import make_inputs, small_workload
+from gpu_util import ROW_REL_TOL, row_rel_err, say
+from oracle import protocol as ref
+
+pytestmark = pytest.mark.gpu
+
+WLS = [
+    small_workload("attn_shared", seq_lens=(37, 0, 70, 5), hidden=128, num_experts=12, top_k=3, intermediate=96,
+                   shared_intermediate=64, token_cap=72),
+    small_workload("attn_routed_only", seq_lens=(19, 33), hidden=64, num_experts=8, top_k=2, intermediate=48,
+                   shared_intermediate=0, token_cap=40),
+    small_workload("attn_wide", seq_lens=(40, 17), hidden=128, num_experts=160, top_k=6, intermediate=64,
+                   shared_intermediate=128, token_cap=48, zipf_bias=1.0),
+]
+
+
+def _attn(wl):
+    return dataclasses.replace(wl, attention_routes=1)
+
+
+def _slot_off(s, win_off, peer, stage=0):
+    L = s.layout
+    return win_off + (L.in_slots_off - L.in_off) + (peer * s.wl.ring_depth + stage) * L.slot_bytes
+
+
+def _read(s, off, n, dt):
+    return np.frombuffer(afd.afd_debug_read(s.win, off, n * np.dtype(dt).itemsize), dt).copy()
+
+
+def _header(s, win_off, peer):
+    off = _slot_off(s, win_off, peer) + s.layout.field_off[0]
+    return _read(s, off, 12 + s.wl.num_experts, np.int32), off
+
+
+def _message_oracle(orc, wl, inp, p):
+    """The oracle's routing and stable dispatch of peer p's message alone,
+    its expert outputs in grouped order and its shared-expert rows."""
+    x, l = inp["x"][p], inp["l"][p]
+    ids, _ = orc.route(l, wl.top_k, wl.renormalize)
+    counts, eoff, perm, _ = orc.dispatch(ids, wl.num_experts)
+    Y = orc.experts(x, eoff, perm, wl.top_k, inp["W13"], inp["W2"])
+    S = orc.shared(x, inp["Ws13"], inp["Ws2"]) if wl.shared_intermediate else None
+    return counts, perm, Y, S
+
+
+def _ffn_routed_outputs(wl, inp):
+    with FfnSession(wl, inp, poll_timeout_us=200_000) as s:
+        s.step()
+        assert s.status().status == 0
+        return [o.copy() for o in s.outputs_f32()]
+
+
+@pytest.mark.parametrize("wl", WLS, ids=lambda w: w.name)
+def test_attention_routed_run(orc, wl):
+    inp = make_inputs(wl)
+    base = _ffn_routed_outputs(wl, inp)
+    awl = _attn(wl)
+    H, K = wl.hidden, wl.top_k
+    with FfnSession(awl, inp, poll_timeout_us=200_000) as s:
+        L = s.layout
+        r = ref.window_layout(wl.num_peers, wl.ring_depth, wl.token_cap, H, wl.num_experts,
+                              shared=wl.shared_intermediate > 0, top_k=K)
+        assert L.slot_bytes == r["slot_bytes"] and L.field_bytes[1] == 0
+        say(f"[attn] {wl.name}: pack")
+        s.pack_all()
+        msgs = {}
+        for p, n in enumerate(wl.seq_lens):
+            hw, _ = _header(s, L.in_off, p)
+            d = ref.decode_header(hw, wl.num_experts)
+            assert d["num_tokens"] == n and d["routed_tokens"] == n * K
+            assert d["shared_tokens"] == (n if wl.shared_intermediate else 0)
+            if n == 0:
+                assert not d["counts"].any()
+                continue
+            counts, perm, Y, S = msgs[p] = _message_oracle(orc, wl, inp, p)
+            np.testing.assert_array_equal(d["counts"], counts)
+            so = _slot_off(s, L.in_off, p)
+            rx = _read(s, so + L.field_off[2], n * K * H, np.uint16).reshape(n * K, H)
+            np.testing.assert_array_equal(rx, inp["x"][p][perm // K])
+        say(f"[attn] {wl.name}: run")
+        s.run()
+        s.ffn_stream.synchronize()
+        st = s.status()
+        assert st.status == 0 and st.total_tokens == wl.total_tokens
+        for p, (counts, perm, Y, S) in msgs.items():
+            n = wl.seq_lens[p]
+            hw, _ = _header(s, L.ret_off, p)
+            d = ref.decode_header(hw, wl.num_experts)
+            assert d["num_tokens"] == n and d["routed_tokens"] == n * K
+            np.testing.assert_array_equal(d["counts"], counts)
+            so = _slot_off(s, L.ret_off, p)
+            ry = _read(s, so + L.field_off[2], n * K * H, np.uint16).reshape(n * K, H)
+            ry = (ry.astype(np.uint32) << 16).view(np.float32)
+            assert row_rel_err(ry, Y) <= ROW_REL_TOL, p
+            if S is not None:
+                rs = _read(s, so + L.field_off[4], n * H, np.uint16).reshape(n, H)
+                assert row_rel_err((rs.astype(np.uint32) << 16).view(np.float32), S) <= ROW_REL_TOL, p
+        say(f"[attn] {wl.name}: unpack")
+        s.unpack_all()
+        full = _oracle_out(orc, wl, inp)
+        for p, o in enumerate(s.outputs_f32()):
+            if wl.seq_lens[p]:
+                assert s.peer_status(p).status == 0
+            np.testing.assert_array_equal(o, base[p])
+            assert row_rel_err(o, full[p]) <= ROW_REL_TOL, p
+
+
+def _oracle_out(orc, wl, inp):
+    return orc.ffn(inp["x"], inp["l"], inp["W13"], inp["W2"], inp.get("Ws13"), inp.get("Ws2"),
+                   K=wl.top_k)["out_p"]
+
+
+def test_group_list_checked(orc):
+    wl = _attn(WLS[0])
+    inp = make_inputs(wl)
+    base = _ffn_routed_outputs(WLS[0], inp)
+    with FfnSession(wl, inp, poll_timeout_us=200_000) as s:
+        L = s.layout
+        s.pack_all()
+        hw, off = _header(s, L.in_off, 2)
+        c0 = ref.HEADER_WORDS
+        bad_sum = hw.copy()
+        bad_sum[c0] += 1
+        e1 = c0 + int(np.argmax(hw[c0:]))
+        bad_neg = hw.copy()
+        bad_neg[e1] -= hw[e1] + 1  # -1, the list sum kept by the next change
+        bad_neg[c0 + (e1 - c0 + 1) % wl.num_experts] += hw[e1] + 1
+        for bad in (bad_sum, bad_neg):
+            afd.afd_debug_write(s.win, off, bad.tobytes())
+            s.run()
+            st = s.status()
+            assert st.status == afd.AFD_ERR_HEADER and st.failed_peer == 2, (st.status, st.failed_peer)
+            assert afd.afd_window_poll(s.win, 1, wl.num_peers) == [0] * wl.num_peers
+        afd.afd_debug_write(s.win, off, hw.tobytes())
+        s.run()
+        s.ffn_stream.synchronize()
+        assert s.status().status == 0
+        s.unpack_all()
+        for p, o in enumerate(s.outputs_f32()):
+            np.testing.assert_array_equal(o, base[p])
+
+
+def test_any_ready_subset():
+    wl = WLS[0]
+    inp = make_inputs(wl)
+    base = _ffn_routed_outputs(wl, inp)
+    with FfnSession(_attn(wl), inp, poll_timeout_us=200_000) as s:
+        for served in ((0, 2), (1, 3)):
+            for p in served:
+                s.pack(p)
+            for p in served:
+                s.peer_streams[p].synchronize()
+            afd.afd_ffn_run_ready(s.win, 0, 0, s.packed.data_ptr(), 4, 0, s.ffn_stream.cuda_stream)
+            st = s.status()
+            mask = sum(1 << p for p in served)
+            assert st.status == 0 and st.served_mask == mask, (st.status, st.served_mask)
+            for p in served:
+                s.unpack(p)
+                s.peer_streams[p].synchronize()
+                if wl.seq_lens[p]:
+                    assert s.peer_status(p).status == 0
+                np.testing.assert_array_equal(s.outputs_f32()[p], base[p])
