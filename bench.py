@@ -69,7 +69,7 @@ def measured_traffic(wl, kernel):
         sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
     except OSError:
         return None
-    if side.get("workload") != wl.name or side.get("kernel_source_sha256") != sha:
+    if wl.attention_routes or side.get("workload") != wl.name or side.get("kernel_source_sha256") != sha:
         return None
     b = side["bytes_per_launch"].get(kernel)
     return None if b is None else int(b["read"] + b["written"])
@@ -100,6 +100,32 @@ def cpu_baseline(wl, inp, target_s=15.0):
                       f"a1-a7 in float64, {dt:.1f} s"}
 
 
+def peer_side_ms(torch, sess, n):
+    """Untimed pass: per step, the slowest peer's pack and unpack (HIP events
+    on each peer's stream; not part of the FFN step)."""
+    P = sess.wl.num_peers
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(P)]
+    pk, up = [], []
+    for _ in range(n):
+        for p in range(P):
+            ev[p][0].record(sess.peer_streams[p])
+            sess.pack(p)
+            ev[p][1].record(sess.peer_streams[p])
+        for ps in sess.peer_streams:
+            ps.synchronize()
+        sess.run()
+        sess.ffn_stream.synchronize()
+        for p in range(P):
+            ev[p][2].record(sess.peer_streams[p])
+            sess.unpack(p)
+            ev[p][3].record(sess.peer_streams[p])
+        for ps in sess.peer_streams:
+            ps.synchronize()
+        pk.append(max(ev[p][0].elapsed_time(ev[p][1]) for p in range(P)))
+        up.append(max(ev[p][2].elapsed_time(ev[p][3]) for p in range(P)))
+    return {"pack": round(float(np.mean(pk)), 4), "unpack": round(float(np.mean(up)), 4)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -108,6 +134,9 @@ def main():
     ap.add_argument("--workload", default="prefill")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-profile", action="store_true", help="no per-kernel events (pure step timing)")
+    ap.add_argument("--attention-routes", action="store_true",
+                    help="attention-routed window: the peers route, group and combine; the FFN side merges "
+                         "their group lists")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run only a plain 1 GiB device-to-device copy, 10 times (scale for HBM byte counters)")
     args = ap.parse_args()
@@ -134,6 +163,9 @@ def main():
     from combine_afd_slot_amd.inputs import WORKLOADS, make_inputs
 
     wl = WORKLOADS[args.workload]
+    if args.attention_routes:
+        import dataclasses
+        wl = dataclasses.replace(wl, attention_routes=1)
     log(f"[bench] workload {wl.name}: seq_lens={wl.seq_lens} H={wl.hidden} E={wl.num_experts} "
         f"K={wl.top_k} I={wl.intermediate} Is={wl.shared_intermediate}")
     t0 = time.time()
@@ -184,6 +216,11 @@ def main():
         tot, runs = afd.afd_profile_read(sess.win, reset=True)
         afd.afd_profile_enable(sess.win, 0)
         kern_all = {k: round(v / max(runs, 1), 4) for k, v in tot.items()}
+        if wl.attention_routes:  # the slots hold the attention-routed run's kernels
+            ren = {"route_topk": "merge_group_lists", "permute": "dispatch_plan",
+                   "combine_split_publish": "return_copy_publish"}
+            kern_all = {ren.get(k, k): v for k, v in kern_all.items() if k != "scan_offsets"}
+    peer_ms = peer_side_ms(torch, sess, min(args.steps, 10))
     sess.close()
 
     ms = float(np.mean(step_ms))
@@ -212,7 +249,10 @@ def main():
         "mfma_frac_step": round(alg["flops"] / (ms * 1e-3) / (MFMA_BF16_PEAK_TFLOPS * 1e12), 4),
         "hbm_frac_step": round(alg["bytes"] / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9), 4),
         "expert_counts_min_max": [int(counts.min()), int(counts.max())],
+        "peer_side_ms_max_over_peers": peer_ms,
     }
+    if wl.attention_routes:
+        line["config"]["attention_routes"] = 1
     if kern:
         line["kernel_ms"] = {k: round(v, 4) for k, v in kern.items()}
         line["kernel_ms_all_separate_pass"] = kern_all

@@ -465,6 +465,8 @@ hipError_t launch_unpack(const DevCtx& c, int peer, int stage, int seq_len, int 
 __global__ __launch_bounds__(64) void k_wait(DevCtx c, int s, int layer, long long timeout, int max_take,
                                              long long gather) {
     __shared__ int s_flag[kMaxPeers], s_err[kMaxPeers], s_ntok[kMaxPeers], s_shut[kMaxPeers], s_layer[kMaxPeers];
+    __shared__ int s_rt[kMaxPeers], s_gneg[kMaxPeers];
+    __shared__ unsigned long long s_gsum[kMaxPeers];
     const int p = threadIdx.x;
     int* st = c.run_status + s * kStatusWords;
     const bool in = p < c.P;
@@ -533,18 +535,7 @@ __global__ __launch_bounds__(64) void k_wait(DevCtx c, int s, int layer, long lo
                 err = inbound_check(h, p, s, layer < 0 ? hl : layer, c.token_cap, f, c.has_shared,
                                     c.attn_routes ? c.K : 1);
             }
-            if (err == AFD_OK && c.attn_routes) {
-                // the group list: non-negative, and it covers every routed row
-                const int* cnt = (const int*)hq + AFD_HDR_WORDS;
-                long long sum = 0;
-                bool neg = false;
-                for (int e = 0; e < c.E; ++e) {
-                    const int v = cnt[e];
-                    neg |= v < 0;
-                    sum += v;
-                }
-                if (neg || sum != h.routed_tokens) err = AFD_ERR_HEADER;
-            }
+            s_rt[p] = err == AFD_OK ? h.routed_tokens : -1;  // group list to check below
             if (err == AFD_OK) {
                 ntok = h.num_tokens;
                 shut = (h.flags & (int)AFD_FLAG_SHUTDOWN) != 0;
@@ -555,8 +546,30 @@ __global__ __launch_bounds__(64) void k_wait(DevCtx c, int s, int layer, long lo
         s_ntok[p] = ntok;
         s_shut[p] = shut;
         s_layer[p] = hl;
+        if (!(take && err == AFD_OK)) s_rt[p] = -1;
+        s_gsum[p] = 0;
+        s_gneg[p] = 0;
     }
     __syncthreads();
+    if (c.attn_routes) {
+        // each group list non-negative and covering every routed row: the
+        // P*E counts spread over the lanes, so their loads go out together
+        const int E = c.E, n = c.P * E;
+        for (int i = p; i < n; i += 64) {
+            const int q = i / E;
+            if (s_rt[q] < 0) continue;
+            const int v = ((const int*)(slot_ptr(c, c.in_win, q, s) + c.foff[AFD_FIELD_HEADER]))[AFD_HDR_WORDS + i - q * E];
+            if (v < 0) s_gneg[q] = 1;
+            else atomicAdd(&s_gsum[q], (unsigned long long)v);
+        }
+        __syncthreads();
+        if (in && s_rt[p] >= 0 && (s_gneg[p] || s_gsum[p] != (unsigned long long)s_rt[p])) {
+            s_err[p] = AFD_ERR_HEADER;
+            s_ntok[p] = 0;
+            s_shut[p] = 0;
+        }
+        __syncthreads();
+    }
     if (threadIdx.x == 0) {
         int status = taken ? AFD_OK : AFD_ERR_TIMEOUT, failed = -1, shut = 0;
         for (int q = 0; q < c.P; ++q) {
