@@ -38,7 +38,7 @@ EXPORTS = (
     "afd_layout_compute", "afd_window_create", "afd_window_destroy", "afd_window_layout",
     "afd_slot_pack", "afd_weights_pack", "afd_ffn_run", "afd_ffn_run_ready", "afd_layer_table_set", "afd_ffn_run_table",
     "afd_ffn_loop_create", "afd_ffn_loop_launch", "afd_ffn_loop_destroy",
-    "afd_slot_unpack", "afd_window_status", "afd_peer_status",
+    "afd_slot_unpack", "afd_slot_unpack_ranks", "afd_window_status", "afd_peer_status",
     "afd_window_poll", "afd_debug_routing", "afd_debug_read", "afd_debug_write",
     "afd_profile_enable", "afd_profile_read", "afd_profile_kernel_name",
     "afd_header_encode", "afd_header_decode", "afd_last_error", "afd_status_string",
@@ -59,7 +59,8 @@ class WindowConfig(ctypes.Structure):
                 ("intermediate", ctypes.c_int32), ("shared_intermediate", ctypes.c_int32),
                 ("routed_scaling_factor", ctypes.c_float), ("renormalize", ctypes.c_int32),
                 ("poll_timeout_us", ctypes.c_int32), ("attention_routes", ctypes.c_int32),
-                ("reserved", ctypes.c_int32 * 3)]
+                ("route_experts", ctypes.c_int32), ("expert_offset", ctypes.c_int32),
+                ("reserved", ctypes.c_int32 * 1)]
 
 
 class Layout(ctypes.Structure):
@@ -112,6 +113,7 @@ def lib():
             "afd_ffn_loop_launch": [vp, vp],
             "afd_ffn_loop_destroy": [vp],
             "afd_slot_unpack": [vp, i32, i32, i32, vp, vp],
+            "afd_slot_unpack_ranks": [vp, i32, i32, i32, i32, vp, vp],
             "afd_window_status": [vp, i32, vp, P(RunInfo)],
             "afd_peer_status": [vp, i32, i32, vp, P(RunInfo)],
             "afd_window_poll": [vp, i32, vp],
@@ -153,7 +155,7 @@ def _check(rc: int) -> int:
 
 def make_config(num_peers, token_cap, hidden, num_experts, top_k, intermediate, shared_intermediate,
                 ring_depth=1, routed_scaling_factor=1.0, renormalize=1, poll_timeout_us=2_000_000,
-                attention_routes=0) -> WindowConfig:
+                attention_routes=0, route_experts=0, expert_offset=0) -> WindowConfig:
     c = WindowConfig()
     c.struct_size = ctypes.sizeof(WindowConfig)
     c.num_peers, c.ring_depth, c.token_cap = num_peers, ring_depth, token_cap
@@ -161,6 +163,7 @@ def make_config(num_peers, token_cap, hidden, num_experts, top_k, intermediate, 
     c.intermediate, c.shared_intermediate = intermediate, shared_intermediate
     c.routed_scaling_factor, c.renormalize, c.poll_timeout_us = routed_scaling_factor, renormalize, poll_timeout_us
     c.attention_routes = attention_routes
+    c.route_experts, c.expert_offset = route_experts, expert_offset
     return c
 
 
@@ -232,6 +235,12 @@ def afd_ffn_loop_destroy(loop) -> int:
 
 def afd_slot_unpack(win, peer, stage, seq_len, out_ptr, stream=0) -> int:
     return _check(lib().afd_slot_unpack(win, peer, stage, seq_len, out_ptr or None, stream or None))
+
+
+def afd_slot_unpack_ranks(wins, peer, stage, seq_len, out_ptr, stream=0) -> int:
+    arr = (ctypes.c_void_p * len(wins))(*wins)
+    return _check(lib().afd_slot_unpack_ranks(arr, len(wins), peer, stage, seq_len, out_ptr or None,
+                                              stream or None))
 
 
 def afd_window_status(win, stage=0, stream=0) -> RunInfo:

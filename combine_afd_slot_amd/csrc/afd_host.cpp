@@ -4,6 +4,7 @@
 // anything is enqueued.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
@@ -43,18 +44,29 @@ int32_t validate(const afd_window_config* c) {
     if (!c) return fail(AFD_ERR_INVALID, "config is NULL");
     if (c->struct_size != sizeof(afd_window_config))
         return fail(AFD_ERR_INVALID, "struct_size %u != %zu", c->struct_size, sizeof(afd_window_config));
-    for (int i = 0; i < 3; ++i)
+    for (int i = 0; i < 1; ++i)
         if (c->reserved[i] != 0) return fail(AFD_ERR_INVALID, "reserved[%d] must be 0", i);
     if (c->attention_routes != 0 && c->attention_routes != 1)
         return fail(AFD_ERR_INVALID, "attention_routes must be 0 or 1");
+    if (c->route_experts != 0) {
+        if (!c->attention_routes) return fail(AFD_ERR_INVALID, "route_experts needs attention_routes = 1");
+        if (c->route_experts > afd::kMaxExperts) return fail(AFD_ERR_INVALID, "route_experts above 1024");
+        if (c->expert_offset < 0 || c->num_experts < 1 ||
+            (int64_t)c->expert_offset + c->num_experts > c->route_experts)
+            return fail(AFD_ERR_INVALID, "expert range [%d, %d+%d) not inside [0, route_experts %d)",
+                        c->expert_offset, c->expert_offset, c->num_experts, c->route_experts);
+    } else if (c->expert_offset != 0) {
+        return fail(AFD_ERR_INVALID, "expert_offset needs route_experts > 0");
+    }
     if (c->num_peers < 1 || c->num_peers > afd::kMaxPeers) return fail(AFD_ERR_INVALID, "num_peers out of [1,64]");
     if (c->ring_depth < 1 || c->ring_depth > 4) return fail(AFD_ERR_INVALID, "ring_depth out of [1,4]");
     if (c->token_cap < 1) return fail(AFD_ERR_INVALID, "token_cap must be >= 1");
     if (c->hidden < 8 || c->hidden % 8) return fail(AFD_ERR_INVALID, "hidden must be a positive multiple of 8");
     if (c->num_experts < 1 || c->num_experts > afd::kMaxExperts)
         return fail(AFD_ERR_INVALID, "num_experts out of [1,1024]");
-    if (c->top_k < 1 || c->top_k > c->num_experts || c->top_k > afd::kMaxTopK)
-        return fail(AFD_ERR_INVALID, "top_k out of [1, min(num_experts,16)]");
+    const int32_t routed_over = c->route_experts ? c->route_experts : c->num_experts;
+    if (c->top_k < 1 || c->top_k > routed_over || c->top_k > afd::kMaxTopK)
+        return fail(AFD_ERR_INVALID, "top_k out of [1, min(experts routed over,16)]");
     if (c->intermediate < 8 || c->intermediate % 8)
         return fail(AFD_ERR_INVALID, "intermediate must be a positive multiple of 8");
     if (c->shared_intermediate < 0 || c->shared_intermediate % 8)
@@ -85,7 +97,7 @@ struct WsLayout {
     int64_t ctrl_ints;
     // control-word offsets inside ctrl (in ints)
     int64_t c_seen_in, c_ret_seq, c_seen_ret, c_cur_seq, c_off, c_T, c_done, c_run_status, c_peer_status;
-    int64_t c_layer_cur, c_nlayers, c_rr;
+    int64_t c_layer_cur, c_nlayers, c_rr, c_prow;
 };
 
 WsLayout ws_layout(const afd_window_config& c) {
@@ -107,6 +119,7 @@ WsLayout ws_layout(const afd_window_config& c) {
     w.c_layer_cur = ci; ci += 1;
     w.c_nlayers = ci; ci += 1;
     w.c_rr = ci; ci += R;
+    w.c_prow = ci; ci += P;
     w.ctrl_ints = ci;
     int64_t cur = 0;
     auto take = [&](int64_t bytes) {
@@ -290,7 +303,10 @@ void fill_ctx(afd_window* w) {
     d.layer_cur = ctrl + L.c_layer_cur;
     d.nlayers = ctrl + L.c_nlayers;
     d.rr = ctrl + L.c_rr;
+    d.prow = ctrl + L.c_prow;
     d.attn_routes = c.attention_routes;
+    d.Eg = c.route_experts ? c.route_experts : c.num_experts;
+    d.e0 = c.expert_offset;
     d.NBp = (c.token_cap + afd::kRouteChunk - 1) / afd::kRouteChunk;
     d.pid = (int*)(ws + L.pid);
     d.pwt = (float*)(ws + L.pwt);
@@ -665,6 +681,9 @@ int32_t afd_slot_unpack(afd_window* w, int32_t peer, int32_t stage, int32_t seq_
     const int idx = peer * c.ring_depth + stage;
     if (seq_len != w->packed_len[idx])
         return fail(AFD_ERR_SHAPE, "seq_len %d differs from the packed length %d", seq_len, w->packed_len[idx]);
+    if (w->ctx.Eg != c.num_experts)
+        return fail(AFD_ERR_INVALID, "the window owns experts [%d, %d) of %d: combine with afd_slot_unpack_ranks",
+                    c.expert_offset, c.expert_offset + c.num_experts, w->ctx.Eg);
     if (seq_len == 0) {
         w->inflight[idx] = 0;
         return AFD_OK;  // nothing was sent, nothing to wait for
@@ -676,6 +695,66 @@ int32_t afd_slot_unpack(afd_window* w, int32_t peer, int32_t stage, int32_t seq_
                                       (hipStream_t)peer_stream);
     if (e != hipSuccess) return hip_fail(e, "unpack launch");
     w->inflight[idx] = 0;
+    return AFD_OK;
+}
+
+int32_t afd_slot_unpack_ranks(afd_window* const* wins, int32_t n_wins, int32_t peer, int32_t stage, int32_t seq_len,
+                              void* out, void* peer_stream) {
+    if (!wins || n_wins < 1 || n_wins > afd::kMaxRanks)
+        return fail(AFD_ERR_INVALID, "n_wins must be in [1, %d] with a window array", afd::kMaxRanks);
+    for (int i = 0; i < n_wins; ++i)
+        if (!wins[i]) return fail(AFD_ERR_INVALID, "window %d is NULL", i);
+    const afd_window_config& c0 = wins[0]->cfg;
+    const int Eg = wins[0]->ctx.Eg;
+    if (!c0.attention_routes) return fail(AFD_ERR_INVALID, "windows must be attention-routed");
+    if (peer < 0 || peer >= c0.num_peers) return fail(AFD_ERR_INVALID, "peer %d out of range", peer);
+    if (stage < 0 || stage >= c0.ring_depth) return fail(AFD_ERR_INVALID, "stage %d out of range", stage);
+    const int idx = peer * c0.ring_depth + stage;
+    std::vector<std::pair<int, int>> ranges;
+    int n_shared = 0;
+    for (int i = 0; i < n_wins; ++i) {
+        const afd_window* w = wins[i];
+        const afd_window_config& c = w->cfg;
+        if (!c.attention_routes || w->ctx.Eg != Eg || c.num_peers != c0.num_peers || c.ring_depth != c0.ring_depth ||
+            c.token_cap != c0.token_cap || c.hidden != c0.hidden || c.top_k != c0.top_k ||
+            c.renormalize != c0.renormalize || c.routed_scaling_factor != c0.routed_scaling_factor ||
+            w->device != wins[0]->device)
+            return fail(AFD_ERR_INVALID, "window %d does not fit window 0 (configuration or device)", i);
+        for (int j = 0; j < i; ++j)
+            if (wins[j] == w) return fail(AFD_ERR_INVALID, "window %d given twice", i);
+        ranges.push_back({c.expert_offset, c.expert_offset + c.num_experts});
+        n_shared += c.shared_intermediate > 0;
+        if (seq_len != w->packed_len[idx])
+            return fail(AFD_ERR_SHAPE, "seq_len %d differs from window %d's packed length %d", seq_len, i,
+                        w->packed_len[idx]);
+        if (seq_len > 0 && !w->inflight[idx])
+            return fail(AFD_ERR_INVALID, "window %d has no message of (peer %d, stage %d) in flight", i, peer, stage);
+    }
+    std::sort(ranges.begin(), ranges.end());
+    int next = 0;
+    for (const auto& r : ranges) {
+        if (r.first != next) return fail(AFD_ERR_INVALID, "the windows' expert ranges do not partition [0, %d)", Eg);
+        next = r.second;
+    }
+    if (next != Eg) return fail(AFD_ERR_INVALID, "the windows' expert ranges do not partition [0, %d)", Eg);
+    if (n_shared > 1) return fail(AFD_ERR_INVALID, "more than one window has a shared expert");
+    if (seq_len == 0) {
+        for (int i = 0; i < n_wins; ++i) wins[i]->inflight[idx] = 0;
+        return AFD_OK;
+    }
+    if (!out || !aligned(out, 16)) return fail(AFD_ERR_INVALID, "out must be a 16-byte aligned device pointer");
+    std::vector<const afd::DevCtx*> ctx(n_wins);
+    std::vector<int> echo(n_wins);
+    std::vector<long long> timeout(n_wins);
+    for (int i = 0; i < n_wins; ++i) {
+        ctx[i] = &wins[i]->ctx;
+        echo[i] = wins[i]->pack_seq[idx];
+        timeout[i] = (long long)wins[i]->cfg.poll_timeout_us * wins[i]->ticks_per_us;
+    }
+    hipError_t e = afd::launch_unpack_ranks(ctx.data(), n_wins, peer, stage, seq_len, echo.data(), out,
+                                            timeout.data(), (hipStream_t)peer_stream);
+    if (e != hipSuccess) return hip_fail(e, "unpack launch");
+    for (int i = 0; i < n_wins; ++i) wins[i]->inflight[idx] = 0;
     return AFD_OK;
 }
 

@@ -72,10 +72,13 @@ struct DevCtx {
     int* Tptr;         // [1]   total tokens of the current run
     int* run_status;   // [R][kStatusWords]
     int* rr;           // [R]   first peer an any-ready run of the stage scans (rotates for fairness)
+    int* prow;         // [P]   attention-routed runs: routed rows of each peer's message
     int* layer_cur;    // [1]   layer of the current run (from the headers in layer-table runs)
     // attention-side routing (attn_routes): the routed rows arrive grouped by
     // expert, the peer keeps the top-k weights and combines on return
     int attn_routes;
+    int Eg;            // experts the peers route over (E unless the window owns a segment)
+    int e0;            // first expert of the window's segment
     int NBp;           // routing chunks of one message: ceil(token_cap / kRouteChunk)
     int* pid;          // [P*R][token_cap*K] expert of pair (t, k) of the (peer, stage) message
     float* pwt;        // [P*R][token_cap*K] its weight
@@ -145,6 +148,9 @@ hipError_t launch_pack_weights(const DevCtx& c, const afd_moe_weights& src, char
                                int64_t total, hipStream_t st);
 hipError_t launch_pack(const DevCtx& c, int peer, int stage, int layer, int seq_len, const void* hidden,
                        const float* logits, uint32_t flags, int seq, hipStream_t st);
+constexpr int kMaxRanks = 16;  // windows combined by one afd_slot_unpack_ranks
+hipError_t launch_unpack_ranks(const DevCtx* const* ctx, int n, int peer, int stage, int seq_len, const int* echo,
+                               void* out, const long long* timeout_ticks, hipStream_t st);
 hipError_t launch_unpack(const DevCtx& c, int peer, int stage, int seq_len, int expect_echo, void* out,
                          long long timeout_ticks, hipStream_t st);
 // One FFN run; `ev` (may be null) holds kProfileSlots+1 events recorded

@@ -173,7 +173,16 @@ __global__ __launch_bounds__(256) void k_pack_payload(char* slot, int64_t o_rt, 
     }
 }
 
+// counts != nullptr (attention-routed): the header's group list; routed_tokens
+// is its sum (all pairs, or the pairs of the window's experts).
 __global__ void k_pack_publish(char* slot, int* flag, afd_header_fields f, const int* counts) {
+    if (counts) {
+        int sum = 0;
+        for (int e = threadIdx.x; e < f.n_counts; e += 64) sum += counts[e];
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) sum += __shfl_xor(sum, o);
+        f.routed_tokens = sum;
+    }
     if (threadIdx.x == 0) {
         header_encode(f, counts, (int32_t*)slot);
         __threadfence();
@@ -192,13 +201,15 @@ __global__ void k_pack_publish(char* slot, int* flag, afd_header_fields f, const
 // expert scans its column of chunk histograms.  k_pscatter: the row of pair
 // f = t*K + k among the grouped rows is goff[e] + (pairs of e in earlier
 // chunks) + (earlier tokens of the chunk that chose e), and token t's hidden
-// row is copied there, once per k.
+// row is copied there, once per k.  A window that owns experts [e0, e0+E)
+// of the Eg the peers route over keeps only the pairs of those (expert ids
+// local, e - e0); the other pairs keep their weight with id -1 and no row.
 // ---------------------------------------------------------------------------
 template <int EPL>
 __global__ __launch_bounds__(64 * kRouteChunk) void k_proute(DevCtx c, int idx, const float* logits, int n) {
     __shared__ int hist[kMaxExperts];
     const int lane = threadIdx.x & 63;
-    const int E = c.E, K = c.K;
+    const int E = c.E, K = c.K, Eg = c.Eg;
     for (int e = threadIdx.x; e < E; e += blockDim.x) hist[e] = 0;
     const int t = (int)blockIdx.x * kRouteChunk + (int)(threadIdx.x >> 6);
     const bool live = t < n;
@@ -207,22 +218,23 @@ __global__ __launch_bounds__(64 * kRouteChunk) void k_proute(DevCtx c, int idx, 
 #pragma unroll
     for (int j = 0; j < EPL; ++j) {
         const int e = lane + 64 * j;
-        const float x = e < E ? logits[(int64_t)r * E + e] : -INFINITY;
+        const float x = e < Eg ? logits[(int64_t)r * Eg + e] : -INFINITY;
         v[j] = x == x ? x : -INFINITY;  // (the same rule as the FFN side)
     }
     __syncthreads();  // hist zeroed
     if (live) {
         int rank[EPL];
         float wt[EPL];
-        route_token<EPL>(v, E, K, c.renorm, lane, rank, wt);
+        route_token<EPL>(v, Eg, K, c.renorm, lane, rank, wt);
         const int64_t base = (int64_t)idx * c.token_cap * K + (int64_t)t * K;
 #pragma unroll
         for (int j = 0; j < EPL; ++j) {
-            const int e = lane + 64 * j;
-            if (e < E && rank[j] < K) {
-                c.pid[base + rank[j]] = e;
+            const int e = lane + 64 * j - c.e0;  // local id
+            if (lane + 64 * j < Eg && rank[j] < K) {
+                const bool mine = e >= 0 && e < E;
+                c.pid[base + rank[j]] = mine ? e : -1;
                 c.pwt[base + rank[j]] = wt[j];
-                atomicAdd(&hist[e], 1);
+                if (mine) atomicAdd(&hist[e], 1);
             }
         }
     }
@@ -256,7 +268,7 @@ __global__ __launch_bounds__(256) void k_pscatter(DevCtx c, int idx, char* slot,
     const int E = c.E, K = c.K, tid = threadIdx.x;
     const int b = blockIdx.x, t0 = b * kRouteChunk, nt = min(kRouteChunk, n - t0), np = nt * K;
     const int64_t pbase = (int64_t)idx * c.token_cap * K;
-    int e = 0;
+    int e = -1;  // (-1: a pair of another window's experts)
     if (tid < np) e = c.pid[pbase + (int64_t)t0 * K + tid];
     {
         const int per = (E + 255) / 256;
@@ -274,11 +286,13 @@ __global__ __launch_bounds__(256) void k_pscatter(DevCtx c, int idx, char* slot,
     }
     for (int q = tid; q < E; q += 256) emask[q] = 0u;
     __syncthreads();
-    if (tid < np) atomicOr(&emask[e], 1u << (tid / K));
+    if (e >= 0) atomicOr(&emask[e], 1u << (tid / K));
     __syncthreads();
     if (tid < np) {
         const int tl = tid / K;
-        const int pos = s_goff[e] + c.pbase[((int64_t)idx * E + e) * c.NBp + b] + __popc(emask[e] & ((1u << tl) - 1u));
+        const int pos = e < 0 ? -1
+                              : s_goff[e] + c.pbase[((int64_t)idx * E + e) * c.NBp + b] +
+                                    __popc(emask[e] & ((1u << tl) - 1u));
         c.ppos[pbase + (int64_t)t0 * K + tid] = pos;
         s_pos[tid] = pos;
     }
@@ -287,7 +301,7 @@ __global__ __launch_bounds__(256) void k_pscatter(DevCtx c, int idx, char* slot,
     uint4* rx = (uint4*)(slot + c.foff[AFD_FIELD_ROUTED_X]);
     for (int i = tid; i < np * H8; i += 256) {
         const int j = i / H8, ch = i - j * H8;
-        rx[(int64_t)s_pos[j] * H8 + ch] = hidden[(int64_t)(t0 + j / K) * H8 + ch];
+        if (s_pos[j] >= 0) rx[(int64_t)s_pos[j] * H8 + ch] = hidden[(int64_t)(t0 + j / K) * H8 + ch];
     }
 }
 
@@ -308,10 +322,10 @@ hipError_t launch_pack(const DevCtx& c, int peer, int stage, int layer, int seq_
         if (c.attn_routes && seq_len > 0) {
             const int idx = peer * c.R + stage;
             const int nb = (seq_len + kRouteChunk - 1) / kRouteChunk;
-            if (c.E <= 64) k_proute<1><<<nb, 64 * kRouteChunk, 0, st>>>(c, idx, logits, seq_len);
-            else if (c.E <= 128) k_proute<2><<<nb, 64 * kRouteChunk, 0, st>>>(c, idx, logits, seq_len);
-            else if (c.E <= 256) k_proute<4><<<nb, 64 * kRouteChunk, 0, st>>>(c, idx, logits, seq_len);
-            else if (c.E <= 512) k_proute<8><<<nb, 64 * kRouteChunk, 0, st>>>(c, idx, logits, seq_len);
+            if (c.Eg <= 64) k_proute<1><<<nb, 64 * kRouteChunk, 0, st>>>(c, idx, logits, seq_len);
+            else if (c.Eg <= 128) k_proute<2><<<nb, 64 * kRouteChunk, 0, st>>>(c, idx, logits, seq_len);
+            else if (c.Eg <= 256) k_proute<4><<<nb, 64 * kRouteChunk, 0, st>>>(c, idx, logits, seq_len);
+            else if (c.Eg <= 512) k_proute<8><<<nb, 64 * kRouteChunk, 0, st>>>(c, idx, logits, seq_len);
             else k_proute<16><<<nb, 64 * kRouteChunk, 0, st>>>(c, idx, logits, seq_len);
             k_pscan<<<c.E, 256, 0, st>>>(c, idx, nb);
             k_pscatter<<<nb, 256, 0, st>>>(c, idx, slot, (const uint4*)hidden, seq_len);
@@ -409,6 +423,94 @@ __global__ __launch_bounds__(256) void k_pcombine(DevCtx c, int idx, const int* 
             out[(int64_t)t * H8 + ch] = combine_chunk<KK>(yv, wk, sq, c.has_shared, c.rsf);
         }
     }
+}
+
+// Expert-parallel segments: each pair's row comes back from the window of
+// the FFN rank that owns its expert (the one whose pack gave the pair a
+// row); the weights are the same in every window (same routing code), the
+// shared row comes from the window with the shared expert.  The sum runs
+// over k in order with the arithmetic of k_combine, so the result does not
+// depend on how the experts are split.
+struct RankView {
+    const int* st;    // the window's status words of this unpack
+    const int* ppos;  // its rows of the message's pairs (-1: another rank's)
+    const float* pwt;
+    const u32x4* rx;  // its returned routed rows
+    const u32x4* sx;  // its returned shared rows
+};
+struct RankViews {
+    RankView r[kMaxRanks];
+    int n, shared;  // windows; the one with the shared expert (-1: none)
+};
+
+template <int KK>
+__global__ __launch_bounds__(256) void k_rcombine(RankViews v, int64_t pb, u32x4* out, int n, int H8, float rsf) {
+#pragma unroll
+    for (int i = 0; i < kMaxRanks; ++i)
+        if (i < v.n && *v.r[i].st != AFD_OK) return;
+    const bool shared = v.shared >= 0;
+    const u32x4* sx = nullptr;
+#pragma unroll
+    for (int i = 0; i < kMaxRanks; ++i)
+        if (i == v.shared) sx = v.r[i].sx;
+    for (int t = blockIdx.x; t < n; t += gridDim.x) {
+        const u32x4* row[KK];
+        float wk[KK];
+#pragma unroll
+        for (int k = 0; k < KK; ++k) {
+            const int64_t f = pb + (int64_t)t * KK + k;
+            row[k] = nullptr;
+            wk[k] = v.r[0].pwt[f];
+#pragma unroll
+            for (int i = 0; i < kMaxRanks; ++i)
+                if (i < v.n) {
+                    const int pos = v.r[i].ppos[f];
+                    if (pos >= 0 && pos < n * KK) row[k] = v.r[i].rx + (int64_t)pos * H8;
+                }
+        }
+        for (int ch = threadIdx.x; ch < H8; ch += blockDim.x) {
+            u32x4 yv[KK];
+#pragma unroll
+            for (int k = 0; k < KK; ++k) yv[k] = row[k] ? row[k][ch] : (u32x4)0u;
+            const u32x4 sq = shared ? sx[(int64_t)t * H8 + ch] : (u32x4)0u;
+            out[(int64_t)t * H8 + ch] = combine_chunk<KK>(yv, wk, sq, shared, rsf);
+        }
+    }
+}
+
+hipError_t launch_unpack_ranks(const DevCtx* const* ctx, int n, int peer, int stage, int seq_len, const int* echo,
+                               void* out, const long long* timeout_ticks, hipStream_t st) {
+    if (n < 1 || n > kMaxRanks) return hipErrorInvalidValue;
+    RankViews v{};
+    v.n = n;
+    v.shared = -1;
+    for (int i = 0; i < n; ++i) {
+        const DevCtx& c = *ctx[i];
+        k_unpack_wait<<<1, 64, 0, st>>>(c, peer, stage, echo[i], seq_len, timeout_ticks[i]);
+        const int idx = peer * c.R + stage;
+        const char* slot = c.ret_win + c.slots_off + (int64_t)idx * c.slot_bytes;
+        v.r[i].st = c.peer_status + idx * kStatusWords;
+        v.r[i].ppos = c.ppos;
+        v.r[i].pwt = c.pwt;
+        v.r[i].rx = (const u32x4*)(slot + c.foff[AFD_FIELD_ROUTED_X]);
+        v.r[i].sx = (const u32x4*)(slot + c.foff[AFD_FIELD_SHARED_X]);
+        if (c.has_shared) v.shared = i;
+    }
+    const DevCtx& c = *ctx[0];
+    const int64_t pb = (int64_t)(peer * c.R + stage) * c.token_cap * c.K;
+    int grid = seq_len < 2048 ? seq_len : 2048;
+    if (grid < 1) grid = 1;
+    switch (c.K) {
+#define AFD_RCOMBINE_CASE(k) \
+    case k: k_rcombine<k><<<grid, 256, 0, st>>>(v, pb, (u32x4*)out, seq_len, c.H / 8, c.rsf); break;
+        AFD_RCOMBINE_CASE(1) AFD_RCOMBINE_CASE(2) AFD_RCOMBINE_CASE(3) AFD_RCOMBINE_CASE(4)
+        AFD_RCOMBINE_CASE(5) AFD_RCOMBINE_CASE(6) AFD_RCOMBINE_CASE(7) AFD_RCOMBINE_CASE(8)
+        AFD_RCOMBINE_CASE(9) AFD_RCOMBINE_CASE(10) AFD_RCOMBINE_CASE(11) AFD_RCOMBINE_CASE(12)
+        AFD_RCOMBINE_CASE(13) AFD_RCOMBINE_CASE(14) AFD_RCOMBINE_CASE(15) AFD_RCOMBINE_CASE(16)
+#undef AFD_RCOMBINE_CASE
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
 }
 
 hipError_t launch_unpack(const DevCtx& c, int peer, int stage, int seq_len, int expect_echo, void* out,
@@ -533,7 +635,7 @@ __global__ __launch_bounds__(64) void k_wait(DevCtx c, int s, int layer, long lo
             if (err == AFD_OK) {
                 hl = h.layer_idx;
                 err = inbound_check(h, p, s, layer < 0 ? hl : layer, c.token_cap, f, c.has_shared,
-                                    c.attn_routes ? c.K : 1);
+                                    c.attn_routes ? c.K : 1, c.Eg != c.E);
             }
             s_rt[p] = err == AFD_OK ? h.routed_tokens : -1;  // group list to check below
             if (err == AFD_OK) {
@@ -1052,6 +1154,7 @@ __global__ __launch_bounds__(256) void k_gscan(DevCtx c, const int* status, int 
                 c.peer_counts[b * E + e0 + j] = v[j];
                 run += v[j];
             }
+        if (tid == 255) c.prow[b] = run;  // the peer's routed rows
         return;
     }
     const int e = (b - P) * 256 + tid;
@@ -1103,7 +1206,7 @@ __global__ __launch_bounds__(256) void k_gdispatch(DevCtx c, int* status, int s)
         plan_publish(c, T, s_eoff, s_t, s_c);
     }
     plan_fill(c, T, s_eoff, s_t);
-    const int n = min(T * K, s_eoff[E]);  // (equal: k_wait checked every group list)
+    const int n = min(T * K, s_eoff[E]);  // (k_wait checked that every group list covers its rows)
     const int capK = c.token_cap * K;
     const int stride = (int)gridDim.x * 256;
     for (int pos = (int)blockIdx.x * 256 + tid; pos < n; pos += stride) {
@@ -1916,7 +2019,7 @@ __global__ __launch_bounds__(256) void k_retcopy(DevCtx c, const int* status, in
     const int T = *c.Tptr;
     if (st != AFD_OK) return;
     const int H8 = c.H / 8, capK = c.token_cap * c.K;
-    const int nr = T * c.K, rows = nr + (c.has_shared ? T : 0);
+    const int nr = min(T * c.K, c.eoff[c.E]), rows = nr + (c.has_shared ? T : 0);
     for (int row = blockIdx.x; row < rows; row += gridDim.x) {
         const u32x4* src;
         u32x4* dst;
@@ -1957,7 +2060,7 @@ __global__ __launch_bounds__(64) void k_publish(DevCtx c, const int* status, int
         f.layer_idx = layer < 0 ? *c.layer_cur : layer;
         f.stage_idx = s;
         f.num_tokens = n_p;
-        f.routed_tokens = n_p * (c.attn_routes ? c.K : 1);
+        f.routed_tokens = c.attn_routes ? c.prow[p] : n_p;
         f.shared_tokens = c.has_shared ? n_p : 0;
         f.src_peer = p;
         f.n_counts = c.E;

@@ -95,12 +95,15 @@ AFD_HD int32_t header_decode(const int32_t* w, int32_t expect_counts, afd_header
 // shared: the window carries shared rows (every token has one); routed-only
 // messages carry none (shared_tokens 0).  kmul: routed rows per token (1
 // when the FFN routes, top_k when the attention side sends its routed rows).
+// segmented: the window owns part of the experts, so a message carries only
+// the pairs of those (at most num_tokens * kmul rows).
 AFD_HD int32_t inbound_check(const afd_header_fields& f, int32_t peer, int32_t stage, int32_t layer,
-                             int32_t token_cap, int32_t flag_seq, bool shared, int32_t kmul) {
+                             int32_t token_cap, int32_t flag_seq, bool shared, int32_t kmul, bool segmented) {
     if (f.src_peer != peer || f.stage_idx != stage || f.layer_idx != layer) return AFD_ERR_HEADER;
     if (f.num_tokens < 0 || f.num_tokens > token_cap) return AFD_ERR_HEADER;
-    if (f.routed_tokens != f.num_tokens * kmul || f.shared_tokens != (shared ? f.num_tokens : 0))
-        return AFD_ERR_HEADER;
+    const bool routed_ok = segmented ? f.routed_tokens >= 0 && f.routed_tokens <= f.num_tokens * kmul
+                                     : f.routed_tokens == f.num_tokens * kmul;
+    if (!routed_ok || f.shared_tokens != (shared ? f.num_tokens : 0)) return AFD_ERR_HEADER;
     if (f.seq != flag_seq) return AFD_ERR_HEADER;
     return AFD_OK;
 }

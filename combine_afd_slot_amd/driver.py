@@ -30,7 +30,8 @@ class FfnSession:
         self.cfg = afd.make_config(wl.num_peers, wl.token_cap, wl.hidden, wl.num_experts, wl.top_k,
                                    wl.intermediate, wl.shared_intermediate, ring_depth=wl.ring_depth,
                                    routed_scaling_factor=wl.routed_scaling_factor, renormalize=wl.renormalize,
-                                   poll_timeout_us=poll_timeout_us, attention_routes=wl.attention_routes)
+                                   poll_timeout_us=poll_timeout_us, attention_routes=wl.attention_routes,
+                                   route_experts=wl.route_experts, expert_offset=wl.expert_offset)
         self.win = afd.afd_window_create(self.cfg)
         self.layout = afd.afd_window_layout(self.win)
         self.peer_streams = [torch.cuda.Stream(device=self.dev) for _ in range(wl.num_peers)]

@@ -60,6 +60,8 @@ class Workload:
     seed: int = 0
     ring_depth: int = 1
     attention_routes: int = 0       # 1: the attention side routes (grouped routed rows, sender combines)
+    route_experts: int = 0          # experts the peers route over when the window owns a segment (0: all)
+    expert_offset: int = 0          # first expert of the window's segment
     notes: str = field(default="", compare=False)
 
     @property

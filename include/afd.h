@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define AFD_ABI_VERSION 5
+#define AFD_ABI_VERSION 6
 
 /* Header flags bit 1: shutdown sentinel ("Window and slot layout"). */
 #define AFD_FLAG_SHUTDOWN 0x2u
@@ -114,7 +114,26 @@ typedef struct afd_window afd_window; /* opaque, library-owned */
  * fields 0 bytes), nothing is copied into them, and headers carry
  * shared_tokens = 0 (the attention side adds its own shared branch to the
  * returned routed output); renormalize 0 or 1;
- * poll_timeout_us >= 1. */
+ * poll_timeout_us >= 1.
+ *
+ * attention_routes = 1: the attention side routes ("[RFC]: Async GPU
+ * Connector", "Data flow"): afd_slot_pack takes the router logits, selects
+ * and weighs the top_k experts with the same code as the FFN side, sorts the
+ * message's (token, expert) pairs stably and writes the routed rows grouped
+ * by expert, the group list (rows per expert) in the header's counts; no
+ * logits travel (route_table 0 bytes, routed_x token_cap*top_k rows).  The
+ * FFN runs send the expert outputs back in the order they came and
+ * afd_slot_unpack combines them with the weights the pack kept.
+ * Expert-parallel segmentation (same section; "Capacity and ring depth":
+ * expert_per_rank): with route_experts > 0 the peers route over
+ * route_experts experts and this window is the FFN rank that owns experts
+ * [expert_offset, expert_offset + num_experts); a pack sends it only the
+ * pairs of those experts (routed_tokens = their number, at most
+ * num_tokens*top_k) and the outputs are combined over all ranks' windows
+ * by afd_slot_unpack_ranks.  route_experts 0 means num_experts (one rank).
+ * Limits: route_experts > 0 needs attention_routes = 1, top_k <=
+ * route_experts <= 1024, 0 <= expert_offset, expert_offset + num_experts
+ * <= route_experts; with route_experts 0, expert_offset must be 0. */
 typedef struct afd_window_config {
     uint32_t struct_size;
     int32_t num_peers;           /* P: attention peers fanned in by this FFN replica        */
@@ -129,8 +148,10 @@ typedef struct afd_window_config {
     int32_t renormalize;         /* 1: top-k weights renormalised to sum to 1                */
     int32_t poll_timeout_us;     /* bound of every device-side flag wait                     */
     int32_t attention_routes;    /* 0: the FFN routes (logits travel); 1: the attention side
-                                    routes and sends rows grouped by expert (see below)      */
-    int32_t reserved[3];         /* must be 0                                                */
+                                    routes and sends rows grouped by expert (see above)      */
+    int32_t route_experts;       /* experts the peers route over (0: num_experts)            */
+    int32_t expert_offset;       /* first of the num_experts experts this window owns        */
+    int32_t reserved[1];         /* must be 0                                                */
 } afd_window_config;
 
 /* Byte layout of the library's single device allocation.  The inbound
@@ -317,11 +338,35 @@ int32_t afd_ffn_loop_destroy(afd_ffn_loop* loop);
  * flag of (peer, stage), check its header (echo_seq must be the seq this
  * peer sent, num_tokens must equal seq_len), and copy the output rows
  * [seq_len][H] bf16 to `out` (device).  seq_len == 0: returns without waiting
- * (an empty message creates no wait; "Data flow").
+ * (an empty message creates no wait; "Data flow").  Attention-routed
+ * window: out[t] = rsf * sum over k, in k order, of w[t,k] * (returned row of
+ * pair (t, k)) + the returned shared row, in fp32, rounded to bf16 (the FFN
+ * side's combine).
  * Errors: AFD_ERR_SHAPE (seq_len differs from the packed length),
- * AFD_ERR_INVALID; device-side ones via afd_peer_status. */
+ * AFD_ERR_INVALID (also: a window that owns only part of the routed
+ * experts, which afd_slot_unpack_ranks combines); device-side ones via
+ * afd_peer_status. */
 int32_t afd_slot_unpack(afd_window* w, int32_t peer, int32_t stage, int32_t seq_len, void* out,
                         void* peer_stream);
+
+/* Attention side, expert-parallel segmentation ("[RFC]: Async GPU
+ * Connector", "Data flow": the sender's combine takes every FFN rank's
+ * returned rows): wins[0..n_wins) are the windows of all FFN ranks, whose
+ * expert ranges [expert_offset, expert_offset + num_experts) must partition
+ * [0, route_experts); at most one of them has a shared expert.  Waits for
+ * the return of (peer, stage) in every window (bounded, on the device),
+ * checks each header as afd_slot_unpack does, then writes
+ * out[t] = rsf * sum over k, in k order, of w[t,k] * (the row of pair (t, k)
+ * returned by the rank that owns its expert) + the shared row, in fp32,
+ * rounded to bf16.  Every window must have the peer's message of seq_len
+ * tokens in flight; the windows must agree on num_peers, ring_depth,
+ * token_cap, hidden, top_k, route_experts, renormalize and
+ * routed_scaling_factor.  1 <= n_wins <= 16.  Each window's afd_peer_status
+ * reports its own wait; `out` is written only if every wait succeeded.
+ * Errors: AFD_ERR_INVALID (arguments, windows that do not fit together),
+ * AFD_ERR_SHAPE (seq_len differs from a window's packed length). */
+int32_t afd_slot_unpack_ranks(afd_window* const* wins, int32_t n_wins, int32_t peer, int32_t stage,
+                              int32_t seq_len, void* out, void* peer_stream);
 
 /* Synchronize `stream` and read the status word of the last afd_ffn_run of
  * `stage`.  Off the hot path. */

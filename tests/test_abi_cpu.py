@@ -28,7 +28,7 @@ def test_library_exports_every_declared_symbol():
     missing = [s for s in declared if not hasattr(L, s)]
     assert not missing, missing
     assert sorted(afd.EXPORTS) == declared
-    assert afd.afd_abi_version() == 5
+    assert afd.afd_abi_version() == 6
 
 
 CFGS = [
@@ -109,18 +109,29 @@ def test_slot_fields_disjoint_aligned_viewable(kw):
     dict(ring_depth=5), dict(token_cap=0), dict(hidden=60), dict(num_experts=0), dict(top_k=0),
     dict(top_k=9), dict(intermediate=12), dict(shared_intermediate=-8), dict(renormalize=2),
     dict(poll_timeout_us=0), dict(attention_routes=2), dict(attention_routes=-1),
+    dict(route_experts=16), dict(expert_offset=1),
+    dict(attention_routes=1, route_experts=1025), dict(attention_routes=1, route_experts=12, expert_offset=5),
+    dict(attention_routes=1, route_experts=12, expert_offset=-1),
 ])
+
 def test_config_rejected(bad):
     kw = dict(CFGS[0])
     cfg = afd.make_config(**kw)
     for k, v in bad.items():
         if k == "reserved":
-            cfg.reserved[2] = v
+            cfg.reserved[0] = v
         else:
             setattr(cfg, k, v)
     with pytest.raises(afd.AfdError) as ei:
         afd.afd_layout_compute(cfg)
     assert ei.value.code == afd.AFD_ERR_INVALID
+
+def test_segment_config_accepted():
+    # a window owning experts [8, 16) of 32 routed over; top_k may exceed its own experts
+    cfg = afd.make_config(**dict(CFGS[0], top_k=10, attention_routes=1, route_experts=32, expert_offset=8))
+    L = afd.afd_layout_compute(cfg)
+    r = ref.window_layout(2, 1, 16, 64, 8, shared=True, top_k=10)
+    assert L.slot_bytes == r["slot_bytes"] and L.field_bytes[2] == r["field_bytes"]["routed_x"]
 
 
 def test_header_codec_round_trip_against_reference():

@@ -189,3 +189,90 @@ def test_any_ready_subset():
                 if wl.seq_lens[p]:
                     assert s.peer_status(p).status == 0
                 np.testing.assert_array_equal(s.outputs_f32()[p], base[p])
+
+
+def _segment_sessions(wl, inp, F, shared_rank):
+    """F windows on one GPU standing for F FFN ranks: rank r owns experts
+    [r*E/F, (r+1)*E/F) (its weights are that slice) and rank shared_rank the
+    shared expert; the peers route over all E experts."""
+    E = wl.num_experts
+    El = E // F
+    out = []
+    for r in range(F):
+        rwl = dataclasses.replace(wl, attention_routes=1, num_experts=El, route_experts=E, expert_offset=r * El,
+                                  shared_intermediate=wl.shared_intermediate if r == shared_rank else 0)
+        rinp = dict(inp, W13=inp["W13"][r * El:(r + 1) * El], W2=inp["W2"][r * El:(r + 1) * El])
+        if r != shared_rank:
+            rinp["Ws13"] = rinp["Ws2"] = None
+        out.append(FfnSession(rwl, rinp, poll_timeout_us=200_000))
+    return out
+
+
+@pytest.mark.parametrize("F,shared_rank", [(2, 0), (4, 3)])
+def test_expert_segments(orc, F, shared_rank):
+    """Expert-parallel segmentation ("[RFC]: Async GPU Connector", "Data
+    flow"; "Capacity and ring depth": expert_per_rank): each rank's window
+    gets only the pairs of its experts, grouped, with its group list; the
+    sender's combine over all ranks equals the single-rank result bit for
+    bit."""
+    wl = WLS[0]
+    E, K, H = wl.num_experts, wl.top_k, wl.hidden
+    El = E // F
+    inp = make_inputs(wl)
+    base = _ffn_routed_outputs(wl, inp)
+    sess = _segment_sessions(wl, inp, F, shared_rank)
+    torch = sess[0].torch
+    try:
+        say(f"[segments] F={F}: pack")
+        for s in sess:
+            s.pack_all()
+        for p, n in enumerate(wl.seq_lens):
+            if n == 0:
+                continue
+            ids, _ = orc.route(inp["l"][p], K, wl.renormalize)
+            for r, s in enumerate(sess):
+                # the oracle's stable dispatch with other ranks' experts in one last group
+                loc = ids - r * El
+                mapped = np.where((loc >= 0) & (loc < El), loc, El).astype(np.int32)
+                counts, _, perm, _ = orc.dispatch(mapped, El + 1)
+                nr = int(counts[:El].sum())
+                d = ref.decode_header(_header(s, s.layout.in_off, p)[0], El)
+                np.testing.assert_array_equal(d["counts"], counts[:El])
+                assert d["routed_tokens"] == nr and d["num_tokens"] == n
+                assert d["shared_tokens"] == (n if r == shared_rank else 0)
+                so = _slot_off(s, s.layout.in_off, p)
+                rx = _read(s, so + s.layout.field_off[2], nr * H, np.uint16).reshape(nr, H)
+                np.testing.assert_array_equal(rx, inp["x"][p][perm[:nr] // K])
+        say(f"[segments] F={F}: runs")
+        for s in sess:
+            s.run()
+            s.ffn_stream.synchronize()
+            st = s.status()
+            assert st.status == 0 and st.total_tokens == wl.total_tokens, st.status
+        wins = [s.win for s in sess]
+        # a rank missing, or the single-window unpack: rejected before any wait
+        with pytest.raises(afd.AfdError) as ei:
+            afd.afd_slot_unpack_ranks(wins[1:], 0, 0, wl.seq_lens[0], sess[0].out[0].data_ptr(),
+                                      sess[0].peer_streams[0].cuda_stream)
+        assert ei.value.code == afd.AFD_ERR_INVALID
+        with pytest.raises(afd.AfdError) as ei:
+            sess[0].unpack(0)
+        assert ei.value.code == afd.AFD_ERR_INVALID
+        say(f"[segments] F={F}: combine over ranks")
+        out = [torch.empty((n, H), dtype=torch.bfloat16, device=sess[0].dev) for n in wl.seq_lens]
+        for p, n in enumerate(wl.seq_lens):
+            afd.afd_slot_unpack_ranks(wins, p, 0, n, out[p].data_ptr() if n else 0,
+                                      sess[0].peer_streams[p].cuda_stream)
+        for ps in sess[0].peer_streams:
+            ps.synchronize()
+        full = _oracle_out(orc, wl, inp)
+        for p, o in enumerate(out):
+            if wl.seq_lens[p]:
+                for s in sess:
+                    assert s.peer_status(p).status == 0
+            o = o.float().cpu().numpy()
+            np.testing.assert_array_equal(o, base[p])
+            assert row_rel_err(o, full[p]) <= ROW_REL_TOL, p
+    finally:
+        for s in sess:
+            s.close()
