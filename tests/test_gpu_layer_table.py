@@ -8,8 +8,11 @@ iteration count, device-side spinning on the ready flags, serialized buffer
 reuse).  Each layer has its own seeded weights; every run is checked against
 the oracle with the weights of the layer its headers name, and the replays
 of the captured loop bit for bit against eager layer-table runs of the same
-inputs.
+inputs.  The loop also runs on an attention-routed window, where every stage
+of the ring keeps its own routing state on the peer side.
 """
+import dataclasses
+
 import numpy as np
 import pytest
 
@@ -151,14 +154,15 @@ def _dev_inputs(s, inp):
     return x, lg, out
 
 
-def test_captured_loop_replays(orc):
+@pytest.mark.parametrize("attention_routes", [0, 1])
+def test_captured_loop_replays(orc, attention_routes):
     """Four runs on stages 1, 2, 3, 0 (ring depth 4) captured once and
     replayed three times, with eager runs and host synchronization between
     the replays.  Each replay's messages are packed and complete before it is
     launched, and unpacked after it, so no stream waits on the device for
     work queued on another (a waiting kernel may hold a hardware queue that
     other streams share); the stages are reused across replays."""
-    wl = LOOP_WL
+    wl = dataclasses.replace(LOOP_WL, attention_routes=attention_routes)
     ws = _layer_weights(wl, N_LAYERS)
     layers = (1, 0, 2, 1)
     n_runs, R, first = len(layers), wl.ring_depth, 1
