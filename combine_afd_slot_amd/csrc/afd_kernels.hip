@@ -200,8 +200,8 @@ __global__ void k_pack_publish(char* slot, int* flag, afd_header_fields f, const
 // the FFN side (route_token); chunk histograms.  k_pscan: one workgroup per
 // expert scans its column of chunk histograms.  k_pscatter: the row of pair
 // f = t*K + k among the grouped rows is goff[e] + (pairs of e in earlier
-// chunks) + (earlier tokens of the chunk that chose e), and token t's hidden
-// row is copied there, once per k.  A window that owns experts [e0, e0+E)
+// chunks) + (earlier tokens of the chunk that chose e); k_pcopy then copies
+// token t's hidden row there, once per k.  A window that owns experts [e0, e0+E)
 // of the Eg the peers route over keeps only the pairs of those (expert ids
 // local, e - e0); the other pairs keep their weight with id -1 and no row.
 // ---------------------------------------------------------------------------
@@ -264,7 +264,6 @@ __global__ __launch_bounds__(256) void k_pscatter(DevCtx c, int idx, char* slot,
     __shared__ int sh[16];
     __shared__ int s_goff[kMaxExperts];
     __shared__ uint32_t emask[kMaxExperts];
-    __shared__ int s_pos[kRouteChunk * kMaxTopK];
     const int E = c.E, K = c.K, tid = threadIdx.x;
     const int b = blockIdx.x, t0 = b * kRouteChunk, nt = min(kRouteChunk, n - t0), np = nt * K;
     const int64_t pbase = (int64_t)idx * c.token_cap * K;
@@ -294,14 +293,21 @@ __global__ __launch_bounds__(256) void k_pscatter(DevCtx c, int idx, char* slot,
                               : s_goff[e] + c.pbase[((int64_t)idx * E + e) * c.NBp + b] +
                                     __popc(emask[e] & ((1u << tl) - 1u));
         c.ppos[pbase + (int64_t)t0 * K + tid] = pos;
-        s_pos[tid] = pos;
     }
-    __syncthreads();
-    const int H8 = c.H / 8;
+}
+
+// The grouped rows: pair f's token row to row ppos[f] (one workgroup per
+// pair at a time, a grid wide enough to keep every CU's loads in flight).
+__global__ __launch_bounds__(256) void k_pcopy(DevCtx c, int idx, char* slot, const uint4* hidden, int n) {
+    const int K = c.K, H8 = c.H / 8, np = n * K;
+    const int* ppos = c.ppos + (int64_t)idx * c.token_cap * K;
     uint4* rx = (uint4*)(slot + c.foff[AFD_FIELD_ROUTED_X]);
-    for (int i = tid; i < np * H8; i += 256) {
-        const int j = i / H8, ch = i - j * H8;
-        if (s_pos[j] >= 0) rx[(int64_t)s_pos[j] * H8 + ch] = hidden[(int64_t)(t0 + j / K) * H8 + ch];
+    for (int f = blockIdx.x; f < np; f += gridDim.x) {
+        const int pos = ppos[f];
+        if (pos < 0) continue;  // (a pair of another window's experts)
+        const uint4* src = hidden + (int64_t)(f / K) * H8;
+        uint4* dst = rx + (int64_t)pos * H8;
+        for (int ch = threadIdx.x; ch < H8; ch += blockDim.x) dst[ch] = src[ch];
     }
 }
 
@@ -329,6 +335,8 @@ hipError_t launch_pack(const DevCtx& c, int peer, int stage, int layer, int seq_
             else k_proute<16><<<nb, 64 * kRouteChunk, 0, st>>>(c, idx, logits, seq_len);
             k_pscan<<<c.E, 256, 0, st>>>(c, idx, nb);
             k_pscatter<<<nb, 256, 0, st>>>(c, idx, slot, (const uint4*)hidden, seq_len);
+            const int np = seq_len * c.K;
+            k_pcopy<<<np < 4096 ? np : 4096, 256, 0, st>>>(c, idx, slot, (const uint4*)hidden, seq_len);
         }
     }
     afd_header_fields f;
