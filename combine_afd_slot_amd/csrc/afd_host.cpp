@@ -93,7 +93,7 @@ int32_t validate(const afd_window_config* c) {
 struct WsLayout {
     int64_t ctrl, peer_counts, blk_counts, blk_base, counts, eoff, tstart1, tstart2;
     int64_t tinfo1, tinfo2, seg1, seg2, tctr, psrc, max_tiles1, max_tiles2;
-    int64_t ids, wts, perm, inv, tok_src, sh_src, h, hs, y, ys, wtable, pid, pwt, ppos, pblk, pbase, pcnt, retmap, bytes;
+    int64_t ids, wts, perm, inv, tok_src, sh_src, h, hs, y, ys, wtable, pid, pwt, ppos, pblk, pbase, pcnt, retoff, retoffs, bytes;
     int64_t ctrl_ints;
     // control-word offsets inside ctrl (in ints)
     int64_t c_seen_in, c_ret_seq, c_seen_ret, c_cur_seq, c_off, c_T, c_done, c_run_status, c_peer_status;
@@ -176,7 +176,8 @@ WsLayout ws_layout(const afd_window_config& c) {
         w.pblk = take(ar * 4 * msgs * E * nbp);
         w.pbase = take(ar * 4 * msgs * E * nbp);
         w.pcnt = take(ar * 4 * msgs * E);
-        w.retmap = take(ar * 4 * np);
+        w.retoff = take(ar * 4 * np);
+        w.retoffs = take(ar * 4 * tmax);
     }
     w.bytes = cur;
     return w;
@@ -314,7 +315,10 @@ void fill_ctx(afd_window* w) {
     d.pblk = (int*)(ws + L.pblk);
     d.pbase = (int*)(ws + L.pbase);
     d.pcnt = (int*)(ws + L.pcnt);
-    d.retmap = (int*)(ws + L.retmap);
+    d.retoff = (uint32_t*)(ws + L.retoff);
+    d.retoffs = (uint32_t*)(ws + L.retoffs);
+    d.ret_bytes = (uint32_t)w->lay.window_bytes;  // (below 4 GiB: checked by validate)
+    d.direct_ret = c.attention_routes && w->lay.window_bytes < ((int64_t)1 << 30);
     d.wtable = (const afd::Weights*)(ws + L.wtable);
     d.peer_status = ctrl + L.c_peer_status;
     d.peer_counts = (int*)(ws + L.peer_counts);

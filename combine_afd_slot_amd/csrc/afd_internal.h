@@ -86,7 +86,10 @@ struct DevCtx {
     int* pblk;         // [P*R][E][NBp] chunk histograms of the message's pairs
     int* pbase;        // [P*R][E][NBp] pairs of the expert in earlier chunks
     int* pcnt;         // [P*R][E] the message's group list (pairs per expert)
-    int* retmap;       // [Tmax*K] peer * token_cap*K + row in the peer's slot, of each grouped row
+    uint32_t* retoff;  // [Tmax*K] return-window byte offset of each grouped row's return row
+    uint32_t* retoffs; // [Tmax]   return-window byte offset of each shared row's return row
+    int direct_ret;    // the down GEMM stores straight into the return slots (window < 1 GiB)
+    uint32_t ret_bytes;  // bytes of the return window
     int* nlayers;      // [1]   entries of the layer table (0: none set)
     const Weights* wtable;  // [kMaxLayers] packed weights of each layer (layer-table runs)
     int* peer_status;  // [P*R][kStatusWords]

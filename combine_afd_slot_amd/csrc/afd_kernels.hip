@@ -1215,7 +1215,6 @@ __global__ __launch_bounds__(256) void k_gdispatch(DevCtx c, int* status, int s)
     }
     plan_fill(c, T, s_eoff, s_t);
     const int n = min(T * K, s_eoff[E]);  // (k_wait checked that every group list covers its rows)
-    const int capK = c.token_cap * K;
     const int stride = (int)gridDim.x * 256;
     for (int pos = (int)blockIdx.x * 256 + tid; pos < n; pos += stride) {
         int lo = 0, hi = E;  // s_eoff[lo] <= pos < s_eoff[hi]
@@ -1232,8 +1231,10 @@ __global__ __launch_bounds__(256) void k_gdispatch(DevCtx c, int* status, int s)
             else ph = mid;
         }
         const int local = c.blk_counts[pl * E + lo] + q - c.blk_base[pl * E + lo];
-        c.psrc[pos] = (uint64_t)(slot_ptr(c, c.in_win, pl, s) + c.foff[AFD_FIELD_ROUTED_X] + (int64_t)local * c.H * 2);
-        c.retmap[pos] = pl * capK + local;
+        const int64_t so = c.slots_off + (int64_t)(pl * c.R + s) * c.slot_bytes + c.foff[AFD_FIELD_ROUTED_X] +
+                           (int64_t)local * c.H * 2;  // (same layout in both windows)
+        c.psrc[pos] = (uint64_t)(c.in_win + so);
+        c.retoff[pos] = (uint32_t)so;
     }
     if (c.has_shared) {
         bool bad = false;
@@ -1241,6 +1242,7 @@ __global__ __launch_bounds__(256) void k_gdispatch(DevCtx c, int* status, int s)
             const int p = peer_of(c, t), r = t - c.off[p];
             const char* slot = slot_ptr(c, c.in_win, p, s);
             c.sh_src[t] = (uint64_t)(slot + c.foff[AFD_FIELD_SHARED_X] + (int64_t)r * c.H * 2);
+            c.retoffs[t] = (uint32_t)(slot - c.in_win + c.foff[AFD_FIELD_SHARED_X] + (int64_t)r * c.H * 2);
             bad |= ((const int*)(slot + c.foff[AFD_FIELD_SHARED_IDX]))[r] != r;
         }
         if (bad) atomicCAS(status, AFD_OK, AFD_ERR_HEADER);
@@ -1314,6 +1316,13 @@ constexpr int kBlockBytes = 32 * kRowBytes;             // 2 KB per 32-row block
 constexpr int kXStageBytes = kBX * kRowBytes;           // 16 KB of token rows
 constexpr int kStageBytes = (kBX + kBW) * kRowBytes;    // 32 KB
 constexpr int kGemmWaves = kGemmThreads / 64;           // 4
+// Down GEMM of an attention-routed run storing straight into the return
+// slots: two tables (the current tile's and the next one's) of the tile's
+// 256 row offsets sit in LDS past the ring and the tile-index slot; rows past
+// the tile get an offset past any such window (those windows are < 1 GiB).
+constexpr int kRetTabOff = kStages * kStageBytes + 64;
+constexpr int kSmemBytes = kRetTabOff + 2 * kBX * 4;
+constexpr uint32_t kRetPast = 0x40000000u;
 constexpr int kXInstr = kBX / kRowsPerLoad / kGemmWaves;  // 4 token-row loads per wave and step
 constexpr int kWInstr = kBW / kRowsPerLoad / kGemmWaves;  // 4 weight-row loads per wave and step
 static_assert(kGemmWaves == 4 && kTileBlocks == 8 && kBK == 32 && kStages == 4,
@@ -1395,6 +1404,8 @@ struct GemmTile {
     int r0;                // first token row of the tile (h / y / ys row; fan-in token for shared rows)
     int rows, Ig, nt;      // valid token rows, the group's intermediate width, column tile
     bool sh;
+    int par;               // which of the two return-offset tables is this tile's (down GEMM)
+    uint32_t rofs;         // down GEMM storing into the return slots: this thread's row's offset
 };
 
 
@@ -1698,6 +1709,12 @@ __device__ __forceinline__ void gemm_setup(const DevCtx& c, const Weights& w, in
                         : w.w2 + ((int64_t)e * c.nt2 + t.nt) * t.nk * kWTileBytes;
     t.wlane = (uint32_t)wid * 1024u + (uint32_t)(threadIdx.x & 63) * 16u;
     t.cx = lcx;
+    if (MODE == 2 && c.direct_ret) {
+        // row threadIdx.x of the tile: its return-window offset, or past the
+        // window's end (the store's range check drops it)
+        const int r = threadIdx.x;
+        t.rofs = r < t.rows ? (t.sh ? c.retoffs : c.retoff)[t.r0 + r] : kRetPast;
+    }
 #pragma unroll
     for (int i = 0; i < kXInstr; ++i) {
         const int r = (wid + kGemmWaves * i) * kRowsPerLoad + lrow;
@@ -1784,7 +1801,8 @@ __device__ __forceinline__ float agpr(float x) {
 // between the last MFMA and the first accumulator read.
 template <int MODE, int NV>
 __device__ __forceinline__ void gemm_epilogue_ib(const f32x16 (&acc)[NV > 0 ? NV : 1][4], const DevCtx& c,
-                                                 const GemmTile& t, int lane, int ww, int wx, int ib) {
+                                                 const GemmTile& t, const char* smem, int lane, int ww, int wx,
+                                                 int ib) {
     const int lj = lane & 31;
     const uint32_t rb = (uint32_t)((wx + 2 * ib) * 32 + 4 * (lane >> 5));  // this lane's first row of the block
     if (MODE == 1) {
@@ -1815,20 +1833,39 @@ __device__ __forceinline__ void gemm_epilogue_ib(const f32x16 (&acc)[NV > 0 ? NV
         }
     } else {
         // bf16 rows: routed rows into y (permuted order), shared rows into ys
-        // (token order); one code path for both, so the accumulators never
-        // have to live across a branch
+        // (token order), or -- attention-routed runs -- each row straight to
+        // its return row (offsets from the tile's LDS table, the buffer over
+        // the whole return window); one store loop for all, so the
+        // accumulators never have to live across a branch
         const uint32_t ldb = (uint32_t)c.H * 2;
-        const __amdgpu_buffer_rsrc_t rs = out_rsrc((t.sh ? c.ys : c.y) + (int64_t)t.r0 * c.H, t.rows * ldb);
+        const bool direct = c.direct_ret;
+        const char* ob = direct ? c.ret_win : (const char*)((t.sh ? c.ys : c.y) + (int64_t)t.r0 * c.H);
+        const __amdgpu_buffer_rsrc_t rs = out_rsrc(ob, direct ? c.ret_bytes : t.rows * ldb);
+        uint32_t ro[4][4];  // byte offsets of this lane's rows rb + 8q + i
+        if (direct) {
+            const u32x4* tab = (const u32x4*)(smem + kRetTabOff + t.par * (kBX * 4));
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const u32x4 o = tab[(rb >> 2) + 2 * q];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) ro[q][i] = o[i];
+            }
+        } else {
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) ro[q][i] = (rb + 8 * q + i) * ldb;
+        }
 #pragma unroll
         for (int jb = 0; jb < 4; ++jb) {
             const int col = t.nt * kBW + (ww * 4 + jb) * 32 + lj;
-            const uint32_t cb = (col < c.H ? 0u : 0x80000000u) + (uint32_t)col * 2 + rb * ldb;
+            const uint32_t cb = (col < c.H ? 0u : 0x80000000u) + (uint32_t)col * 2;
 #pragma unroll
             for (int v = 0; v < 16; v += 2) {
                 const uint32_t pk = pk_bf16(agpr(acc[ib][jb][v]), agpr(acc[ib][jb][v + 1]));
-                const uint32_t r = (uint32_t)(8 * (v >> 2) + (v & 3));
-                __builtin_amdgcn_raw_buffer_store_b16((uint16_t)pk, rs, (int)(cb + r * ldb), 0, 0);
-                __builtin_amdgcn_raw_buffer_store_b16((uint16_t)(pk >> 16), rs, (int)(cb + (r + 1) * ldb), 0, 0);
+                const int q = v >> 2, i = v & 3;
+                __builtin_amdgcn_raw_buffer_store_b16((uint16_t)pk, rs, (int)(cb + ro[q][i]), 0, 0);
+                __builtin_amdgcn_raw_buffer_store_b16((uint16_t)(pk >> 16), rs, (int)(cb + ro[q][i + 1]), 0, 0);
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
@@ -1865,6 +1902,7 @@ __device__ __forceinline__ void gemm_run(const DevCtx& c, const Weights& w, Gemm
     for (; kt < t.nk; ++kt) gemm_step<MODE, NV, NX, true>(acc, t, smem, kt, wid, lane, wl, tl, fa, fb);
 
     gemm_boundary<MODE>(c, w, sc, smem, tid, wid, lrow, lcx, next, tn);
+    tn.par = t.par ^ 1;
 
     // Epilogue, token block by token block, with the next tile's first
     // steps issued in between: the global-to-LDS traffic of those loads
@@ -1874,7 +1912,10 @@ __device__ __forceinline__ void gemm_run(const DevCtx& c, const Weights& w, Gemm
 #pragma unroll
     for (int ib = 0; ib < (NV > kStages - 1 ? NV : kStages - 1); ++ib) {
         if (ib < kStages - 1 && next >= 0) gemm_prologue_step<MODE>(tn, smem, wid, ib);
-        if (ib < NV) gemm_epilogue_ib<MODE, NV>(acc, c, t, lane, ww, wx, ib);
+        // the next tile's return offsets into its table (its load was issued at set-up)
+        if (MODE == 2 && ib == 0 && next >= 0 && c.direct_ret)
+            ((uint32_t*)(smem + kRetTabOff + tn.par * (kBX * 4)))[threadIdx.x] = tn.rofs;
+        if (ib < NV) gemm_epilogue_ib<MODE, NV>(acc, c, t, smem, lane, ww, wx, ib);
     }
 }
 
@@ -1887,7 +1928,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(DevCtx c, const int* s
     // (With a second __shared__ variable the compiler attaches alias scopes
     // to LDS accesses and then makes every LDS read wait for the direct-to-
     // LDS loads in flight; with one array it does not.)
-    __shared__ __attribute__((aligned(1024))) char smem[kStages * kStageBytes + 64];
+    __shared__ __attribute__((aligned(1024))) char smem[kSmemBytes];
     int* slot = (int*)(smem + kStages * kStageBytes);
     GemmSched sc;
     sc.seg = MODE == 1 ? c.seg1 : c.seg2;
@@ -1927,6 +1968,8 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(DevCtx c, const int* s
     if (tile >= 0) {
         gemm_setup<MODE>(c, w, tile, wid, lrow, lcx, t);
         gemm_prologue<MODE>(t, smem, wid);
+        t.par = 0;
+        if (MODE == 2 && c.direct_ret) ((uint32_t*)(smem + kRetTabOff))[threadIdx.x] = t.rofs;
     }
     while (tile >= 0) {
         int next;
@@ -2019,27 +2062,21 @@ __global__ __launch_bounds__(256) void k_combine(DevCtx c, const int* status, in
 
 // Attention-routed runs: no combine on the FFN side ("[RFC]: Async GPU
 // Connector", "Data flow", step 4: the expert outputs go back in the order
-// they came, the sender combines).  GEMM row pos goes to row retmap[pos] of
-// its peer's return routed_x, shared row t to row t - off[p] of its peer's
-// return shared_x.  One workgroup per row.
+// they came, the sender combines).  GEMM row pos goes to return-window byte
+// offset retoff[pos] (its row in its peer's return routed_x), shared row t to
+// retoffs[t].  One workgroup per row.  Used when the down GEMM cannot store
+// there itself (a return window of 1 GiB or more).
 __global__ __launch_bounds__(256) void k_retcopy(DevCtx c, const int* status, int s) {
     const int st = *status;
     const int T = *c.Tptr;
     if (st != AFD_OK) return;
-    const int H8 = c.H / 8, capK = c.token_cap * c.K;
+    const int H8 = c.H / 8;
     const int nr = min(T * c.K, c.eoff[c.E]), rows = nr + (c.has_shared ? T : 0);
     for (int row = blockIdx.x; row < rows; row += gridDim.x) {
-        const u32x4* src;
-        u32x4* dst;
-        if (row < nr) {
-            const int m = c.retmap[row], p = m / capK, r = m - p * capK;
-            src = (const u32x4*)(c.y + (int64_t)row * c.H);
-            dst = (u32x4*)(slot_ptr(c, c.ret_win, p, s) + c.foff[AFD_FIELD_ROUTED_X] + (int64_t)r * c.H * 2);
-        } else {
-            const int t = row - nr, p = peer_of(c, t), r = t - c.off[p];
-            src = (const u32x4*)(c.ys + (int64_t)t * c.H);
-            dst = (u32x4*)(slot_ptr(c, c.ret_win, p, s) + c.foff[AFD_FIELD_SHARED_X] + (int64_t)r * c.H * 2);
-        }
+        const bool routed = row < nr;
+        const int m = routed ? row : row - nr;
+        const u32x4* src = (const u32x4*)((routed ? c.y : c.ys) + (int64_t)m * c.H);
+        u32x4* dst = (u32x4*)(c.ret_win + (routed ? c.retoff : c.retoffs)[m]);
         for (int ch = threadIdx.x; ch < H8; ch += blockDim.x) __builtin_nontemporal_store(src[ch], &dst[ch]);
     }
 }
@@ -2121,7 +2158,8 @@ hipError_t launch_ffn(const DevCtx& c, int stage, int layer, const Weights& w, l
     int cgrid = Tmax < num_cu * 8 ? Tmax : num_cu * 8;
     if (cgrid < 1) cgrid = 1;
     if (c.attn_routes) {
-        k_retcopy<<<num_cu * 8, 256, 0, st>>>(c, status, stage);
+        // (the down GEMM stored every row into the return slots itself unless the window is too large)
+        if (!c.direct_ret) k_retcopy<<<num_cu * 8, 256, 0, st>>>(c, status, stage);
         k_publish<<<c.P, 64, 0, st>>>(c, status, stage, layer);
         mark();
         return hipGetLastError();
