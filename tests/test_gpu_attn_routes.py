@@ -276,3 +276,22 @@ def test_expert_segments(orc, F, shared_rank):
     finally:
         for s in sess:
             s.close()
+
+
+def test_large_window_copies_the_returns(orc):
+    """A return window of 1 GiB or more: the down GEMM keeps its own output
+    rows and a copy kernel moves them into the return slots; the outputs are
+    the same bits as an FFN-routed window's."""
+    wl = small_workload("attn_large_window", seq_lens=(40, 17), hidden=4096, num_experts=16, top_k=8,
+                        intermediate=64, shared_intermediate=64, token_cap=8192)
+    inp = make_inputs(wl)
+    base = _ffn_routed_outputs(wl, inp)
+    with FfnSession(_attn(wl), inp, poll_timeout_us=200_000) as s:
+        assert s.layout.window_bytes >= 1 << 30
+        s.step()
+        assert s.status().status == 0
+        full = _oracle_out(orc, wl, inp)
+        for p, o in enumerate(s.outputs_f32()):
+            assert s.peer_status(p).status == 0
+            np.testing.assert_array_equal(o, base[p])
+            assert row_rel_err(o, full[p]) <= ROW_REL_TOL, p
