@@ -37,7 +37,7 @@ HDR_WORDS = 12
 EXPORTS = (
     "afd_layout_compute", "afd_window_create", "afd_window_destroy", "afd_window_layout",
     "afd_slot_pack", "afd_weights_pack", "afd_ffn_run", "afd_ffn_run_ready", "afd_layer_table_set", "afd_ffn_run_table",
-    "afd_ffn_loop_create", "afd_ffn_loop_launch", "afd_ffn_loop_destroy",
+    "afd_ffn_loop_create", "afd_ffn_loop_launch", "afd_ffn_loop_destroy", "afd_ffn_serve", "afd_ffn_serve_result",
     "afd_slot_unpack", "afd_slot_unpack_ranks", "afd_window_status", "afd_peer_status",
     "afd_window_poll", "afd_debug_routing", "afd_debug_read", "afd_debug_write",
     "afd_profile_enable", "afd_profile_read", "afd_profile_kernel_name",
@@ -112,6 +112,8 @@ def lib():
             "afd_ffn_loop_create": [vp, i32, i32, vp, P(vp)],
             "afd_ffn_loop_launch": [vp, vp],
             "afd_ffn_loop_destroy": [vp],
+            "afd_ffn_serve": [vp, i32, i32, i32, i32, vp],
+            "afd_ffn_serve_result": [vp, vp, P(i32), P(i32), P(i32)],
             "afd_slot_unpack": [vp, i32, i32, i32, vp, vp],
             "afd_slot_unpack_ranks": [vp, i32, i32, i32, i32, vp, vp],
             "afd_window_status": [vp, i32, vp, P(RunInfo)],
@@ -235,6 +237,17 @@ def afd_ffn_loop_destroy(loop) -> int:
 
 def afd_slot_unpack(win, peer, stage, seq_len, out_ptr, stream=0) -> int:
     return _check(lib().afd_slot_unpack(win, peer, stage, seq_len, out_ptr or None, stream or None))
+
+
+def afd_ffn_serve(win, first_stage, n_items, max_peers=0, gather_us=0, stream=0) -> int:
+    return _check(lib().afd_ffn_serve(win, first_stage, n_items, max_peers, gather_us, stream or None))
+
+
+def afd_ffn_serve_result(win, stream=0):
+    """(stop status, items done, stop item) of the last afd_ffn_serve on `stream`."""
+    st, done, item = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+    _check(lib().afd_ffn_serve_result(win, stream or None, ctypes.byref(st), ctypes.byref(done), ctypes.byref(item)))
+    return st.value, done.value, item.value
 
 
 def afd_slot_unpack_ranks(wins, peer, stage, seq_len, out_ptr, stream=0) -> int:

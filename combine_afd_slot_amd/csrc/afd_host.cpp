@@ -97,7 +97,7 @@ struct WsLayout {
     int64_t ctrl_ints;
     // control-word offsets inside ctrl (in ints)
     int64_t c_seen_in, c_ret_seq, c_seen_ret, c_cur_seq, c_off, c_T, c_done, c_run_status, c_peer_status;
-    int64_t c_layer_cur, c_nlayers, c_rr, c_prow;
+    int64_t c_layer_cur, c_nlayers, c_rr, c_prow, c_serve;
 };
 
 WsLayout ws_layout(const afd_window_config& c) {
@@ -120,6 +120,7 @@ WsLayout ws_layout(const afd_window_config& c) {
     w.c_nlayers = ci; ci += 1;
     w.c_rr = ci; ci += R;
     w.c_prow = ci; ci += P;
+    w.c_serve = ci; ci += 3;
     w.ctrl_ints = ci;
     int64_t cur = 0;
     auto take = [&](int64_t bytes) {
@@ -305,6 +306,7 @@ void fill_ctx(afd_window* w) {
     d.nlayers = ctrl + L.c_nlayers;
     d.rr = ctrl + L.c_rr;
     d.prow = ctrl + L.c_prow;
+    d.serve = ctrl + L.c_serve;
     d.attn_routes = c.attention_routes;
     d.Eg = c.route_experts ? c.route_experts : c.num_experts;
     d.e0 = c.expert_offset;
@@ -660,6 +662,39 @@ int32_t afd_ffn_loop_launch(afd_ffn_loop* l, void* stream) {
     if (!l) return fail(AFD_ERR_INVALID, "loop is NULL");
     hipError_t e = hipGraphLaunch(l->exec, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "loop launch");
+    return AFD_OK;
+}
+
+int32_t afd_ffn_serve(afd_window* w, int32_t first_stage, int32_t n_items, int32_t max_peers, int32_t gather_us,
+                      void* stream) {
+    if (!w) return fail(AFD_ERR_INVALID, "window is NULL");
+    const afd_window_config& c = w->cfg;
+    if (first_stage < 0 || first_stage >= c.ring_depth)
+        return fail(AFD_ERR_INVALID, "first_stage %d out of range", first_stage);
+    if (n_items < 1) return fail(AFD_ERR_INVALID, "n_items %d < 1", n_items);
+    if (max_peers < 0 || max_peers > c.num_peers)
+        return fail(AFD_ERR_INVALID, "max_peers %d outside 0..%d", max_peers, c.num_peers);
+    if (gather_us < 0 || gather_us > c.poll_timeout_us)
+        return fail(AFD_ERR_INVALID, "gather_us %d outside 0..poll_timeout_us", gather_us);
+    if (w->n_layers < 1) return fail(AFD_ERR_INVALID, "no layer table set (afd_layer_table_set)");
+    hipError_t e = afd::launch_serve_begin(w->ctx, (hipStream_t)stream);
+    for (int i = 0; i < n_items && e == hipSuccess; ++i)
+        e = afd::launch_ffn(w->ctx, (first_stage + i) % c.ring_depth, -1, afd::Weights{}, poll_ticks(w), w->num_cu,
+                            nullptr, (hipStream_t)stream, max_peers, (long long)gather_us * w->ticks_per_us, i);
+    if (e != hipSuccess) return hip_fail(e, "serve launch");
+    return AFD_OK;
+}
+
+int32_t afd_ffn_serve_result(afd_window* w, void* stream, int32_t* status, int32_t* items_done, int32_t* stop_item) {
+    if (!w || !status || !items_done || !stop_item) return fail(AFD_ERR_INVALID, "NULL argument");
+    hipError_t e = hipStreamSynchronize((hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+    int32_t words[3];
+    e = hipMemcpy(words, w->ctx.serve, sizeof words, hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return hip_fail(e, "hipMemcpy");
+    *status = words[0];
+    *items_done = words[1];
+    *stop_item = words[2];
     return AFD_OK;
 }
 

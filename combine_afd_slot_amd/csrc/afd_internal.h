@@ -73,6 +73,7 @@ struct DevCtx {
     int* run_status;   // [R][kStatusWords]
     int* rr;           // [R]   first peer an any-ready run of the stage scans (rotates for fairness)
     int* prow;         // [P]   attention-routed runs: routed rows of each peer's message
+    int* serve;        // [3]   serve loop: stop status (0: running), items done, stop item
     int* layer_cur;    // [1]   layer of the current run (from the headers in layer-table runs)
     // attention-side routing (attn_routes): the routed rows arrive grouped by
     // expert, the peer keeps the top-k weights and combines on return
@@ -160,7 +161,11 @@ hipError_t launch_unpack(const DevCtx& c, int peer, int stage, int seq_len, int 
 // between the launches.  max_take = 0: the work item is every peer of the
 // stage; max_take > 0: at most max_take of the peers that are ready (an
 // any-ready run), after waiting gather_ticks past the first one for more.
+// serve_item >= 0: item serve_item of an afd_ffn_serve loop (skipped once
+// the loop has stopped; its outcome recorded in the serve words).
 hipError_t launch_ffn(const DevCtx& c, int stage, int layer, const Weights& w, long long timeout_ticks,
-                      int num_cu, hipEvent_t* ev, hipStream_t st, int max_take = 0, long long gather_ticks = 0);
+                      int num_cu, hipEvent_t* ev, hipStream_t st, int max_take = 0, long long gather_ticks = 0,
+                      int serve_item = -1);
+hipError_t launch_serve_begin(const DevCtx& c, hipStream_t st);
 
 }  // namespace afd

@@ -573,11 +573,28 @@ hipError_t launch_unpack(const DevCtx& c, int peer, int stage, int seq_len, int 
 // taken.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(64) void k_wait(DevCtx c, int s, int layer, long long timeout, int max_take,
-                                             long long gather) {
+                                             long long gather, int serve_item) {
     __shared__ int s_flag[kMaxPeers], s_err[kMaxPeers], s_ntok[kMaxPeers], s_shut[kMaxPeers], s_layer[kMaxPeers];
     __shared__ int s_rt[kMaxPeers], s_gneg[kMaxPeers];
     __shared__ unsigned long long s_gsum[kMaxPeers];
     const int p = threadIdx.x;
+    if (serve_item >= 0) {
+        const int stop = c.serve[0];
+        if (stop != AFD_OK) {
+            // an earlier item of this serve loop stopped it: consume nothing,
+            // and every later kernel of the run sees a non-OK status
+            if (p == 0) {
+                int* st = c.run_status + s * kStatusWords;
+                st[0] = stop;
+                st[1] = -1;
+                st[3] = 0;
+                st[4] = 0;
+                st[5] = 0;
+                *c.Tptr = 0;
+            }
+            return;
+        }
+    }
     int* st = c.run_status + s * kStatusWords;
     const bool in = p < c.P;
     const int idx = p * c.R + s;
@@ -2087,7 +2104,17 @@ __global__ __launch_bounds__(256) void k_retcopy(DevCtx c, const int* status, in
 // the inbound seq consumed, its per-expert pair counts, then a release store
 // of its return flag = the FFN side's next return seq.  An empty message gets
 // no reply and so creates no wait.
-__global__ __launch_bounds__(64) void k_publish(DevCtx c, const int* status, int s, int layer) {
+__global__ __launch_bounds__(64) void k_publish(DevCtx c, const int* status, int s, int layer, int serve_item) {
+    if (serve_item >= 0 && blockIdx.x == 0 && threadIdx.x == 0 && c.serve[0] == AFD_OK) {
+        // the item's outcome: one more done, or the stop of the loop
+        const int r = *status;
+        if (r == AFD_OK) {
+            c.serve[1] += 1;
+        } else {
+            c.serve[0] = r;
+            c.serve[2] = serve_item;
+        }
+    }
     if (*status != AFD_OK) return;
     const int p = blockIdx.x, lane = threadIdx.x;  // one wavefront per peer
     const int n_p = c.off[p + 1] - c.off[p];
@@ -2118,8 +2145,21 @@ __global__ __launch_bounds__(64) void k_publish(DevCtx c, const int* status, int
 // ---------------------------------------------------------------------------
 // layer < 0: a layer-table run (the layer from the headers, the weights from
 // the device table; `w` is unused).
+__global__ void k_serve_begin(DevCtx c) {
+    if (threadIdx.x == 0) {
+        c.serve[0] = AFD_OK;
+        c.serve[1] = 0;
+        c.serve[2] = -1;
+    }
+}
+
+hipError_t launch_serve_begin(const DevCtx& c, hipStream_t st) {
+    k_serve_begin<<<1, 64, 0, st>>>(c);
+    return hipGetLastError();
+}
+
 hipError_t launch_ffn(const DevCtx& c, int stage, int layer, const Weights& w, long long timeout_ticks, int num_cu,
-                      hipEvent_t* ev, hipStream_t st, int max_take, long long gather_ticks) {
+                      hipEvent_t* ev, hipStream_t st, int max_take, long long gather_ticks, int serve_item) {
     int* status = c.run_status + stage * kStatusWords;
     const int Tmax = c.P * c.token_cap;
     // ev == nullptr: no events; otherwise ev[i] is recorded before kernel
@@ -2131,7 +2171,7 @@ hipError_t launch_ffn(const DevCtx& c, int stage, int layer, const Weights& w, l
         ++slot;
     };
     mark();
-    k_wait<<<1, 64, 0, st>>>(c, stage, layer, timeout_ticks, max_take, gather_ticks);
+    k_wait<<<1, 64, 0, st>>>(c, stage, layer, timeout_ticks, max_take, gather_ticks, serve_item);
     mark();
     if (c.attn_routes) {
         // (the routing slots: the merge of the group lists, then the dispatch)
@@ -2160,7 +2200,7 @@ hipError_t launch_ffn(const DevCtx& c, int stage, int layer, const Weights& w, l
     if (c.attn_routes) {
         // (the down GEMM stored every row into the return slots itself unless the window is too large)
         if (!c.direct_ret) k_retcopy<<<num_cu * 8, 256, 0, st>>>(c, status, stage);
-        k_publish<<<c.P, 64, 0, st>>>(c, status, stage, layer);
+        k_publish<<<c.P, 64, 0, st>>>(c, status, stage, layer, serve_item);
         mark();
         return hipGetLastError();
     }
@@ -2174,7 +2214,7 @@ hipError_t launch_ffn(const DevCtx& c, int stage, int layer, const Weights& w, l
 #undef AFD_COMBINE_CASE
         default: return hipErrorInvalidValue;
     }
-    k_publish<<<c.P, 64, 0, st>>>(c, status, stage, layer);
+    k_publish<<<c.P, 64, 0, st>>>(c, status, stage, layer, serve_item);
     mark();
     return hipGetLastError();
 }

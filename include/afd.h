@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define AFD_ABI_VERSION 6
+#define AFD_ABI_VERSION 7
 
 /* Header flags bit 1: shutdown sentinel ("Window and slot layout"). */
 #define AFD_FLAG_SHUTDOWN 0x2u
@@ -333,6 +333,28 @@ int32_t afd_ffn_loop_create(afd_window* w, int32_t n_runs, int32_t first_stage, 
 int32_t afd_ffn_loop_launch(afd_ffn_loop* loop, void* stream);
 /* Frees the loop's graph; NULL is accepted. */
 int32_t afd_ffn_loop_destroy(afd_ffn_loop* loop);
+
+/* Connector-driven FFN loop ("[RFC]: Async AFD for Prefill on Ascend NPU",
+ * "Asynchronous work-item contract" and "FFN execution modes": the FFN side
+ * drains work items as they become ready, with bounded waits and a shutdown
+ * sentinel, and no host round trip per item).  Enqueues n_items layer-table
+ * runs on `stream` without any host synchronisation: item i on stage
+ * (first_stage + i) % ring_depth, every peer of the stage (max_peers 0) or,
+ * as afd_ffn_run_ready, at most max_peers ready peers after a gather window
+ * of gather_us.  The first item that ends in shutdown, a timeout or an error
+ * stops the loop on the device: the remaining items of the call consume
+ * nothing and publish nothing (their stage status reads the stop status).
+ * afd_ffn_serve_result synchronizes `stream` and reports the stop status
+ * (AFD_OK: every item ran), the items that ran to completion, and the item
+ * that stopped the loop (-1: none).  Peers may keep packing on their own
+ * streams while the loop runs (each item waits on the device for its
+ * stage's messages).  Errors: AFD_ERR_INVALID (NULL window, first_stage out
+ * of range, n_items < 1, max_peers outside 0..num_peers, gather_us outside
+ * 0..poll_timeout_us, no layer table), AFD_ERR_DEVICE. */
+int32_t afd_ffn_serve(afd_window* w, int32_t first_stage, int32_t n_items, int32_t max_peers, int32_t gather_us,
+                      void* stream);
+int32_t afd_ffn_serve_result(afd_window* w, void* stream, int32_t* status, int32_t* items_done,
+                             int32_t* stop_item);
 
 /* Attention side, peer `peer`: wait (bounded, on the device) for the return
  * flag of (peer, stage), check its header (echo_seq must be the seq this

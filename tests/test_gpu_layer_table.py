@@ -237,3 +237,70 @@ def test_loop_create_argument_errors():
         assert ei.value.code == afd.AFD_ERR_INVALID
         afd.afd_profile_enable(s.win, 0)
         afd.afd_ffn_loop_destroy(None)
+
+
+SERVE_WL = small_workload("serve", seq_lens=(21, 34), hidden=128, num_experts=8, top_k=2, intermediate=64,
+                          shared_intermediate=64, token_cap=40, ring_depth=2)
+
+
+def test_serve_loop(orc):
+    """The connector-driven loop (afd_ffn_serve): items run back to back with
+    no host synchronisation; the first timeout or shutdown stops the loop on
+    the device and the items after it consume nothing."""
+    wl = SERVE_WL
+    ws = _layer_weights(wl, 2)
+    with FfnSession(wl, make_inputs(wl), poll_timeout_us=20_000, weights=False) as s:
+        torch = s.torch
+        st_ = s.ffn_stream.cuda_stream
+        with pytest.raises(afd.AfdError) as ei:  # no layer table yet
+            afd.afd_ffn_serve(s.win, 0, 2, 0, 0, st_)
+        assert ei.value.code == afd.AFD_ERR_INVALID
+        packed, keep = _pack_layers(s, ws)
+        afd.afd_layer_table_set(s.win, [b.data_ptr() for b in packed], st_)
+        for args in ((0, 0, 0, 0), (2, 1, 0, 0), (0, 1, 3, 0), (0, 1, 1, 20_001)):
+            with pytest.raises(afd.AfdError) as ei:
+                afd.afd_ffn_serve(s.win, *args, st_)
+            assert ei.value.code == afd.AFD_ERR_INVALID, args
+
+        def pack(stage, layer, inp, peers=(0, 1), flags=0):
+            x, lg, out = _dev_inputs(s, inp)
+            torch.cuda.synchronize(s.dev)
+            for p in peers:
+                n = 0 if flags else wl.seq_lens[p]
+                afd.afd_slot_pack(s.win, p, stage, layer, n, x[p].data_ptr() if n else 0,
+                                  lg[p].data_ptr() if n else 0, flags, s.peer_streams[p].cuda_stream)
+            for ps in s.peer_streams:
+                ps.synchronize()
+            return out
+
+        def unpack(stage, out, peers=(0, 1)):
+            for p in peers:
+                afd.afd_slot_unpack(s.win, p, stage, wl.seq_lens[p], out[p].data_ptr(), s.peer_streams[p].cuda_stream)
+            for ps in s.peer_streams:
+                ps.synchronize()
+            return [o.float().cpu().numpy() for o in out]
+
+        # two items ready (stage 0 layer 1, stage 1 layer 0); the third times out, the fourth is skipped
+        inps = [make_inputs(wl.with_(seed=700 + i), with_weights=False) for i in range(3)]
+        outs = [pack(0, 1, inps[0]), pack(1, 0, inps[1])]
+        say("[serve] four items, two ready")
+        afd.afd_ffn_serve(s.win, 0, 4, 0, 0, st_)
+        assert afd.afd_ffn_serve_result(s.win, st_) == (afd.AFD_ERR_TIMEOUT, 2, 2)
+        for stage, layer, out, inp in ((0, 1, outs[0], inps[0]), (1, 0, outs[1], inps[1])):
+            got = unpack(stage, out)
+            ref = _oracle(orc, wl, inp, ws[layer])
+            for p in range(wl.num_peers):
+                assert row_rel_err(got[p], ref[p]) <= ROW_REL_TOL, (stage, p)
+        # every peer sends the shutdown sentinel on stage 0: the loop stops at its first item
+        pack(0, 0, inps[2], flags=afd.AFD_FLAG_SHUTDOWN)
+        say("[serve] shutdown")
+        afd.afd_ffn_serve(s.win, 0, 3, 0, 0, st_)
+        assert afd.afd_ffn_serve_result(s.win, st_) == (afd.AFD_SHUTDOWN, 0, 0)
+        # any-ready items: only peer 1 has a message on stage 1
+        out = pack(1, 1, inps[2], peers=(1,))
+        say("[serve] any-ready")
+        afd.afd_ffn_serve(s.win, 1, 2, 2, 0, st_)
+        assert afd.afd_ffn_serve_result(s.win, st_) == (afd.AFD_ERR_TIMEOUT, 1, 1)
+        got = unpack(1, out, peers=(1,))
+        ref = _oracle(orc, wl, inps[2], ws[1])
+        assert row_rel_err(got[1], ref[1]) <= ROW_REL_TOL
