@@ -11,6 +11,17 @@
  * with the router weights, and writes each peer's slice of the result into
  * that peer's return slot, publishing a return flag per peer.
  *
+ * Beyond that single run: a device table of every layer's weights with the
+ * layer taken from the headers (afd_layer_table_set, afd_ffn_run_table) and
+ * runs captured into a replayable graph (afd_ffn_loop_*); runs that serve
+ * whichever peers are ready (afd_ffn_run_ready) and a loop of runs stopped
+ * on the device by a timeout or shutdown (afd_ffn_serve); windows without a
+ * shared expert (routed-only protocol); and attention-routed windows, where
+ * the peers route, send their rows grouped by expert and combine the
+ * returned rows themselves, optionally with the experts split over several
+ * FFN ranks' windows (attention_routes, route_experts, expert_offset,
+ * afd_slot_unpack_ranks).
+ *
  * Sources (page titles; sections):
  *   "[RFC]: Async GPU Connector" (vllm-project/afd-plugin issue 233):
  *     "Window and slot layout", "Capacity and ring depth", "Data flow",
@@ -24,7 +35,8 @@
  *     contract" (write before ready; ready only when all participants
  *     published; layer and counts consumed on the device; completion) and
  *     "FFN execution modes" (fixed-shape buffers sized by the maximum
- *     reserved token count; device-side blocking receive).
+ *     reserved token count; device-side blocking receive; layer-select
+ *     operators and graph mode), "Architecture", "Shared-expert ownership".
  *
  * Conventions for every entry point:
  *   - Return value: an afd_status (0 = AFD_OK).  Errors that the host can see
