@@ -208,7 +208,7 @@ def _segment_sessions(wl, inp, F, shared_rank):
     return out
 
 
-@pytest.mark.parametrize("F,shared_rank", [(2, 0), (4, 3)])
+@pytest.mark.parametrize("F,shared_rank", [(2, 0), (4, 3), (6, 5)])
 def test_expert_segments(orc, F, shared_rank):
     """Expert-parallel segmentation ("[RFC]: Async GPU Connector", "Data
     flow"; "Capacity and ring depth": expert_per_rank): each rank's window
