@@ -4,8 +4,11 @@ Routing ids, per-expert counts and offsets, the dispatch permutation and its
 inverse, and the split offsets must match bit for bit; outputs within 2e-2
 per-row relative error.  Small workloads are checked on every output row;
 the full-size workloads on every routing artefact and on sampled output
-rows that the oracle computes one token at a time.
+rows that the oracle computes one token at a time; the full-size inputs also
+go through an attention-routed window, whose outputs must be the same bits.
 """
+import dataclasses
+
 import numpy as np
 import pytest
 
@@ -116,7 +119,9 @@ def test_full_size_sampled(orc, name):
                                        renorm=wl.renormalize)
     np.testing.assert_array_equal(ids_t, ids[tok])
     say(f"[parity-full] {name}: GPU run")
-    with FfnSession(wl, inp) as s:
+    # the same inputs through an attention-routed window too (the peers route
+    # and combine): its outputs must be the same bits
+    with FfnSession(wl, inp) as s, FfnSession(dataclasses.replace(wl, attention_routes=1), inp) as sa:
         del inp["W13"], inp["W2"]
         s.step()
         st = s.status()
@@ -129,3 +134,7 @@ def test_full_size_sampled(orc, name):
         # properties that hold on every row: finite, and the same scale as the sample
         assert np.isfinite(out).all()
         assert 0.25 < np.abs(out).mean() / np.abs(out_ref).mean() < 4.0
+        say(f"[parity-full] {name}: attention-routed run")
+        sa.step()
+        assert sa.status().status == 0
+        np.testing.assert_array_equal(np.concatenate(sa.outputs_f32()), out)
