@@ -295,3 +295,64 @@ def test_large_window_copies_the_returns(orc):
             assert s.peer_status(p).status == 0
             np.testing.assert_array_equal(o, base[p])
             assert row_rel_err(o, full[p]) <= ROW_REL_TOL, p
+
+
+def _random_workloads(n, seed=2024):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        P = int(rng.integers(1, 6))
+        cap = int(rng.integers(8, 72))
+        seq = tuple(int(v) for v in rng.integers(0, cap + 1, P))
+        if sum(seq) == 0:
+            seq = (cap,) + seq[1:]
+        E = int(rng.integers(2, 41))
+        K = int(rng.integers(1, min(E, 8) + 1))
+        out.append(small_workload(
+            f"random{i}", seq_lens=seq, hidden=int(rng.choice([64, 128, 192])), num_experts=E, top_k=K,
+            intermediate=int(rng.choice([32, 64, 96])), shared_intermediate=int(rng.choice([0, 64])),
+            token_cap=cap, renormalize=int(rng.integers(0, 2)),
+            routed_scaling_factor=float(rng.choice([1.0, 2.5])), seed=100 + i))
+    return out
+
+
+@pytest.mark.parametrize("wl", _random_workloads(8), ids=lambda w: w.name)
+def test_random_configurations(orc, wl):
+    """Seeded random small configurations (peers, lengths with empty peers,
+    experts, top_k, widths, shared expert or not, renormalisation, scaling):
+    attention-routed outputs equal FFN-routed ones bit for bit and the
+    oracle's within the row tolerance; where the expert count allows, the
+    same with the experts split over ranks."""
+    say(f"[random] {wl.name}: P={wl.num_peers} seq={wl.seq_lens} E={wl.num_experts} K={wl.top_k} "
+        f"H={wl.hidden} I={wl.intermediate} Is={wl.shared_intermediate} renorm={wl.renormalize}")
+    inp = make_inputs(wl)
+    base = _ffn_routed_outputs(wl, inp)
+    ref = orc.ffn(inp["x"], inp["l"], inp["W13"], inp["W2"], inp.get("Ws13"), inp.get("Ws2"), K=wl.top_k,
+                  rsf=wl.routed_scaling_factor, renorm=wl.renormalize)["out_p"]
+    for p, o in enumerate(base):
+        assert row_rel_err(o, ref[p]) <= ROW_REL_TOL, p
+    with FfnSession(_attn(wl), inp, poll_timeout_us=200_000) as s:
+        s.step()
+        assert s.status().status == 0
+        for p, o in enumerate(s.outputs_f32()):
+            np.testing.assert_array_equal(o, base[p])
+    F = next((f for f in (3, 2) if wl.num_experts % f == 0), 0)
+    if F:
+        sess = _segment_sessions(wl, inp, F, shared_rank=F - 1)
+        try:
+            for s in sess:
+                s.pack_all()
+            for s in sess:
+                s.run()
+                s.ffn_stream.synchronize()
+                assert s.status().status == 0
+            torch = sess[0].torch
+            wins = [s.win for s in sess]
+            for p, n in enumerate(wl.seq_lens):
+                o = torch.empty((n, wl.hidden), dtype=torch.bfloat16, device=sess[0].dev)
+                afd.afd_slot_unpack_ranks(wins, p, 0, n, o.data_ptr() if n else 0, sess[0].peer_streams[p].cuda_stream)
+                sess[0].peer_streams[p].synchronize()
+                np.testing.assert_array_equal(o.float().cpu().numpy(), base[p])
+        finally:
+            for s in sess:
+                s.close()
