@@ -243,11 +243,12 @@ SERVE_WL = small_workload("serve", seq_lens=(21, 34), hidden=128, num_experts=8,
                           shared_intermediate=64, token_cap=40, ring_depth=2)
 
 
-def test_serve_loop(orc):
+@pytest.mark.parametrize("attention_routes", [0, 1])
+def test_serve_loop(orc, attention_routes):
     """The connector-driven loop (afd_ffn_serve): items run back to back with
     no host synchronisation; the first timeout or shutdown stops the loop on
     the device and the items after it consume nothing."""
-    wl = SERVE_WL
+    wl = dataclasses.replace(SERVE_WL, attention_routes=attention_routes)
     ws = _layer_weights(wl, 2)
     with FfnSession(wl, make_inputs(wl), poll_timeout_us=20_000, weights=False) as s:
         torch = s.torch
