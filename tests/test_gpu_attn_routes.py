@@ -356,3 +356,47 @@ def test_random_configurations(orc, wl):
         finally:
             for s in sess:
                 s.close()
+
+
+LIMIT_WLS = [
+    # 64 peers (the most a window takes), ragged and empty messages
+    small_workload("limit_peers", seq_lens=tuple(int(v) for v in np.random.default_rng(7).integers(0, 9, 64)),
+                   hidden=64, num_experts=16, top_k=4, intermediate=32, shared_intermediate=32, token_cap=8),
+    # 1024 experts and top_k 16 (the most routing takes), no shared expert
+    small_workload("limit_experts", seq_lens=(40, 23), hidden=64, num_experts=1024, top_k=16, intermediate=32,
+                   shared_intermediate=0, token_cap=48),
+]
+
+
+@pytest.mark.parametrize("wl", LIMIT_WLS, ids=lambda w: w.name)
+def test_limits(orc, wl):
+    """The configuration limits: every output row against the oracle; the
+    attention-routed window and expert segments give the same bits."""
+    inp = make_inputs(wl)
+    base = _ffn_routed_outputs(wl, inp)
+    ref = _oracle_out(orc, wl, inp)
+    for p, o in enumerate(base):
+        assert row_rel_err(o, ref[p]) <= ROW_REL_TOL, p
+    with FfnSession(_attn(wl), inp, poll_timeout_us=200_000) as s:
+        s.step()
+        assert s.status().status == 0
+        for p, o in enumerate(s.outputs_f32()):
+            np.testing.assert_array_equal(o, base[p])
+    sess = _segment_sessions(wl, inp, 4, shared_rank=0)
+    try:
+        for s in sess:
+            s.pack_all()
+        for s in sess:
+            s.run()
+            s.ffn_stream.synchronize()
+            assert s.status().status == 0
+        torch = sess[0].torch
+        wins = [s.win for s in sess]
+        for p, n in enumerate(wl.seq_lens):
+            o = torch.empty((n, wl.hidden), dtype=torch.bfloat16, device=sess[0].dev)
+            afd.afd_slot_unpack_ranks(wins, p, 0, n, o.data_ptr() if n else 0, sess[0].peer_streams[p].cuda_stream)
+            sess[0].peer_streams[p].synchronize()
+            np.testing.assert_array_equal(o.float().cpu().numpy(), base[p])
+    finally:
+        for s in sess:
+            s.close()
