@@ -22,6 +22,8 @@
  *              (total_tokens is the sum of seq_lens), Step 3 (fan-in: peers
  *              concatenated along tokens in subgroup order), Step 4 (split
  *              back by the recorded seq_lens).
+ *   [NPU-RFC]  "[RFC]: Async AFD for Prefill on Ascend NPU", "Architecture"
+ *              (the routed W1 + SwiGLU grouped GEMM, quantised).
  *   [P2P-UG]   "NCCL_P2P_CONNECTOR_USER_GUIDE.md", Configuration
  *              (compute_gate_on_attention=true: router logits travel to the
  *              FFN, which runs the expert path).
@@ -441,6 +443,157 @@ int oracle_token_rows(int64_t T, int64_t H, int E, int K, int64_t I, int64_t Is,
                 for (int64_t c = 0; c < H; ++c) o[c] = rsf * o[c];
                 if (Is > 0) {
                     swiglu_row(H, Is, X + t * H, Ws13, Ws2, act, y);
+                    for (int64_t c = 0; c < H; ++c) o[c] += y[c];
+                }
+            }
+        }
+        free(act);
+        free(y);
+    }
+    return bad ? ORC_ERR_ARG : ORC_OK;
+}
+
+/* ---------------------------------------------------------------------------
+ * FP8 for the quantised W1 (gate/up) GEMM ([NPU-RFC] "[RFC]: Async AFD for
+ * Prefill on Ascend NPU", "Architecture": the routed W1 + SwiGLU grouped
+ * GEMM with quantisation).  The pages name no format; the reading taken is
+ * OCP FP8 E4M3 ("E4M3FN": 1 sign, 4 exponent bits with bias 7, 3 mantissa
+ * bits, subnormals, largest finite 448, no infinities), round to nearest even
+ * with saturation to +-448, one scale per row: a token's hidden row (dynamic)
+ * and a W13 row (one output channel).
+ *
+ * e4m3 code of an fp32 value, from the format's definition.  Zero results
+ * carry no sign.
+ * ------------------------------------------------------------------------- */
+uint8_t oracle_e4m3_encode(float v) {
+    union { float f; uint32_t u; } b;
+    b.f = v;
+    const uint32_t sign = b.u >> 31, a = b.u & 0x7FFFFFFFu;
+    uint32_t code;
+    if (a >= 0x43E00000u) {               /* |v| >= 448 (and inf): saturate */
+        code = 0x7E;
+    } else if (a < 0x00800000u) {         /* fp32 zero or subnormal: below 2^-126 */
+        code = 0;
+    } else {
+        const int e = (int)(a >> 23) - 127;   /* |v| = 1.m * 2^e */
+        const uint32_t M = (a & 0x7FFFFFu) | 0x800000u;  /* 24-bit significand */
+        if (e >= -6) {                    /* normal e4m3: keep 3 fraction bits */
+            uint32_t q = M >> 20;         /* 1.xxx as 8..15 */
+            const uint32_t rem = M & 0xFFFFFu, half = 0x80000u;
+            if (rem > half || (rem == half && (q & 1u))) ++q;
+            int E = e + 7;
+            if (q == 16) { q = 8; ++E; }
+            code = (E > 15 || (E == 15 && (q & 7u) == 7u)) ? 0x7Eu : ((uint32_t)E << 3) | (q & 7u);
+        } else {                          /* subnormal e4m3: multiples of 2^-9 */
+            const int s = 14 - e;         /* M * 2^(e-23) / 2^-9 = M >> s */
+            if (s >= 32) {
+                code = 0;
+            } else {
+                uint32_t q = M >> s;
+                const uint32_t rem = M & ((1u << s) - 1u), half = 1u << (s - 1);
+                if (rem > half || (rem == half && (q & 1u))) ++q;
+                code = q;                 /* q == 8 is the smallest normal, code 0x08 */
+            }
+        }
+    }
+    return (uint8_t)(code == 0 ? 0 : (sign << 7) | code);
+}
+
+/* Value of an e4m3 code (0x7F / 0xFF, NaN, are never produced). */
+double oracle_e4m3_decode(uint8_t c) {
+    const int E = (c >> 3) & 15, q = c & 7;
+    const double m = E == 0 ? ldexp((double)q, -9) : ldexp(1.0 + q / 8.0, E - 7);
+    return (c & 0x80) ? -m : m;
+}
+
+/* Quantise n rows of H bf16 values, one scale per row: amax = max |x|;
+ * r = 448 / amax (fp32, correctly rounded); code = e4m3(x * r) with the
+ * product in fp32; the row's dequantisation scale is d = amax / 448 (fp32)
+ * and x is taken as decode(code) * d (deq, in double).  A zero row has d = 1
+ * and zero codes.  codes: [n][H]; d: [n]; deq: [n][H] (either may be NULL). */
+int oracle_quant_rows(int64_t n, int64_t H, const uint16_t* x, uint8_t* codes, float* d, double* deq) {
+    if (n < 0 || H < 1 || !x) return ORC_ERR_ARG;
+    for (int64_t i = 0; i < n; ++i) {
+        const uint16_t* row = x + i * H;
+        float amax = 0.0f;
+        for (int64_t h = 0; h < H; ++h) {
+            const float v = fabsf((float)bf16_to_double(row[h]));
+            if (v > amax) amax = v;
+        }
+        const float r = amax > 0.0f ? 448.0f / amax : 0.0f;
+        const float di = amax > 0.0f ? amax / 448.0f : 1.0f;
+        if (d) d[i] = di;
+        for (int64_t h = 0; h < H; ++h) {
+            const float v = (float)bf16_to_double(row[h]) * r;
+            const uint8_t c = oracle_e4m3_encode(v);
+            if (codes) codes[i * H + h] = c;
+            if (deq) deq[i * H + h] = oracle_e4m3_decode(c) * (double)di;
+        }
+    }
+    return ORC_OK;
+}
+
+/* One SwiGLU row on operands given in double (the dequantised fp8 token row
+ * and gate/up rows); W2 stays bf16.  The same formula as swiglu_row. */
+static void swiglu_row_d(int64_t H, int64_t I, const double* x, const double* w13, const uint16_t* w2,
+                         double* act, double* y) {
+    for (int64_t j = 0; j < I; ++j) {
+        const double* wg = w13 + j * H;
+        const double* wu = w13 + (I + j) * H;
+        double g = 0.0, u = 0.0;
+        for (int64_t h = 0; h < H; ++h) {
+            g += x[h] * wg[h];
+            u += x[h] * wu[h];
+        }
+        act[j] = (g / (1.0 + exp(-g))) * u;
+    }
+    for (int64_t c = 0; c < H; ++c) {
+        const uint16_t* wr = w2 + c * I;
+        double s = 0.0;
+        for (int64_t j = 0; j < I; ++j) s += act[j] * bf16_to_double(wr[j]);
+        y[c] = s;
+    }
+}
+
+/* oracle_token_rows with the gate/up operands in double: Xd [T][H] and the
+ * dequantised W13d [E][2I][H], Ws13d [2Is][H] (the fp8 W1 path); routing
+ * and combine as there. */
+int oracle_token_rows_d(int64_t T, int64_t H, int E, int K, int64_t I, int64_t Is, double rsf, int renorm,
+                        const double* Xd, const float* L, const double* W13d, const uint16_t* W2,
+                        const double* Ws13d, const uint16_t* Ws2, int64_t n, const int64_t* tok, double* out,
+                        int32_t* ids, double* w) {
+    if (T < 0 || H < 1 || E < 1 || K < 1 || K > E || I < 1 || n < 0) return ORC_ERR_ARG;
+    for (int64_t q = 0; q < n; ++q)
+        if (tok[q] < 0 || tok[q] >= T) return ORC_ERR_ARG;
+    int bad = 0;
+#pragma omp parallel
+    {
+        int64_t amax = I > Is ? I : Is;
+        double* act = (double*)malloc(sizeof(double) * (size_t)amax);
+        double* y = (double*)malloc(sizeof(double) * (size_t)H);
+        if (!act || !y) {
+#pragma omp atomic write
+            bad = 1;
+        } else {
+#pragma omp for schedule(dynamic, 1)
+            for (int64_t q = 0; q < n; ++q) {
+                int64_t t = tok[q];
+                int rc = oracle_route(1, E, K, renorm, L + t * E, ids + q * K, w + q * K);
+                if (rc) {
+#pragma omp atomic write
+                    bad = 1;
+                    continue;
+                }
+                double* o = out + q * H;
+                for (int64_t c = 0; c < H; ++c) o[c] = 0.0;
+                for (int k = 0; k < K; ++k) {
+                    int e = ids[q * K + k];
+                    swiglu_row_d(H, I, Xd + t * H, W13d + (int64_t)e * 2 * I * H, W2 + (int64_t)e * H * I, act, y);
+                    for (int64_t c = 0; c < H; ++c) o[c] += w[q * K + k] * y[c];
+                }
+                for (int64_t c = 0; c < H; ++c) o[c] = rsf * o[c];
+                if (Is > 0) {
+                    swiglu_row_d(H, Is, Xd + t * H, Ws13d, Ws2, act, y);
                     for (int64_t c = 0; c < H; ++c) o[c] += y[c];
                 }
             }

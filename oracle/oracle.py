@@ -57,6 +57,13 @@ def lib():
                                  P, P, P, P, P, P, P, P, P, P, P, P]
         L.oracle_token_rows.argtypes = [i64, i64, i32, i32, i64, i64, dbl, i32, P, P, P, P, P, P,
                                         i64, P, P, P, P]
+        L.oracle_e4m3_encode.argtypes = [ctypes.c_float]
+        L.oracle_e4m3_encode.restype = ctypes.c_uint8
+        L.oracle_e4m3_decode.argtypes = [ctypes.c_uint8]
+        L.oracle_e4m3_decode.restype = dbl
+        L.oracle_quant_rows.argtypes = [i64, i64, P, P, P, P]
+        L.oracle_token_rows_d.argtypes = [i64, i64, i32, i32, i64, i64, dbl, i32, P, P, P, P, P, P,
+                                          i64, P, P, P, P]
         L.oracle_num_threads.restype = ctypes.c_int
         L.oracle_set_threads.argtypes = [i32]
         _lib = L
@@ -212,3 +219,63 @@ def timed_token_rows(X, L, tokens, W13, W2, Ws13=None, Ws2=None, K=2, rsf=1.0, r
     t0 = time.perf_counter()
     r = token_rows(X, L, tokens, W13, W2, Ws13, Ws2, K=K, rsf=rsf, renorm=renorm)
     return r, time.perf_counter() - t0
+
+
+# ---------------------------------------------------------------------------
+# fp8 (E4M3) W1 path: codec, per-row quantisation, the per-token path on
+# dequantised gate/up operands (afd_oracle.c, "FP8 for the quantised W1").
+def e4m3_encode(v):
+    v = np.asarray(v, dtype=np.float32)
+    return np.array([lib().oracle_e4m3_encode(float(a)) for a in v.ravel()], np.uint8).reshape(v.shape)
+
+
+def e4m3_decode(c):
+    c = np.asarray(c, dtype=np.uint8)
+    return np.array([lib().oracle_e4m3_decode(int(a)) for a in c.ravel()], np.float64).reshape(c.shape)
+
+
+def quant_rows(x):
+    """Rows of bf16 bit patterns -> (e4m3 codes, fp32 row scales d, dequantised float64 rows)."""
+    x = np.ascontiguousarray(x, dtype=np.uint16)
+    H = x.shape[-1]
+    flat = x.reshape(-1, H)
+    n = flat.shape[0]
+    codes = np.zeros((n, H), np.uint8)
+    d = np.zeros(n, np.float32)
+    deq = np.zeros((n, H), np.float64)
+    _check(lib().oracle_quant_rows(n, H, _p(flat), _p(codes), _p(d), _p(deq)), "quant_rows")
+    return codes.reshape(x.shape), d.reshape(x.shape[:-1]), deq.reshape(x.shape)
+
+
+def token_rows_d(Xd, L, tokens, W13d, W2, Ws13d=None, Ws2=None, K=2, rsf=1.0, renorm=1):
+    """oracle token_rows with double gate/up operands (the fp8 W1 path)."""
+    Xd = np.ascontiguousarray(Xd, dtype=np.float64)
+    L = np.ascontiguousarray(L, dtype=np.float32)
+    T, H = Xd.shape
+    E = W13d.shape[0]
+    I = W13d.shape[1] // 2
+    Is = 0 if Ws13d is None else Ws13d.shape[0] // 2
+    tok = np.ascontiguousarray(tokens, dtype=np.int64)
+    n = tok.shape[0]
+    out = np.zeros((n, H), np.float64)
+    ids = np.zeros((n, K), np.int32)
+    w = np.zeros((n, K), np.float64)
+    _check(lib().oracle_token_rows_d(T, H, E, K, I, Is, float(rsf), int(renorm), _p(Xd), _p(L),
+                                     _p(np.ascontiguousarray(W13d, np.float64)), _p(np.ascontiguousarray(W2)),
+                                     _p(None if Ws13d is None else np.ascontiguousarray(Ws13d, np.float64)),
+                                     _p(None if Ws2 is None else np.ascontiguousarray(Ws2)),
+                                     n, _p(tok), _p(out), _p(ids), _p(w)), "token_rows_d")
+    return out, ids, w
+
+
+def ffn_fp8(x, l, W13, W2, Ws13=None, Ws2=None, K=2, rsf=1.0, renorm=1):
+    """The whole path with the gate/up GEMMs on e4m3 operands (token rows and
+    W13 / Ws13 rows quantised per row), every token; per-peer outputs."""
+    X = np.concatenate([np.asarray(a, np.uint16).reshape(-1, W13.shape[2]) for a in x])
+    Lc = np.concatenate([np.asarray(a, np.float32).reshape(-1, W13.shape[0]) for a in l])
+    _, _, Xd = quant_rows(X)
+    _, _, W13d = quant_rows(W13)
+    Ws13d = None if Ws13 is None else quant_rows(Ws13)[2]
+    out, _, _ = token_rows_d(Xd, Lc, np.arange(X.shape[0]), W13d, W2, Ws13d, Ws2, K=K, rsf=rsf, renorm=renorm)
+    off = np.concatenate([[0], np.cumsum([np.asarray(a).shape[0] for a in x])])
+    return [out[off[p]:off[p + 1]] for p in range(len(x))]
