@@ -60,7 +60,7 @@ class WindowConfig(ctypes.Structure):
                 ("routed_scaling_factor", ctypes.c_float), ("renormalize", ctypes.c_int32),
                 ("poll_timeout_us", ctypes.c_int32), ("attention_routes", ctypes.c_int32),
                 ("route_experts", ctypes.c_int32), ("expert_offset", ctypes.c_int32),
-                ("reserved", ctypes.c_int32 * 1)]
+                ("w1_fp8", ctypes.c_int32), ("reserved", ctypes.c_int32 * 1)]
 
 
 class Layout(ctypes.Structure):
@@ -157,7 +157,7 @@ def _check(rc: int) -> int:
 
 def make_config(num_peers, token_cap, hidden, num_experts, top_k, intermediate, shared_intermediate,
                 ring_depth=1, routed_scaling_factor=1.0, renormalize=1, poll_timeout_us=2_000_000,
-                attention_routes=0, route_experts=0, expert_offset=0) -> WindowConfig:
+                attention_routes=0, route_experts=0, expert_offset=0, w1_fp8=0) -> WindowConfig:
     c = WindowConfig()
     c.struct_size = ctypes.sizeof(WindowConfig)
     c.num_peers, c.ring_depth, c.token_cap = num_peers, ring_depth, token_cap
@@ -166,6 +166,7 @@ def make_config(num_peers, token_cap, hidden, num_experts, top_k, intermediate, 
     c.routed_scaling_factor, c.renormalize, c.poll_timeout_us = routed_scaling_factor, renormalize, poll_timeout_us
     c.attention_routes = attention_routes
     c.route_experts, c.expert_offset = route_experts, expert_offset
+    c.w1_fp8 = w1_fp8
     return c
 
 

@@ -48,6 +48,11 @@ int32_t validate(const afd_window_config* c) {
         if (c->reserved[i] != 0) return fail(AFD_ERR_INVALID, "reserved[%d] must be 0", i);
     if (c->attention_routes != 0 && c->attention_routes != 1)
         return fail(AFD_ERR_INVALID, "attention_routes must be 0 or 1");
+    if (c->w1_fp8 != 0 && c->w1_fp8 != 1) return fail(AFD_ERR_INVALID, "w1_fp8 must be 0 or 1");
+    if (c->w1_fp8 && (c->attention_routes || c->hidden % 64))
+        return fail(AFD_ERR_INVALID, "w1_fp8 needs attention_routes = 0 and hidden a multiple of 64");
+    if (c->w1_fp8 && (int64_t)c->num_peers * c->token_cap * c->hidden >= ((int64_t)1 << 32))
+        return fail(AFD_ERR_INVALID, "w1_fp8: num_peers*token_cap*hidden must stay below 4 GiB");
     if (c->route_experts != 0) {
         if (!c->attention_routes) return fail(AFD_ERR_INVALID, "route_experts needs attention_routes = 1");
         if (c->route_experts > afd::kMaxExperts) return fail(AFD_ERR_INVALID, "route_experts above 1024");
@@ -93,7 +98,7 @@ int32_t validate(const afd_window_config* c) {
 struct WsLayout {
     int64_t ctrl, peer_counts, blk_counts, blk_base, counts, eoff, tstart1, tstart2;
     int64_t tinfo1, tinfo2, seg1, seg2, tctr, psrc, max_tiles1, max_tiles2;
-    int64_t ids, wts, perm, inv, tok_src, sh_src, h, hs, y, ys, wtable, pid, pwt, ppos, pblk, pbase, pcnt, retoff, retoffs, bytes;
+    int64_t ids, wts, perm, inv, tok_src, sh_src, h, hs, y, ys, wtable, pid, pwt, ppos, pblk, pbase, pcnt, retoff, retoffs, xq, sx, sxp, bytes;
     int64_t ctrl_ints;
     // control-word offsets inside ctrl (in ints)
     int64_t c_seen_in, c_ret_seq, c_seen_ret, c_cur_seq, c_off, c_T, c_done, c_run_status, c_peer_status;
@@ -180,6 +185,13 @@ WsLayout ws_layout(const afd_window_config& c) {
         w.retoff = take(ar * 4 * np);
         w.retoffs = take(ar * 4 * tmax);
     }
+    {
+        // fp8 W1: quantised token rows and their scales
+        const int64_t q = c.w1_fp8 ? 1 : 0;
+        w.xq = take(q * tmax * c.hidden);
+        w.sx = take(q * 4 * tmax);
+        w.sxp = take(q * 4 * np);
+    }
     w.bytes = cur;
     return w;
 }
@@ -207,7 +219,7 @@ void layout_from(const afd_window_config& c, afd_layout* L, WsLayout* wl) {
     L->workspace_off = L->ret_off + afd::align_up(L->window_bytes);
     L->workspace_bytes = w.bytes;
     L->total_bytes = L->workspace_off + w.bytes;
-    int64_t off[4];
+    int64_t off[6];
     afd::packed_weight_layout(c, off, &L->packed_weight_bytes);
     if (wl) *wl = w;
 }
@@ -215,9 +227,10 @@ void layout_from(const afd_window_config& c, afd_layout* L, WsLayout* wl) {
 }  // namespace
 
 namespace afd {
-void packed_weight_layout(const afd_window_config& c, int64_t off[4], int64_t* total) {
+void packed_weight_layout(const afd_window_config& c, int64_t off[6], int64_t* total) {
     const int64_t E = c.num_experts, H = c.hidden, I = c.intermediate, Is = c.shared_intermediate;
-    const int64_t nk1 = (H + kBK - 1) / kBK, nt2 = (H + kBW - 1) / kBW;
+    // (fp8 W1: a gate/up tile row holds 64 depth values of one byte)
+    const int64_t nk1 = c.w1_fp8 ? H / 64 : (H + kBK - 1) / kBK, nt2 = (H + kBW - 1) / kBW;
     const int64_t nt1 = (I + kBW / 2 - 1) / (kBW / 2), nk2 = (I + kBK - 1) / kBK;
     const int64_t nt1s = (Is + kBW / 2 - 1) / (kBW / 2), nk2s = (Is + kBK - 1) / kBK;
     int64_t cur = 0;
@@ -229,6 +242,10 @@ void packed_weight_layout(const afd_window_config& c, int64_t off[4], int64_t* t
     cur += E * nt2 * nk2 * kWTileBytes;
     off[3] = cur;  // ws2
     cur += nt2 * nk2s * kWTileBytes;
+    off[4] = cur;  // sw13 (fp8 W1 only)
+    cur += c.w1_fp8 ? align_up(4 * E * 2 * I) : 0;
+    off[5] = cur;  // sws13
+    cur += c.w1_fp8 ? align_up(4 * 2 * Is) : 0;
     *total = cur;
 }
 }  // namespace afd
@@ -309,6 +326,10 @@ void fill_ctx(afd_window* w) {
     d.serve = ctrl + L.c_serve;
     d.attn_routes = c.attention_routes;
     d.Eg = c.route_experts ? c.route_experts : c.num_experts;
+    d.w1_fp8 = c.w1_fp8;
+    d.xq = (uint8_t*)(ws + L.xq);
+    d.sx = (float*)(ws + L.sx);
+    d.sxp = (float*)(ws + L.sxp);
     d.e0 = c.expert_offset;
     d.NBp = (c.token_cap + afd::kRouteChunk - 1) / afd::kRouteChunk;
     d.pid = (int*)(ws + L.pid);
@@ -379,11 +400,13 @@ long long poll_ticks(const afd_window* w) { return (long long)w->cfg.poll_timeou
 
 // The four packed regions of one layer's weights (afd_weights_pack layout).
 afd::Weights packed_weights_of(const afd_window_config& c, const void* packed) {
-    int64_t off[4], total = 0;
+    int64_t off[6], total = 0;
     afd::packed_weight_layout(c, off, &total);
     const char* pw = (const char*)packed;
-    return afd::Weights{pw + off[0], pw + off[2], c.shared_intermediate > 0 ? pw + off[1] : nullptr,
-                        c.shared_intermediate > 0 ? pw + off[3] : nullptr};
+    const bool sh = c.shared_intermediate > 0;
+    return afd::Weights{pw + off[0], pw + off[2], sh ? pw + off[1] : nullptr, sh ? pw + off[3] : nullptr,
+                        c.w1_fp8 ? (const float*)(pw + off[4]) : nullptr,
+                        c.w1_fp8 && sh ? (const float*)(pw + off[5]) : nullptr};
 }
 
 }  // namespace
@@ -540,7 +563,7 @@ int32_t afd_weights_pack(afd_window* w, const afd_moe_weights* src, void* dst, i
         (c.shared_intermediate > 0 && (!aligned(src->ws13, 16) || !aligned(src->ws2, 16))))
         return fail(AFD_ERR_INVALID, "weights must be 16-byte aligned");
     if (!aligned(dst, 256)) return fail(AFD_ERR_INVALID, "packed weights must be 256-byte aligned");
-    int64_t off[4], total = 0;
+    int64_t off[6], total = 0;
     afd::packed_weight_layout(c, off, &total);
     if (dst_bytes < total)
         return fail(AFD_ERR_INVALID, "packed weights need %lld bytes, got %lld", (long long)total, (long long)dst_bytes);

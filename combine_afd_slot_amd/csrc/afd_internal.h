@@ -78,6 +78,10 @@ struct DevCtx {
     // attention-side routing (attn_routes): the routed rows arrive grouped by
     // expert, the peer keeps the top-k weights and combines on return
     int attn_routes;
+    int w1_fp8;        // gate/up GEMMs on e4m3 operands
+    uint8_t* xq;       // [Tmax][H] e4m3 codes of the token rows (fp8 W1)
+    float* sx;         // [Tmax]   their dequantisation scales
+    float* sxp;        // [Tmax*K] the scale of each permuted pair's token row
     int Eg;            // experts the peers route over (E unless the window owns a segment)
     int e0;            // first expert of the window's segment
     int NBp;           // routing chunks of one message: ceil(token_cap / kRouteChunk)
@@ -142,13 +146,16 @@ struct Weights {
     const char* w2;
     const char* ws13;
     const char* ws2;
+    const float* sw13;   // fp8 W1: dequantisation scale of each W13 row ([E][2I])
+    const float* sws13;  // and of each Ws13 row ([2Is])
 };
 
-// Byte offsets of the four packed regions and the total (host).
-void packed_weight_layout(const afd_window_config& c, int64_t off[4], int64_t* total);
+// Byte offsets of the packed regions (w13, ws13, w2, ws2, then the fp8 row
+// scales sw13, sws13) and the total (host).
+void packed_weight_layout(const afd_window_config& c, int64_t off[6], int64_t* total);
 
 // Launchers (afd_kernels.hip).  All return the launch's hipError_t.
-hipError_t launch_pack_weights(const DevCtx& c, const afd_moe_weights& src, char* dst, const int64_t off[4],
+hipError_t launch_pack_weights(const DevCtx& c, const afd_moe_weights& src, char* dst, const int64_t off[6],
                                int64_t total, hipStream_t st);
 hipError_t launch_pack(const DevCtx& c, int peer, int stage, int layer, int seq_len, const void* hidden,
                        const float* logits, uint32_t flags, int seq, hipStream_t st);

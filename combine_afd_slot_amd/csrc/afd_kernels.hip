@@ -43,6 +43,32 @@ __device__ inline uint32_t pk_bf16(float a, float b) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){a, b}, bf16x2_t));
 }
 
+// OCP FP8 E4M3 code of an fp32 value (bias 7, subnormals of 2^-9, largest
+// finite 448 = code 0x7E, no infinities): round to nearest even, saturate to
+// +-448; a zero result carries no sign.  Subnormal results: the value in
+// units of 2^-9, rounded; normal results: the value scaled by a power of two
+// to [8, 16), rounded, the exponent bumped when that reaches 16.
+__device__ inline uint32_t e4m3_code(float v) {
+    const float a = fabsf(v);
+    uint32_t c;
+    if (!(a < 448.0f)) {
+        c = 0x7Eu;
+    } else if (a < 0.015625f) {  // below 2^-6
+        c = (uint32_t)__builtin_rintf(a * 512.0f);  // 0 .. 8 (8: the smallest normal, code 0x08)
+    } else {
+        int e = (int)((__float_as_uint(a) >> 23) & 0xFF) - 127;        // a in [2^e, 2^(e+1))
+        float m = __builtin_rintf(a * __uint_as_float((uint32_t)(127 + 3 - e) << 23));  // 8 .. 16
+        if (m == 16.0f) {
+            m = 8.0f;
+            ++e;
+        }
+        const int E = e + 7;
+        c = E > 15 ? 0x7Eu : ((uint32_t)E << 3) | ((uint32_t)m - 8u);
+        if (c == 0x7Fu) c = 0x7Eu;
+    }
+    return c == 0u ? 0u : c | (v < 0.0f ? 0x80u : 0u);
+}
+
 __device__ inline char* slot_ptr(const DevCtx& c, char* win, int p, int s) {
     return win + c.slots_off + (int64_t)(p * c.R + s) * c.slot_bytes;
 }
@@ -846,6 +872,38 @@ __global__ __launch_bounds__(64 * kRouteChunk) void k_route(DevCtx c, int* statu
         }
     }
     if (si_bad) atomicCAS(status, AFD_OK, AFD_ERR_HEADER);
+    if (c.w1_fp8 && live) {
+        // fp8 W1: the token row's e4m3 codes and scale (r = 448 / max|x|,
+        // code = e4m3(x * r), value = code * max|x| / 448)
+        const u32x4* xr = (const u32x4*)(slot + c.foff[AFD_FIELD_ROUTED_X] + (int64_t)r * c.H * 2);
+        const int n8 = c.H / 8;
+        float amax = 0.0f;
+        for (int i = lane; i < n8; i += 64) {
+            const u32x4 v8 = xr[i];
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                amax = fmaxf(amax, fmaxf(fabsf(bf2f(v8[j] & 0xffffu)), fabsf(bf2f(v8[j] >> 16))));
+        }
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
+        const float rs = amax > 0.0f ? __fdiv_rn(448.0f, amax) : 0.0f;
+        uint2* dst = (uint2*)(c.xq + (int64_t)t * c.H);
+        for (int i = lane; i < n8; i += 64) {
+            const u32x4 v8 = xr[i];
+            uint32_t q[2] = {0u, 0u};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const uint32_t lo = e4m3_code(bf2f(v8[j] & 0xffffu) * rs), hi = e4m3_code(bf2f(v8[j] >> 16) * rs);
+                q[j >> 1] |= (lo | (hi << 8)) << (16 * (j & 1));
+            }
+            dst[i] = make_uint2(q[0], q[1]);
+        }
+        if (lane == 0) {
+            c.sx[t] = amax > 0.0f ? __fdiv_rn(amax, 448.0f) : 1.0f;
+            c.tok_src[t] = (uint64_t)(c.xq + (int64_t)t * c.H);  // the GEMM reads the codes
+            if (c.has_shared) c.sh_src[t] = (uint64_t)(c.xq + (int64_t)t * c.H);
+        }
+    }
     __syncthreads();
     for (int e = threadIdx.x; e < E; e += blockDim.x) c.blk_counts[(int64_t)e * c.NB + blockIdx.x] = hist[e];
 }
@@ -1140,6 +1198,7 @@ __global__ __launch_bounds__(256) void k_permute(DevCtx c, const int* status) {
         if (pos < T * K) {
             c.perm[pos] = f;
             c.psrc[pos] = ltok[tl];
+            if (c.w1_fp8) c.sxp[pos] = c.sx[t0 + tl];
         }
         c.inv[f] = pos;
     }
@@ -1358,10 +1417,39 @@ __device__ inline int swz4(int r) { return ((r >> 1) ^ (r >> 2)) & 3; }
 // row r of a tile holds depth values kt*32 + 8*(p ^ swz4(r)) .. +7 of the
 // tile's weight row r, or zeros past the matrix.
 // ---------------------------------------------------------------------------
+// fp8 W1: each W13 / Ws13 row's max |w|, one wavefront per row, into the
+// row-scale arrays of the packed weights (rows e*2I + j, then 2I*E + j for
+// the shared rows); k_wscale turns them into dequantisation scales once the
+// tiles are written.
+__global__ __launch_bounds__(256) void k_wamax(DevCtx c, afd_moe_weights src, float* sw13, float* sws13) {
+    const int64_t nr = (int64_t)c.E * 2 * c.I, ns = c.has_shared ? 2 * (int64_t)c.Is : 0;
+    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (row >= nr + ns) return;
+    const u32x4* x = (const u32x4*)((row < nr ? (const uint16_t*)src.w13 + row * c.H
+                                               : (const uint16_t*)src.ws13 + (row - nr) * c.H));
+    float amax = 0.0f;
+    for (int i = lane; i < c.H / 8; i += 64) {
+        const u32x4 v8 = x[i];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) amax = fmaxf(amax, fmaxf(fabsf(bf2f(v8[j] & 0xffffu)), fabsf(bf2f(v8[j] >> 16))));
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
+    if (lane == 0) (row < nr ? sw13[row] : sws13[row - nr]) = amax;
+}
+
+__global__ __launch_bounds__(256) void k_wscale(float* s, int64_t n) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) s[i] = s[i] > 0.0f ? __fdiv_rn(s[i], 448.0f) : 1.0f;
+}
+
 __global__ __launch_bounds__(256) void k_pack_weights(DevCtx c, afd_moe_weights src, char* dst, int64_t off1,
-                                                      int64_t off2, int64_t off3, int64_t total) {
+                                                      int64_t off2, int64_t off3, int64_t total, const float* amax13,
+                                                      const float* amaxs13) {
     const int64_t H = c.H, I = c.I, Is = c.Is;
-    const int64_t nk1 = (H + kBK - 1) / kBK, nk2 = (I + kBK - 1) / kBK, nk2s = (Is + kBK - 1) / kBK;
+    const bool f8 = c.w1_fp8;  // gate/up tiles of e4m3 codes: 64 depth values a row
+    const int64_t nk1 = f8 ? H / 64 : (H + kBK - 1) / kBK, nk2 = (I + kBK - 1) / kBK, nk2s = (Is + kBK - 1) / kBK;
     const int64_t nt1 = c.nt1, nt1s = (Is + kBW / 2 - 1) / (kBW / 2), nt2 = c.nt2;
     const int64_t nchunks = total / 16;
     for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < nchunks; q += (int64_t)gridDim.x * blockDim.x) {
@@ -1371,7 +1459,8 @@ __global__ __launch_bounds__(256) void k_pack_weights(DevCtx c, afd_moe_weights 
         const int64_t tile = local / kWTileBytes;
         const int within = (int)(local % kWTileBytes);
         const int r = within / kRowBytes, p = (within % kRowBytes) / 16;
-        const int64_t k0 = (int64_t)(tile % (region < 2 ? nk1 : region == 2 ? nk2 : nk2s)) * kBK + 8 * (p ^ swz4(r));
+        const int64_t ks = tile % (region < 2 ? nk1 : region == 2 ? nk2 : nk2s);
+        const int64_t k0 = f8 && region < 2 ? ks * 64 + 16 * (p ^ swz4(r)) : ks * kBK + 8 * (p ^ swz4(r));
         const int64_t tt = tile / (region < 2 ? nk1 : region == 2 ? nk2 : nk2s);  // column tile (and expert)
         const uint16_t* row = nullptr;
         if (region == 0 || region == 1) {
@@ -1389,18 +1478,44 @@ __global__ __launch_bounds__(256) void k_pack_weights(DevCtx c, afd_moe_weights 
                 row = region == 2 ? (const uint16_t*)src.w2 + ((tt / nt2) * H + n) * I : (const uint16_t*)src.ws2 + n * Is;
         }
         u32x4 v = {0u, 0u, 0u, 0u};
-        if (row) v = *(const u32x4*)(row + k0);
+        if (row && f8 && region < 2) {
+            // 16 codes of the row: r = 448 / max|w|, code = e4m3(w * r)
+            const int64_t srow = (row - (region == 0 ? (const uint16_t*)src.w13 : (const uint16_t*)src.ws13)) / H;
+            const float am = region == 0 ? amax13[srow] : amaxs13[srow];
+            const float rs = am > 0.0f ? __fdiv_rn(448.0f, am) : 0.0f;
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const u32x4 w8 = *(const u32x4*)(row + k0 + 8 * h);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const uint32_t lo = e4m3_code(bf2f(w8[j] & 0xffffu) * rs), hi = e4m3_code(bf2f(w8[j] >> 16) * rs);
+                    v[2 * h + (j >> 1)] |= (lo | (hi << 8)) << (16 * (j & 1));
+                }
+            }
+        } else if (row) {
+            v = *(const u32x4*)(row + k0);
+        }
         *(u32x4*)(dst + byte) = v;
     }
 }
 
-hipError_t launch_pack_weights(const DevCtx& c, const afd_moe_weights& src, char* dst, const int64_t off[4],
+hipError_t launch_pack_weights(const DevCtx& c, const afd_moe_weights& src, char* dst, const int64_t off[6],
                                int64_t total, hipStream_t st) {
-    const int64_t nchunks = total / 16;
+    // (the tiles end at off[4]; the fp8 row scales follow)
+    const int64_t nchunks = off[4] / 16;
     const int64_t blocks = std::min<int64_t>((nchunks + 255) / 256, 65536);
-    if (blocks <= 0) return hipSuccess;
-    hipLaunchKernelGGL(k_pack_weights, dim3((unsigned)blocks), dim3(256), 0, st, c, src, dst, off[1], off[2], off[3],
-                       total);
+    float* s13 = (float*)(dst + off[4]);
+    float* ss13 = (float*)(dst + off[5]);
+    const int64_t nr = (int64_t)c.E * 2 * c.I, ns = c.has_shared ? 2 * (int64_t)c.Is : 0;
+    if (c.w1_fp8) hipLaunchKernelGGL(k_wamax, dim3((unsigned)((nr + ns + 3) / 4)), dim3(256), 0, st, c, src, s13, ss13);
+    if (blocks > 0)
+        hipLaunchKernelGGL(k_pack_weights, dim3((unsigned)blocks), dim3(256), 0, st, c, src, dst, off[1], off[2],
+                           off[3], off[4], s13, ss13);
+    if (c.w1_fp8) {
+        hipLaunchKernelGGL(k_wscale, dim3((unsigned)((nr + 255) / 256)), dim3(256), 0, st, s13, nr);
+        if (ns) hipLaunchKernelGGL(k_wscale, dim3((unsigned)((ns + 255) / 256)), dim3(256), 0, st, ss13, ns);
+    }
+    (void)total;
     return hipGetLastError();
 }
 
@@ -1421,8 +1536,10 @@ struct GemmTile {
     int r0;                // first token row of the tile (h / y / ys row; fan-in token for shared rows)
     int rows, Ig, nt;      // valid token rows, the group's intermediate width, column tile
     bool sh;
-    int par;               // which of the two return-offset tables is this tile's (down GEMM)
-    uint32_t rofs;         // down GEMM storing into the return slots: this thread's row's offset
+    int par;               // which of the two LDS row tables is this tile's
+    uint32_t rofs;         // this thread's row's entry of the table: its return offset (down GEMM
+                           // storing into the return slots) or its token scale (fp8 gate/up GEMM)
+    float dw[4];           // fp8 gate/up GEMM: this lane's gate (0, 1) and up (2, 3) column scales
 };
 
 
@@ -1626,6 +1743,61 @@ __device__ __forceinline__ void gemm_step(f32x16 (&acc)[NV > 0 ? NV : 1][4], con
     __builtin_amdgcn_sched_barrier(0);
 }
 
+// fp8 gate/up GEMM: a step is 64 depth values (each 64-byte row holds e4m3
+// codes).  A lane's operand for the block-scaled MFMA is its slice-0 chunk
+// followed by its slice-1 chunk (the two 16-byte reads of a bf16 step); any
+// split of the 64 values over a lane pair works as long as both operands use
+// the same one.  Unit E8M0 scales (127); the row scales apply in the epilogue.
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ i32x8 cat_frag(bf16x8 lo, bf16x8 hi) {
+    return __builtin_shufflevector(__builtin_bit_cast(i32x4, lo), __builtin_bit_cast(i32x4, hi), 0, 1, 2, 3, 4, 5,
+                                   6, 7);
+}
+
+template <int NV>
+__device__ __forceinline__ void gemm_mfma_f8(f32x16 (&acc)[NV > 0 ? NV : 1][4], const GemmFrags<NV>& a,
+                                             const GemmFrags<NV>& b) {
+#pragma unroll
+    for (int ib = 0; ib < NV; ++ib) {
+        const i32x8 x = cat_frag(a.x[ib], b.x[ib]);
+#pragma unroll
+        for (int jb = 0; jb < 4; ++jb)
+            acc[ib][jb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(x, cat_frag(a.w[jb], b.w[jb]), acc[ib][jb],
+                                                                          0, 0, 0, 127, 0, 127);
+    }
+}
+
+// One fp8 step: slice 1 of stage kt (with the weight loads of step kt+3),
+// then every MFMA of the step, then -- once stage kt+1 has landed -- slice 0
+// of stage kt+1 (with the token loads of step kt+3).  The load pattern and
+// the waits are the bf16 step's.
+template <int NV, int NX>
+__device__ __forceinline__ void gemm_step_f8(f32x16 (&acc)[NV > 0 ? NV : 1][4], const GemmTile& t, char* smem, int kt,
+                                             int wid, int lane, uint32_t wl, uint32_t tl, GemmFrags<NV>& a,
+                                             GemmFrags<NV>& b) {
+    char* const ld = smem + ((kt + kStages - 1) & (kStages - 1)) * kStageBytes;
+    const int kl = min(kt + kStages - 1, t.nk - 1);
+    {
+        const char* bb = t.bbase + (int64_t)kl * kWTileBytes;
+        gemm_frags_loads<1, NV, kWInstr>(b, smem + (kt & (kStages - 1)) * kStageBytes, 1, wl, tl, [&](int i) {
+            dma16(bb + (t.wlane + i * kGemmWaves * 1024), (lds_ptr_t)(ld + kXStageBytes + (wid + kGemmWaves * i) * 1024));
+        });
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): slice 1 is in
+    gemm_mfma_f8(acc, a, b);
+    __builtin_amdgcn_sched_barrier(0);
+    AFD_WAIT_VMCNT(NX + 2 * kWInstr);
+    AFD_BARRIER();
+    {
+        const char* ab = t.abase + (int64_t)kl * t.astep;
+        gemm_frags_loads<1, NV, NX>(a, smem + ((kt + 1) & (kStages - 1)) * kStageBytes, 0, wl, tl, [&](int i) {
+            dma16(ab + t.xo[i], (lds_ptr_t)(ld + (wid + kGemmWaves * i) * 1024));
+        });
+    }
+    __builtin_amdgcn_sched_barrier(0);
+}
+
 // Tile scheduler of a workgroup.  Tiles are taken dynamically: a workgroup
 // on XCD x (x = b % kXcds: workgroups are dispatched to the XCDs round-
 // robin) takes tiles from the shared-expert segment x, then from the routed
@@ -1706,14 +1878,16 @@ __device__ __forceinline__ void gemm_setup(const DevCtx& c, const Weights& w, in
     const int e = j - c.has_shared;
     t.Ig = t.sh ? c.Is : c.I;
     t.Kdim = MODE == 1 ? c.H : t.Ig;
-    t.nk = (t.Kdim + kBK - 1) / kBK;
-    t.kfull = t.Kdim / kBK;
+    // (fp8 gate/up: e4m3 rows, 64 depth values a step; hidden is a multiple of 64)
+    const bool f8 = MODE == 1 && c.w1_fp8;
+    t.nk = f8 ? c.H / 64 : (t.Kdim + kBK - 1) / kBK;
+    t.kfull = f8 ? t.nk : t.Kdim / kBK;
     t.tail_clamp = (uint32_t)t.Kdim * 2 - 16;
     // Token rows: slot rows through their row addresses (gate/up; 32-bit
     // byte offsets from the window, which stays below 4 GiB: checked at
     // create) or rows of the depth-block-major h / hs (down).
     if (MODE == 1) {
-        t.abase = c.in_win;
+        t.abase = c.w1_fp8 ? (const char*)c.xq : c.in_win;  // (fp8: the quantised token rows)
         t.astep = kRowBytes;
     } else {
         t.abase = (const char*)(t.sh ? c.hs : c.h);
@@ -1726,6 +1900,21 @@ __device__ __forceinline__ void gemm_setup(const DevCtx& c, const Weights& w, in
                         : w.w2 + ((int64_t)e * c.nt2 + t.nt) * t.nk * kWTileBytes;
     t.wlane = (uint32_t)wid * 1024u + (uint32_t)(threadIdx.x & 63) * 16u;
     t.cx = lcx;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) t.dw[i] = 1.0f;
+    if (f8) {
+        t.tail_clamp = (uint32_t)c.H - 16;
+        const int r = threadIdx.x;  // row r of the tile: its token scale, for the LDS table
+        t.rofs = __float_as_uint(r < t.rows ? (t.sh ? c.sx : c.sxp)[t.r0 + r] : 0.0f);
+        const float* sw = t.sh ? w.sws13 : w.sw13 + (int64_t)e * 2 * c.I;
+        const int lj = threadIdx.x & 31;
+#pragma unroll
+        for (int jb = 0; jb < 2; ++jb) {
+            const int col = t.nt * (kBW / 2) + (wid >> 1) * 64 + jb * 32 + lj;
+            t.dw[jb] = col < t.Ig ? sw[col] : 0.0f;
+            t.dw[2 + jb] = col < t.Ig ? sw[t.Ig + col] : 0.0f;
+        }
+    }
     if (MODE == 2 && c.direct_ret) {
         // row threadIdx.x of the tile: its return-window offset, or past the
         // window's end (the store's range check drops it)
@@ -1737,7 +1926,7 @@ __device__ __forceinline__ void gemm_setup(const DevCtx& c, const Weights& w, in
         const int r = (wid + kGemmWaves * i) * kRowsPerLoad + lrow;
         const int m = t.r0 + (r < t.rows ? r : 0);
         uint32_t o;
-        if (MODE == 1) o = (uint32_t)((t.sh ? c.sh_src[m] : c.psrc[m]) - (uint64_t)c.in_win);
+        if (MODE == 1) o = (uint32_t)((t.sh ? c.sh_src[m] : c.psrc[m]) - (uint64_t)t.abase);
         else o = (uint32_t)m * kRowBytes;
         t.xo[i] = o + lcx;
     }
@@ -1827,6 +2016,22 @@ __device__ __forceinline__ void gemm_epilogue_ib(const f32x16 (&acc)[NV > 0 ? NV
         // Column block jb is one 32-deep block of h: rows of 64 bytes.
         const int64_t hrows = t.sh ? c.hsrows : c.hrows;
         char* hb = (char*)(t.sh ? c.hs : c.h);
+        // fp8: the token scales of this lane's rows rb + 8q + i (1 otherwise)
+        float dx[4][4];
+        if (c.w1_fp8) {
+            const u32x4* tab = (const u32x4*)(smem + kRetTabOff + t.par * (kBX * 4));
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const u32x4 o = tab[(rb >> 2) + 2 * q];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) dx[q][i] = __uint_as_float(o[i]);
+            }
+        } else {
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) dx[q][i] = 1.0f;
+        }
 #pragma unroll
         for (int jb = 0; jb < 2; ++jb) {
             const int col0 = t.nt * (kBW / 2) + ww * 64 + jb * 32;
@@ -1838,7 +2043,9 @@ __device__ __forceinline__ void gemm_epilogue_ib(const f32x16 (&acc)[NV > 0 ? NV
                 float o[2];
 #pragma unroll
                 for (int q = 0; q < 2; ++q) {
-                    const float g = agpr(acc[ib][jb][v + q]), u = agpr(acc[ib][jb + 2][v + q]);
+                    const float sxr = dx[(v + q) >> 2][(v + q) & 3];
+                    const float g = agpr(acc[ib][jb][v + q]) * sxr * t.dw[jb];
+                    const float u = agpr(acc[ib][jb + 2][v + q]) * sxr * t.dw[2 + jb];
                     o[q] = g * __builtin_amdgcn_rcpf(1.f + __expf(-g)) * u;
                 }
                 const uint32_t pk = pk_bf16(o[0], o[1]);
@@ -1893,7 +2100,7 @@ __device__ __forceinline__ void gemm_epilogue_ib(const f32x16 (&acc)[NV > 0 ? NV
 // with NV valid token blocks (its blocks wx, wx+2, .. below tb).  Steps 0 ..
 // kStages-2 have been issued into stages 0 ...; on return `next` and `tn`
 // describe the next tile (next < 0: none), whose first steps are loading.
-template <int MODE, int NV, int NX>
+template <int MODE, int NV, int NX, bool F8>
 __device__ __forceinline__ void gemm_run(const DevCtx& c, const Weights& w, GemmSched& sc, const GemmTile& t,
                                          char* smem, int tid, int wid, int lane, int ww, int wx, uint32_t wl,
                                          uint32_t tl, int lrow, uint32_t lcx, int& next, GemmTile& tn) {
@@ -1913,10 +2120,16 @@ __device__ __forceinline__ void gemm_run(const DevCtx& c, const Weights& w, Gemm
     gemm_frags<MODE, NV>(fa, smem, 0, wl, tl);
     int kt = 0;
     const int kg = min(t.kfull, max(t.nk - kGrabAhead, 0));
-    for (; kt < kg; ++kt) gemm_step<MODE, NV, NX, false>(acc, t, smem, kt, wid, lane, wl, tl, fa, fb);
-    if (wid == 0) sched_issue(sc, tid);  // the next tile
-    for (; kt < t.kfull; ++kt) gemm_step<MODE, NV, NX, false>(acc, t, smem, kt, wid, lane, wl, tl, fa, fb);
-    for (; kt < t.nk; ++kt) gemm_step<MODE, NV, NX, true>(acc, t, smem, kt, wid, lane, wl, tl, fa, fb);
+    if (F8) {
+        for (; kt < kg; ++kt) gemm_step_f8<NV, NX>(acc, t, smem, kt, wid, lane, wl, tl, fa, fb);
+        if (wid == 0) sched_issue(sc, tid);  // the next tile
+        for (; kt < t.nk; ++kt) gemm_step_f8<NV, NX>(acc, t, smem, kt, wid, lane, wl, tl, fa, fb);
+    } else {
+        for (; kt < kg; ++kt) gemm_step<MODE, NV, NX, false>(acc, t, smem, kt, wid, lane, wl, tl, fa, fb);
+        if (wid == 0) sched_issue(sc, tid);  // the next tile
+        for (; kt < t.kfull; ++kt) gemm_step<MODE, NV, NX, false>(acc, t, smem, kt, wid, lane, wl, tl, fa, fb);
+        for (; kt < t.nk; ++kt) gemm_step<MODE, NV, NX, true>(acc, t, smem, kt, wid, lane, wl, tl, fa, fb);
+    }
 
     gemm_boundary<MODE>(c, w, sc, smem, tid, wid, lrow, lcx, next, tn);
     tn.par = t.par ^ 1;
@@ -1930,7 +2143,7 @@ __device__ __forceinline__ void gemm_run(const DevCtx& c, const Weights& w, Gemm
     for (int ib = 0; ib < (NV > kStages - 1 ? NV : kStages - 1); ++ib) {
         if (ib < kStages - 1 && next >= 0) gemm_prologue_step<MODE>(tn, smem, wid, ib);
         // the next tile's return offsets into its table (its load was issued at set-up)
-        if (MODE == 2 && ib == 0 && next >= 0 && c.direct_ret)
+        if (ib == 0 && next >= 0 && ((MODE == 2 && c.direct_ret) || (MODE == 1 && c.w1_fp8)))
             ((uint32_t*)(smem + kRetTabOff + tn.par * (kBX * 4)))[threadIdx.x] = tn.rofs;
         if (ib < NV) gemm_epilogue_ib<MODE, NV>(acc, c, t, smem, lane, ww, wx, ib);
     }
@@ -1986,14 +2199,19 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(DevCtx c, const int* s
         gemm_setup<MODE>(c, w, tile, wid, lrow, lcx, t);
         gemm_prologue<MODE>(t, smem, wid);
         t.par = 0;
-        if (MODE == 2 && c.direct_ret) ((uint32_t*)(smem + kRetTabOff))[threadIdx.x] = t.rofs;
+        if ((MODE == 2 && c.direct_ret) || (MODE == 1 && c.w1_fp8))
+            ((uint32_t*)(smem + kRetTabOff))[threadIdx.x] = t.rofs;
     }
     while (tile >= 0) {
         int next;
         GemmTile tn;
         // this wave's valid token blocks NV = ceil((tb - wx) / 2) and the
         // token-row loads per wave and step NX = ceil(tb / 2)
-#define AFD_RUN(NV, NX) gemm_run<MODE, NV, NX>(c, w, sc, t, smem, tid, wid, lane, ww, wx, wl, tl, lrow, lcx, next, tn)
+#define AFD_RUN(NV, NX)                                                                                          \
+    if (MODE == 1 && c.w1_fp8)                                                                                  \
+        gemm_run<MODE, NV, NX, true>(c, w, sc, t, smem, tid, wid, lane, ww, wx, wl, tl, lrow, lcx, next, tn);  \
+    else                                                                                                        \
+        gemm_run<MODE, NV, NX, false>(c, w, sc, t, smem, tid, wid, lane, ww, wx, wl, tl, lrow, lcx, next, tn)
         switch (t.tb * 2 + wx) {  // key 2 tb + wx -> (NV, NX)
             case 17: case 16: case 14: AFD_RUN(4, 4); break;  // tb 8, tb 7 wx 0
             case 15: AFD_RUN(3, 4); break;                    // tb 7 wx 1

@@ -31,7 +31,8 @@ class FfnSession:
                                    wl.intermediate, wl.shared_intermediate, ring_depth=wl.ring_depth,
                                    routed_scaling_factor=wl.routed_scaling_factor, renormalize=wl.renormalize,
                                    poll_timeout_us=poll_timeout_us, attention_routes=wl.attention_routes,
-                                   route_experts=wl.route_experts, expert_offset=wl.expert_offset)
+                                   route_experts=wl.route_experts, expert_offset=wl.expert_offset,
+                                   w1_fp8=wl.w1_fp8)
         self.win = afd.afd_window_create(self.cfg)
         self.layout = afd.afd_window_layout(self.win)
         self.peer_streams = [torch.cuda.Stream(device=self.dev) for _ in range(wl.num_peers)]

@@ -62,6 +62,7 @@ class Workload:
     attention_routes: int = 0       # 1: the attention side routes (grouped routed rows, sender combines)
     route_experts: int = 0          # experts the peers route over when the window owns a segment (0: all)
     expert_offset: int = 0          # first expert of the window's segment
+    w1_fp8: int = 0                 # 1: gate/up GEMMs on e4m3 operands
     notes: str = field(default="", compare=False)
 
     @property

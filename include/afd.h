@@ -67,7 +67,7 @@
 extern "C" {
 #endif
 
-#define AFD_ABI_VERSION 7
+#define AFD_ABI_VERSION 8
 
 /* Header flags bit 1: shutdown sentinel ("Window and slot layout"). */
 #define AFD_FLAG_SHUTDOWN 0x2u
@@ -145,7 +145,18 @@ typedef struct afd_window afd_window; /* opaque, library-owned */
  * by afd_slot_unpack_ranks.  route_experts 0 means num_experts (one rank).
  * Limits: route_experts > 0 needs attention_routes = 1, top_k <=
  * route_experts <= 1024, 0 <= expert_offset, expert_offset + num_experts
- * <= route_experts; with route_experts 0, expert_offset must be 0. */
+ * <= route_experts; with route_experts 0, expert_offset must be 0.
+ *
+ * w1_fp8 = 1: the gate/up GEMMs (W13 and the shared Ws13) run on OCP FP8
+ * E4M3 operands ("[RFC]: Async AFD for Prefill on Ascend NPU",
+ * "Architecture": the routed W1 + SwiGLU grouped GEMM, quantised): each
+ * token row is quantised when it is routed and each W13 / Ws13 row when the
+ * weights are packed, one scale per row (r = 448 / max|x| and code =
+ * e4m3(x * r) in fp32, round to nearest even, saturating; the row's value is
+ * code * max|x| / 448); products accumulate in fp32 and both scales apply
+ * before SwiGLU.  The down GEMM stays bf16.  Needs attention_routes = 0 and
+ * hidden a multiple of 64; the packed weights then hold e4m3 gate/up tiles
+ * and their row scales (layout.packed_weight_bytes). */
 typedef struct afd_window_config {
     uint32_t struct_size;
     int32_t num_peers;           /* P: attention peers fanned in by this FFN replica        */
@@ -163,6 +174,7 @@ typedef struct afd_window_config {
                                     routes and sends rows grouped by expert (see above)      */
     int32_t route_experts;       /* experts the peers route over (0: num_experts)            */
     int32_t expert_offset;       /* first of the num_experts experts this window owns        */
+    int32_t w1_fp8;              /* 1: gate/up GEMMs on e4m3 operands (see above)            */
     int32_t reserved[1];         /* must be 0                                                */
 } afd_window_config;
 

@@ -28,7 +28,7 @@ def test_library_exports_every_declared_symbol():
     missing = [s for s in declared if not hasattr(L, s)]
     assert not missing, missing
     assert sorted(afd.EXPORTS) == declared
-    assert afd.afd_abi_version() == 7
+    assert afd.afd_abi_version() == 8
 
 
 CFGS = [
@@ -112,6 +112,7 @@ def test_slot_fields_disjoint_aligned_viewable(kw):
     dict(route_experts=16), dict(expert_offset=1),
     dict(attention_routes=1, route_experts=1025), dict(attention_routes=1, route_experts=12, expert_offset=5),
     dict(attention_routes=1, route_experts=12, expert_offset=-1),
+    dict(w1_fp8=2), dict(w1_fp8=1, hidden=96), dict(w1_fp8=1, attention_routes=1),
 ])
 
 def test_config_rejected(bad):
@@ -165,3 +166,16 @@ def test_header_self_check_rejects(word, value):
 def test_status_strings():
     assert afd.status_string(afd.AFD_ERR_TIMEOUT) == "AFD_ERR_TIMEOUT"
     assert afd.status_string(123) == "AFD_UNKNOWN"
+
+
+@pytest.mark.parametrize("kw", [c for c in CFGS if c["hidden"] % 64 == 0 and not c.get("attention_routes")])
+def test_packed_weight_bytes_fp8(kw):
+    # e4m3 gate/up tiles (256 rows x 64 depth values of one byte), bf16 down
+    # tiles, then one fp32 scale per W13 row and per Ws13 row (256-aligned)
+    L = afd.afd_layout_compute(afd.make_config(**kw, w1_fp8=1))
+    E, H, I, Is = kw["num_experts"], kw["hidden"], kw["intermediate"], kw["shared_intermediate"]
+    cdiv = lambda a, b: -(-a // b)
+    a256 = lambda n: cdiv(n, 256) * 256
+    tiles = (E * cdiv(I, 128) * (H // 64) + cdiv(Is, 128) * (H // 64)
+             + E * cdiv(H, 256) * cdiv(I, 32) + cdiv(H, 256) * cdiv(Is, 32))
+    assert L.packed_weight_bytes == tiles * 16384 + a256(4 * E * 2 * I) + a256(4 * 2 * Is)
