@@ -30,6 +30,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
+MFMA_FP8_PEAK_TFLOPS = 5000.0    # MI355X dense fp8 MFMA, published
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, published
 
 
@@ -45,13 +46,14 @@ def algorithmic(wl, counts):
     touched = int((np.asarray(counts) > 0).sum())
     g1_flops = 4.0 * H * I * pairs + 4.0 * H * Is * T
     g2_flops = 2.0 * H * I * pairs + 2.0 * H * Is * T
-    w13_bytes = touched * 2 * I * H * 2 + (2 * Is * H * 2 if Is else 0)
+    wb = 1 if wl.w1_fp8 else 2  # bytes per gate/up weight (e4m3 codes, or bf16)
+    w13_bytes = touched * 2 * I * H * wb + (2 * Is * H * wb if Is else 0)
     w2_bytes = touched * H * I * 2 + (H * Is * 2 if Is else 0)
     io_bytes = T * H * 2 + T * E * 4 + T * H * 2
     return {
         "flops": g1_flops + g2_flops,
         "bytes": w13_bytes + w2_bytes + io_bytes,
-        "gemm_gate_up_swiglu": {"flops": g1_flops, "bytes": w13_bytes + T * H * 2 * (K + 1) + 2 * pairs * I},
+        "gemm_gate_up_swiglu": {"flops": g1_flops, "bytes": w13_bytes + T * H * wb * (K + 1) + 2 * pairs * I},
         "gemm_down": {"flops": g2_flops, "bytes": w2_bytes + 2 * pairs * I + 2 * T * Is},
         "touched_experts": touched,
     }
@@ -69,7 +71,7 @@ def measured_traffic(wl, kernel):
         sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
     except OSError:
         return None
-    if wl.attention_routes or side.get("workload") != wl.name or side.get("kernel_source_sha256") != sha:
+    if wl.attention_routes or wl.w1_fp8 or side.get("workload") != wl.name or side.get("kernel_source_sha256") != sha:
         return None
     b = side["bytes_per_launch"].get(kernel)
     return None if b is None else int(b["read"] + b["written"])
@@ -137,6 +139,8 @@ def main():
     ap.add_argument("--attention-routes", action="store_true",
                     help="attention-routed window: the peers route, group and combine; the FFN side merges "
                          "their group lists")
+    ap.add_argument("--w1-fp8", action="store_true",
+                    help="gate/up GEMMs on e4m3 operands (token and W13 rows quantised per row); down GEMM bf16")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run only a plain 1 GiB device-to-device copy, 10 times (scale for HBM byte counters)")
     args = ap.parse_args()
@@ -163,9 +167,9 @@ def main():
     from combine_afd_slot_amd.inputs import WORKLOADS, make_inputs
 
     wl = WORKLOADS[args.workload]
-    if args.attention_routes:
+    if args.attention_routes or args.w1_fp8:
         import dataclasses
-        wl = dataclasses.replace(wl, attention_routes=1)
+        wl = dataclasses.replace(wl, attention_routes=int(args.attention_routes), w1_fp8=int(args.w1_fp8))
     log(f"[bench] workload {wl.name}: seq_lens={wl.seq_lens} H={wl.hidden} E={wl.num_experts} "
         f"K={wl.top_k} I={wl.intermediate} Is={wl.shared_intermediate}")
     t0 = time.time()
@@ -240,7 +244,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "fp8-e4m3 gate/up, bf16 down" if wl.w1_fp8 else "bf16",
         "data": "synthetic",
         "config": {"workload": wl.name, "peers": wl.num_peers, "seq_lens": list(wl.seq_lens),
                    "total_tokens": T, "hidden": wl.hidden, "experts": wl.num_experts, "top_k": wl.top_k,
@@ -253,18 +257,21 @@ def main():
     }
     if wl.attention_routes:
         line["config"]["attention_routes"] = 1
+    if wl.w1_fp8:
+        line["config"]["w1_fp8"] = 1
+    peak = MFMA_FP8_PEAK_TFLOPS if wl.w1_fp8 else MFMA_BF16_PEAK_TFLOPS  # the dominant GEMM's operand type
     if kern:
         line["kernel_ms"] = {k: round(v, 4) for k, v in kern.items()}
         line["kernel_ms_all_separate_pass"] = kern_all
         dom = "gemm_gate_up_swiglu"  # twice the down GEMM's weights and flops
         # decode-shaped steps stream weights: bound by HBM; prefill steps by MFMA
         ai = alg[dom]["flops"] / alg[dom]["bytes"]
-        ridge = MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+        ridge = peak * 1e12 / (HBM_PEAK_GBS * 1e9)
         if ai >= ridge:
             ach = alg[dom]["flops"] / (kern[dom] * 1e-3) / 1e12
             line["roofline"] = {"kernel": dom, "bound": "mfma", "achieved": round(ach, 1),
-                                "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                                "frac": round(ach / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": measured_traffic(wl, dom)}
+                                "peak": peak, "unit": "TFLOP/s",
+                                "frac": round(ach / peak, 4), "traffic": measured_traffic(wl, dom)}
         else:
             ach = alg[dom]["bytes"] / (kern[dom] * 1e-3) / 1e9
             line["roofline"] = {"kernel": dom, "bound": "hbm", "achieved": round(ach, 1),
