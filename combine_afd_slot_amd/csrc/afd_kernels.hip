@@ -877,18 +877,43 @@ __global__ __launch_bounds__(64 * kRouteChunk) void k_route(DevCtx c, int* statu
         // code = e4m3(x * r), value = code * max|x| / 448)
         const u32x4* xr = (const u32x4*)(slot + c.foff[AFD_FIELD_ROUTED_X] + (int64_t)r * c.H * 2);
         const int n8 = c.H / 8;
+        // the row's first 8 chunks a lane stay in registers for the encode
+        // pass (all of a row up to hidden 4096), the rest are read again
+        constexpr int kKeep = 8;
+        u32x4 keep[kKeep];
         float amax = 0.0f;
-        for (int i = lane; i < n8; i += 64) {
+#pragma unroll
+        for (int j = 0; j < kKeep; ++j) keep[j] = lane + 64 * j < n8 ? xr[lane + 64 * j] : (u32x4)0u;
+        for (int i = lane + 64 * kKeep; i < n8; i += 64) {
             const u32x4 v8 = xr[i];
 #pragma unroll
             for (int j = 0; j < 4; ++j)
                 amax = fmaxf(amax, fmaxf(fabsf(bf2f(v8[j] & 0xffffu)), fabsf(bf2f(v8[j] >> 16))));
         }
 #pragma unroll
+        for (int k = 0; k < kKeep; ++k)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                amax = fmaxf(amax, fmaxf(fabsf(bf2f(keep[k][j] & 0xffffu)), fabsf(bf2f(keep[k][j] >> 16))));
+#pragma unroll
         for (int o = 32; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
         const float rs = amax > 0.0f ? __fdiv_rn(448.0f, amax) : 0.0f;
         uint2* dst = (uint2*)(c.xq + (int64_t)t * c.H);
-        for (int i = lane; i < n8; i += 64) {
+#pragma unroll
+        for (int k = 0; k < kKeep; ++k) {
+            const int i = lane + 64 * k;
+            if (i < n8) {
+                uint32_t q[2] = {0u, 0u};
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const uint32_t lo = e4m3_code(bf2f(keep[k][j] & 0xffffu) * rs);
+                    const uint32_t hi = e4m3_code(bf2f(keep[k][j] >> 16) * rs);
+                    q[j >> 1] |= (lo | (hi << 8)) << (16 * (j & 1));
+                }
+                dst[i] = make_uint2(q[0], q[1]);
+            }
+        }
+        for (int i = lane + 64 * kKeep; i < n8; i += 64) {
             const u32x4 v8 = xr[i];
             uint32_t q[2] = {0u, 0u};
 #pragma unroll

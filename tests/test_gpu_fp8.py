@@ -26,6 +26,9 @@ WLS = [
                    shared_intermediate=136, token_cap=160, zipf_bias=1.0, w1_fp8=1),
     small_workload("fp8_wide", seq_lens=(64, 64), hidden=1024, num_experts=8, top_k=2, intermediate=256,
                    shared_intermediate=256, token_cap=64, w1_fp8=1),
+    # rows longer than the 4096 values the quantising wavefront keeps in registers
+    small_workload("fp8_long_rows", seq_lens=(9, 14), hidden=4608, num_experts=4, top_k=2, intermediate=64,
+                   shared_intermediate=64, token_cap=16, w1_fp8=1),
 ]
 
 
