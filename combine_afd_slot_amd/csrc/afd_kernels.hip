@@ -69,6 +69,16 @@ __device__ inline uint32_t e4m3_code(float v) {
     return c == 0u ? 0u : c | (v < 0.0f ? 0x80u : 0u);
 }
 
+// Four e4m3 codes in a word (a in the low byte), by the hardware conversion
+// (v_cvt_pk_fp8_f32, round to nearest even).  For inputs clamped to +-448 it
+// gives e4m3_code's codes, but may give a sign to a zero; that changes no sum.
+__device__ inline uint32_t pack4_e4m3(float a, float b, float c, float d) {
+    const auto cl = [](float x) { return fminf(fmaxf(x, -448.0f), 448.0f); };
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(cl(a), cl(b), 0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(cl(c), cl(d), w, true);
+    return (uint32_t)w;
+}
+
 __device__ inline char* slot_ptr(const DevCtx& c, char* win, int p, int s) {
     return win + c.slots_off + (int64_t)(p * c.R + s) * c.slot_bytes;
 }
@@ -903,25 +913,19 @@ __global__ __launch_bounds__(64 * kRouteChunk) void k_route(DevCtx c, int* statu
         for (int k = 0; k < kKeep; ++k) {
             const int i = lane + 64 * k;
             if (i < n8) {
-                uint32_t q[2] = {0u, 0u};
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const uint32_t lo = e4m3_code(bf2f(keep[k][j] & 0xffffu) * rs);
-                    const uint32_t hi = e4m3_code(bf2f(keep[k][j] >> 16) * rs);
-                    q[j >> 1] |= (lo | (hi << 8)) << (16 * (j & 1));
-                }
-                dst[i] = make_uint2(q[0], q[1]);
+                const u32x4 v8 = keep[k];
+                dst[i] = make_uint2(pack4_e4m3(bf2f(v8[0] & 0xffffu) * rs, bf2f(v8[0] >> 16) * rs,
+                                               bf2f(v8[1] & 0xffffu) * rs, bf2f(v8[1] >> 16) * rs),
+                                    pack4_e4m3(bf2f(v8[2] & 0xffffu) * rs, bf2f(v8[2] >> 16) * rs,
+                                               bf2f(v8[3] & 0xffffu) * rs, bf2f(v8[3] >> 16) * rs));
             }
         }
         for (int i = lane + 64 * kKeep; i < n8; i += 64) {
             const u32x4 v8 = xr[i];
-            uint32_t q[2] = {0u, 0u};
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const uint32_t lo = e4m3_code(bf2f(v8[j] & 0xffffu) * rs), hi = e4m3_code(bf2f(v8[j] >> 16) * rs);
-                q[j >> 1] |= (lo | (hi << 8)) << (16 * (j & 1));
-            }
-            dst[i] = make_uint2(q[0], q[1]);
+            dst[i] = make_uint2(pack4_e4m3(bf2f(v8[0] & 0xffffu) * rs, bf2f(v8[0] >> 16) * rs,
+                                           bf2f(v8[1] & 0xffffu) * rs, bf2f(v8[1] >> 16) * rs),
+                                pack4_e4m3(bf2f(v8[2] & 0xffffu) * rs, bf2f(v8[2] >> 16) * rs,
+                                           bf2f(v8[3] & 0xffffu) * rs, bf2f(v8[3] >> 16) * rs));
         }
         if (lane == 0) {
             c.sx[t] = amax > 0.0f ? __fdiv_rn(amax, 448.0f) : 1.0f;
