@@ -190,7 +190,7 @@ WsLayout ws_layout(const afd_window_config& c) {
         const int64_t q = c.w1_fp8 ? 1 : 0;
         w.xq = take(q * tmax * c.hidden);
         w.sx = take(q * 4 * tmax);
-        w.sxp = take(q * 4 * np);
+        w.sxp = take(q * 4 * (np + tmax));
     }
     w.bytes = cur;
     return w;

@@ -81,7 +81,8 @@ struct DevCtx {
     int w1_fp8;        // gate/up GEMMs on e4m3 operands
     uint8_t* xq;       // [Tmax][H] e4m3 codes of the token rows (fp8 W1)
     float* sx;         // [Tmax]   their dequantisation scales
-    float* sxp;        // [Tmax*K] the scale of each permuted pair's token row
+    float* sxp;        // [Tmax*K + Tmax] the scale of each permuted pair's token row, then of
+                       //   each shared row (token t at Tmax*K + t)
     int Eg;            // experts the peers route over (E unless the window owns a segment)
     int e0;            // first expert of the window's segment
     int NBp;           // routing chunks of one message: ceil(token_cap / kRouteChunk)

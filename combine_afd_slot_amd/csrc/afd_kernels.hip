@@ -928,7 +928,9 @@ __global__ __launch_bounds__(64 * kRouteChunk) void k_route(DevCtx c, int* statu
                                            bf2f(v8[3] & 0xffffu) * rs, bf2f(v8[3] >> 16) * rs));
         }
         if (lane == 0) {
-            c.sx[t] = amax > 0.0f ? __fdiv_rn(amax, 448.0f) : 1.0f;
+            const float d = amax > 0.0f ? __fdiv_rn(amax, 448.0f) : 1.0f;
+            c.sx[t] = d;
+            c.sxp[(int64_t)c.hrows + t] = d;  // (the shared row's scale, beside the pairs')
             c.tok_src[t] = (uint64_t)(c.xq + (int64_t)t * c.H);  // the GEMM reads the codes
             if (c.has_shared) c.sh_src[t] = (uint64_t)(c.xq + (int64_t)t * c.H);
         }
@@ -1893,7 +1895,7 @@ __device__ __forceinline__ int sched_next(GemmSched& s, int lane) {
 
 // Per-tile state of the wave: group, rows, depth, and the row offsets of its
 // load instructions.
-template <int MODE>
+template <int MODE, bool F8>
 __device__ __forceinline__ void gemm_setup(const DevCtx& c, const Weights& w, int tile, int wid, int lrow, uint32_t lcx,
                                            GemmTile& t) {
     // (every value here is wave-uniform: keep them in scalar registers)
@@ -1908,7 +1910,7 @@ __device__ __forceinline__ void gemm_setup(const DevCtx& c, const Weights& w, in
     t.Ig = t.sh ? c.Is : c.I;
     t.Kdim = MODE == 1 ? c.H : t.Ig;
     // (fp8 gate/up: e4m3 rows, 64 depth values a step; hidden is a multiple of 64)
-    const bool f8 = MODE == 1 && c.w1_fp8;
+    constexpr bool f8 = F8;
     t.nk = f8 ? c.H / 64 : (t.Kdim + kBK - 1) / kBK;
     t.kfull = f8 ? t.nk : t.Kdim / kBK;
     t.tail_clamp = (uint32_t)t.Kdim * 2 - 16;
@@ -1916,7 +1918,7 @@ __device__ __forceinline__ void gemm_setup(const DevCtx& c, const Weights& w, in
     // byte offsets from the window, which stays below 4 GiB: checked at
     // create) or rows of the depth-block-major h / hs (down).
     if (MODE == 1) {
-        t.abase = c.w1_fp8 ? (const char*)c.xq : c.in_win;  // (fp8: the quantised token rows)
+        t.abase = F8 ? (const char*)c.xq : c.in_win;  // (fp8: the quantised token rows)
         t.astep = kRowBytes;
     } else {
         t.abase = (const char*)(t.sh ? c.hs : c.h);
@@ -1929,12 +1931,10 @@ __device__ __forceinline__ void gemm_setup(const DevCtx& c, const Weights& w, in
                         : w.w2 + ((int64_t)e * c.nt2 + t.nt) * t.nk * kWTileBytes;
     t.wlane = (uint32_t)wid * 1024u + (uint32_t)(threadIdx.x & 63) * 16u;
     t.cx = lcx;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) t.dw[i] = 1.0f;
-    if (f8) {
+    if constexpr (F8) {
         t.tail_clamp = (uint32_t)c.H - 16;
         const int r = threadIdx.x;  // row r of the tile: its token scale, for the LDS table
-        t.rofs = __float_as_uint(r < t.rows ? (t.sh ? c.sx : c.sxp)[t.r0 + r] : 0.0f);
+        t.rofs = __float_as_uint(r < t.rows ? c.sxp[(t.sh ? (int64_t)c.hrows : 0) + t.r0 + r] : 0.0f);
         const float* sw = t.sh ? w.sws13 : w.sw13 + (int64_t)e * 2 * c.I;
         const int lj = threadIdx.x & 31;
 #pragma unroll
@@ -1982,7 +1982,7 @@ __device__ __forceinline__ void gemm_prologue(const GemmTile& t, char* smem, int
 // Tile boundary, between the last depth step of the current tile and its
 // epilogue: once every wave is done with the ring, resolve the next tile and
 // set it up (its first loads are issued during the epilogue).
-template <int MODE>
+template <int MODE, bool F8>
 __device__ __forceinline__ void gemm_boundary(const DevCtx& c, const Weights& w, GemmSched& sc, char* smem, int tid,
                                               int wid, int lrow, uint32_t lcx, int& next, GemmTile& tn) {
     int* slot = (int*)(smem + kStages * kStageBytes);
@@ -1994,7 +1994,7 @@ __device__ __forceinline__ void gemm_boundary(const DevCtx& c, const Weights& w,
     }
     __syncthreads();
     next = __builtin_amdgcn_readfirstlane(*slot);
-    if (next >= 0) gemm_setup<MODE>(c, w, next, wid, lrow, lcx, tn);
+    if (next >= 0) gemm_setup<MODE, F8>(c, w, next, wid, lrow, lcx, tn);
 }
 
 // Word 3 of a raw buffer descriptor on gfx9-family GPUs (32-bit data
@@ -2034,7 +2034,7 @@ __device__ __forceinline__ float agpr(float x) {
 // buffer stores, so the code stays straight-line (a divergent branch would
 // keep every accumulator live across it).  The caller pads the wait states
 // between the last MFMA and the first accumulator read.
-template <int MODE, int NV>
+template <int MODE, int NV, bool F8>
 __device__ __forceinline__ void gemm_epilogue_ib(const f32x16 (&acc)[NV > 0 ? NV : 1][4], const DevCtx& c,
                                                  const GemmTile& t, const char* smem, int lane, int ww, int wx,
                                                  int ib) {
@@ -2045,9 +2045,9 @@ __device__ __forceinline__ void gemm_epilogue_ib(const f32x16 (&acc)[NV > 0 ? NV
         // Column block jb is one 32-deep block of h: rows of 64 bytes.
         const int64_t hrows = t.sh ? c.hsrows : c.hrows;
         char* hb = (char*)(t.sh ? c.hs : c.h);
-        // fp8: the token scales of this lane's rows rb + 8q + i (1 otherwise)
+        // fp8: the token scales of this lane's rows rb + 8q + i
         float dx[4][4];
-        if (c.w1_fp8) {
+        if constexpr (F8) {
             const u32x4* tab = (const u32x4*)(smem + kRetTabOff + t.par * (kBX * 4));
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
@@ -2055,11 +2055,6 @@ __device__ __forceinline__ void gemm_epilogue_ib(const f32x16 (&acc)[NV > 0 ? NV
 #pragma unroll
                 for (int i = 0; i < 4; ++i) dx[q][i] = __uint_as_float(o[i]);
             }
-        } else {
-#pragma unroll
-            for (int q = 0; q < 4; ++q)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) dx[q][i] = 1.0f;
         }
 #pragma unroll
         for (int jb = 0; jb < 2; ++jb) {
@@ -2072,9 +2067,12 @@ __device__ __forceinline__ void gemm_epilogue_ib(const f32x16 (&acc)[NV > 0 ? NV
                 float o[2];
 #pragma unroll
                 for (int q = 0; q < 2; ++q) {
-                    const float sxr = dx[(v + q) >> 2][(v + q) & 3];
-                    const float g = agpr(acc[ib][jb][v + q]) * sxr * t.dw[jb];
-                    const float u = agpr(acc[ib][jb + 2][v + q]) * sxr * t.dw[2 + jb];
+                    float g = agpr(acc[ib][jb][v + q]), u = agpr(acc[ib][jb + 2][v + q]);
+                    if constexpr (F8) {
+                        const float sxr = dx[(v + q) >> 2][(v + q) & 3];
+                        g = g * sxr * t.dw[jb];
+                        u = u * sxr * t.dw[2 + jb];
+                    }
                     o[q] = g * __builtin_amdgcn_rcpf(1.f + __expf(-g)) * u;
                 }
                 const uint32_t pk = pk_bf16(o[0], o[1]);
@@ -2160,7 +2158,7 @@ __device__ __forceinline__ void gemm_run(const DevCtx& c, const Weights& w, Gemm
         for (; kt < t.nk; ++kt) gemm_step<MODE, NV, NX, true>(acc, t, smem, kt, wid, lane, wl, tl, fa, fb);
     }
 
-    gemm_boundary<MODE>(c, w, sc, smem, tid, wid, lrow, lcx, next, tn);
+    gemm_boundary<MODE, F8>(c, w, sc, smem, tid, wid, lrow, lcx, next, tn);
     tn.par = t.par ^ 1;
 
     // Epilogue, token block by token block, with the next tile's first
@@ -2172,22 +2170,16 @@ __device__ __forceinline__ void gemm_run(const DevCtx& c, const Weights& w, Gemm
     for (int ib = 0; ib < (NV > kStages - 1 ? NV : kStages - 1); ++ib) {
         if (ib < kStages - 1 && next >= 0) gemm_prologue_step<MODE>(tn, smem, wid, ib);
         // the next tile's return offsets into its table (its load was issued at set-up)
-        if (ib == 0 && next >= 0 && ((MODE == 2 && c.direct_ret) || (MODE == 1 && c.w1_fp8)))
+        if (ib == 0 && next >= 0 && ((MODE == 2 && c.direct_ret) || F8))
             ((uint32_t*)(smem + kRetTabOff + tn.par * (kBX * 4)))[threadIdx.x] = tn.rofs;
-        if (ib < NV) gemm_epilogue_ib<MODE, NV>(acc, c, t, smem, lane, ww, wx, ib);
+        if (ib < NV) gemm_epilogue_ib<MODE, NV, F8>(acc, c, t, smem, lane, ww, wx, ib);
     }
 }
 
-template <int MODE>
-__global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(DevCtx c, const int* status, Weights w_arg, int layer) {
-    if (*status != AFD_OK) return;
-    // layer < 0: the layer-table entry of the run's layer (checked by k_wait)
-    const Weights w = layer < 0 ? c.wtable[*c.layer_cur] : w_arg;
-    // One LDS array: the operand ring and, past it, the tile-index slot.
-    // (With a second __shared__ variable the compiler attaches alias scopes
-    // to LDS accesses and then makes every LDS read wait for the direct-to-
-    // LDS loads in flight; with one array it does not.)
-    __shared__ __attribute__((aligned(1024))) char smem[kSmemBytes];
+// The tile loop of one workgroup; F8: the gate/up GEMM on e4m3 operands
+// (decided once per launch, so the bf16 loop carries none of it).
+template <int MODE, bool F8>
+__device__ __forceinline__ void gemm_tiles(const DevCtx& c, const Weights& w, char* smem) {
     int* slot = (int*)(smem + kStages * kStageBytes);
     GemmSched sc;
     sc.seg = MODE == 1 ? c.seg1 : c.seg2;
@@ -2225,22 +2217,17 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(DevCtx c, const int* s
     int tile = __builtin_amdgcn_readfirstlane(*slot);
     GemmTile t;
     if (tile >= 0) {
-        gemm_setup<MODE>(c, w, tile, wid, lrow, lcx, t);
+        gemm_setup<MODE, F8>(c, w, tile, wid, lrow, lcx, t);
         gemm_prologue<MODE>(t, smem, wid);
         t.par = 0;
-        if ((MODE == 2 && c.direct_ret) || (MODE == 1 && c.w1_fp8))
-            ((uint32_t*)(smem + kRetTabOff))[threadIdx.x] = t.rofs;
+        if ((MODE == 2 && c.direct_ret) || F8) ((uint32_t*)(smem + kRetTabOff))[threadIdx.x] = t.rofs;
     }
     while (tile >= 0) {
         int next;
         GemmTile tn;
         // this wave's valid token blocks NV = ceil((tb - wx) / 2) and the
         // token-row loads per wave and step NX = ceil(tb / 2)
-#define AFD_RUN(NV, NX)                                                                                          \
-    if (MODE == 1 && c.w1_fp8)                                                                                  \
-        gemm_run<MODE, NV, NX, true>(c, w, sc, t, smem, tid, wid, lane, ww, wx, wl, tl, lrow, lcx, next, tn);  \
-    else                                                                                                        \
-        gemm_run<MODE, NV, NX, false>(c, w, sc, t, smem, tid, wid, lane, ww, wx, wl, tl, lrow, lcx, next, tn)
+#define AFD_RUN(NV, NX) gemm_run<MODE, NV, NX, F8>(c, w, sc, t, smem, tid, wid, lane, ww, wx, wl, tl, lrow, lcx, next, tn)
         switch (t.tb * 2 + wx) {  // key 2 tb + wx -> (NV, NX)
             case 17: case 16: case 14: AFD_RUN(4, 4); break;  // tb 8, tb 7 wx 0
             case 15: AFD_RUN(3, 4); break;                    // tb 7 wx 1
@@ -2257,6 +2244,24 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(DevCtx c, const int* s
     }
     // drain this wave's surplus loads before the workgroup ends
     AFD_WAIT_VMCNT(0);
+}
+
+template <int MODE>
+__global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(DevCtx c, const int* status, Weights w_arg, int layer) {
+    if (*status != AFD_OK) return;
+    // layer < 0: the layer-table entry of the run's layer (checked by k_wait)
+    const Weights w = layer < 0 ? c.wtable[*c.layer_cur] : w_arg;
+    // One LDS array: the operand ring and, past it, the tile-index slot and
+    // the row tables.  (With a second __shared__ variable the compiler
+    // attaches alias scopes to LDS accesses and then makes every LDS read
+    // wait for the direct-to-LDS loads in flight; with one array it does not.)
+    __shared__ __attribute__((aligned(1024))) char smem[kSmemBytes];
+    if constexpr (MODE == 1) {
+        if (c.w1_fp8) gemm_tiles<MODE, true>(c, w, smem);
+        else gemm_tiles<MODE, false>(c, w, smem);
+    } else {
+        gemm_tiles<MODE, false>(c, w, smem);
+    }
 }
 
 // ---------------------------------------------------------------------------
