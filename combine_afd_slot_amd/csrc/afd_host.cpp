@@ -49,10 +49,11 @@ int32_t validate(const afd_window_config* c) {
     if (c->attention_routes != 0 && c->attention_routes != 1)
         return fail(AFD_ERR_INVALID, "attention_routes must be 0 or 1");
     if (c->w1_fp8 != 0 && c->w1_fp8 != 1) return fail(AFD_ERR_INVALID, "w1_fp8 must be 0 or 1");
-    if (c->w1_fp8 && (c->attention_routes || c->hidden % 64))
-        return fail(AFD_ERR_INVALID, "w1_fp8 needs attention_routes = 0 and hidden a multiple of 64");
-    if (c->w1_fp8 && (int64_t)c->num_peers * c->token_cap * c->hidden >= ((int64_t)1 << 32))
-        return fail(AFD_ERR_INVALID, "w1_fp8: num_peers*token_cap*hidden must stay below 4 GiB");
+    if (c->w1_fp8 && c->hidden % 64) return fail(AFD_ERR_INVALID, "w1_fp8 needs hidden a multiple of 64");
+    // quantised rows: one per token, or (attention-routed) one per GEMM row
+    if (c->w1_fp8 && (int64_t)c->num_peers * c->token_cap * (c->attention_routes ? c->top_k + 1 : 1) * c->hidden >=
+                         ((int64_t)1 << 32))
+        return fail(AFD_ERR_INVALID, "w1_fp8: the quantised rows must stay below 4 GiB");
     if (c->route_experts != 0) {
         if (!c->attention_routes) return fail(AFD_ERR_INVALID, "route_experts needs attention_routes = 1");
         if (c->route_experts > afd::kMaxExperts) return fail(AFD_ERR_INVALID, "route_experts above 1024");
@@ -188,7 +189,7 @@ WsLayout ws_layout(const afd_window_config& c) {
     {
         // fp8 W1: quantised token rows and their scales
         const int64_t q = c.w1_fp8 ? 1 : 0;
-        w.xq = take(q * tmax * c.hidden);
+        w.xq = take(q * (c.attention_routes ? np + tmax : tmax) * c.hidden);
         w.sx = take(q * 4 * tmax);
         w.sxp = take(q * 4 * (np + tmax));
     }

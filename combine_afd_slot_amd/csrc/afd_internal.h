@@ -79,7 +79,8 @@ struct DevCtx {
     // expert, the peer keeps the top-k weights and combines on return
     int attn_routes;
     int w1_fp8;        // gate/up GEMMs on e4m3 operands
-    uint8_t* xq;       // [Tmax][H] e4m3 codes of the token rows (fp8 W1)
+    uint8_t* xq;       // [Tmax][H] e4m3 codes of the token rows (fp8 W1); attention-routed:
+                       //   [Tmax*K + Tmax][H], each GEMM row's (pairs, then shared rows)
     float* sx;         // [Tmax]   their dequantisation scales
     float* sxp;        // [Tmax*K + Tmax] the scale of each permuted pair's token row, then of
                        //   each shared row (token t at Tmax*K + t)

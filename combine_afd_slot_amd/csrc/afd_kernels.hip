@@ -1356,6 +1356,47 @@ __global__ __launch_bounds__(256) void k_gdispatch(DevCtx c, int* status, int s)
     }
 }
 
+// fp8 W1 on an attention-routed window: every GEMM row (the grouped pair
+// rows, then the shared rows) quantised like a token row in k_route, one
+// wavefront a row: codes to its own xq row, scale beside it, and the row
+// address pointed there.  Pair rows are copies of their token's row, so
+// they get that row's codes and scale.
+__global__ __launch_bounds__(256) void k_gquant(DevCtx c, const int* status) {
+    const int st = *status;
+    const int T = *c.Tptr;
+    if (st != AFD_OK) return;
+    const int lane = threadIdx.x & 63, n8 = c.H / 8;
+    const int nr = min(T * c.K, c.eoff[c.E]), rows = nr + (c.has_shared ? T : 0);
+    for (int g = (int)blockIdx.x * 4 + (int)(threadIdx.x >> 6); g < rows; g += (int)gridDim.x * 4) {
+        const bool routed = g < nr;
+        const int64_t q = routed ? g : (int64_t)c.hrows + (g - nr);  // its xq / sxp row
+        uint64_t* src = routed ? &c.psrc[g] : &c.sh_src[g - nr];
+        const u32x4* xr = (const u32x4*)*src;
+        float amax = 0.0f;
+        for (int i = lane; i < n8; i += 64) {
+            const u32x4 v8 = xr[i];
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                amax = fmaxf(amax, fmaxf(fabsf(bf2f(v8[j] & 0xffffu)), fabsf(bf2f(v8[j] >> 16))));
+        }
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
+        const float rs = amax > 0.0f ? __fdiv_rn(448.0f, amax) : 0.0f;
+        uint2* dst = (uint2*)(c.xq + q * c.H);
+        for (int i = lane; i < n8; i += 64) {
+            const u32x4 v8 = xr[i];
+            dst[i] = make_uint2(pack4_e4m3(bf2f(v8[0] & 0xffffu) * rs, bf2f(v8[0] >> 16) * rs,
+                                           bf2f(v8[1] & 0xffffu) * rs, bf2f(v8[1] >> 16) * rs),
+                                pack4_e4m3(bf2f(v8[2] & 0xffffu) * rs, bf2f(v8[2] >> 16) * rs,
+                                           bf2f(v8[3] & 0xffffu) * rs, bf2f(v8[3] >> 16) * rs));
+        }
+        if (lane == 0) {
+            c.sxp[q] = amax > 0.0f ? __fdiv_rn(amax, 448.0f) : 1.0f;
+            *src = (uint64_t)(c.xq + q * c.H);
+        }
+    }
+}
+
 // ---------------------------------------------------------------------------
 // a4/a5/a6: grouped GEMMs on MFMA (v_mfma_f32_32x32x16_bf16).
 //
@@ -2431,6 +2472,7 @@ hipError_t launch_ffn(const DevCtx& c, int stage, int layer, const Weights& w, l
         mark();
         mark();
         k_gdispatch<<<c.NB, 256, 0, st>>>(c, status, stage);
+        if (c.w1_fp8) k_gquant<<<num_cu * 4, 256, 0, st>>>(c, status);
     } else {
         if (c.E <= 64) k_route<1><<<c.NB, 64 * kRouteChunk, 0, st>>>(c, status, stage);
         else if (c.E <= 128) k_route<2><<<c.NB, 64 * kRouteChunk, 0, st>>>(c, status, stage);

@@ -154,9 +154,10 @@ typedef struct afd_window afd_window; /* opaque, library-owned */
  * weights are packed, one scale per row (r = 448 / max|x| and code =
  * e4m3(x * r) in fp32, round to nearest even, saturating; the row's value is
  * code * max|x| / 448); products accumulate in fp32 and both scales apply
- * before SwiGLU.  The down GEMM stays bf16.  Needs attention_routes = 0 and
- * hidden a multiple of 64; the packed weights then hold e4m3 gate/up tiles
- * and their row scales (layout.packed_weight_bytes). */
+ * before SwiGLU.  The down GEMM stays bf16.  Needs hidden a multiple of 64;
+ * the packed weights then hold e4m3 gate/up tiles and their row scales
+ * (layout.packed_weight_bytes).  In an attention-routed window the FFN side
+ * quantises each arriving row (copies of a token row get that row's codes). */
 typedef struct afd_window_config {
     uint32_t struct_size;
     int32_t num_peers;           /* P: attention peers fanned in by this FFN replica        */

@@ -112,7 +112,7 @@ def test_slot_fields_disjoint_aligned_viewable(kw):
     dict(route_experts=16), dict(expert_offset=1),
     dict(attention_routes=1, route_experts=1025), dict(attention_routes=1, route_experts=12, expert_offset=5),
     dict(attention_routes=1, route_experts=12, expert_offset=-1),
-    dict(w1_fp8=2), dict(w1_fp8=1, hidden=96), dict(w1_fp8=1, attention_routes=1),
+    dict(w1_fp8=2), dict(w1_fp8=1, hidden=96),
 ])
 
 def test_config_rejected(bad):

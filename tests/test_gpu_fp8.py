@@ -49,3 +49,21 @@ def test_fp8_against_oracle(orc, wl):
         s.step()
         bf = s.outputs_f32()
     assert any(o.size and not np.array_equal(o, bf[p]) for p, o in enumerate(out))
+
+
+@pytest.mark.parametrize("wl", WLS[:3], ids=lambda w: w.name)
+def test_fp8_attention_routed_same_bits(wl):
+    """An attention-routed window quantises each arriving row on the FFN side;
+    pair rows are copies of their token's row, so every GEMM row gets the
+    codes and scale of the FFN-routed path and the outputs are the same bits."""
+    import dataclasses
+    inp = make_inputs(wl)
+    with FfnSession(wl, inp, poll_timeout_us=200_000) as s:
+        s.step()
+        assert s.status().status == 0
+        base = [o.copy() for o in s.outputs_f32()]
+    with FfnSession(dataclasses.replace(wl, attention_routes=1), inp, poll_timeout_us=200_000) as s:
+        s.step()
+        assert s.status().status == 0
+        for p, o in enumerate(s.outputs_f32()):
+            np.testing.assert_array_equal(o, base[p])
