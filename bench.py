@@ -13,8 +13,9 @@ between two launches, so the timed steps carry only those two.)  An untimed
 pass afterwards, with an event between every two kernels, gives the
 per-kernel breakdown.
 
-Prints one JSON line.  Default workload: the prefill shape (2 peers,
-seq_lens [1024, 3072], H=2048, 64 experts, top-6, I=1408, shared 2816).
+Prints one JSON line.  Default workload: the largest one, skewed routing
+over large experts (2 peers x 4096 tokens, H=7168, 256 experts, top-8,
+I=2048, one shared expert of 2048, a Zipf(1.1) per-expert logit bias).
 """
 from __future__ import annotations
 
@@ -59,47 +60,98 @@ def algorithmic(wl, counts):
     }
 
 
+def _variant(wl):
+    return ("_attention_routed" if wl.attention_routes else "") + ("_w1_fp8" if wl.w1_fp8 else "")
+
+
 def measured_traffic(wl, kernel):
     """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
-    summary, or None if it was measured on another workload or on a different
-    kernel source than the one built now."""
+    summary of this workload (profiles/hbm_bytes_<workload>.json), or None
+    if there is none or it was measured on a kernel source other than the
+    one built now."""
     import hashlib
-    path = os.path.join(ROOT, "profiles", "hbm_bytes_prefill_gemm.json")
+    path = os.path.join(ROOT, "profiles", f"hbm_bytes_{wl.name}{_variant(wl)}.json")
     src = os.path.join(ROOT, "combine_afd_slot_amd", "csrc", "afd_kernels.hip")
     try:
         side = json.load(open(path))
         sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
     except OSError:
         return None
-    if wl.attention_routes or wl.w1_fp8 or side.get("workload") != wl.name or side.get("kernel_source_sha256") != sha:
+    if side.get("workload") != wl.name or side.get("kernel_source_sha256") != sha:
         return None
     b = side["bytes_per_launch"].get(kernel)
     return None if b is None else int(b["read"] + b["written"])
 
 
-def cpu_baseline(wl, inp, target_s=15.0):
-    """The oracle as it stands, timed on a bounded prefix sample of each peer."""
-    from oracle import oracle
-    oracle.lib()
-    T = wl.total_tokens
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
-    def run(frac):
-        n = [max(1, int(round(s * frac))) if s else 0 for s in wl.seq_lens]
-        x = [inp["x"][p][:n[p]] for p in range(wl.num_peers)]
-        l = [inp["l"][p][:n[p]] for p in range(wl.num_peers)]
-        t0 = time.perf_counter()
+
+# workloads whose whole oracle run fits the baseline's time budget on the
+# measurement host's cores (about 3 s for decode, 9 s for prefill)
+FULL_ORACLE = ("tiny", "decode", "prefill")
+
+
+def _oracle_run(oracle, wl, inp, n):
+    """One timed oracle pass (steady clock) over the first n[p] tokens of each peer."""
+    x = [inp["x"][p][:n[p]] for p in range(wl.num_peers)]
+    l = [inp["l"][p][:n[p]] for p in range(wl.num_peers)]
+    t0 = time.perf_counter()
+    if wl.w1_fp8:
+        oracle.ffn_fp8(x, l, inp["W13"], inp["W2"], inp.get("Ws13"), inp.get("Ws2"), K=wl.top_k,
+                       rsf=wl.routed_scaling_factor, renorm=wl.renormalize)
+    else:
         oracle.ffn(x, l, inp["W13"], inp["W2"], inp.get("Ws13"), inp.get("Ws2"), K=wl.top_k,
                    rsf=wl.routed_scaling_factor, renorm=wl.renormalize)
-        return sum(n), time.perf_counter() - t0
+    return time.perf_counter() - t0
 
-    frac = min(1.0, 32.0 / T)
-    n, dt = run(frac)
-    if dt < target_s / 4 and frac < 1.0:
-        frac = min(1.0, frac * target_s / max(dt, 1e-3))
-        n, dt = run(frac)
-    return {"value": n / dt, "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
-            "sample": f"first {n} of {T} tokens (each peer's leading {frac:.4f} share), whole oracle path "
-                      f"a1-a7 in float64, {dt:.1f} s"}
+
+def cpu_baseline(wl, inp, target_s=8.0):
+    """The oracle as it stands (float64 C, OpenMP over the host's threads),
+    timed on this workload's inputs: the median of 3 runs, over every token
+    where that fits the budget, else over a labelled prefix sample of each
+    peer; plus 1-thread times of the whole oracle on the tiny and decode
+    workloads."""
+    from oracle import oracle
+    from combine_afd_slot_amd.inputs import WORKLOADS, make_inputs
+    oracle.lib()
+    T = wl.total_tokens
+    threads = oracle.num_threads()
+    if wl.name in FULL_ORACLE and not wl.w1_fp8:
+        n = list(wl.seq_lens)
+        label = f"every token ({T}), whole oracle path a1-a7 in float64"
+    else:
+        frac = min(1.0, 32.0 / T)
+        n = [max(1, int(round(v * frac))) if v else 0 for v in wl.seq_lens]
+        dt = _oracle_run(oracle, wl, inp, n)
+        if dt < target_s and frac < 1.0:
+            frac = min(1.0, frac * target_s / max(dt, 1e-3))
+            n = [max(1, int(round(v * frac))) if v else 0 for v in wl.seq_lens]
+        label = (f"first {sum(n)} of {T} tokens (each peer's leading {frac:.4f} share), whole oracle path "
+                 f"a1-a7 in float64" + (" with the fp8 W1 operands" if wl.w1_fp8 else ""))
+    runs = sorted(_oracle_run(oracle, wl, inp, n) for _ in range(3))
+    med = runs[1]
+    one = {}
+    oracle.set_threads(1)
+    try:
+        for name in ("tiny", "decode"):
+            w1 = WORKLOADS[name]
+            i1 = inp if w1.name == wl.name and not wl.w1_fp8 else make_inputs(w1)
+            reps = 3 if name == "tiny" else 1
+            ts = sorted(_oracle_run(oracle, w1, i1, list(w1.seq_lens)) for _ in range(reps))
+            one[name] = {"tokens_per_s": round(w1.total_tokens / ts[len(ts) // 2], 2),
+                         "runs": reps, "s": round(ts[len(ts) // 2], 4)}
+    finally:
+        oracle.set_threads(threads)
+    return {"value": round(sum(n) / med, 2), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": label, "runs_s": [round(r, 3) for r in runs], "stat": "median of 3",
+            "nproc": os.cpu_count(), "cpu_model": _cpu_model(), "one_thread_whole_oracle": one}
 
 
 def peer_side_ms(torch, sess, n):
@@ -133,7 +185,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="prefill")
+    ap.add_argument("--workload", default="skew",
+                    help="tiny | prefill | fanin4 | skew | decode (default: skew, the largest workload)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-profile", action="store_true", help="no per-kernel events (pure step timing)")
     ap.add_argument("--attention-routes", action="store_true",
@@ -278,7 +331,7 @@ def main():
                                 "peak": HBM_PEAK_GBS, "unit": "GB/s",
                                 "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": measured_traffic(wl, dom)}
     if not args.no_cpu_baseline:
-        log("[bench] timing the CPU oracle on a bounded sample")
+        log("[bench] timing the CPU oracle (median of 3)")
         line["cpu_baseline"] = cpu_baseline(wl, inp)
     print(json.dumps(line), flush=True)
 

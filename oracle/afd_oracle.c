@@ -513,6 +513,8 @@ double oracle_e4m3_decode(uint8_t c) {
  * and zero codes.  codes: [n][H]; d: [n]; deq: [n][H] (either may be NULL). */
 int oracle_quant_rows(int64_t n, int64_t H, const uint16_t* x, uint8_t* codes, float* d, double* deq) {
     if (n < 0 || H < 1 || !x) return ORC_ERR_ARG;
+    /* rows are independent: threads take whole rows */
+#pragma omp parallel for schedule(static)
     for (int64_t i = 0; i < n; ++i) {
         const uint16_t* row = x + i * H;
         float amax = 0.0f;
@@ -600,6 +602,67 @@ int oracle_token_rows_d(int64_t T, int64_t H, int E, int K, int64_t I, int64_t I
         }
         free(act);
         free(y);
+    }
+    return bad ? ORC_ERR_ARG : ORC_OK;
+}
+
+/* ---------------------------------------------------------------------------
+ * The fp8 W1 path grouped by expert, as oracle_experts / oracle_shared are
+ * for bf16: expert e runs over its dispatch group [expert_offsets[e],
+ * expert_offsets[e+1]) with the double gate/up operands (the dequantised
+ * fp8 rows) and bf16 W2.  Each row is the swiglu_row_d of oracle_token_rows_d
+ * on the same operands, so for the same routing the combined rows equal that
+ * routine's rows; it exists because walking the experts one group at a time
+ * keeps an expert's weights hot while its rows run, which the full-size
+ * workloads need.
+ *   Xd: [T][H]; W13d: [E][2I][H]; W2: [E][H][I] bf16; Y: [T*K][H].
+ * ------------------------------------------------------------------------- */
+int oracle_experts_d(int64_t T, int64_t H, int E, int K, int64_t I, const double* Xd,
+                     const int32_t* expert_offsets, const int32_t* perm,
+                     const double* W13d, const uint16_t* W2, double* Y) {
+    if (T < 0 || H < 1 || E < 1 || K < 1 || I < 1 || !Xd || !expert_offsets || !perm || !W13d || !W2 || !Y)
+        return ORC_ERR_ARG;
+    int bad = 0;
+    for (int e = 0; e < E; ++e) {
+        const double* w13 = W13d + (int64_t)e * 2 * I * H;
+        const uint16_t* w2 = W2 + (int64_t)e * H * I;
+        int64_t lo = expert_offsets[e], hi = expert_offsets[e + 1];
+#pragma omp parallel
+        {
+            double* act = (double*)malloc(sizeof(double) * (size_t)I);
+            if (!act) {
+#pragma omp atomic write
+                bad = 1;
+            } else {
+#pragma omp for schedule(dynamic, 1)
+                for (int64_t i = lo; i < hi; ++i) {
+                    int64_t t = perm[i] / K;
+                    swiglu_row_d(H, I, Xd + t * H, w13, w2, act, Y + i * H);
+                }
+                free(act);
+            }
+        }
+    }
+    return bad ? ORC_ERR_ARG : ORC_OK;
+}
+
+/* The shared expert on the double gate/up operands (Ws13d [2Is][H], bf16
+ * Ws2 [H][Is]) over every row of Xd [T][H]; S: [T][H]. */
+int oracle_shared_d(int64_t T, int64_t H, int64_t Is, const double* Xd, const double* Ws13d,
+                    const uint16_t* Ws2, double* S) {
+    if (T < 0 || H < 1 || Is < 1 || !Xd || !Ws13d || !Ws2 || !S) return ORC_ERR_ARG;
+    int bad = 0;
+#pragma omp parallel
+    {
+        double* act = (double*)malloc(sizeof(double) * (size_t)Is);
+        if (!act) {
+#pragma omp atomic write
+            bad = 1;
+        } else {
+#pragma omp for schedule(dynamic, 1)
+            for (int64_t t = 0; t < T; ++t) swiglu_row_d(H, Is, Xd + t * H, Ws13d, Ws2, act, S + t * H);
+            free(act);
+        }
     }
     return bad ? ORC_ERR_ARG : ORC_OK;
 }

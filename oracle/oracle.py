@@ -64,6 +64,8 @@ def lib():
         L.oracle_quant_rows.argtypes = [i64, i64, P, P, P, P]
         L.oracle_token_rows_d.argtypes = [i64, i64, i32, i32, i64, i64, dbl, i32, P, P, P, P, P, P,
                                           i64, P, P, P, P]
+        L.oracle_experts_d.argtypes = [i64, i64, i32, i32, i64, P, P, P, P, P, P]
+        L.oracle_shared_d.argtypes = [i64, i64, i64, P, P, P, P]
         L.oracle_num_threads.restype = ctypes.c_int
         L.oracle_set_threads.argtypes = [i32]
         _lib = L
@@ -268,14 +270,58 @@ def token_rows_d(Xd, L, tokens, W13d, W2, Ws13d=None, Ws2=None, K=2, rsf=1.0, re
     return out, ids, w
 
 
-def ffn_fp8(x, l, W13, W2, Ws13=None, Ws2=None, K=2, rsf=1.0, renorm=1):
-    """The whole path with the gate/up GEMMs on e4m3 operands (token rows and
-    W13 / Ws13 rows quantised per row), every token; per-peer outputs."""
+def experts_d(Xd, eoff, perm, K, W13d, W2):
+    """oracle experts (grouped by expert) on double gate/up operands."""
+    Xd = np.ascontiguousarray(Xd, dtype=np.float64)
+    T, H = Xd.shape
+    E = W13d.shape[0]
+    I = W13d.shape[1] // 2
+    Y = np.zeros((T * K, H), dtype=np.float64)
+    _check(lib().oracle_experts_d(T, H, E, K, I, _p(Xd), _p(np.ascontiguousarray(eoff, np.int32)),
+                                  _p(np.ascontiguousarray(perm, np.int32)),
+                                  _p(np.ascontiguousarray(W13d, np.float64)), _p(np.ascontiguousarray(W2)), _p(Y)),
+           "experts_d")
+    return Y
+
+
+def shared_d(Xd, Ws13d, Ws2):
+    """oracle shared expert on double gate/up operands."""
+    Xd = np.ascontiguousarray(Xd, dtype=np.float64)
+    T, H = Xd.shape
+    Is = Ws13d.shape[0] // 2
+    S = np.zeros((T, H), dtype=np.float64)
+    _check(lib().oracle_shared_d(T, H, Is, _p(Xd), _p(np.ascontiguousarray(Ws13d, np.float64)),
+                                 _p(np.ascontiguousarray(Ws2)), _p(S)), "shared_d")
+    return S
+
+
+def _fp8_operands(x, W13, Ws13):
     X = np.concatenate([np.asarray(a, np.uint16).reshape(-1, W13.shape[2]) for a in x])
-    Lc = np.concatenate([np.asarray(a, np.float32).reshape(-1, W13.shape[0]) for a in l])
     _, _, Xd = quant_rows(X)
     _, _, W13d = quant_rows(W13)
     Ws13d = None if Ws13 is None else quant_rows(Ws13)[2]
-    out, _, _ = token_rows_d(Xd, Lc, np.arange(X.shape[0]), W13d, W2, Ws13d, Ws2, K=K, rsf=rsf, renorm=renorm)
+    return Xd, W13d, Ws13d
+
+
+def ffn_fp8(x, l, W13, W2, Ws13=None, Ws2=None, K=2, rsf=1.0, renorm=1):
+    """The whole path with the gate/up GEMMs on e4m3 operands (token rows and
+    W13 / Ws13 rows quantised per row): route, dispatch, the experts one
+    dispatch group at a time, the shared expert, combine; per-peer outputs."""
+    Xd, W13d, Ws13d = _fp8_operands(x, W13, Ws13)
+    Lc = np.concatenate([np.asarray(a, np.float32).reshape(-1, W13.shape[0]) for a in l])
+    ids, w = route(Lc, K, renorm)
+    _, eoff, perm, inv = dispatch(ids, W13.shape[0])
+    Y = experts_d(Xd, eoff, perm, K, W13d, W2)
+    S = None if Ws13d is None else shared_d(Xd, Ws13d, Ws2)
+    out = combine(w, inv, Y, S, rsf)
+    off = np.concatenate([[0], np.cumsum([np.asarray(a).shape[0] for a in x])])
+    return [out[off[p]:off[p + 1]] for p in range(len(x))]
+
+
+def ffn_fp8_tokens(x, l, W13, W2, Ws13=None, Ws2=None, K=2, rsf=1.0, renorm=1):
+    """ffn_fp8 one token at a time (token_rows_d over every token)."""
+    Xd, W13d, Ws13d = _fp8_operands(x, W13, Ws13)
+    Lc = np.concatenate([np.asarray(a, np.float32).reshape(-1, W13.shape[0]) for a in l])
+    out, _, _ = token_rows_d(Xd, Lc, np.arange(Xd.shape[0]), W13d, W2, Ws13d, Ws2, K=K, rsf=rsf, renorm=renorm)
     off = np.concatenate([[0], np.cumsum([np.asarray(a).shape[0] for a in x])])
     return [out[off[p]:off[p + 1]] for p in range(len(x))]

@@ -67,3 +67,75 @@ def test_fp8_attention_routed_same_bits(wl):
         assert s.status().status == 0
         for p, o in enumerate(s.outputs_f32()):
             np.testing.assert_array_equal(o, base[p])
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name", ["decode", "prefill"])
+def test_fp8_full_size_every_row(orc, name):
+    """The fp8 W1 path on the full-size decode and prefill workloads: every
+    output row against the oracle's fp8 path."""
+    import dataclasses
+    from combine_afd_slot_amd.inputs import WORKLOADS
+    wl = dataclasses.replace(WORKLOADS[name], w1_fp8=1)
+    say(f"[fp8-full] {name}: generating inputs")
+    inp = make_inputs(wl)
+    with FfnSession(wl, inp) as s:
+        say(f"[fp8-full] {name}: GPU run")
+        s.step()
+        st = s.status()
+        assert st.status == 0 and st.total_tokens == wl.total_tokens
+        out = [o.copy() for o in s.outputs_f32()]
+    say(f"[fp8-full] {name}: oracle fp8 path on all {wl.total_tokens} tokens")
+    ref = orc.ffn_fp8(inp["x"], inp["l"], inp["W13"], inp["W2"], inp.get("Ws13"), inp.get("Ws2"), K=wl.top_k,
+                      rsf=wl.routed_scaling_factor, renorm=wl.renormalize)
+    errs = [row_rel_err(o, ref[p]) for p, o in enumerate(out)]
+    say(f"[fp8-full] {name}: max row rel err {max(errs):.3e} over all {wl.total_tokens} rows")
+    assert max(errs) <= ROW_REL_TOL
+
+
+@pytest.mark.parametrize("F,shared_rank", [(2, 1), (4, 0)])
+def test_fp8_expert_segments_same_bits(F, shared_rank):
+    """fp8 W1 on attention-routed windows split into F expert segments: each
+    rank's FFN side quantises only the rows of its experts (its row count
+    comes from its group lists), and the sender's combine over the ranks
+    gives the FFN-routed fp8 run's outputs bit for bit."""
+    import dataclasses
+    from combine_afd_slot_amd import afd
+    wl = WLS[2]  # 40 experts, top-6, ragged lengths, Zipf bias
+    E, H = wl.num_experts, wl.hidden
+    El = E // F
+    inp = make_inputs(wl)
+    with FfnSession(wl, inp, poll_timeout_us=200_000) as s:
+        s.step()
+        assert s.status().status == 0
+        base = [o.copy() for o in s.outputs_f32()]
+    sess = []
+    try:
+        for r in range(F):
+            rwl = dataclasses.replace(wl, attention_routes=1, num_experts=El, route_experts=E, expert_offset=r * El,
+                                      shared_intermediate=wl.shared_intermediate if r == shared_rank else 0)
+            rinp = dict(inp, W13=inp["W13"][r * El:(r + 1) * El], W2=inp["W2"][r * El:(r + 1) * El])
+            if r != shared_rank:
+                rinp["Ws13"] = rinp["Ws2"] = None
+            sess.append(FfnSession(rwl, rinp, poll_timeout_us=200_000))
+        for x in sess:
+            x.pack_all()
+        for x in sess:
+            x.run()
+            x.ffn_stream.synchronize()
+            assert x.status().status == 0
+        torch = sess[0].torch
+        out = [torch.empty((n, H), dtype=torch.bfloat16, device=sess[0].dev) for n in wl.seq_lens]
+        wins = [x.win for x in sess]
+        for p, n in enumerate(wl.seq_lens):
+            afd.afd_slot_unpack_ranks(wins, p, 0, n, out[p].data_ptr() if n else 0,
+                                      sess[0].peer_streams[p].cuda_stream)
+        for ps in sess[0].peer_streams:
+            ps.synchronize()
+        for p, o in enumerate(out):
+            for x in sess:
+                assert x.peer_status(p).status == 0
+            np.testing.assert_array_equal(o.float().cpu().numpy(), base[p])
+    finally:
+        for x in sess:
+            x.close()

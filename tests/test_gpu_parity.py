@@ -2,10 +2,10 @@
 
 Routing ids, per-expert counts and offsets, the dispatch permutation and its
 inverse, and the split offsets must match bit for bit; outputs within 2e-2
-per-row relative error.  Small workloads are checked on every output row;
-the full-size workloads on every routing artefact and on sampled output
-rows that the oracle computes one token at a time; the full-size inputs also
-go through an attention-routed window, whose outputs must be the same bits.
+per-row relative error.  Every output row is compared, on the small
+workloads and on the four full-size ones (the skew workload one peer at a
+time); the full-size inputs also go through an attention-routed window,
+whose outputs must be the same bits.
 """
 import dataclasses
 
@@ -88,53 +88,79 @@ def test_ties_and_negative_zero(orc):
         check_routing(s.routing(), ref, wl)
 
 
-def _sampled_tokens(wl, per_peer=4):
-    off = np.concatenate([[0], np.cumsum(wl.seq_lens)])
-    rng = np.random.default_rng(7)
-    tok = []
-    for p in range(wl.num_peers):
-        n = wl.seq_lens[p]
-        if n == 0:
-            continue
-        pick = {off[p], off[p + 1] - 1}
-        pick.update(int(off[p] + v) for v in rng.integers(0, n, per_peer))
-        tok.extend(sorted(pick))
-    return np.array(tok, dtype=np.int64)
-
-
-@pytest.mark.timeout(900)
-@pytest.mark.parametrize("name", ["decode", "prefill", "fanin4", "skew"])
-def test_full_size_sampled(orc, name):
-    wl = WORKLOADS[name]
-    say(f"[parity-full] {name}: generating inputs")
-    inp = make_inputs(wl, progress=lambda what: say(f"[parity-full] {name}: drawing {what}"))
-    say(f"[parity-full] {name}: oracle routing + dispatch on all {wl.total_tokens} tokens")
-    ids, w = orc.route(inp["L"], wl.top_k, wl.renormalize)
-    counts, eoff, perm, inv = orc.dispatch(ids, wl.num_experts)
-    ref = {"ids": ids, "w": w, "counts": counts, "expert_offsets": eoff, "perm": perm, "inv": inv}
-    tok = _sampled_tokens(wl)
-    say(f"[parity-full] {name}: oracle output rows for {len(tok)} sampled tokens")
-    out_ref, ids_t, _ = orc.token_rows(inp["X"], inp["L"], tok, inp["W13"], inp["W2"], inp.get("Ws13"),
-                                       inp.get("Ws2"), K=wl.top_k, rsf=wl.routed_scaling_factor,
-                                       renorm=wl.renormalize)
-    np.testing.assert_array_equal(ids_t, ids[tok])
-    say(f"[parity-full] {name}: GPU run")
-    # the same inputs through an attention-routed window too (the peers route
-    # and combine): its outputs must be the same bits
+def _gpu_full_size(wl, inp, name):
+    """One FFN-routed run and one attention-routed run of the same inputs;
+    returns (routing artefacts, FFN-routed outputs per peer as float32).
+    The attention-routed outputs must be the same bits."""
     with FfnSession(wl, inp) as s, FfnSession(dataclasses.replace(wl, attention_routes=1), inp) as sa:
-        del inp["W13"], inp["W2"]
+        say(f"[parity-full] {name}: GPU run")
         s.step()
         st = s.status()
-        assert st.status == 0 and st.total_tokens == wl.total_tokens
-        check_routing(s.routing(), ref, wl)
-        out = np.concatenate(s.outputs_f32())
-        err = row_rel_err(out[tok], out_ref)
-        say(f"[parity-full] {name}: max row rel err {err:.3e} over {len(tok)} rows")
-        assert err <= ROW_REL_TOL
-        # properties that hold on every row: finite, and the same scale as the sample
-        assert np.isfinite(out).all()
-        assert 0.25 < np.abs(out).mean() / np.abs(out_ref).mean() < 4.0
+        assert st.status == 0 and st.total_tokens == wl.total_tokens, st.status
+        for p in range(wl.num_peers):
+            assert s.peer_status(p).status == 0
+        routing = s.routing()
+        out = [o.copy() for o in s.outputs_f32()]
         say(f"[parity-full] {name}: attention-routed run")
         sa.step()
         assert sa.status().status == 0
-        np.testing.assert_array_equal(np.concatenate(sa.outputs_f32()), out)
+        for p, o in enumerate(sa.outputs_f32()):
+            np.testing.assert_array_equal(o, out[p])
+    return routing, out
+
+
+def _oracle_routing(orc, wl, inp):
+    ids, w = orc.route(inp["L"], wl.top_k, wl.renormalize)
+    counts, eoff, perm, inv = orc.dispatch(ids, wl.num_experts)
+    return {"ids": ids, "w": w, "counts": counts, "expert_offsets": eoff, "perm": perm, "inv": inv}
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name", ["decode", "prefill", "fanin4"])
+def test_full_size_every_row(orc, name):
+    """Full-size workloads, in the launch configuration the benchmark times:
+    routing artefacts bit-exact on every token, and every output row of every
+    peer within the row tolerance of the whole oracle path."""
+    wl = WORKLOADS[name]
+    say(f"[parity-full] {name}: generating inputs")
+    inp = make_inputs(wl)
+    routing, out = _gpu_full_size(wl, inp, name)
+    check_routing(routing, _oracle_routing(orc, wl, inp), wl)
+    say(f"[parity-full] {name}: oracle on all {wl.total_tokens} tokens")
+    ref = orc.ffn(inp["x"], inp["l"], inp["W13"], inp["W2"], inp.get("Ws13"), inp.get("Ws2"), K=wl.top_k,
+                  rsf=wl.routed_scaling_factor, renorm=wl.renormalize)
+    errs = [row_rel_err(out[p], ref["out_p"][p]) for p in range(wl.num_peers)]
+    say(f"[parity-full] {name}: max row rel err per peer {['%.3e' % e for e in errs]} "
+        f"over all {wl.total_tokens} rows")
+    assert max(errs) <= ROW_REL_TOL
+
+
+@pytest.fixture(scope="module")
+def skew_run(orc):
+    """The skew workload (2 x 4096 tokens, H 7168, 256 experts, top-8, Zipf
+    bias) run once on the GPU for the per-peer oracle checks below."""
+    wl = WORKLOADS["skew"]
+    say("[parity-full] skew: generating inputs")
+    inp = make_inputs(wl)
+    routing, out = _gpu_full_size(wl, inp, "skew")
+    check_routing(routing, _oracle_routing(orc, wl, inp), wl)
+    c = routing["counts"]
+    say(f"[parity-full] skew: expert rows max {c.max()} (expert {int(c.argmax())}), "
+        f"{int((c == 0).sum())} experts empty, {int(((c > 0) & (c < 16)).sum())} with 1-15 rows")
+    yield wl, inp, out
+    out.clear()
+    inp.clear()
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("peer", [0, 1])
+def test_full_size_skew_every_row(orc, skew_run, peer):
+    """Every output row of one skew peer against the oracle run over that
+    peer's tokens alone (each token's row depends on that token only)."""
+    wl, inp, out = skew_run
+    say(f"[parity-full] skew: oracle on peer {peer}'s {wl.seq_lens[peer]} tokens")
+    ref = orc.ffn([inp["x"][peer]], [inp["l"][peer]], inp["W13"], inp["W2"], inp.get("Ws13"), inp.get("Ws2"),
+                  K=wl.top_k, rsf=wl.routed_scaling_factor, renorm=wl.renormalize)
+    err = row_rel_err(out[peer], ref["out"])
+    say(f"[parity-full] skew: peer {peer} max row rel err {err:.3e} over all {wl.seq_lens[peer]} rows")
+    assert err <= ROW_REL_TOL

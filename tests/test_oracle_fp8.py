@@ -97,3 +97,36 @@ def test_fp8_path_close_to_bf16_path():
     for p in range(2):
         rel = np.abs(q[p] - b[p]).max(axis=1) / np.abs(b[p]).max(axis=1)
         assert 0 < rel.max() < 0.15, rel.max()
+
+
+@pytest.mark.parametrize("Is,renorm,rsf", [(48, 1, 1.0), (0, 0, 1.5)])
+def test_grouped_fp8_path_equals_per_token_path(Is, renorm, rsf):
+    """The grouped fp8 path (experts one dispatch group at a time) gives the
+    per-token fp8 routine's rows bit for bit: the same operands and the same
+    order of every sum, with the pairs of each token gathered by the
+    dispatch permutation."""
+    wl = small_workload("fp8_grouped", seq_lens=(23, 0, 40), hidden=96, num_experts=9, top_k=3, intermediate=56,
+                        shared_intermediate=Is, token_cap=48, zipf_bias=0.7)
+    inp = make_inputs(wl)
+    a = orc.ffn_fp8(inp["x"], inp["l"], inp["W13"], inp["W2"], inp.get("Ws13"), inp.get("Ws2"), K=3, rsf=rsf,
+                    renorm=renorm)
+    b = orc.ffn_fp8_tokens(inp["x"], inp["l"], inp["W13"], inp["W2"], inp.get("Ws13"), inp.get("Ws2"), K=3,
+                           rsf=rsf, renorm=renorm)
+    for p in range(wl.num_peers):
+        np.testing.assert_array_equal(a[p], b[p])
+
+
+def test_grouped_double_path_reduces_to_bf16_path():
+    """experts_d / shared_d on the exact bf16 values equal the bf16 grouped
+    routines (experts / shared) bit for bit."""
+    wl = small_workload("fp8_reduce_g", seq_lens=(17, 6), hidden=64, num_experts=6, top_k=2, intermediate=40,
+                        shared_intermediate=24, token_cap=24)
+    inp = make_inputs(wl)
+    f = lambda a: (np.asarray(a, np.uint32) << 16).view(np.float32).astype(np.float64)
+    X = np.concatenate(inp["x"])
+    ids, w = orc.route(np.concatenate(inp["l"]), 2)
+    _, eoff, perm, _ = orc.dispatch(ids, wl.num_experts)
+    np.testing.assert_array_equal(orc.experts_d(f(X), eoff, perm, 2, f(inp["W13"]), inp["W2"]),
+                                  orc.experts(X, eoff, perm, 2, inp["W13"], inp["W2"]))
+    np.testing.assert_array_equal(orc.shared_d(f(X), f(inp["Ws13"]), inp["Ws2"]),
+                                  orc.shared(X, inp["Ws13"], inp["Ws2"]))
