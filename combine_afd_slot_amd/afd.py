@@ -30,12 +30,13 @@ AFD_ERR_DEVICE = -8
 AFD_FLAG_SHUTDOWN = 0x2
 AFD_NUM_FIELDS = 5
 AFD_PROFILE_SLOTS = 8
+AFD_STATIC_WINDOW_BYTES = 32 << 20  # the static window of afd_window_create_static
 FIELDS = ("header", "route_table", "routed_x", "shared_idx", "shared_x")
 HDR_WORDS = 12
 
 # Every symbol include/afd.h declares.
 EXPORTS = (
-    "afd_layout_compute", "afd_window_create", "afd_window_destroy", "afd_window_layout",
+    "afd_layout_compute", "afd_window_create", "afd_window_create_static", "afd_window_destroy", "afd_window_layout",
     "afd_slot_pack", "afd_weights_pack", "afd_ffn_run", "afd_ffn_run_ready", "afd_layer_table_set", "afd_ffn_run_table",
     "afd_ffn_loop_create", "afd_ffn_loop_launch", "afd_ffn_loop_destroy", "afd_ffn_serve", "afd_ffn_serve_result",
     "afd_slot_unpack", "afd_slot_unpack_ranks", "afd_window_status", "afd_peer_status",
@@ -101,6 +102,7 @@ def lib():
         sig = {
             "afd_layout_compute": [P(WindowConfig), P(Layout)],
             "afd_window_create": [P(WindowConfig), P(vp)],
+            "afd_window_create_static": [P(WindowConfig), P(vp)],
             "afd_window_destroy": [vp],
             "afd_window_layout": [vp, P(Layout)],
             "afd_slot_pack": [vp, i32, i32, i32, i32, vp, vp, u32, vp],
@@ -179,6 +181,13 @@ def afd_layout_compute(cfg: WindowConfig) -> Layout:
 def afd_window_create(cfg: WindowConfig) -> int:
     h = ctypes.c_void_p()
     _check(lib().afd_window_create(ctypes.byref(cfg), ctypes.byref(h)))
+    return h.value
+
+
+def afd_window_create_static(cfg: WindowConfig) -> int:
+    """afd_window_create in the library's static device array (no allocation)."""
+    h = ctypes.c_void_p()
+    _check(lib().afd_window_create_static(ctypes.byref(cfg), ctypes.byref(h)))
     return h.value
 
 

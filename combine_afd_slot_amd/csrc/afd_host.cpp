@@ -260,9 +260,12 @@ struct afd_window {
     long long ticks_per_us = 100;
     char* base = nullptr;
     afd::DevCtx ctx{};
-    std::vector<int32_t> pack_seq;    // [P*R] last seq sent by the peer (host side of the peer)
-    std::vector<int32_t> packed_len;  // [P*R]
-    std::vector<uint8_t> inflight;    // [P*R]
+    // per (peer, stage) = p * ring_depth + s; fixed arrays, so that a window
+    // needs no host allocation beyond its handle
+    int32_t pack_seq[afd::kMaxPeers * afd::kMaxRing] = {};    // last seq sent by the peer (host side of the peer)
+    int32_t packed_len[afd::kMaxPeers * afd::kMaxRing] = {};
+    uint8_t inflight[afd::kMaxPeers * afd::kMaxRing] = {};
+    bool is_static = false;  // placed in the library's static device array (afd_window_create_static)
     int profile = 0;  // 0 off, 1 every kernel, 2 the two GEMMs, 3 the gate/up GEMM
     hipEvent_t ev[AFD_PROFILE_SLOTS + 1] = {};
     bool ev_pending = false;
@@ -412,6 +415,52 @@ afd::Weights packed_weights_of(const afd_window_config& c, const void* packed) {
 
 }  // namespace
 
+namespace {
+
+// Device properties, the layout and the zeroed control words of a window
+// whose memory (lay.total_bytes at base) is in place.
+int32_t window_init(afd_window* w, const afd_window_config* cfg, char* base, hipStream_t zero_stream) {
+    const afd_layout& L = w->lay;
+    (void)hipDeviceGetAttribute(&w->num_cu, hipDeviceAttributeMultiprocessorCount, w->device);
+    if (w->num_cu < 1) w->num_cu = 1;
+    int khz = 0;
+    if (hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, w->device) == hipSuccess && khz > 0)
+        w->ticks_per_us = khz / 1000 > 0 ? khz / 1000 : 1;
+    w->base = base;
+    // Flags, mirrors and status words start at zero; the slots are left as
+    // they are (a slot is only read after its flag announces it).  A fill
+    // kernel, not a memset, so that no memset node is ever recorded.
+    hipError_t e = afd::launch_zero(base + L.in_off, L.in_slots_off - L.in_off, zero_stream);
+    if (e == hipSuccess) e = afd::launch_zero(base + L.ret_off, L.ret_slots_off - L.ret_off, zero_stream);
+    if (e == hipSuccess)
+        e = afd::launch_zero(base + L.workspace_off + w->wl.ctrl, 4 * w->wl.ctrl_ints, zero_stream);
+    if (e == hipSuccess) e = hipStreamSynchronize(zero_stream);
+    if (e != hipSuccess) return hip_fail(e, "window init");
+    fill_ctx(w);
+    const char* lg = getenv("AFD_LOG");
+    if (lg && lg[0] == '1')
+        fprintf(stderr, "[afd] window%s: P=%d R=%d token_cap=%d slot=%lld B window=%lld B workspace=%lld B total=%lld B\n",
+                w->is_static ? " (static)" : "", cfg->num_peers, cfg->ring_depth, cfg->token_cap,
+                (long long)L.slot_bytes, (long long)L.window_bytes, (long long)L.workspace_bytes,
+                (long long)L.total_bytes);
+    return AFD_OK;
+}
+
+// ---------------------------------------------------------------------------
+// The allocation-free window (afd_window_create_static).  One static device
+// array per GPU the library runs on, held until the process ends; in host
+// code `scratch` names a host-side stand-in, so its device address is looked
+// up once per device (with that device current) and only that address is
+// used: kernel arguments and fills take g_scratch[d].
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) char scratch[AFD_STATIC_WINDOW_BYTES];
+std::mutex g_static_mu;
+char* g_scratch[kMaxDevices] = {};                 // device address of `scratch`, per device
+bool g_static_busy[kMaxDevices] = {};              // a static window of that device is open
+alignas(afd_window) unsigned char g_static_handle[kMaxDevices][sizeof(afd_window)];
+
+}  // namespace
+
 extern "C" {
 
 int32_t afd_abi_version(void) { return AFD_ABI_VERSION; }
@@ -456,6 +505,7 @@ int32_t afd_header_decode(const int32_t* words, int32_t nwords, int32_t expect_c
     return AFD_OK;
 }
 
+
 int32_t afd_window_create(const afd_window_config* cfg, afd_window** out) {
     if (!out) return fail(AFD_ERR_INVALID, "out is NULL");
     *out = nullptr;
@@ -470,39 +520,59 @@ int32_t afd_window_create(const afd_window_config* cfg, afd_window** out) {
         delete w;
         return hip_fail(e, "hipGetDevice");
     }
-    (void)hipDeviceGetAttribute(&w->num_cu, hipDeviceAttributeMultiprocessorCount, w->device);
-    if (w->num_cu < 1) w->num_cu = 1;
-    int khz = 0;
-    if (hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, w->device) == hipSuccess && khz > 0)
-        w->ticks_per_us = khz / 1000 > 0 ? khz / 1000 : 1;
-    e = hipMalloc((void**)&w->base, (size_t)w->lay.total_bytes);
+    char* base = nullptr;
+    e = hipMalloc((void**)&base, (size_t)w->lay.total_bytes);
     if (e != hipSuccess) {
         delete w;
         return hip_fail(e, "hipMalloc(window)");
     }
-    // Flags, mirrors and status words start at zero; the slots are left as
-    // they are (a slot is only read after its flag announces it).
-    const afd_layout& L = w->lay;
-    e = hipMemset(w->base + L.in_off, 0, (size_t)(L.in_slots_off - L.in_off));
-    if (e == hipSuccess) e = hipMemset(w->base + L.ret_off, 0, (size_t)(L.ret_slots_off - L.ret_off));
-    if (e == hipSuccess) e = hipMemset(w->base + L.workspace_off + w->wl.ctrl, 0, (size_t)(4 * w->wl.ctrl_ints));
-    if (e == hipSuccess) e = hipDeviceSynchronize();
-    if (e != hipSuccess) {
-        (void)hipFree(w->base);
+    rc = window_init(w, cfg, base, nullptr);
+    if (rc) {
+        (void)hipFree(base);
         delete w;
-        return hip_fail(e, "window init");
+        return rc;
     }
-    const int pr = cfg->num_peers * cfg->ring_depth;
-    w->pack_seq.assign(pr, 0);
-    w->packed_len.assign(pr, 0);
-    w->inflight.assign(pr, 0);
-    fill_ctx(w);
     for (int i = 0; i <= AFD_PROFILE_SLOTS; ++i) (void)hipEventCreate(&w->ev[i]);
-    const char* lg = getenv("AFD_LOG");
-    if (lg && lg[0] == '1')
-        fprintf(stderr, "[afd] window: P=%d R=%d token_cap=%d slot=%lld B window=%lld B workspace=%lld B total=%lld B\n",
-                cfg->num_peers, cfg->ring_depth, cfg->token_cap, (long long)L.slot_bytes, (long long)L.window_bytes,
-                (long long)L.workspace_bytes, (long long)L.total_bytes);
+    *out = w;
+    return AFD_OK;
+}
+
+int32_t afd_window_create_static(const afd_window_config* cfg, afd_window** out) {
+    if (!out) return fail(AFD_ERR_INVALID, "out is NULL");
+    *out = nullptr;
+    int32_t rc = validate(cfg);
+    if (rc) return rc;
+    afd_layout lay;
+    WsLayout wl;
+    layout_from(*cfg, &lay, &wl);
+    if (lay.total_bytes > (int64_t)AFD_STATIC_WINDOW_BYTES)
+        return fail(AFD_ERR_CAPACITY, "window needs %lld bytes, more than the %lld of the static window",
+                    (long long)lay.total_bytes, (long long)AFD_STATIC_WINDOW_BYTES);
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (dev < 0 || dev >= kMaxDevices) return fail(AFD_ERR_INVALID, "device %d out of range", dev);
+    std::lock_guard<std::mutex> g(g_static_mu);
+    if (g_static_busy[dev])
+        return fail(AFD_ERR_INVALID, "the static window of device %d is open: destroy it first", dev);
+    if (!g_scratch[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p) return hip_fail(e != hipSuccess ? e : hipErrorInvalidSymbol, "hipGetSymbolAddress(scratch)");
+        g_scratch[dev] = (char*)p;
+    }
+    afd_window* w = new (g_static_handle[dev]) afd_window();
+    w->cfg = *cfg;
+    w->lay = lay;
+    w->wl = wl;
+    w->device = dev;
+    w->is_static = true;
+    rc = window_init(w, cfg, g_scratch[dev], nullptr);
+    if (rc) {
+        w->~afd_window();
+        return rc;
+    }
+    g_static_busy[dev] = true;
     *out = w;
     return AFD_OK;
 }
@@ -513,11 +583,18 @@ int32_t afd_window_destroy(afd_window* w) {
     if (w->base) {
         hipError_t e = hipDeviceSynchronize();
         if (e != hipSuccess) rc = hip_fail(e, "hipDeviceSynchronize");
-        (void)hipFree(w->base);
+        if (!w->is_static) (void)hipFree(w->base);
     }
     for (int i = 0; i <= AFD_PROFILE_SLOTS; ++i)
         if (w->ev[i]) (void)hipEventDestroy(w->ev[i]);
-    delete w;
+    if (w->is_static) {
+        std::lock_guard<std::mutex> g(g_static_mu);
+        const int dev = w->device;
+        w->~afd_window();
+        g_static_busy[dev] = false;
+    } else {
+        delete w;
+    }
     return rc;
 }
 
@@ -903,6 +980,7 @@ int32_t afd_debug_write(afd_window* w, int64_t offset, int64_t bytes, const void
 int32_t afd_profile_enable(afd_window* w, int32_t on) {
     if (!w) return fail(AFD_ERR_INVALID, "window is NULL");
     if (on < 0 || on > 3) return fail(AFD_ERR_INVALID, "profile mode must be 0, 1, 2 or 3");
+    if (on && w->is_static) return fail(AFD_ERR_INVALID, "a static window has no profiling events");
     std::lock_guard<std::mutex> g(w->prof_mu);
     prof_collect(w);
     w->profile = on;

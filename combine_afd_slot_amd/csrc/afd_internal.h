@@ -15,6 +15,7 @@ namespace afd {
 constexpr int kRouteChunk = 16;
 constexpr int kMaxTopK = 16;
 constexpr int kMaxPeers = 64;
+constexpr int kMaxRing = 4;      // ring_depth limit (stages in flight per peer)
 constexpr int kMaxLayers = 1024;  // entries of the device layer table
 constexpr int kMaxExperts = 1024;
 
@@ -176,5 +177,7 @@ hipError_t launch_ffn(const DevCtx& c, int stage, int layer, const Weights& w, l
                       int num_cu, hipEvent_t* ev, hipStream_t st, int max_take = 0, long long gather_ticks = 0,
                       int serve_item = -1);
 hipError_t launch_serve_begin(const DevCtx& c, hipStream_t st);
+// Zero `bytes` bytes (a multiple of 4) at p on st with a fill kernel.
+hipError_t launch_zero(void* p, int64_t bytes, hipStream_t st);
 
 }  // namespace afd

@@ -2446,6 +2446,20 @@ __global__ void k_serve_begin(DevCtx c) {
     }
 }
 
+__global__ __launch_bounds__(256) void k_zero(uint32_t* p, int64_t n) {
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) p[i] = 0u;
+}
+
+hipError_t launch_zero(void* p, int64_t bytes, hipStream_t st) {
+    const int64_t n = bytes / 4;
+    if (n <= 0) return hipSuccess;
+    int64_t grid = (n + 255) / 256;
+    if (grid > 1024) grid = 1024;
+    k_zero<<<(int)grid, 256, 0, st>>>((uint32_t*)p, n);
+    return hipGetLastError();
+}
+
 hipError_t launch_serve_begin(const DevCtx& c, hipStream_t st) {
     k_serve_begin<<<1, 64, 0, st>>>(c);
     return hipGetLastError();

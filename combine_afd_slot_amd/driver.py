@@ -21,7 +21,8 @@ def _dev_bf16(torch, a: np.ndarray, dev):
 class FfnSession:
     """One FFN replica window with P simulated peers on separate streams."""
 
-    def __init__(self, wl, inputs: dict, device="cuda:0", poll_timeout_us=5_000_000, weights=True):
+    def __init__(self, wl, inputs: dict, device="cuda:0", poll_timeout_us=5_000_000, weights=True,
+                 static_window=False):
         import torch
         self.torch = torch
         self.wl = wl
@@ -33,7 +34,9 @@ class FfnSession:
                                    poll_timeout_us=poll_timeout_us, attention_routes=wl.attention_routes,
                                    route_experts=wl.route_experts, expert_offset=wl.expert_offset,
                                    w1_fp8=wl.w1_fp8)
-        self.win = afd.afd_window_create(self.cfg)
+        # static_window: the window in the library's static device array
+        # (afd_window_create_static: no device allocation)
+        self.win = (afd.afd_window_create_static if static_window else afd.afd_window_create)(self.cfg)
         self.layout = afd.afd_window_layout(self.win)
         self.peer_streams = [torch.cuda.Stream(device=self.dev) for _ in range(wl.num_peers)]
         self.ffn_stream = torch.cuda.Stream(device=self.dev)

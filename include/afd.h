@@ -67,7 +67,7 @@
 extern "C" {
 #endif
 
-#define AFD_ABI_VERSION 8
+#define AFD_ABI_VERSION 9
 
 /* Header flags bit 1: shutdown sentinel ("Window and slot layout"). */
 #define AFD_FLAG_SHUTDOWN 0x2u
@@ -247,6 +247,27 @@ int32_t afd_layout_compute(const afd_window_config* cfg, afd_layout* out);
  * (one hipMalloc), zero every flag and mirror, log the size when AFD_LOG=1.
  * The connector init of "Plugin boundary"/"Window and slot layout". */
 int32_t afd_window_create(const afd_window_config* cfg, afd_window** out);
+
+/* afd_window_create without any device allocation, for callers that cannot
+ * call hipMalloc (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  The window (flags, slots and FFN
+ * workspace: layout.total_bytes, as afd_window_create would allocate) is
+ * placed in a static device array of AFD_STATIC_WINDOW_BYTES that the
+ * library holds on every GPU it runs on until the process ends.  The call
+ * zeroes the flags, mirrors and status words with a fill kernel on the null
+ * stream and synchronizes it; it calls no hipMalloc, hipFree or other
+ * allocating routine, and profiling events are not available on such a
+ * window.  One static window per device may be open at a time: every call on
+ * a GPU shares that GPU's array, which keeps the last window's contents, so
+ * a second afd_window_create_static on the device before the first is
+ * destroyed is rejected, and work of two windows over the array must never
+ * overlap.  All other entry points take the window as usual;
+ * afd_window_destroy releases the array for the next static window (it
+ * frees nothing).  Errors: AFD_ERR_INVALID (cfg, out, the device's static
+ * window already open), AFD_ERR_CAPACITY (layout.total_bytes above
+ * AFD_STATIC_WINDOW_BYTES; use afd_window_create), AFD_ERR_DEVICE. */
+#define AFD_STATIC_WINDOW_BYTES (32ll << 20)
+int32_t afd_window_create_static(const afd_window_config* cfg, afd_window** out);
 
 /* Free everything.  NULL is accepted.  Waits for the device to go idle. */
 int32_t afd_window_destroy(afd_window* w);

@@ -28,7 +28,7 @@ def test_library_exports_every_declared_symbol():
     missing = [s for s in declared if not hasattr(L, s)]
     assert not missing, missing
     assert sorted(afd.EXPORTS) == declared
-    assert afd.afd_abi_version() == 8
+    assert afd.afd_abi_version() == 9
 
 
 CFGS = [
