@@ -328,6 +328,7 @@ void fill_ctx(afd_window* w) {
     d.rr = ctrl + L.c_rr;
     d.prow = ctrl + L.c_prow;
     d.serve = ctrl + L.c_serve;
+    d.route_done = ctrl + L.c_done;
     d.attn_routes = c.attention_routes;
     d.Eg = c.route_experts ? c.route_experts : c.num_experts;
     d.w1_fp8 = c.w1_fp8;

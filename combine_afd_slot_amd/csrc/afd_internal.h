@@ -36,9 +36,10 @@ constexpr int kTileBlocks = kBX / 32;
 constexpr int kXcds = 8;
 
 // Tile segments of a GEMM: the shared expert's tiles (the longest) cut into
-// kXcds cost-balanced segments, then the routed experts' tiles cut the same
-// way; segment s covers tiles [seg[s], seg[s+1]).
-constexpr int kSegs = 2 * kXcds;
+// kXcds cost-balanced segments, then the heavy routed experts' tiles and the
+// light routed experts' tiles (one token block) cut the same way; segment s
+// covers tiles [seg[s], seg[s+1]).
+constexpr int kSegs = 3 * kXcds;
 
 // Per-stage run status words: [status, failed_peer, seq of peer 0, T].
 // Run status words: [status, failed_peer, seq of peer 0, T, served peers
@@ -75,6 +76,7 @@ struct DevCtx {
     int* rr;           // [R]   first peer an any-ready run of the stage scans (rotates for fairness)
     int* prow;         // [P]   attention-routed runs: routed rows of each peer's message
     int* serve;        // [3]   serve loop: stop status (0: running), items done, stop item
+    int* route_done;   // routing workgroups finished in this run (small work items; the last resets it)
     int* layer_cur;    // [1]   layer of the current run (from the headers in layer-table runs)
     // attention-side routing (attn_routes): the routed rows arrive grouped by
     // expert, the peer keeps the top-k weights and combines on return

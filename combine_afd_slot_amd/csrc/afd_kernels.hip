@@ -832,20 +832,15 @@ __device__ inline bool chunk_range(const DevCtx& c, int b, int& t0, int& t1, int
 // GPU Connector", "Attention gate and FFN expert compute": grouped_topk with
 // a single group.)  The chunk's expert histogram goes to blk_counts[e][b].
 // ---------------------------------------------------------------------------
-template <int EPL>
-__global__ __launch_bounds__(64 * kRouteChunk) void k_route(DevCtx c, int* status, int s) {
-    const int st = *status;  // loaded together with the peer offsets of chunk_range
-    int t_begin, t_end, p;
-    const bool have = chunk_range(c, blockIdx.x, t_begin, t_end, p);
-    if (st != AFD_OK || !have) return;
-    __shared__ int hist[kMaxExperts];
-    const int lane = threadIdx.x & 63;
+// One token's routing by one wavefront: token t of the fan-in, row r of its
+// peer's slot.  Writes its expert ids and weights (rank order), its token-row
+// (and shared-row) address, and for the fp8 W1 GEMMs its e4m3 codes and row
+// scale; calls sel(e) in the lane that selected expert e.  Returns whether
+// the token's shared_idx entry is wrong (one FFN replica owns every shared
+// row: shared_idx must be 0..n_p-1).
+template <int EPL, typename Sel>
+__device__ __forceinline__ bool route_one(const DevCtx& c, const char* slot, int t, int r, int lane, Sel sel) {
     const int E = c.E, K = c.K;
-    for (int e = threadIdx.x; e < E; e += blockDim.x) hist[e] = 0;
-    const char* slot = slot_ptr(c, c.in_win, p, s);
-    const int t = t_begin + (int)(threadIdx.x >> 6);
-    const bool live = t < t_end;
-    const int r = min(t, t_end - 1) - c.off[p];  // row of the token in its peer's slot
     float v[EPL];
     {
         const float* lg = (const float*)(slot + c.foff[AFD_FIELD_ROUTE_TABLE]) + (int64_t)r * E;
@@ -856,18 +851,15 @@ __global__ __launch_bounds__(64 * kRouteChunk) void k_route(DevCtx c, int* statu
             v[j] = x == x ? x : -INFINITY;  // NaN logits are out of contract; keep the order total
         }
     }
-    // the token's row addresses and the check of its shared row (one FFN
-    // replica owns every shared row: shared_idx must be 0..n_p-1)
     bool si_bad = false;
-    if (live && lane == 0) {
+    if (lane == 0) {
         c.tok_src[t] = (uint64_t)(slot + c.foff[AFD_FIELD_ROUTED_X] + (int64_t)r * c.H * 2);
         if (c.has_shared) {  // (a routed-only window carries no shared rows)
             c.sh_src[t] = (uint64_t)(slot + c.foff[AFD_FIELD_SHARED_X] + (int64_t)r * c.H * 2);
             si_bad = ((const int*)(slot + c.foff[AFD_FIELD_SHARED_IDX]))[r] != r;
         }
     }
-    __syncthreads();  // hist zeroed
-    if (live) {
+    {
         int rank[EPL];
         float wt[EPL];
         route_token<EPL>(v, E, K, c.renorm, lane, rank, wt);
@@ -877,12 +869,11 @@ __global__ __launch_bounds__(64 * kRouteChunk) void k_route(DevCtx c, int* statu
             if (e < E && rank[j] < K) {
                 c.ids[(int64_t)t * K + rank[j]] = e;
                 c.wts[(int64_t)t * K + rank[j]] = wt[j];
-                atomicAdd(&hist[e], 1);
+                sel(e);
             }
         }
     }
-    if (si_bad) atomicCAS(status, AFD_OK, AFD_ERR_HEADER);
-    if (c.w1_fp8 && live) {
+    if (c.w1_fp8) {
         // fp8 W1: the token row's e4m3 codes and scale (r = 448 / max|x|,
         // code = e4m3(x * r), value = code * max|x| / 448)
         const u32x4* xr = (const u32x4*)(slot + c.foff[AFD_FIELD_ROUTED_X] + (int64_t)r * c.H * 2);
@@ -935,6 +926,25 @@ __global__ __launch_bounds__(64 * kRouteChunk) void k_route(DevCtx c, int* statu
             if (c.has_shared) c.sh_src[t] = (uint64_t)(c.xq + (int64_t)t * c.H);
         }
     }
+    return si_bad;
+}
+
+template <int EPL>
+__global__ __launch_bounds__(64 * kRouteChunk) void k_route(DevCtx c, int* status, int s) {
+    const int st = *status;  // loaded together with the peer offsets of chunk_range
+    int t_begin, t_end, p;
+    const bool have = chunk_range(c, blockIdx.x, t_begin, t_end, p);
+    if (st != AFD_OK || !have) return;
+    __shared__ int hist[kMaxExperts];
+    const int lane = threadIdx.x & 63;
+    const int E = c.E;
+    for (int e = threadIdx.x; e < E; e += blockDim.x) hist[e] = 0;
+    const char* slot = slot_ptr(c, c.in_win, p, s);
+    const int t = t_begin + (int)(threadIdx.x >> 6);
+    __syncthreads();  // hist zeroed
+    bool si_bad = false;
+    if (t < t_end) si_bad = route_one<EPL>(c, slot, t, t - c.off[p], lane, [&](int e) { atomicAdd(&hist[e], 1); });
+    if (si_bad) atomicCAS(status, AFD_OK, AFD_ERR_HEADER);
     __syncthreads();
     for (int e = threadIdx.x; e < E; e += blockDim.x) c.blk_counts[(int64_t)e * c.NB + blockIdx.x] = hist[e];
 }
@@ -988,11 +998,28 @@ __global__ __launch_bounds__(256) void k_scan(DevCtx c, const int* status) {
 // row blocks split evenly over ceil(b/kTileBlocks) row tiles and, for the
 // gate/up GEMM, ceil(Ig/(kBW/2)) column tiles (kBW/2 gate + the same kBW/2
 // up rows of W13), for the down GEMM ceil(H/kBW).  Tiles are numbered
-// group-major, column tile next, row tile fastest (row tiles of one column
-// tile share their weight rows).  The cost of a tile is (32-row blocks it
-// holds) x (depth steps).  The shared group's tiles and the routed groups'
-// tiles are each cut into kXcds segments of equal cost, one of each per XCD.
+// group-major (the order inside a group is below).  The cost of a tile is (32-row blocks it
+// holds) x (depth steps).
+//
+// Plan order: the shared group, then the heavy routed groups, then the light
+// routed groups (1 to 32 rows: tiles of a single token block, whose time is
+// the streaming of their weight rows), each in expert order.  The shared
+// tiles, the heavy routed tiles and the light routed tiles are each cut into
+// kXcds segments of equal cost, one of each class per XCD.
+//
+// Inside a group the tiles run in panels of kPanel column tiles: panel by
+// panel, and in a panel row tile by row tile with the panel's column tiles
+// fastest.  The workgroups of one XCD take consecutive tiles of a segment at
+// about the same time, so the tiles in flight on an XCD form a block of a
+// few row tiles by up to kPanel column tiles that share both operands: each
+// token-row block is fetched once per panel instead of once per column tile,
+// and each weight tile once per row-tile pass of the panel.  (kPanel = 1 is
+// plain column-tile order.)
 // ---------------------------------------------------------------------------
+#ifndef AFD_TILE_PANEL
+#define AFD_TILE_PANEL 4
+#endif
+constexpr int kPanel = AFD_TILE_PANEL;
 struct PlanGroup {
     int M, mt, blocks, nt, nk;
 };
@@ -1011,7 +1038,7 @@ __device__ inline PlanGroup plan_group(const DevCtx& c, int T, const int* s_eoff
 }
 
 // Block-wide exclusive prefix sums of four int64 values per thread.  `sh`
-// holds 16 values.
+// holds 4 values per wavefront (64 for 1024 threads).
 __device__ void block_excl_scan4(long long (&v)[4], long long* sh) {
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
     long long x[4];
@@ -1038,35 +1065,61 @@ __device__ void block_excl_scan4(long long (&v)[4], long long* sh) {
     __syncthreads();
 }
 
-// Tile and cost prefixes over the groups of both GEMMs into LDS:
-// s_t[m][j] / s_c[m][j] = tiles / cost of GEMM m+1 before group j (j = G:
-// the totals).
+// A light group: a routed expert with 1 to 32 rows (one token block).
+__device__ inline bool plan_light(const DevCtx& c, const int* s_eoff, int j) {
+    if (c.has_shared && j == 0) return false;
+    const int e = j - c.has_shared;
+    const int M = s_eoff[e + 1] - s_eoff[e];
+    return M >= 1 && M <= 32;
+}
+
+// The plan order of the groups and the tile and cost prefixes of both GEMMs
+// over it, into LDS: s_ord[q] = the group at plan position q (heavy groups,
+// the shared one first, then light ones, each in index order), *s_nh = the
+// number of heavy groups (light positions start there), s_t[m][q] / s_c[m][q]
+// = tiles / cost of GEMM m+1 before position q (q = G: the totals).
 __device__ void plan_prefix(const DevCtx& c, int T, const int* s_eoff, int (*s_t)[kMaxExperts + 2],
-                            long long (*s_c)[kMaxExperts + 2], long long* sh) {
-    const int tid = threadIdx.x, G = c.G;
-    const int per = (G + 255) / 256;
+                            long long (*s_c)[kMaxExperts + 2], int* s_ord, int* s_nh, long long* sh) {
+    const int tid = threadIdx.x, G = c.G, NT = blockDim.x;
+    const int per = (G + NT - 1) / NT;
     const int j0 = tid * per, j1 = min(G, j0 + per);
+    {
+        int nl = 0;
+        for (int j = j0; j < j1; ++j) nl += plan_light(c, s_eoff, j) ? 1 : 0;
+        long long v[4] = {nl, 0, 0, 0};
+        block_excl_scan4(v, sh);  // v[0]: light groups before j0
+        if (tid == NT - 1) *s_nh = G - (int)(v[0] + nl);
+        __syncthreads();
+        const int nh = *s_nh;
+        int lr = (int)v[0];
+        for (int j = j0; j < j1; ++j) {
+            const bool l = plan_light(c, s_eoff, j);
+            s_ord[l ? nh + lr : j - lr] = j;
+            lr += l ? 1 : 0;
+        }
+        __syncthreads();
+    }
     long long v[4] = {0, 0, 0, 0};  // tiles of GEMM 1, 2; cost of GEMM 1, 2
-    for (int j = j0; j < j1; ++j) {
+    for (int q = j0; q < j1; ++q) {
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
-            const PlanGroup g = plan_group(c, T, s_eoff, j, m + 1);
+            const PlanGroup g = plan_group(c, T, s_eoff, s_ord[q], m + 1);
             v[m] += g.mt * g.nt;
             v[2 + m] += (long long)g.nt * g.blocks * g.nk;
         }
     }
     block_excl_scan4(v, sh);
-    for (int j = j0; j < j1; ++j) {
+    for (int q = j0; q < j1; ++q) {
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
-            const PlanGroup g = plan_group(c, T, s_eoff, j, m + 1);
-            s_t[m][j] = (int)v[m];
-            s_c[m][j] = v[2 + m];
+            const PlanGroup g = plan_group(c, T, s_eoff, s_ord[q], m + 1);
+            s_t[m][q] = (int)v[m];
+            s_c[m][q] = v[2 + m];
             v[m] += g.mt * g.nt;
             v[2 + m] += (long long)g.nt * g.blocks * g.nk;
         }
     }
-    if (tid == 255)
+    if (tid == NT - 1)
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
             s_t[m][G] = (int)v[m];
@@ -1076,30 +1129,29 @@ __device__ void plan_prefix(const DevCtx& c, int T, const int* s_eoff, int (*s_t
 }
 
 // The plan's global tables (one workgroup): tile prefixes, the zeroed tile
-// counters and the segment boundaries.  Boundary b <= kXcds cuts the shared
-// group (cost Ch, tiles [0, th)) at cost Ch*b/kXcds, boundary kXcds + b the
-// routed groups at Ch + (C - Ch)*b/kXcds; each is the first tile whose cost
-// prefix reaches the target.
+// counters and the segment boundaries.  Class k (0 shared, 1 heavy routed, 2
+// light routed: plan positions [0, hs), [hs, nh), [nh, G)) with cost range
+// [C0, C1) has boundaries k*kXcds + b, b < kXcds, at cost C0 + (C1-C0)*b/kXcds:
+// the first tile whose cost prefix reaches it (boundary kSegs: the end).
 __device__ void plan_publish(const DevCtx& c, int T, const int* s_eoff, int (*s_t)[kMaxExperts + 2],
-                             long long (*s_c)[kMaxExperts + 2]) {
+                             long long (*s_c)[kMaxExperts + 2], const int* s_ord, int nh) {
     const int tid = threadIdx.x, G = c.G;
     if (tid < 2 * kSegs) c.tctr[tid] = 0;
     for (int m = 0; m < 2; ++m) {
         int* tstart = m == 0 ? c.tstart1 : c.tstart2;
-        for (int j = tid; j <= G; j += 256) tstart[j] = s_t[m][j];
+        for (int j = tid; j <= G; j += (int)blockDim.x) tstart[j] = s_t[m][j];
         int* seg = m == 0 ? c.seg1 : c.seg2;
         if (tid <= kSegs) {
             const int hs = c.has_shared ? 1 : 0;
-            const int total = s_t[m][G];
-            const long long C = s_c[m][G], Ch = s_c[m][hs];
-            const int th = s_t[m][hs];
-            const bool heavy = tid < kXcds;
-            const int lo_t = heavy ? 0 : th, hi_t = heavy ? th : total;
-            const long long S = heavy ? Ch * tid / kXcds : Ch + (C - Ch) * (tid - kXcds) / kXcds;
+            const int cls = tid / kXcds, b = tid % kXcds;
+            const int q0 = cls == 0 ? 0 : cls == 1 ? hs : cls == 2 ? nh : G;
+            const int q1 = cls == 0 ? hs : cls == 1 ? nh : G;
+            const int lo_t = s_t[m][q0], hi_t = s_t[m][q1];
+            const long long C0 = s_c[m][q0], C1 = s_c[m][q1];
+            const long long S = C0 + (C1 - C0) * b / kXcds;
             int res;
-            if (tid == 0) res = 0;
-            else if (tid == kXcds) res = th;
-            else if (tid == kSegs || S >= C) res = total;
+            if (b == 0 || cls == 3) res = lo_t;
+            else if (S >= C1) res = hi_t;
             else {
                 int lo = 0, hi = G;
                 while (hi - lo > 1) {
@@ -1109,48 +1161,58 @@ __device__ void plan_publish(const DevCtx& c, int T, const int* s_eoff, int (*s_
                 }
                 // skip groups with no tiles that share the same cost start
                 while (lo + 1 < G && s_c[m][lo + 1] <= S) ++lo;
-                const PlanGroup g = plan_group(c, T, s_eoff, lo, m + 1);
+                const PlanGroup g = plan_group(c, T, s_eoff, s_ord[lo], m + 1);
                 const long long u = (S - s_c[m][lo] + g.nk - 1) / g.nk;  // in 32-row blocks
-                int nt = (int)(u / g.blocks);
-                const int rem = (int)(u - (long long)nt * g.blocks);
-                // first row tile that starts at or after block `rem`
-                int mt = (rem * g.mt + g.blocks - 1) / g.blocks;
+                // the panel holding block-column u, then the first row tile
+                // of that panel starting at or after its remaining blocks
+                const int pw = min(kPanel, g.nt), np = (g.nt + pw - 1) / pw;
+                int pp = min((int)(u / ((long long)pw * g.blocks)), np - 1);
+                const int w = min(pw, g.nt - pp * pw);
+                const long long rb = (u - (long long)pp * pw * g.blocks + w - 1) / w;  // blocks into the panel
+                int mt = (int)((rb * g.mt + g.blocks - 1) / g.blocks);
                 if (mt >= g.mt) {
-                    ++nt;
+                    ++pp;
                     mt = 0;
                 }
-                res = s_t[m][lo] + nt * g.mt + mt;
+                res = min(s_t[m][lo] + pp * pw * g.mt + mt * w, s_t[m][lo] + g.mt * g.nt);
             }
             seg[tid] = min(max(res, lo_t), hi_t);
         }
     }
 }
 
-// This workgroup's share of the tile descriptors of both GEMMs (the tile
-// list is split evenly over the grid): tile i belongs to the group whose
+// Share `part` of `nparts` of the tile descriptors of both GEMMs (the tile
+// list split evenly): tile i belongs to the group at the plan position whose
 // tile range holds i; row tile mt of a group holds its 32-row blocks
 // [mt*b/mt_n, (mt+1)*b/mt_n).
-__device__ void plan_fill(const DevCtx& c, int T, const int* s_eoff, int (*s_t)[kMaxExperts + 2]) {
+__device__ void plan_fill(const DevCtx& c, int T, const int* s_eoff, int (*s_t)[kMaxExperts + 2], const int* s_ord,
+                          int part, int nparts) {
     const int G = c.G;
     for (int m = 0; m < 2; ++m) {
         int4* tinfo = m == 0 ? c.tinfo1 : c.tinfo2;
         const int maxt = m == 0 ? c.max_tiles1 : c.max_tiles2;
         const int total = min(s_t[m][G], maxt);
-        const int per = (total + (int)gridDim.x - 1) / (int)gridDim.x;
-        const int i1 = min(total, ((int)blockIdx.x + 1) * per);
-        for (int i = (int)blockIdx.x * per + threadIdx.x; i < i1; i += blockDim.x) {
+        const int per = (total + nparts - 1) / nparts;
+        const int i1 = min(total, (part + 1) * per);
+        for (int i = part * per + (int)threadIdx.x; i < i1; i += blockDim.x) {
             int lo = 0, hi = G;  // s_t[m][lo] <= i < s_t[m][hi]
             while (hi - lo > 1) {
                 const int mid = (lo + hi) >> 1;
                 if (s_t[m][mid] <= i) lo = mid;
                 else hi = mid;
             }
-            const PlanGroup g = plan_group(c, T, s_eoff, lo, m + 1);
+            const int j = s_ord[lo];
+            const PlanGroup g = plan_group(c, T, s_eoff, j, m + 1);
             const int local = i - s_t[m][lo];
-            const int nt = local / g.mt, mt = local - nt * g.mt;
+            // panel pp of width w, row tile mt, column tile nt (panel order)
+            const int pw = min(kPanel, g.nt);
+            const int pp = min(local / (pw * g.mt), (g.nt - 1) / pw);
+            const int w = min(pw, g.nt - pp * pw);
+            const int within = local - pp * pw * g.mt;
+            const int mt = within / w, nt = pp * pw + within % w;
             const int b0 = mt * g.blocks / g.mt, b1 = (mt + 1) * g.blocks / g.mt;
-            const int row0 = (c.has_shared && lo == 0) ? 0 : s_eoff[lo - c.has_shared];
-            tinfo[i] = make_int4(lo, nt | ((b1 - b0) << 16), row0 + b0 * 32, min(b1 * 32, g.M) - b0 * 32);
+            const int row0 = (c.has_shared && j == 0) ? 0 : s_eoff[j - c.has_shared];
+            tinfo[i] = make_int4(j, nt | ((b1 - b0) << 16), row0 + b0 * 32, min(b1 * 32, g.M) - b0 * 32);
         }
     }
 }
@@ -1171,10 +1233,12 @@ __global__ __launch_bounds__(256) void k_permute(DevCtx c, const int* status) {
     static_assert(kRouteChunk <= 32 && kRouteChunk * kMaxTopK <= 256, "chunk masks and one pair per thread");
     static_assert(kMaxExperts <= 4 * 256, "at most four expert counts per thread");
     __shared__ int sh[16];
-    __shared__ long long sh4[16];
+    __shared__ long long sh4[64];
     __shared__ int s_eoff[kMaxExperts + 1];
     __shared__ int s_t[2][kMaxExperts + 2];
     __shared__ long long s_c[2][kMaxExperts + 2];
+    __shared__ int s_ord[kMaxExperts + 1];
+    __shared__ int s_nh;
     __shared__ uint32_t emask[kMaxExperts];
     __shared__ uint64_t ltok[kRouteChunk];
     const int E = c.E, K = c.K, tid = threadIdx.x;
@@ -1213,12 +1277,12 @@ __global__ __launch_bounds__(256) void k_permute(DevCtx c, const int* status) {
     for (int q = tid; q < E; q += 256) emask[q] = 0u;
     if (tid < nt) ltok[tid] = trow;
     __syncthreads();
-    plan_prefix(c, T, s_eoff, s_t, s_c, sh4);
+    plan_prefix(c, T, s_eoff, s_t, s_c, s_ord, &s_nh, sh4);
     if (blockIdx.x == 0) {
         for (int e = tid; e <= E; e += 256) c.eoff[e] = s_eoff[e];
-        plan_publish(c, T, s_eoff, s_t, s_c);
+        plan_publish(c, T, s_eoff, s_t, s_c, s_ord, s_nh);
     }
-    plan_fill(c, T, s_eoff, s_t);
+    plan_fill(c, T, s_eoff, s_t, s_ord, (int)blockIdx.x, (int)gridDim.x);
     if (!have) return;
     if (tid < np) atomicOr(&emask[e], 1u << (tid / K));
     __syncthreads();
@@ -1231,6 +1295,120 @@ __global__ __launch_bounds__(256) void k_permute(DevCtx c, const int* status) {
             c.psrc[pos] = ltok[tl];
             if (c.w1_fp8) c.sxp[pos] = c.sx[t0 + tl];
         }
+        c.inv[f] = pos;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// a2 + a3 in one launch, for work items of at most kSmallT tokens (decode-
+// shaped batches): k_route's grid routes the chunks, and the last of its
+// workgroups to finish (a device-scope counter: each releases its writes
+// before counting itself, the last acquires them) builds the per-expert
+// counts, the stable dispatch order and the GEMM plan of k_scan + k_permute,
+// without their launches.  From the routed ids it sets bit t of each
+// selected expert's token mask; pair f = t*K + k then goes to eoff[e] +
+// (tokens before t that chose e), the stable position k_permute computes
+// from its chunk bases.
+// ---------------------------------------------------------------------------
+#ifndef AFD_SMALL_T
+#define AFD_SMALL_T 256
+#endif
+constexpr int kSmallT = AFD_SMALL_T;
+constexpr int kSmallW = kSmallT / 32;  // mask words per expert
+
+template <int EPL>
+__global__ __launch_bounds__(64 * kRouteChunk) void k_route_small(DevCtx c, int* status, int s) {
+    __shared__ int sh[16];
+    __shared__ long long sh4[64];
+    __shared__ int s_eoff[kMaxExperts + 1];
+    __shared__ int s_t[2][kMaxExperts + 2];
+    __shared__ long long s_c[2][kMaxExperts + 2];
+    __shared__ int s_ord[kMaxExperts + 1];
+    __shared__ int s_nh;
+    __shared__ uint32_t emask[kMaxExperts][kSmallW];
+    __shared__ int s_last;
+    const int tid = threadIdx.x, lane = tid & 63;
+    {
+        // every workgroup counts itself, whatever it had to do
+        const int st = *status;
+        int t_begin, t_end, p;
+        const bool have = chunk_range(c, blockIdx.x, t_begin, t_end, p);
+        const int t = t_begin + (tid >> 6);
+        bool bad = false;
+        if (st == AFD_OK && have && t < t_end)
+            bad = route_one<EPL>(c, slot_ptr(c, c.in_win, p, s), t, t - c.off[p], lane, [](int) {});
+        if (bad) atomicCAS(status, AFD_OK, AFD_ERR_HEADER);
+        __syncthreads();
+        if (tid == 0) {
+            // release the workgroup's routing (its stores completed at the barrier)
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+            s_last = atomicAdd(c.route_done, 1) == (int)gridDim.x - 1;
+        }
+        __syncthreads();
+        if (!s_last) return;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");  // every workgroup's routing
+    if (tid == 0) *c.route_done = 0;  // (the next run's launch starts after this one)
+    const int st = __hip_atomic_load(status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const int T = *c.Tptr;
+    if (st != AFD_OK) return;
+    const int E = c.E, K = c.K, NT = blockDim.x;
+    if (T > kSmallT) {  // (the launcher picks this kernel only when P * token_cap <= kSmallT)
+        if (tid == 0) atomicCAS(status, AFD_OK, AFD_ERR_INVALID);
+        return;
+    }
+    for (int i = tid; i < E * kSmallW; i += NT) (&emask[0][0])[i] = 0u;
+    __syncthreads();
+    for (int f = tid; f < T * K; f += NT) {
+        const int t = f / K, e = c.ids[f];
+        atomicOr(&emask[e][t >> 5], 1u << (t & 31));
+    }
+    __syncthreads();
+    // counts (bincount), expert offsets, per-peer counts
+    {
+        int cnt = 0;
+        if (tid < E)
+#pragma unroll
+            for (int w = 0; w < kSmallW; ++w) cnt += __popc(emask[tid][w]);
+        const int run = block_excl_scan(tid < E ? cnt : 0, sh);
+        if (tid < E) {
+            s_eoff[tid] = run;
+            c.counts[tid] = cnt;
+            c.eoff[tid] = run;
+        }
+        if (tid == E - 1) {
+            s_eoff[E] = run + cnt;
+            c.eoff[E] = run + cnt;
+        }
+    }
+    for (int i = tid; i < c.P * E; i += NT) {
+        const int q = i / E, e = i - q * E;
+        const int a = c.off[q], b = c.off[q + 1];
+        int n = 0;
+        for (int w = a >> 5; a < b && w <= (b - 1) >> 5; ++w) {
+            uint32_t m = emask[e][w];
+            const int lo = w * 32;
+            if (a > lo) m &= ~0u << (a - lo);
+            if (b < lo + 32) m &= (1u << (b - lo)) - 1u;
+            n += __popc(m);
+        }
+        c.peer_counts[q * E + e] = n;
+    }
+    __syncthreads();
+    plan_prefix(c, T, s_eoff, s_t, s_c, s_ord, &s_nh, sh4);
+    plan_publish(c, T, s_eoff, s_t, s_c, s_ord, s_nh);
+    plan_fill(c, T, s_eoff, s_t, s_ord, 0, 1);  // (this one workgroup writes every tile)
+    // the stable dispatch position of every pair
+    for (int f = tid; f < T * K; f += NT) {
+        const int t = f / K;
+        const int e = c.ids[f];
+        int below = 0;
+        for (int w = 0; w < (t >> 5); ++w) below += __popc(emask[e][w]);
+        below += __popc(emask[e][t >> 5] & ((1u << (t & 31)) - 1u));
+        const int pos = s_eoff[e] + below;
+        c.perm[pos] = f;
+        c.psrc[pos] = c.tok_src[t];
+        if (c.w1_fp8) c.sxp[pos] = c.sx[t];
         c.inv[f] = pos;
     }
 }
@@ -1291,10 +1469,12 @@ __global__ __launch_bounds__(256) void k_gscan(DevCtx c, const int* status, int 
 // k_retcopy.  Shared rows: addresses and the shared_idx check as in k_route.
 __global__ __launch_bounds__(256) void k_gdispatch(DevCtx c, int* status, int s) {
     __shared__ int sh[16];
-    __shared__ long long sh4[16];
+    __shared__ long long sh4[64];
     __shared__ int s_eoff[kMaxExperts + 1];
     __shared__ int s_t[2][kMaxExperts + 2];
     __shared__ long long s_c[2][kMaxExperts + 2];
+    __shared__ int s_ord[kMaxExperts + 1];
+    __shared__ int s_nh;
     const int st = *status;
     const int T = *c.Tptr;
     if (st != AFD_OK) return;
@@ -1315,12 +1495,12 @@ __global__ __launch_bounds__(256) void k_gdispatch(DevCtx c, int* status, int s)
         if (tid == 255) s_eoff[E] = run;
     }
     __syncthreads();
-    plan_prefix(c, T, s_eoff, s_t, s_c, sh4);
+    plan_prefix(c, T, s_eoff, s_t, s_c, s_ord, &s_nh, sh4);
     if (blockIdx.x == 0) {
         for (int e = tid; e <= E; e += 256) c.eoff[e] = s_eoff[e];
-        plan_publish(c, T, s_eoff, s_t, s_c);
+        plan_publish(c, T, s_eoff, s_t, s_c, s_ord, s_nh);
     }
-    plan_fill(c, T, s_eoff, s_t);
+    plan_fill(c, T, s_eoff, s_t, s_ord, (int)blockIdx.x, (int)gridDim.x);
     const int n = min(T * K, s_eoff[E]);  // (k_wait checked that every group list covers its rows)
     const int stride = (int)gridDim.x * 256;
     for (int pos = (int)blockIdx.x * 256 + tid; pos < n; pos += stride) {
@@ -1872,27 +2052,43 @@ __device__ __forceinline__ void gemm_step_f8(f32x16 (&acc)[NV > 0 ? NV : 1][4], 
 
 // Tile scheduler of a workgroup.  Tiles are taken dynamically: a workgroup
 // on XCD x (x = b % kXcds: workgroups are dispatched to the XCDs round-
-// robin) takes tiles from the shared-expert segment x, then from the routed
-// segment x, then from the segments of XCD x+1, x+2, ...: every XCD starts
-// on its share of the longest tiles, and the tiles of one segment, which
-// share weight rows, stay in one XCD's L2 until other XCDs run dry.  Wave 0
-// owns the grabbing: the grab of the next tile is issued kGrabAhead depth
-// steps before the current tile ends (late enough that a workgroup does not
-// hold a tile that an idle one could run, early enough that the atomic has
-// returned when the tile ends), resolved at the tile boundary and broadcast
-// through LDS.  When the current segment is drained, one batch of loads
-// (a lane per segment) finds the next segment with tiles left.
+// robin) takes tiles from the shared-expert segment x, then from the heavy
+// routed segment x, then from the segments of XCD x+1, x+2, ..., and last
+// from the light segments x, x+1, ...: every XCD starts on its share of the
+// longest tiles, and the tiles of one segment, which share weight rows, stay
+// in one XCD's L2 until other XCDs run dry.  One workgroup in kLightEvery
+// takes the light segments first instead: the light tiles' time is the
+// streaming of their weight rows, which a few workgroups do next to the
+// compute-bound tiles of the others, with HBM to spare, rather than all
+// workgroups at once at the end.  Wave 0 owns the grabbing: the grab of the
+// next tile is issued kGrabAhead depth steps before the current tile ends
+// (late enough that a workgroup does not hold a tile that an idle one could
+// run, early enough that the atomic has returned when the tile ends),
+// resolved at the tile boundary and broadcast through LDS.  When the current
+// segment is drained, one batch of loads (a lane per segment) finds the next
+// segment with tiles left.
+#ifndef AFD_LIGHT_EVERY
+#define AFD_LIGHT_EVERY 5
+#endif
+constexpr int kLightEvery = AFD_LIGHT_EVERY;
 constexpr int kGrabAhead = 3;
 
 struct GemmSched {
     const int* seg;
     int* ctr;
     int x;                // this workgroup's XCD
+    bool lf;              // light segments first
     int tries, si, pend;  // wave 0 only: position in the visiting order, its segment, the pending grab
 };
 
-__device__ __forceinline__ int sched_seg(int x, int k) {  // k-th segment visited from XCD x
-    return (k & 1) * kXcds + (x + (k >> 1)) % kXcds;
+// k-th segment visited by a workgroup on XCD x: shared and heavy segments
+// alternate (x, x+1, ...), the light ones (x, x+1, ...) come last, or first
+// for a light-first workgroup.
+__device__ __forceinline__ int sched_seg(int x, int k, bool lf) {
+    const int kl = lf ? k : k - 2 * kXcds;  // index among the light segments
+    if (kl >= 0 && kl < kXcds) return 2 * kXcds + (x + kl) % kXcds;
+    const int kh = lf ? k - kXcds : k;      // index among the shared / heavy ones
+    return (kh & 1) * kXcds + (x + (kh >> 1)) % kXcds;
 }
 
 // Next tile, or -1 when all are taken (wave 0, all lanes; uniform result).
@@ -1901,7 +2097,7 @@ __device__ __forceinline__ int sched_grab_slow(GemmSched& s, int lane) {
     while (s.tries < kSegs) {
         bool left = false;
         if (lane >= s.tries && lane < kSegs) {
-            const int si = sched_seg(s.x, lane);
+            const int si = sched_seg(s.x, lane, s.lf);
             const int taken = __hip_atomic_load(&s.ctr[si], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             left = s.seg[si] + taken < s.seg[si + 1];
         }
@@ -1911,7 +2107,7 @@ __device__ __forceinline__ int sched_grab_slow(GemmSched& s, int lane) {
             break;
         }
         s.tries = __builtin_ctzll(m);
-        s.si = sched_seg(s.x, s.tries);
+        s.si = sched_seg(s.x, s.tries, s.lf);
         int t = 0;
         if (lane == 0) t = s.seg[s.si] + atomicAdd(&s.ctr[s.si], 1);
         t = __builtin_amdgcn_readfirstlane(t);
@@ -2228,6 +2424,7 @@ __device__ __forceinline__ void gemm_tiles(const DevCtx& c, const Weights& w, ch
     const int total = sc.seg[kSegs];
     if (total <= 0 || total > (MODE == 1 ? c.max_tiles1 : c.max_tiles2)) return;  // nothing, or an insane plan
     sc.x = (int)(blockIdx.x % kXcds);
+    sc.lf = (blockIdx.x / kXcds) % kLightEvery == 0;
     sc.tries = 0;
     sc.si = 0;
     sc.pend = 0;
@@ -2487,6 +2684,16 @@ hipError_t launch_ffn(const DevCtx& c, int stage, int layer, const Weights& w, l
         mark();
         k_gdispatch<<<c.NB, 256, 0, st>>>(c, status, stage);
         if (c.w1_fp8) k_gquant<<<num_cu * 4, 256, 0, st>>>(c, status);
+    } else if (Tmax <= kSmallT) {
+        // small work items: routing, counts, dispatch order and plan in one launch
+        // (its time lands in the routing slot)
+        if (c.E <= 64) k_route_small<1><<<c.NB, 64 * kRouteChunk, 0, st>>>(c, status, stage);
+        else if (c.E <= 128) k_route_small<2><<<c.NB, 64 * kRouteChunk, 0, st>>>(c, status, stage);
+        else if (c.E <= 256) k_route_small<4><<<c.NB, 64 * kRouteChunk, 0, st>>>(c, status, stage);
+        else if (c.E <= 512) k_route_small<8><<<c.NB, 64 * kRouteChunk, 0, st>>>(c, status, stage);
+        else k_route_small<16><<<c.NB, 64 * kRouteChunk, 0, st>>>(c, status, stage);
+        mark();
+        mark();
     } else {
         if (c.E <= 64) k_route<1><<<c.NB, 64 * kRouteChunk, 0, st>>>(c, status, stage);
         else if (c.E <= 128) k_route<2><<<c.NB, 64 * kRouteChunk, 0, st>>>(c, status, stage);
