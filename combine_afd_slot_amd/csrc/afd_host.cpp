@@ -266,6 +266,7 @@ struct afd_window {
     int32_t packed_len[afd::kMaxPeers * afd::kMaxRing] = {};
     uint8_t inflight[afd::kMaxPeers * afd::kMaxRing] = {};
     bool is_static = false;  // placed in the library's static device array (afd_window_create_static)
+    bool poison = false;     // AFD_POISON=1 at creation: slots filled with NaN before each pack / reply
     int profile = 0;  // 0 off, 1 every kernel, 2 the two GEMMs, 3 the gate/up GEMM
     hipEvent_t ev[AFD_PROFILE_SLOTS + 1] = {};
     bool ev_pending = false;
@@ -329,6 +330,7 @@ void fill_ctx(afd_window* w) {
     d.prow = ctrl + L.c_prow;
     d.serve = ctrl + L.c_serve;
     d.route_done = ctrl + L.c_done;
+    d.poison = w->poison ? 1 : 0;
     d.attn_routes = c.attention_routes;
     d.Eg = c.route_experts ? c.route_experts : c.num_experts;
     d.w1_fp8 = c.w1_fp8;
@@ -428,6 +430,8 @@ int32_t window_init(afd_window* w, const afd_window_config* cfg, char* base, hip
     if (hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, w->device) == hipSuccess && khz > 0)
         w->ticks_per_us = khz / 1000 > 0 ? khz / 1000 : 1;
     w->base = base;
+    const char* pz = getenv("AFD_POISON");
+    w->poison = pz && pz[0] == '1';
     // Flags, mirrors and status words start at zero; the slots are left as
     // they are (a slot is only read after its flag announces it).  A fill
     // kernel, not a memset, so that no memset node is ever recorded.

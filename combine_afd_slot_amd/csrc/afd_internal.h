@@ -77,6 +77,7 @@ struct DevCtx {
     int* prow;         // [P]   attention-routed runs: routed rows of each peer's message
     int* serve;        // [3]   serve loop: stop status (0: running), items done, stop item
     int* route_done;   // routing workgroups finished in this run (small work items; the last resets it)
+    int poison;        // fill slots with 0xFFFFFFFF (NaN as fp32 and bf16) before each pack / reply
     int* layer_cur;    // [1]   layer of the current run (from the headers in layer-table runs)
     // attention-side routing (attn_routes): the routed rows arrive grouped by
     // expert, the peer keeps the top-k weights and combines on return

@@ -187,6 +187,29 @@ __device__ __forceinline__ void route_token(const float (&v)[EPL], int E, int K,
 // shared: the window carries shared rows (shared_x, shared_idx); a routed-
 // only window does not.  grouped: the attention side routes, so no logits
 // travel and the routed rows are written grouped by expert (k_pscatter).
+// Fill n words at p with a pattern (poison mode).
+__global__ __launch_bounds__(256) void k_fill(uint32_t* p, int64_t n, uint32_t v) {
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) p[i] = v;
+}
+
+// Poison mode, FFN side: once the wait has consumed the work item, the
+// return slot of every peer it serves (its payload fields, all rows) is
+// filled with 0xFFFFFFFF before the run writes the reply, so a peer that
+// reads a row the reply did not write sees NaN.  Peers not served keep
+// their return slot (it may hold an earlier reply not yet unpacked).
+__global__ __launch_bounds__(256) void k_poison_ret(DevCtx c, const int* status, int s) {
+    if (status[0] != AFD_OK) return;
+    const uint64_t served = (uint64_t)(uint32_t)status[4] | ((uint64_t)(uint32_t)status[5] << 32);
+    const int p = blockIdx.y;
+    if (!((served >> p) & 1)) return;
+    char* slot = c.ret_win + c.slots_off + (int64_t)(p * c.R + s) * c.slot_bytes;
+    const int64_t o = c.foff[AFD_FIELD_ROUTE_TABLE], n = (c.slot_bytes - o) / 4;
+    uint32_t* q = (uint32_t*)(slot + o);
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) q[i] = 0xFFFFFFFFu;
+}
+
 __global__ __launch_bounds__(256) void k_pack_payload(char* slot, int64_t o_rt, int64_t o_rx, int64_t o_si,
                                                       int64_t o_sx, const uint4* hidden, const float* logits,
                                                       int n, int H, int E, int shared, int grouped) {
@@ -350,6 +373,13 @@ __global__ __launch_bounds__(256) void k_pcopy(DevCtx c, int idx, char* slot, co
 hipError_t launch_pack(const DevCtx& c, int peer, int stage, int layer, int seq_len, const void* hidden,
                        const float* logits, uint32_t flags, int seq, hipStream_t st) {
     char* slot = c.in_win + c.slots_off + (int64_t)(peer * c.R + stage) * c.slot_bytes;
+    if (c.poison) {
+        // poison mode: every payload field of the slot (all token_cap rows)
+        // reads 0xFFFFFFFF -- NaN as fp32 and bf16, -1 as a row index --
+        // unless this message writes it, so a read of a stale row shows
+        const int64_t o = c.foff[AFD_FIELD_ROUTE_TABLE], n = (c.slot_bytes - o) / 4;
+        k_fill<<<(unsigned)std::min<int64_t>((n + 255) / 256, 1024), 256, 0, st>>>((uint32_t*)(slot + o), n, 0xFFFFFFFFu);
+    }
     if (seq_len > 0) {
         int64_t work = (int64_t)seq_len * c.H / 8;
         int64_t lw = (int64_t)seq_len * c.E;
@@ -2676,6 +2706,11 @@ hipError_t launch_ffn(const DevCtx& c, int stage, int layer, const Weights& w, l
     };
     mark();
     k_wait<<<1, 64, 0, st>>>(c, stage, layer, timeout_ticks, max_take, gather_ticks, serve_item);
+    if (c.poison) {
+        const int64_t n = (c.slot_bytes - c.foff[AFD_FIELD_ROUTE_TABLE]) / 4;
+        k_poison_ret<<<dim3((unsigned)std::min<int64_t>((n + 255) / 256, 256), (unsigned)c.P), 256, 0, st>>>(c, status,
+                                                                                                          stage);
+    }
     mark();
     if (c.attn_routes) {
         // (the routing slots: the merge of the group lists, then the dispatch)

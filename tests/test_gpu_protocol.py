@@ -327,3 +327,51 @@ def test_all_peers_empty():
         st = s.status()
         assert st.status == 0 and st.total_tokens == 0
         assert afd.afd_window_poll(s.win, 1, 2) == [0, 0]
+
+
+@pytest.mark.parametrize("attention_routes", [0, 1])
+def test_poison_mode(orc, monkeypatch, attention_routes):
+    """AFD_POISON=1: every pack fills its slot's payload fields, and every run
+    the return slots of the peers it serves, with 0xFFFFFFFF (NaN as bf16 and
+    fp32) before writing, so a kernel that read a row the current message did
+    not write would see NaN.  A full-length message followed by shorter ones
+    (an empty peer among them) must give the oracle's rows and, bit for bit,
+    the rows of a window without poisoning; the rows past each message read
+    as the poison."""
+    import dataclasses
+    wl = small_workload("poison", seq_lens=(96, 0, 51), hidden=256, num_experts=12, top_k=3, intermediate=200,
+                        shared_intermediate=136, token_cap=96, attention_routes=attention_routes)
+    short = dataclasses.replace(wl, seq_lens=(37, 0, 12))
+    full_inp, short_inp = make_inputs(wl), make_inputs(short.with_(seed=5))
+    for k in ("W13", "W2", "Ws13", "Ws2"):
+        short_inp[k] = full_inp[k]
+    with FfnSession(wl, full_inp, poll_timeout_us=200_000) as s:
+        s.step()
+        s.wl = short
+        s.set_inputs(short_inp)
+        s.step()
+        assert s.status().status == 0
+        base = [o.copy() for o in s.outputs_f32()]
+    monkeypatch.setenv("AFD_POISON", "1")
+    with FfnSession(wl, full_inp, poll_timeout_us=200_000) as s:
+        s.step()
+        assert s.status().status == 0
+        s.wl = short
+        s.set_inputs(short_inp)
+        s.step()
+        st = s.status()
+        assert st.status == 0 and st.total_tokens == short.total_tokens
+        ref = _oracle_out(orc, short, short_inp)["out_p"]
+        L, H = s.layout, wl.hidden
+        for p, n in enumerate(short.seq_lens):
+            o = s.outputs_f32()[p]
+            assert np.isfinite(o).all()
+            np.testing.assert_array_equal(o, base[p])
+            assert row_rel_err(o, ref[p]) <= ROW_REL_TOL
+            # rows past the message: inbound and return slots hold the poison
+            rows = (wl.token_cap - n) if not attention_routes else 0
+            if rows:
+                for win in (L.in_off, L.ret_off):
+                    off = _slot_off(s, win, p, 0) + L.field_off[2] + 2 * n * H
+                    past = np.frombuffer(afd.afd_debug_read(s.win, off, 2 * rows * H), np.uint16)
+                    assert (past == 0xFFFF).all(), (p, win)
