@@ -98,17 +98,44 @@ __device__ inline void st_release(int* p, int v) {
 }
 
 // ---------------------------------------------------------------------------
+// Wavefront inclusive prefix sums with DPP moves (register exchanges, no LDS
+// traffic): within each row of 16 lanes add the value 1, 2, 4 and 8 lanes
+// below (lanes past the row's start add 0), then carry row 0's total into
+// row 1 and row 2's into row 3 (row_bcast:15), then rows 0-1's total into
+// rows 2 and 3 (row_bcast:31).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int wave_incl_scan(int x) {
+    x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, true);  // row_shr:1
+    x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, true);  // row_shr:2
+    x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, true);  // row_shr:4
+    x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, true);  // row_shr:8
+    x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);  // row_bcast:15 into rows 1, 3
+    x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);  // row_bcast:31 into rows 2, 3
+    return x;
+}
+template <int CTRL, int ROWS, bool BOUND>
+__device__ __forceinline__ long long dpp64(long long x) {
+    const int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)x, CTRL, ROWS, 0xF, BOUND);
+    const int hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)((uint64_t)x >> 32), CTRL, ROWS, 0xF, BOUND);
+    return (long long)(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
+}
+__device__ __forceinline__ long long wave_incl_scan64(long long x) {
+    x += dpp64<0x111, 0xF, true>(x);
+    x += dpp64<0x112, 0xF, true>(x);
+    x += dpp64<0x114, 0xF, true>(x);
+    x += dpp64<0x118, 0xF, true>(x);
+    x += dpp64<0x142, 0xA, false>(x);
+    x += dpp64<0x143, 0xC, false>(x);
+    return x;
+}
+
+// ---------------------------------------------------------------------------
 // Block-wide exclusive prefix sum of one int per thread (blockDim a multiple
 // of 64, at most 1024).  `sh` holds 16 ints.
 // ---------------------------------------------------------------------------
 __device__ int block_excl_scan(int v, int* sh) {
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-    int x = v;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const int y = __shfl_up(x, o);
-        if (lane >= o) x += y;
-    }
+    const int x = wave_incl_scan(v);
     if (lane == 63) sh[wid] = x;
     __syncthreads();
     int wbase = 0;
@@ -828,12 +855,7 @@ __device__ inline void peer_chunks(const DevCtx& c, int& lo, int& n, int& nc, in
         n = c.off[lane + 1] - lo;
     }
     nc = (n + kRouteChunk - 1) / kRouteChunk;
-    inc = nc;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const int y = __shfl_up(inc, o);
-        if (lane >= o) inc += y;
-    }
+    inc = wave_incl_scan(nc);
 }
 
 // Chunk b's token range [t0, t1) and its peer p (false: no such chunk).
@@ -1073,15 +1095,7 @@ __device__ void block_excl_scan4(long long (&v)[4], long long* sh) {
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
     long long x[4];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) x[q] = v[q];
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const long long y = __shfl_up(x[q], o);
-            if (lane >= o) x[q] += y;
-        }
-    }
+    for (int q = 0; q < 4; ++q) x[q] = wave_incl_scan64(v[q]);
     if (lane == 63)
 #pragma unroll
         for (int q = 0; q < 4; ++q) sh[wid * 4 + q] = x[q];
@@ -1093,6 +1107,15 @@ __device__ void block_excl_scan4(long long (&v)[4], long long* sh) {
         v[q] = x[q] - v[q] + base;
     }
     __syncthreads();
+}
+
+// floor(a / b) for 0 <= a < 2^53, b > 0: a double quotient corrected to
+// the exact one (a 64-bit integer division is a long software sequence).
+__device__ __forceinline__ long long div_floor(long long a, long long b) {
+    long long q = (long long)((double)a / (double)b);
+    while (q > 0 && q * b > a) --q;
+    while ((q + 1) * b <= a) ++q;
+    return q;
 }
 
 // A light group: a routed expert with 1 to 32 rows (one token block).
@@ -1192,14 +1215,14 @@ __device__ void plan_publish(const DevCtx& c, int T, const int* s_eoff, int (*s_
                 // skip groups with no tiles that share the same cost start
                 while (lo + 1 < G && s_c[m][lo + 1] <= S) ++lo;
                 const PlanGroup g = plan_group(c, T, s_eoff, s_ord[lo], m + 1);
-                const long long u = (S - s_c[m][lo] + g.nk - 1) / g.nk;  // in 32-row blocks
+                const long long u = div_floor(S - s_c[m][lo] + g.nk - 1, g.nk);  // in 32-row blocks
                 // the panel holding block-column u, then the first row tile
                 // of that panel starting at or after its remaining blocks
                 const int pw = min(kPanel, g.nt), np = (g.nt + pw - 1) / pw;
-                int pp = min((int)(u / ((long long)pw * g.blocks)), np - 1);
+                int pp = min((int)div_floor(u, (long long)pw * g.blocks), np - 1);
                 const int w = min(pw, g.nt - pp * pw);
-                const long long rb = (u - (long long)pp * pw * g.blocks + w - 1) / w;  // blocks into the panel
-                int mt = (int)((rb * g.mt + g.blocks - 1) / g.blocks);
+                const long long rb = div_floor(u - (long long)pp * pw * g.blocks + w - 1, w);  // blocks into the panel
+                int mt = (int)div_floor(rb * g.mt + g.blocks - 1, g.blocks);
                 if (mt >= g.mt) {
                     ++pp;
                     mt = 0;
