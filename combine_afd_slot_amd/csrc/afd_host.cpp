@@ -99,7 +99,7 @@ int32_t validate(const afd_window_config* c) {
 struct WsLayout {
     int64_t ctrl, peer_counts, blk_counts, blk_base, counts, eoff, tstart1, tstart2;
     int64_t tinfo1, tinfo2, seg1, seg2, tctr, psrc, max_tiles1, max_tiles2;
-    int64_t ids, wts, perm, inv, tok_src, sh_src, h, hs, y, ys, wtable, pid, pwt, ppos, pblk, pbase, pcnt, retoff, retoffs, xq, sx, sxp, bytes;
+    int64_t ids, wts, perm, inv, tok_src, sh_src, h, hs, y, ys, ysp, shp, wtable, pid, pwt, ppos, pblk, pbase, pcnt, retoff, retoffs, xq, sx, sxp, bytes;
     int64_t ctrl_ints;
     // control-word offsets inside ctrl (in ints)
     int64_t c_seen_in, c_ret_seq, c_seen_ret, c_cur_seq, c_off, c_T, c_done, c_run_status, c_peer_status;
@@ -112,6 +112,9 @@ WsLayout ws_layout(const afd_window_config& c) {
     const int64_t tmax = P * c.token_cap, np = tmax * K;
     const int64_t nb = (tmax + afd::kRouteChunk - 1) / afd::kRouteChunk + P;
     const int64_t G = E + (c.shared_intermediate > 0 ? 1 : 0);
+    // depth parts of the shared expert's down GEMM (small windows only)
+    const int64_t nks = (c.shared_intermediate + afd::kBK - 1) / afd::kBK;
+    w.shp = c.shared_intermediate > 0 && tmax <= afd::kShSplitRows ? std::min<int64_t>(afd::kShParts, nks) : 1;
     int64_t ci = 0;
     w.c_seen_in = ci; ci += P * R;
     w.c_ret_seq = ci; ci += P * R;
@@ -152,7 +155,7 @@ WsLayout ws_layout(const afd_window_config& c) {
         const int64_t nt1_s = (c.shared_intermediate + afd::kBW / 2 - 1) / (afd::kBW / 2);
         const int64_t nt2 = (c.hidden + afd::kBW - 1) / afd::kBW;
         w.max_tiles1 = mt_r * nt1_r + mt_s * nt1_s;
-        w.max_tiles2 = (mt_r + mt_s) * nt2;
+        w.max_tiles2 = (mt_r + mt_s * w.shp) * nt2;
     }
     w.tinfo1 = take(16 * w.max_tiles1);
     w.tinfo2 = take(16 * w.max_tiles2);
@@ -171,6 +174,7 @@ WsLayout ws_layout(const afd_window_config& c) {
     w.hs = take(64 * tmax * (c.shared_intermediate > 0 ? (c.shared_intermediate + afd::kBK - 1) / afd::kBK : 1));
     w.y = take(2 * np * c.hidden);
     w.ys = take(2 * tmax * c.hidden);
+    w.ysp = take(w.shp > 1 ? 4 * w.shp * tmax * c.hidden : 0);
     w.wtable = take((int64_t)sizeof(afd::Weights) * afd::kMaxLayers);
     {
         // attention-side routing: per (peer, stage) message state on the peer side
@@ -374,6 +378,8 @@ void fill_ctx(afd_window* w) {
     d.hs = (uint16_t*)(ws + L.hs);
     d.y = (uint16_t*)(ws + L.y);
     d.ys = (uint16_t*)(ws + L.ys);
+    d.shp = (int)L.shp;
+    d.ysp = (float*)(ws + L.ysp);
 }
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }

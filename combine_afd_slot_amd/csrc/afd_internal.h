@@ -41,6 +41,16 @@ constexpr int kXcds = 8;
 // covers tiles [seg[s], seg[s+1]).
 constexpr int kSegs = 3 * kXcds;
 
+// Windows of at most kShSplitRows tokens (Tmax = P * token_cap: one row tile
+// of the shared expert) split the shared expert's down GEMM over its depth
+// into up to kShParts tiles per column tile (decode-sized batches: the
+// routed tiles fill whole rounds of the CUs, and the shared tiles, whose
+// depth is the shared intermediate width, would add a round of their own).
+// Each part writes an fp32 partial row; the consumers sum the parts in
+// order and round the sum to bf16 once.
+constexpr int kShSplitRows = 256;
+constexpr int kShParts = 8;
+
 // Per-stage run status words: [status, failed_peer, seq of peer 0, T].
 // Run status words: [status, failed_peer, seq of peer 0, T, served peers
 // (bits 0..31), served peers (bits 32..63)].
@@ -134,6 +144,8 @@ struct DevCtx {
     uint16_t* hs;      // [ceil(Is/32)][Tmax][32]   bf16 shared activations
     uint16_t* y;       // [Tmax*K][H]  bf16 routed expert outputs, permuted order
     uint16_t* ys;      // [Tmax][H]    bf16 shared expert output, token (= shared row) order
+    int shp;           // depth parts of the shared expert's down GEMM (1: not split)
+    float* ysp;        // [shp][Tmax][H] fp32 partial shared outputs (shp > 1)
 };
 
 // One layer's packed weights (written by k_pack_weights): tiles of 256

@@ -138,8 +138,10 @@ __device__ int block_excl_scan(int v, int* sh) {
     const int x = wave_incl_scan(v);
     if (lane == 63) sh[wid] = x;
     __syncthreads();
-    int wbase = 0;
-    for (int w = 0; w < wid; ++w) wbase += sh[w];
+    // the totals of the waves below this one: one read per lane, summed
+    // across the lanes (no chain of dependent reads)
+    const int below = wave_incl_scan(lane < wid ? sh[lane] : 0);
+    const int wbase = __builtin_amdgcn_readlane(below, 63);
     __syncthreads();
     return x + wbase - v;
 }
@@ -1086,25 +1088,40 @@ __device__ inline PlanGroup plan_group(const DevCtx& c, int T, const int* s_eoff
     g.mt = (g.blocks + kTileBlocks - 1) / kTileBlocks;
     g.nt = mode == 1 ? (Ig + kBW / 2 - 1) / (kBW / 2) : (c.H + kBW - 1) / kBW;
     g.nk = mode == 1 ? (c.H + kBK - 1) / kBK : (Ig + kBK - 1) / kBK;
+    if (mode == 2 && shd && c.shp > 1) {
+        // depth split: column index = part * (column tiles) + column tile,
+        // each part ceil(depth / parts) steps deep at most
+        g.nt *= c.shp;
+        g.nk = (g.nk + c.shp - 1) / c.shp;
+    }
     return g;
 }
 
-// Block-wide exclusive prefix sums of four int64 values per thread.  `sh`
-// holds 4 values per wavefront (64 for 1024 threads).
-__device__ void block_excl_scan4(long long (&v)[4], long long* sh) {
+// Block-wide exclusive prefix sums of four int64 values per thread, over
+// the first nw wavefronts (the values of the others are taken as zero and
+// they do no scan work: on one CU every wavefront's VALU work counts).
+// `sh` holds 4 values per wavefront (64 for 1024 threads).  Every thread
+// of the block calls it.
+__device__ void block_excl_scan4(long long (&v)[4], long long* sh, int nw) {
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    const bool act = wid < nw;  // (wave-uniform)
     long long x[4];
+    if (act) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) x[q] = wave_incl_scan64(v[q]);
-    if (lane == 63)
+        for (int q = 0; q < 4; ++q) x[q] = wave_incl_scan64(v[q]);
+        if (lane == 63)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) sh[wid * 4 + q] = x[q];
+            for (int q = 0; q < 4; ++q) sh[wid * 4 + q] = x[q];
+    }
     __syncthreads();
+    if (act) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        long long base = 0;
-        for (int w = 0; w < wid; ++w) base += sh[w * 4 + q];
-        v[q] = x[q] - v[q] + base;
+        for (int q = 0; q < 4; ++q) {
+            const long long below = wave_incl_scan64(lane < wid ? sh[lane * 4 + q] : 0ll);
+            const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)below, 63);
+            const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)((uint64_t)below >> 32), 63);
+            v[q] = x[q] - v[q] + (long long)(((uint64_t)hi << 32) | lo);
+        }
     }
     __syncthreads();
 }
@@ -1115,6 +1132,17 @@ __device__ __forceinline__ long long div_floor(long long a, long long b) {
     long long q = (long long)((double)a / (double)b);
     while (q > 0 && q * b > a) --q;
     while ((q + 1) * b <= a) ++q;
+    return q;
+}
+
+// floor(a / b) for 0 <= a and 0 < b: below 2^22 from a float quotient (the
+// reciprocal's error keeps the estimate within one of the exact value,
+// which the remainder then fixes), above it by the integer division.
+__device__ __forceinline__ int div_small(int a, int b) {
+    if ((a | b) >= (1 << 22)) return a / b;
+    int q = (int)((float)a * __builtin_amdgcn_rcpf((float)b));
+    const int r = a - q * b;
+    q += r < 0 ? -1 : (r >= b ? 1 : 0);
     return q;
 }
 
@@ -1136,12 +1164,14 @@ __device__ void plan_prefix(const DevCtx& c, int T, const int* s_eoff, int (*s_t
     const int tid = threadIdx.x, G = c.G, NT = blockDim.x;
     const int per = (G + NT - 1) / NT;
     const int j0 = tid * per, j1 = min(G, j0 + per);
+    const int last = (G + per - 1) / per - 1;  // the thread holding group G-1
+    const int nw = last / 64 + 1;              // wavefronts holding groups
     {
         int nl = 0;
         for (int j = j0; j < j1; ++j) nl += plan_light(c, s_eoff, j) ? 1 : 0;
         long long v[4] = {nl, 0, 0, 0};
-        block_excl_scan4(v, sh);  // v[0]: light groups before j0
-        if (tid == NT - 1) *s_nh = G - (int)(v[0] + nl);
+        block_excl_scan4(v, sh, nw);  // v[0]: light groups before j0
+        if (tid == last) *s_nh = G - (int)(v[0] + nl);
         __syncthreads();
         const int nh = *s_nh;
         int lr = (int)v[0];
@@ -1161,7 +1191,7 @@ __device__ void plan_prefix(const DevCtx& c, int T, const int* s_eoff, int (*s_t
             v[2 + m] += (long long)g.nt * g.blocks * g.nk;
         }
     }
-    block_excl_scan4(v, sh);
+    block_excl_scan4(v, sh, nw);
     for (int q = j0; q < j1; ++q) {
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
@@ -1172,7 +1202,7 @@ __device__ void plan_prefix(const DevCtx& c, int T, const int* s_eoff, int (*s_t
             v[2 + m] += (long long)g.nt * g.blocks * g.nk;
         }
     }
-    if (tid == NT - 1)
+    if (tid == last)
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
             s_t[m][G] = (int)v[m];
@@ -1190,47 +1220,49 @@ __device__ void plan_publish(const DevCtx& c, int T, const int* s_eoff, int (*s_
                              long long (*s_c)[kMaxExperts + 2], const int* s_ord, int nh) {
     const int tid = threadIdx.x, G = c.G;
     if (tid < 2 * kSegs) c.tctr[tid] = 0;
-    for (int m = 0; m < 2; ++m) {
-        int* tstart = m == 0 ? c.tstart1 : c.tstart2;
-        for (int j = tid; j <= G; j += (int)blockDim.x) tstart[j] = s_t[m][j];
+    for (int i = tid; i < 2 * (G + 1); i += (int)blockDim.x) {
+        const int m = i / (G + 1), j = i - m * (G + 1);
+        (m == 0 ? c.tstart1 : c.tstart2)[j] = s_t[m][j];
+    }
+    // one thread per (GEMM, boundary): both GEMMs' searches run side by side
+    if (tid < 2 * (kSegs + 1)) {
+        const int m = tid / (kSegs + 1), sb = tid - m * (kSegs + 1);
         int* seg = m == 0 ? c.seg1 : c.seg2;
-        if (tid <= kSegs) {
-            const int hs = c.has_shared ? 1 : 0;
-            const int cls = tid / kXcds, b = tid % kXcds;
-            const int q0 = cls == 0 ? 0 : cls == 1 ? hs : cls == 2 ? nh : G;
-            const int q1 = cls == 0 ? hs : cls == 1 ? nh : G;
-            const int lo_t = s_t[m][q0], hi_t = s_t[m][q1];
-            const long long C0 = s_c[m][q0], C1 = s_c[m][q1];
-            const long long S = C0 + (C1 - C0) * b / kXcds;
-            int res;
-            if (b == 0 || cls == 3) res = lo_t;
-            else if (S >= C1) res = hi_t;
-            else {
-                int lo = 0, hi = G;
-                while (hi - lo > 1) {
-                    const int mid = (lo + hi) >> 1;
-                    if (s_c[m][mid] <= S) lo = mid;
-                    else hi = mid;
-                }
-                // skip groups with no tiles that share the same cost start
-                while (lo + 1 < G && s_c[m][lo + 1] <= S) ++lo;
-                const PlanGroup g = plan_group(c, T, s_eoff, s_ord[lo], m + 1);
-                const long long u = div_floor(S - s_c[m][lo] + g.nk - 1, g.nk);  // in 32-row blocks
-                // the panel holding block-column u, then the first row tile
-                // of that panel starting at or after its remaining blocks
-                const int pw = min(kPanel, g.nt), np = (g.nt + pw - 1) / pw;
-                int pp = min((int)div_floor(u, (long long)pw * g.blocks), np - 1);
-                const int w = min(pw, g.nt - pp * pw);
-                const long long rb = div_floor(u - (long long)pp * pw * g.blocks + w - 1, w);  // blocks into the panel
-                int mt = (int)div_floor(rb * g.mt + g.blocks - 1, g.blocks);
-                if (mt >= g.mt) {
-                    ++pp;
-                    mt = 0;
-                }
-                res = min(s_t[m][lo] + pp * pw * g.mt + mt * w, s_t[m][lo] + g.mt * g.nt);
+        const int hs = c.has_shared ? 1 : 0;
+        const int cls = sb / kXcds, b = sb % kXcds;
+        const int q0 = cls == 0 ? 0 : cls == 1 ? hs : cls == 2 ? nh : G;
+        const int q1 = cls == 0 ? hs : cls == 1 ? nh : G;
+        const int lo_t = s_t[m][q0], hi_t = s_t[m][q1];
+        const long long C0 = s_c[m][q0], C1 = s_c[m][q1];
+        const long long S = C0 + (C1 - C0) * b / kXcds;
+        int res;
+        if (b == 0 || cls == 3) res = lo_t;
+        else if (S >= C1) res = hi_t;
+        else {
+            // the last plan position whose cost prefix is at most S (positions
+            // of groups with no tiles share their successor's prefix)
+            int lo = 0, hi = G;
+            while (hi - lo > 1) {
+                const int mid = (lo + hi) >> 1;
+                if (s_c[m][mid] <= S) lo = mid;
+                else hi = mid;
             }
-            seg[tid] = min(max(res, lo_t), hi_t);
+            const PlanGroup g = plan_group(c, T, s_eoff, s_ord[lo], m + 1);
+            const long long u = div_floor(S - s_c[m][lo] + g.nk - 1, g.nk);  // in 32-row blocks
+            // the panel holding block-column u, then the first row tile
+            // of that panel starting at or after its remaining blocks
+            const int pw = min(kPanel, g.nt), np = (g.nt + pw - 1) / pw;
+            int pp = min((int)div_floor(u, (long long)pw * g.blocks), np - 1);
+            const int w = min(pw, g.nt - pp * pw);
+            const long long rb = div_floor(u - (long long)pp * pw * g.blocks + w - 1, w);  // blocks into the panel
+            int mt = (int)div_floor(rb * g.mt + g.blocks - 1, g.blocks);
+            if (mt >= g.mt) {
+                ++pp;
+                mt = 0;
+            }
+            res = min(s_t[m][lo] + pp * pw * g.mt + mt * w, s_t[m][lo] + g.mt * g.nt);
         }
+        seg[sb] = min(max(res, lo_t), hi_t);
     }
 }
 
@@ -1259,11 +1291,11 @@ __device__ void plan_fill(const DevCtx& c, int T, const int* s_eoff, int (*s_t)[
             const int local = i - s_t[m][lo];
             // panel pp of width w, row tile mt, column tile nt (panel order)
             const int pw = min(kPanel, g.nt);
-            const int pp = min(local / (pw * g.mt), (g.nt - 1) / pw);
+            const int pp = min(div_small(local, pw * g.mt), div_small(g.nt - 1, pw));
             const int w = min(pw, g.nt - pp * pw);
             const int within = local - pp * pw * g.mt;
-            const int mt = within / w, nt = pp * pw + within % w;
-            const int b0 = mt * g.blocks / g.mt, b1 = (mt + 1) * g.blocks / g.mt;
+            const int mt = div_small(within, w), nt = pp * pw + within - mt * w;
+            const int b0 = div_small(mt * g.blocks, g.mt), b1 = div_small((mt + 1) * g.blocks, g.mt);
             const int row0 = (c.has_shared && j == 0) ? 0 : s_eoff[j - c.has_shared];
             tinfo[i] = make_int4(j, nt | ((b1 - b0) << 16), row0 + b0 * 32, min(b1 * 32, g.M) - b0 * 32);
         }
@@ -1368,6 +1400,7 @@ __global__ __launch_bounds__(256) void k_permute(DevCtx c, const int* status) {
 #endif
 constexpr int kSmallT = AFD_SMALL_T;
 constexpr int kSmallW = kSmallT / 32;  // mask words per expert
+constexpr int kSmallIds = kSmallT * kMaxTopK / (64 * kRouteChunk);  // pair slots per thread
 
 template <int EPL>
 __global__ __launch_bounds__(64 * kRouteChunk) void k_route_small(DevCtx c, int* status, int s) {
@@ -1379,6 +1412,9 @@ __global__ __launch_bounds__(64 * kRouteChunk) void k_route_small(DevCtx c, int*
     __shared__ int s_ord[kMaxExperts + 1];
     __shared__ int s_nh;
     __shared__ uint32_t emask[kMaxExperts][kSmallW];
+    __shared__ uint64_t s_src[kSmallT];
+    __shared__ float s_sx[kSmallT];
+    __shared__ int s_off[kMaxPeers + 1];
     __shared__ int s_last;
     const int tid = threadIdx.x, lane = tid & 63;
     {
@@ -1402,19 +1438,37 @@ __global__ __launch_bounds__(64 * kRouteChunk) void k_route_small(DevCtx c, int*
     }
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");  // every workgroup's routing
     if (tid == 0) *c.route_done = 0;  // (the next run's launch starts after this one)
+    // The tail's inputs, loaded together so that their latencies overlap: the
+    // status, the token count, the fan-in offsets, the expert of every pair
+    // slot of the window's Tmax = P * token_cap <= kSmallT tokens (slots past
+    // the run's T * K pairs hold stale values and go unused) and every
+    // token's row address (and fp8 scale).
+    const int E = c.E, K = c.K, NT = blockDim.x, Tm = c.hsrows;
     const int st = __hip_atomic_load(status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const int T = *c.Tptr;
+    int idv[kSmallIds];
+#pragma unroll
+    for (int i = 0; i < kSmallIds; ++i) {
+        const int f = tid + i * NT;
+        idv[i] = f < Tm * K ? c.ids[f] : 0;
+    }
+    const uint64_t tsrc = tid < Tm ? c.tok_src[tid] : 0;
+    const float tsx = c.w1_fp8 && tid < Tm ? c.sx[tid] : 0.0f;
+    const int toff = tid <= c.P ? c.off[tid] : 0;
     if (st != AFD_OK) return;
-    const int E = c.E, K = c.K, NT = blockDim.x;
-    if (T > kSmallT) {  // (the launcher picks this kernel only when P * token_cap <= kSmallT)
+    if (T > kSmallT || Tm > kSmallT || Tm * K > kSmallIds * NT) {  // (the launcher picks this kernel only when Tmax <= kSmallT)
         if (tid == 0) atomicCAS(status, AFD_OK, AFD_ERR_INVALID);
         return;
     }
     for (int i = tid; i < E * kSmallW; i += NT) (&emask[0][0])[i] = 0u;
+    if (tid < T) s_src[tid] = tsrc;
+    if (tid < T) s_sx[tid] = tsx;
+    if (tid <= c.P) s_off[tid] = toff;
     __syncthreads();
-    for (int f = tid; f < T * K; f += NT) {
-        const int t = f / K, e = c.ids[f];
-        atomicOr(&emask[e][t >> 5], 1u << (t & 31));
+#pragma unroll
+    for (int i = 0; i < kSmallIds; ++i) {
+        const int f = tid + i * NT;
+        if (f < T * K) atomicOr(&emask[idv[i]][(f / K) >> 5], 1u << ((f / K) & 31));
     }
     __syncthreads();
     // counts (bincount), expert offsets, per-peer counts
@@ -1436,7 +1490,7 @@ __global__ __launch_bounds__(64 * kRouteChunk) void k_route_small(DevCtx c, int*
     }
     for (int i = tid; i < c.P * E; i += NT) {
         const int q = i / E, e = i - q * E;
-        const int a = c.off[q], b = c.off[q + 1];
+        const int a = s_off[q], b = s_off[q + 1];
         int n = 0;
         for (int w = a >> 5; a < b && w <= (b - 1) >> 5; ++w) {
             uint32_t m = emask[e][w];
@@ -1452,16 +1506,19 @@ __global__ __launch_bounds__(64 * kRouteChunk) void k_route_small(DevCtx c, int*
     plan_publish(c, T, s_eoff, s_t, s_c, s_ord, s_nh);
     plan_fill(c, T, s_eoff, s_t, s_ord, 0, 1);  // (this one workgroup writes every tile)
     // the stable dispatch position of every pair
-    for (int f = tid; f < T * K; f += NT) {
+#pragma unroll
+    for (int i = 0; i < kSmallIds; ++i) {
+        const int f = tid + i * NT;
+        if (f >= T * K) continue;
         const int t = f / K;
-        const int e = c.ids[f];
+        const int e = idv[i];
         int below = 0;
         for (int w = 0; w < (t >> 5); ++w) below += __popc(emask[e][w]);
         below += __popc(emask[e][t >> 5] & ((1u << (t & 31)) - 1u));
         const int pos = s_eoff[e] + below;
         c.perm[pos] = f;
-        c.psrc[pos] = c.tok_src[t];
-        if (c.w1_fp8) c.sxp[pos] = c.sx[t];
+        c.psrc[pos] = s_src[t];
+        if (c.w1_fp8) c.sxp[pos] = s_sx[t];
         c.inv[f] = pos;
     }
 }
@@ -1841,6 +1898,7 @@ struct GemmTile {
     int r0;                // first token row of the tile (h / y / ys row; fan-in token for shared rows)
     int rows, Ig, nt;      // valid token rows, the group's intermediate width, column tile
     bool sh;
+    int part;              // depth part of a split shared down-GEMM tile (-1: whole depth)
     int par;               // which of the two LDS row tables is this tile's
     uint32_t rofs;         // this thread's row's entry of the table: its return offset (down GEMM
                            // storing into the return slots) or its token scale (fp8 gate/up GEMM)
@@ -2204,6 +2262,19 @@ __device__ __forceinline__ void gemm_setup(const DevCtx& c, const Weights& w, in
     t.nk = f8 ? c.H / 64 : (t.Kdim + kBK - 1) / kBK;
     t.kfull = f8 ? t.nk : t.Kdim / kBK;
     t.tail_clamp = (uint32_t)t.Kdim * 2 - 16;
+    // a split shared down-GEMM tile: part p of the column tile covers depth
+    // steps [p*nk/parts, (p+1)*nk/parts); k0 moves both operand bases, and
+    // the depth left from its start stands for K in the tile's K-tail test
+    int k0 = 0;
+    t.part = -1;
+    if (MODE == 2 && t.sh && c.shp > 1) {
+        t.part = t.nt / c.nt2;
+        t.nt -= t.part * c.nt2;
+        k0 = t.part * t.nk / c.shp;
+        const int k1 = (t.part + 1) * t.nk / c.shp;
+        t.Kdim -= k0 * kBK;
+        t.kfull = min(k1 - k0, t.Kdim / kBK);
+    }
     // Token rows: slot rows through their row addresses (gate/up; 32-bit
     // byte offsets from the window, which stays below 4 GiB: checked at
     // create) or rows of the depth-block-major h / hs (down).
@@ -2211,14 +2282,15 @@ __device__ __forceinline__ void gemm_setup(const DevCtx& c, const Weights& w, in
         t.abase = F8 ? (const char*)c.xq : c.in_win;  // (fp8: the quantised token rows)
         t.astep = kRowBytes;
     } else {
-        t.abase = (const char*)(t.sh ? c.hs : c.h);
         t.astep = (uint32_t)(t.sh ? c.hsrows : c.hrows) * kRowBytes;
+        t.abase = (const char*)(t.sh ? c.hs : c.h) + (int64_t)k0 * t.astep;
     }
     // this group's packed weight tiles of column tile nt: nk consecutive tiles
     if (MODE == 1) t.bbase = t.sh ? w.ws13 + (int64_t)t.nt * t.nk * kWTileBytes
                                   : w.w13 + ((int64_t)e * c.nt1 + t.nt) * t.nk * kWTileBytes;
-    else t.bbase = t.sh ? w.ws2 + (int64_t)t.nt * t.nk * kWTileBytes
+    else t.bbase = t.sh ? w.ws2 + ((int64_t)t.nt * t.nk + k0) * kWTileBytes
                         : w.w2 + ((int64_t)e * c.nt2 + t.nt) * t.nk * kWTileBytes;
+    if (t.part >= 0) t.nk = (t.part + 1) * t.nk / c.shp - k0;
     t.wlane = (uint32_t)wid * 1024u + (uint32_t)(threadIdx.x & 63) * 16u;
     t.cx = lcx;
     if constexpr (F8) {
@@ -2369,6 +2441,25 @@ __device__ __forceinline__ void gemm_epilogue_ib(const f32x16 (&acc)[NV > 0 ? NV
                 const uint32_t r = (uint32_t)(8 * (v >> 2) + (v & 3));
                 __builtin_amdgcn_raw_buffer_store_b16((uint16_t)pk, rs, (int)(cb + r * kRowBytes), 0, 0);
                 __builtin_amdgcn_raw_buffer_store_b16((uint16_t)(pk >> 16), rs, (int)(cb + (r + 1) * kRowBytes), 0, 0);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+    } else if (t.part >= 0) {
+        // a split shared tile: its fp32 partial rows, part p's rows of ysp
+        // (token order), 32 consecutive columns of two rows per store
+        const uint32_t ldb = (uint32_t)c.H * 4;
+        const __amdgpu_buffer_rsrc_t rs =
+            out_rsrc(c.ysp + ((int64_t)t.part * c.hsrows + t.r0) * c.H, (uint32_t)t.rows * ldb);
+#pragma unroll
+        for (int jb = 0; jb < 4; ++jb) {
+            const int col = t.nt * kBW + (ww * 4 + jb) * 32 + lj;
+            const uint32_t cb = (col < c.H ? 0u : 0x80000000u) + (uint32_t)col * 4 + rb * ldb;
+#pragma unroll
+            for (int v = 0; v < 16; v += 2) {
+                const uint32_t r = (uint32_t)(8 * (v >> 2) + (v & 3));
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(agpr(acc[ib][jb][v])), rs, (int)(cb + r * ldb), 0, 0);
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(agpr(acc[ib][jb][v + 1])), rs,
+                                                      (int)(cb + (r + 1) * ldb), 0, 0);
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
@@ -2592,6 +2683,42 @@ __device__ __forceinline__ u32x4 combine_chunk(const u32x4 (&yv)[KK], const floa
     return out;
 }
 
+// One 16-byte chunk (8 columns) of token t's shared-expert row: the bf16
+// row of ys, or -- depth-split shared tiles -- the fp32 parts summed in part
+// order and rounded to bf16 (RNE) once.
+__device__ __forceinline__ u32x4 shared_chunk(const DevCtx& c, int t, int ch) {
+    if (c.shp <= 1) return *(const u32x4*)(c.ys + (int64_t)t * c.H + ch * 8);
+    float s[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) s[i] = 0.f;
+    const int64_t pstride = (int64_t)c.hsrows * c.H;
+    const float* p0 = c.ysp + (int64_t)t * c.H + ch * 8;
+    for (int p = 0; p < c.shp; ++p) {
+        const float4 a = *(const float4*)(p0 + p * pstride), b = *(const float4*)(p0 + p * pstride + 4);
+        s[0] += a.x; s[1] += a.y; s[2] += a.z; s[3] += a.w;
+        s[4] += b.x; s[5] += b.y; s[6] += b.z; s[7] += b.w;
+    }
+    u32x4 o;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[i] = pk_bf16(s[2 * i], s[2 * i + 1]);
+    return o;
+}
+
+// Attention-routed runs with depth-split shared tiles: every token's shared
+// row summed from its parts (shared_chunk) into the return slot's shared
+// row (where the down GEMM stores the other rows itself) or into ys (copied
+// there by k_retcopy).
+__global__ __launch_bounds__(256) void k_shsum(DevCtx c, const int* status) {
+    const int st = *status;
+    const int T = *c.Tptr;
+    if (st != AFD_OK) return;
+    const int H8 = c.H / 8;
+    for (int t = blockIdx.x; t < T; t += gridDim.x) {
+        u32x4* dst = c.direct_ret ? (u32x4*)(c.ret_win + c.retoffs[t]) : (u32x4*)(c.ys + (int64_t)t * c.H);
+        for (int ch = threadIdx.x; ch < H8; ch += blockDim.x) dst[ch] = shared_chunk(c, t, ch);
+    }
+}
+
 template <int KK>
 __global__ __launch_bounds__(256) void k_combine(DevCtx c, const int* status, int s, int layer) {
     const int st = *status;  // loaded together with the token count
@@ -2614,7 +2741,7 @@ __global__ __launch_bounds__(256) void k_combine(DevCtx c, const int* status, in
             u32x4 yv[KK];
 #pragma unroll
             for (int k = 0; k < KK; ++k) yv[k] = *(const u32x4*)(c.y + (int64_t)pos[k] * H + ch * 8);
-            const u32x4 sq = c.has_shared ? *(const u32x4*)(c.ys + (int64_t)t * H + ch * 8) : (u32x4)0u;
+            const u32x4 sq = c.has_shared ? shared_chunk(c, t, ch) : (u32x4)0u;
             __builtin_nontemporal_store(combine_chunk<KK>(yv, wk, sq, c.has_shared, c.rsf), &dst[ch]);
         }
     }
@@ -2771,7 +2898,9 @@ hipError_t launch_ffn(const DevCtx& c, int stage, int layer, const Weights& w, l
     int cgrid = Tmax < num_cu * 8 ? Tmax : num_cu * 8;
     if (cgrid < 1) cgrid = 1;
     if (c.attn_routes) {
-        // (the down GEMM stored every row into the return slots itself unless the window is too large)
+        // (the down GEMM stored every row into the return slots itself unless the window is too large;
+        // the shared rows of depth-split tiles are summed from their parts first)
+        if (c.shp > 1) k_shsum<<<cgrid, 256, 0, st>>>(c, status);
         if (!c.direct_ret) k_retcopy<<<num_cu * 8, 256, 0, st>>>(c, status, stage);
         k_publish<<<c.P, 64, 0, st>>>(c, status, stage, layer, serve_item);
         mark();
