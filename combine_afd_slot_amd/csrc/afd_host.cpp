@@ -378,6 +378,7 @@ void fill_ctx(afd_window* w) {
     d.hs = (uint16_t*)(ws + L.hs);
     d.y = (uint16_t*)(ws + L.y);
     d.ys = (uint16_t*)(ws + L.ys);
+    d.ncu = w->num_cu;
     d.shp = (int)L.shp;
     d.ysp = (float*)(ws + L.ysp);
 }

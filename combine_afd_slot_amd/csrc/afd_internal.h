@@ -144,6 +144,7 @@ struct DevCtx {
     uint16_t* hs;      // [ceil(Is/32)][Tmax][32]   bf16 shared activations
     uint16_t* y;       // [Tmax*K][H]  bf16 routed expert outputs, permuted order
     uint16_t* ys;      // [Tmax][H]    bf16 shared expert output, token (= shared row) order
+    int ncu;           // compute units: the GEMMs' grid, for which the planner reserves first tiles
     int shp;           // depth parts of the shared expert's down GEMM (1: not split)
     float* ysp;        // [shp][Tmax][H] fp32 partial shared outputs (shp > 1)
 };

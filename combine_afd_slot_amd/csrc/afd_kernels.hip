@@ -1074,6 +1074,12 @@ __global__ __launch_bounds__(256) void k_scan(DevCtx c, const int* status) {
 #define AFD_TILE_PANEL 4
 #endif
 constexpr int kPanel = AFD_TILE_PANEL;
+// One GEMM workgroup in kLightEvery (by its rank on its XCD) takes the light
+// segments first (the tile scheduler below).
+#ifndef AFD_LIGHT_EVERY
+#define AFD_LIGHT_EVERY 5
+#endif
+constexpr int kLightEvery = AFD_LIGHT_EVERY;
 struct PlanGroup {
     int M, mt, blocks, nt, nk;
 };
@@ -1218,8 +1224,8 @@ __device__ void plan_prefix(const DevCtx& c, int T, const int* s_eoff, int (*s_t
 // the first tile whose cost prefix reaches it (boundary kSegs: the end).
 __device__ void plan_publish(const DevCtx& c, int T, const int* s_eoff, int (*s_t)[kMaxExperts + 2],
                              long long (*s_c)[kMaxExperts + 2], const int* s_ord, int nh) {
+    __shared__ int s_seg[2][kSegs + 1];
     const int tid = threadIdx.x, G = c.G;
-    if (tid < 2 * kSegs) c.tctr[tid] = 0;
     for (int i = tid; i < 2 * (G + 1); i += (int)blockDim.x) {
         const int m = i / (G + 1), j = i - m * (G + 1);
         (m == 0 ? c.tstart1 : c.tstart2)[j] = s_t[m][j];
@@ -1262,7 +1268,27 @@ __device__ void plan_publish(const DevCtx& c, int T, const int* s_eoff, int (*s_
             }
             res = min(s_t[m][lo] + pp * pw * g.mt + mt * w, s_t[m][lo] + g.mt * g.nt);
         }
-        seg[sb] = min(max(res, lo_t), hi_t);
+        seg[sb] = s_seg[m][sb] = min(max(res, lo_t), hi_t);
+    }
+    __syncthreads();
+    // The tile counters start past the tiles that the GEMM workgroups take
+    // without an atomic as their first (sched_first): on XCD x (workgroups b
+    // = x, x + kXcds, ... of the ncu-workgroup grid) the light-first
+    // workgroups, by rank, take the first tiles of the light segment x, the
+    // normal ones the first tiles of the shared, then the heavy segment x,
+    // then the light tiles after the light-first workgroups' share.
+    if (tid < 2 * kSegs) {
+        const int m = tid / kSegs, sidx = tid - m * kSegs;
+        const int cls = sidx / kXcds, x = sidx % kXcds;
+        const int nx = c.ncu > x ? (c.ncu - x + kXcds - 1) / kXcds : 0;
+        const int nlf = (nx + kLightEvery - 1) / kLightEvery, nnorm = nx - nlf;
+        const int size = s_seg[m][sidx + 1] - s_seg[m][sidx];
+        int taken;
+        const int sh = s_seg[m][x + 1] - s_seg[m][x], hv = s_seg[m][kXcds + x + 1] - s_seg[m][kXcds + x];
+        if (cls == 0) taken = min(size, nnorm);
+        else if (cls == 1) taken = min(size, max(0, nnorm - sh));
+        else taken = min(size, nlf + max(0, nnorm - sh - hv));
+        c.tctr[tid] = taken;
     }
 }
 
@@ -2178,10 +2204,6 @@ __device__ __forceinline__ void gemm_step_f8(f32x16 (&acc)[NV > 0 ? NV : 1][4], 
 // resolved at the tile boundary and broadcast through LDS.  When the current
 // segment is drained, one batch of loads (a lane per segment) finds the next
 // segment with tiles left.
-#ifndef AFD_LIGHT_EVERY
-#define AFD_LIGHT_EVERY 5
-#endif
-constexpr int kLightEvery = AFD_LIGHT_EVERY;
 constexpr int kGrabAhead = 3;
 
 struct GemmSched {
@@ -2226,6 +2248,49 @@ __device__ __forceinline__ int sched_grab_slow(GemmSched& s, int lane) {
         ++s.tries;  // lost the race for the segment's last tiles
     }
     return -1;
+}
+
+// First tile of a workgroup (wave 0, all lanes; uniform result).  Without
+// an atomic where the planner reserved one (its tile counters start past
+// these): a light-first workgroup of rank li among the light-first ones of
+// its XCD takes tile li of its light segment; a normal one of rank ni among
+// the normal ones takes tile ni of the concatenation of its shared segment,
+// its heavy segment and the light segment past the light-first share.  The
+// others grab.
+__device__ __forceinline__ int sched_first(GemmSched& s, int lane) {
+    const int i = (int)blockIdx.x / kXcds;
+    int v = 0;
+    if (lane < 6) v = s.seg[(lane >> 1) * kXcds + s.x + (lane & 1)];
+    const int b0 = __builtin_amdgcn_readlane(v, 0), b1 = __builtin_amdgcn_readlane(v, 1);
+    const int b2 = __builtin_amdgcn_readlane(v, 2), b3 = __builtin_amdgcn_readlane(v, 3);
+    const int b4 = __builtin_amdgcn_readlane(v, 4), b5 = __builtin_amdgcn_readlane(v, 5);
+    if (s.lf) {
+        const int li = i / kLightEvery;
+        if (li < b5 - b4) {
+            s.si = 2 * kXcds + s.x;  // (visit 0 of a light-first workgroup)
+            return b4 + li;
+        }
+    } else {
+        const int ni = i - i / kLightEvery - 1;
+        if (ni < b1 - b0) {
+            s.si = s.x;  // (visit 0)
+            return b0 + ni;
+        }
+        if (ni < (b1 - b0) + (b3 - b2)) {
+            s.tries = 1;
+            s.si = kXcds + s.x;  // (visit 1)
+            return b2 + ni - (b1 - b0);
+        }
+        // past the light-first workgroups' share of the light segment (the
+        // visiting order restarts at visit 0 once the segment is drained)
+        const int nx = ((int)gridDim.x - s.x + kXcds - 1) / kXcds;
+        const int li = (nx + kLightEvery - 1) / kLightEvery + ni - (b1 - b0) - (b3 - b2);
+        if (li < b5 - b4) {
+            s.si = 2 * kXcds + s.x;
+            return b4 + li;
+        }
+    }
+    return sched_grab_slow(s, lane);
 }
 
 __device__ __forceinline__ void sched_issue(GemmSched& s, int lane) {  // wave 0
@@ -2590,9 +2655,10 @@ __device__ __forceinline__ void gemm_tiles(const DevCtx& c, const Weights& w, ch
     const uint32_t wl = kXStageBytes + (uint32_t)ww * (MODE == 1 ? 2 : 4) * kBlockBytes + fb;
     const uint32_t tl = (uint32_t)wx * kBlockBytes + fb;
 
-    // first tile
+    // first tile (the planner reserved the first ones for a grid of c.ncu
+    // workgroups, the grid of every launch)
     if (wid == 0) {
-        const int t0 = sched_grab_slow(sc, tid);
+        const int t0 = sched_first(sc, tid);
         if (tid == 0) *slot = t0;
     }
     __syncthreads();
