@@ -2411,9 +2411,12 @@ __device__ __forceinline__ void gemm_prologue(const GemmTile& t, char* smem, int
 // set it up (its first loads are issued during the epilogue).
 template <int MODE, bool F8>
 __device__ __forceinline__ void gemm_boundary(const DevCtx& c, const Weights& w, GemmSched& sc, char* smem, int tid,
-                                              int wid, int lrow, uint32_t lcx, int& next, GemmTile& tn) {
+                                              int wid, int lrow, uint32_t lcx, int nk, int& next, GemmTile& tn) {
     int* slot = (int*)(smem + kStages * kStageBytes);
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS reads are done
+    // the loads past the last step may target the epilogue's staging stage
+    // unless nk is a multiple of kStages: then they land first
+    if (nk & (kStages - 1)) AFD_WAIT_VMCNT(0);
     AFD_BARRIER();
     if (wid == 0) {
         const int t = sched_next(sc, tid);
@@ -2451,25 +2454,65 @@ __device__ __forceinline__ float agpr(float x) {
     return r;
 }
 
+// Accumulator elements converted between two scheduling barriers of the
+// epilogue (the barriers keep the compiler from moving every accumulator out
+// of its AGPR at once).
+#ifndef AFD_EPI_GROUP
+#define AFD_EPI_GROUP 2
+#endif
+constexpr int kEpiGroup = AFD_EPI_GROUP;
+
+// The epilogue stages each 32-row block of a wave's outputs through LDS and
+// writes it with 16-byte stores: a CU's vector-memory unit takes about as
+// long for an instruction of 2-byte lane stores as for one of 16-byte lane
+// stores, so 64 lanes x 16 bytes per instruction (8 KB of a block in 8
+// stores instead of 64) keeps the epilogue's stores from serialising.  The
+// staging area is ring stage kStages-1: the next tile's prologue loads go to
+// stages 0 .. kStages-2, and its step 0, which loads stage kStages-1, starts
+// after a barrier that every wave reaches only after its epilogue.  (Loads
+// past a tile's last step go to stages nk, nk+1, nk+2 mod kStages: when nk is
+// not a multiple of kStages, the boundary waits for them first.)
+constexpr int kEpiStage = (kStages - 1) * kStageBytes;
+constexpr int kEpiWaveBytes = 32 * 128 * 2;  // one wave's 32 rows x 128 bf16 columns
+static_assert(kEpiWaveBytes * kGemmWaves <= kStageBytes, "the epilogue staging fits one ring stage");
+
+// Rows v and v+1 (v even) of a lane's column, packed bf16 (row v low), are
+// regrouped with the neighbouring lane's (lanes 2m and 2m+1 hold adjacent
+// columns; the DPP move quad_perm [1,0,3,2] brings the neighbour's pair):
+// the even lane keeps row v of both columns, the odd lane row v+1, each as
+// one dword whose low half is the even column -- a byte permutation of the
+// two pairs with the lane's selector pair_sel.
+__device__ __forceinline__ uint32_t pair_sel(int lane) { return (lane & 1) ? 0x03020706u : 0x05040100u; }
+
 // Epilogue of token block ib of a tile.  In accumulator (ib, jb) a lane
 // holds output column 32*(weight block) + (lane & 31) and, in register v =
 // 0..15, token row (wx + 2*ib)*32 + 8*(v/4) + 4*(lane/32) + v%4 of the
-// tile.  One store instruction thus writes 32 consecutive columns of each of
-// two rows: whole 64-byte segments.  The stores go through a buffer
-// descriptor that spans the tile's valid rows; lanes of a column past the
-// output width add 2^31 to their offset.  The hardware drops out-of-range
-// buffer stores, so the code stays straight-line (a divergent branch would
-// keep every accumulator live across it).  The caller pads the wait states
-// between the last MFMA and the first accumulator read.
+// tile.  Pairs of rows are regrouped between neighbouring lanes (pair_sel)
+// and written to the wave's staging area in LDS, row-major; each lane then
+// reads back 16 bytes (8 columns of one row) and stores them.  The stores go
+// through a buffer descriptor that spans the tile's valid rows (rows past
+// them fall outside and the hardware drops the stores); a column block past
+// the output width adds 2^31 to its offsets.  Straight-line code (a
+// divergent branch would keep every accumulator live across it).  The
+// caller pads the wait states between the last MFMA and the first
+// accumulator read.  Depth-split shared tiles store their fp32 partial rows
+// directly.
 template <int MODE, int NV, bool F8>
 __device__ __forceinline__ void gemm_epilogue_ib(const f32x16 (&acc)[NV > 0 ? NV : 1][4], const DevCtx& c,
-                                                 const GemmTile& t, const char* smem, int lane, int ww, int wx,
+                                                 const GemmTile& t, char* smem, int lane, int ww, int wx,
                                                  int ib) {
     const int lj = lane & 31;
     const uint32_t rb = (uint32_t)((wx + 2 * ib) * 32 + 4 * (lane >> 5));  // this lane's first row of the block
+    const uint32_t row0 = (uint32_t)((wx + 2 * ib) * 32);                   // the block's first row
+    const uint32_t sel = pair_sel(lane);
+    char* scr = smem + kEpiStage + (2 * ww + wx) * kEpiWaveBytes;
+    // this lane's staging dword for (row 8q + v%4 (+1 for odd lanes), its column pair): row r of
+    // the block at r * RB bytes, column pair at 4 * (lj/2)
+    const uint32_t wq = (uint32_t)((4 * (lane >> 5) + (lane & 1)) * (MODE == 1 ? 64 : 256) + (lj & 30) * 2);
     if (MODE == 1) {
         // h = silu(gate) * up, bf16; gate in weight blocks jb, up in jb + 2.
-        // Column block jb is one 32-deep block of h: rows of 64 bytes.
+        // Column block jb is one 32-deep block of h: 32 rows of 64 bytes,
+        // contiguous (2 KB), staged at jb * 2 KB.
         const int64_t hrows = t.sh ? c.hsrows : c.hrows;
         char* hb = (char*)(t.sh ? c.hs : c.h);
         // fp8: the token scales of this lane's rows rb + 8q + i
@@ -2483,30 +2526,58 @@ __device__ __forceinline__ void gemm_epilogue_ib(const f32x16 (&acc)[NV > 0 ? NV
                 for (int i = 0; i < 4; ++i) dx[q][i] = __uint_as_float(o[i]);
             }
         }
+        // in stages over 8 elements at a time (independent instructions
+        // back to back, not one dependent chain per element)
+#pragma unroll
+        for (int jb = 0; jb < 2; ++jb) {
+#pragma unroll
+            for (int h8 = 0; h8 < 16; h8 += 8) {
+                float g[8], u[8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    g[i] = agpr(acc[ib][jb][h8 + i]);
+                    u[i] = agpr(acc[ib][jb + 2][h8 + i]);
+                }
+                if constexpr (F8) {
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        const float sxr = dx[(h8 + i) >> 2][(h8 + i) & 3];
+                        g[i] = g[i] * sxr * t.dw[jb];
+                        u[i] = u[i] * sxr * t.dw[2 + jb];
+                    }
+                }
+                float e[8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) e[i] = __expf(-g[i]);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) e[i] = __builtin_amdgcn_rcpf(1.f + e[i]);
+                uint32_t pk[4], nb[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    pk[i] = pk_bf16(g[2 * i] * e[2 * i] * u[2 * i], g[2 * i + 1] * e[2 * i + 1] * u[2 * i + 1]);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) nb[i] = (uint32_t)__builtin_amdgcn_mov_dpp((int)pk[i], 0xB1, 0xF, 0xF, false);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int v = h8 + 2 * i;
+                    const uint32_t r = (uint32_t)(8 * (v >> 2) + (v & 3));
+                    *(uint32_t*)(scr + jb * 2048 + r * 64 + wq) = __builtin_amdgcn_perm(nb[i], pk[i], sel);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
 #pragma unroll
         for (int jb = 0; jb < 2; ++jb) {
             const int col0 = t.nt * (kBW / 2) + ww * 64 + jb * 32;
             const __amdgpu_buffer_rsrc_t rs =
                 out_rsrc(hb + ((int64_t)(col0 >> 5) * hrows + t.r0) * kRowBytes, (uint32_t)t.rows * kRowBytes);
-            const uint32_t cb = (col0 + lj < t.Ig ? 0u : 0x80000000u) + (uint32_t)lj * 2 + rb * kRowBytes;
+            // (a block past the width has no place in h; a partial one stores into its padding
+            // columns, which the down GEMM masks)
+            const uint32_t cb = (col0 < t.Ig ? 0u : 0x80000000u) + row0 * kRowBytes + (uint32_t)lane * 16;
 #pragma unroll
-            for (int v = 0; v < 16; v += 2) {
-                float o[2];
-#pragma unroll
-                for (int q = 0; q < 2; ++q) {
-                    float g = agpr(acc[ib][jb][v + q]), u = agpr(acc[ib][jb + 2][v + q]);
-                    if constexpr (F8) {
-                        const float sxr = dx[(v + q) >> 2][(v + q) & 3];
-                        g = g * sxr * t.dw[jb];
-                        u = u * sxr * t.dw[2 + jb];
-                    }
-                    o[q] = g * __builtin_amdgcn_rcpf(1.f + __expf(-g)) * u;
-                }
-                const uint32_t pk = pk_bf16(o[0], o[1]);
-                const uint32_t r = (uint32_t)(8 * (v >> 2) + (v & 3));
-                __builtin_amdgcn_raw_buffer_store_b16((uint16_t)pk, rs, (int)(cb + r * kRowBytes), 0, 0);
-                __builtin_amdgcn_raw_buffer_store_b16((uint16_t)(pk >> 16), rs, (int)(cb + (r + 1) * kRowBytes), 0, 0);
-                __builtin_amdgcn_sched_barrier(0);
+            for (int hh = 0; hh < 2; ++hh) {
+                const u32x4 d = *(const u32x4*)(scr + jb * 2048 + hh * 1024 + lane * 16);
+                __builtin_amdgcn_raw_buffer_store_b128(d, rs, (int)(cb + hh * 1024), 0, 0);
             }
         }
     } else if (t.part >= 0) {
@@ -2525,46 +2596,48 @@ __device__ __forceinline__ void gemm_epilogue_ib(const f32x16 (&acc)[NV > 0 ? NV
                 __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(agpr(acc[ib][jb][v])), rs, (int)(cb + r * ldb), 0, 0);
                 __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(agpr(acc[ib][jb][v + 1])), rs,
                                                       (int)(cb + (r + 1) * ldb), 0, 0);
-                __builtin_amdgcn_sched_barrier(0);
+                if ((v + 2) % kEpiGroup == 0) __builtin_amdgcn_sched_barrier(0);
             }
         }
     } else {
         // bf16 rows: routed rows into y (permuted order), shared rows into ys
         // (token order), or -- attention-routed runs -- each row straight to
         // its return row (offsets from the tile's LDS table, the buffer over
-        // the whole return window); one store loop for all, so the
-        // accumulators never have to live across a branch
+        // the whole return window).  Staged as 32 rows of 256 bytes (the
+        // wave's 128 columns).
+        // in stages over one accumulator (16 elements) at a time
+#pragma unroll
+        for (int jb = 0; jb < 4; ++jb) {
+            float a[16];
+#pragma unroll
+            for (int v = 0; v < 16; ++v) a[v] = agpr(acc[ib][jb][v]);
+            uint32_t pk[8], nb[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) pk[i] = pk_bf16(a[2 * i], a[2 * i + 1]);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) nb[i] = (uint32_t)__builtin_amdgcn_mov_dpp((int)pk[i], 0xB1, 0xF, 0xF, false);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int v = 2 * i;
+                const uint32_t r = (uint32_t)(8 * (v >> 2) + (v & 3));
+                *(uint32_t*)(scr + r * 256 + jb * 64 + wq) = __builtin_amdgcn_perm(nb[i], pk[i], sel);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
         const uint32_t ldb = (uint32_t)c.H * 2;
         const bool direct = c.direct_ret;
         const char* ob = direct ? c.ret_win : (const char*)((t.sh ? c.ys : c.y) + (int64_t)t.r0 * c.H);
         const __amdgpu_buffer_rsrc_t rs = out_rsrc(ob, direct ? c.ret_bytes : t.rows * ldb);
-        uint32_t ro[4][4];  // byte offsets of this lane's rows rb + 8q + i
-        if (direct) {
-            const u32x4* tab = (const u32x4*)(smem + kRetTabOff + t.par * (kBX * 4));
+        // lane: row 4i + lane/16 of the block, columns 8 * (lane % 16) .. + 8 of the wave's 128
+        const int col = t.nt * kBW + ww * 128 + (lane & 15) * 8;  // (H is a multiple of 8)
+        const uint32_t cb = (col < c.H ? 0u : 0x80000000u) + (uint32_t)col * 2;
+        const uint32_t* tab = (const uint32_t*)(smem + kRetTabOff + t.par * (kBX * 4));
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const u32x4 o = tab[(rb >> 2) + 2 * q];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) ro[q][i] = o[i];
-            }
-        } else {
-#pragma unroll
-            for (int q = 0; q < 4; ++q)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) ro[q][i] = (rb + 8 * q + i) * ldb;
-        }
-#pragma unroll
-        for (int jb = 0; jb < 4; ++jb) {
-            const int col = t.nt * kBW + (ww * 4 + jb) * 32 + lj;
-            const uint32_t cb = (col < c.H ? 0u : 0x80000000u) + (uint32_t)col * 2;
-#pragma unroll
-            for (int v = 0; v < 16; v += 2) {
-                const uint32_t pk = pk_bf16(agpr(acc[ib][jb][v]), agpr(acc[ib][jb][v + 1]));
-                const int q = v >> 2, i = v & 3;
-                __builtin_amdgcn_raw_buffer_store_b16((uint16_t)pk, rs, (int)(cb + ro[q][i]), 0, 0);
-                __builtin_amdgcn_raw_buffer_store_b16((uint16_t)(pk >> 16), rs, (int)(cb + ro[q][i + 1]), 0, 0);
-                __builtin_amdgcn_sched_barrier(0);
-            }
+        for (int i = 0; i < 8; ++i) {
+            const uint32_t row = row0 + 4 * i + (lane >> 4);
+            const uint32_t ro = direct ? tab[row] : row * ldb;
+            const u32x4 d = *(const u32x4*)(scr + i * 1024 + lane * 16);
+            __builtin_amdgcn_raw_buffer_store_b128(d, rs, (int)(cb + ro), 0, 0);
         }
     }
 }
@@ -2604,7 +2677,7 @@ __device__ __forceinline__ void gemm_run(const DevCtx& c, const Weights& w, Gemm
         for (; kt < t.nk; ++kt) gemm_step<MODE, NV, NX, true>(acc, t, smem, kt, wid, lane, wl, tl, fa, fb);
     }
 
-    gemm_boundary<MODE, F8>(c, w, sc, smem, tid, wid, lrow, lcx, next, tn);
+    gemm_boundary<MODE, F8>(c, w, sc, smem, tid, wid, lrow, lcx, t.nk, next, tn);
     tn.par = t.par ^ 1;
 
     // Epilogue, token block by token block, with the next tile's first
