@@ -163,25 +163,76 @@ __device__ inline float wave_sum(float x) {
 // (-inf past E).  On return rank[j] is the rank of logit l + 64 j (rank < K:
 // selected, rank k the k-th) and wt[j] its weight.  Shared by the FFN-side
 // routing and the attention-side pack, so both select and weigh alike.
+// The largest of the lanes' 64-bit keys (h high word, l low word, unsigned),
+// in every lane: a running maximum over the row shifts and row broadcasts of
+// wave_incl_scan (lanes shifted in from outside a row contribute 0, the
+// smallest key), lane 63's result broadcast.
+__device__ __forceinline__ void wave_max_key(uint32_t& h, uint32_t& l) {
+#define AFD_MAXKEY_STEP(CTRL, ROWS, BOUND)                                                   \
+    {                                                                                        \
+        const uint32_t nh = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)h, CTRL, ROWS, 0xF, BOUND); \
+        const uint32_t nl = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)l, CTRL, ROWS, 0xF, BOUND); \
+        const bool gt = nh > h || (nh == h && nl > l);                                       \
+        h = gt ? nh : h;                                                                     \
+        l = gt ? nl : l;                                                                     \
+    }
+    AFD_MAXKEY_STEP(0x111, 0xF, true)
+    AFD_MAXKEY_STEP(0x112, 0xF, true)
+    AFD_MAXKEY_STEP(0x114, 0xF, true)
+    AFD_MAXKEY_STEP(0x118, 0xF, true)
+    AFD_MAXKEY_STEP(0x142, 0xA, false)
+    AFD_MAXKEY_STEP(0x143, 0xC, false)
+#undef AFD_MAXKEY_STEP
+    h = (uint32_t)__builtin_amdgcn_readlane((int)h, 63);
+    l = (uint32_t)__builtin_amdgcn_readlane((int)l, 63);
+}
+
 template <int EPL>
 __device__ __forceinline__ void route_token(const float (&v)[EPL], int E, int K, int renorm, int lane,
                                             int (&rank)[EPL], float (&wt)[EPL]) {
-    // Logits past E are -inf and have indices past every valid one, so
-    // they never raise a valid logit's rank.
-#pragma unroll
-    for (int j = 0; j < EPL; ++j) rank[j] = 0;
-#pragma unroll
-    for (int jj = 0; jj < EPL; ++jj) {
-        if (64 * jj >= E) break;
+    if constexpr (EPL == 1) {
+        // Rank by broadcast: each lane counts the logits that precede its
+        // own (larger, or equal with a smaller index).  A logit past E is
+        // -inf with an index past every valid one, so it never raises a
+        // valid logit's rank.
+        rank[0] = 0;
 #pragma unroll 8
         for (int sl = 0; sl < 64; ++sl) {
-            const float x = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v[jj]), sl));
-            const int q = sl + 64 * jj;
+            const float x = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v[0]), sl));
+            rank[0] += (x > v[0] || (x == v[0] && sl < lane)) ? 1 : 0;
+        }
+    } else {
+        // K rounds of a wave-wide maximum over the logits not yet taken, in
+        // the same order (value descending, index ascending): the key of
+        // logit e is its value made unsigned-orderable (-0 taken as +0)
+        // above the complement of e.  Round k's winner gets rank k; the
+        // rest keep rank K.
+        uint32_t kh[EPL];
+        uint32_t live = 0u;
+#pragma unroll
+        for (int j = 0; j < EPL; ++j) {
+            const uint32_t u = __float_as_uint(v[j] + 0.0f);
+            kh[j] = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+            rank[j] = K;
+            if (lane + 64 * j < E) live |= 1u << j;
+        }
+        for (int k = 0; k < K; ++k) {
+            uint32_t bh = 0u, bl = 0u;  // (a valid key is never (0, 0): finite values)
 #pragma unroll
             for (int j = 0; j < EPL; ++j) {
-                const int e = lane + 64 * j;
-                rank[j] += (x > v[j] || (x == v[j] && q < e)) ? 1 : 0;
+                const uint32_t lo = ~(uint32_t)(lane + 64 * j);
+                const bool better = ((live >> j) & 1u) && (kh[j] > bh || (kh[j] == bh && lo > bl));
+                bh = better ? kh[j] : bh;
+                bl = better ? lo : bl;
             }
+            wave_max_key(bh, bl);
+            const int e = (int)~bl;
+#pragma unroll
+            for (int j = 0; j < EPL; ++j)
+                if (e == lane + 64 * j) {
+                    rank[j] = k;
+                    live &= ~(1u << j);
+                }
         }
     }
     // the maximum is the logit of rank 0 (exactly one lane holds it)
