@@ -2883,10 +2883,19 @@ __device__ __forceinline__ u32x4 shared_chunk(const DevCtx& c, int t, int ch) {
     for (int i = 0; i < 8; ++i) s[i] = 0.f;
     const int64_t pstride = (int64_t)c.hsrows * c.H;
     const float* p0 = c.ysp + (int64_t)t * c.H + ch * 8;
-    for (int p = 0; p < c.shp; ++p) {
-        const float4 a = *(const float4*)(p0 + p * pstride), b = *(const float4*)(p0 + p * pstride + 4);
-        s[0] += a.x; s[1] += a.y; s[2] += a.z; s[3] += a.w;
-        s[4] += b.x; s[5] += b.y; s[6] += b.z; s[7] += b.w;
+    // every part's loads first (their latencies overlap), then the sum in part order
+    float4 a[kShParts], b[kShParts];
+#pragma unroll
+    for (int p = 0; p < kShParts; ++p) {
+        const bool have = p < c.shp;
+        a[p] = have ? *(const float4*)(p0 + p * pstride) : make_float4(0.f, 0.f, 0.f, 0.f);
+        b[p] = have ? *(const float4*)(p0 + p * pstride + 4) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+    for (int p = 0; p < kShParts; ++p) {
+        if (p >= c.shp) break;
+        s[0] += a[p].x; s[1] += a[p].y; s[2] += a[p].z; s[3] += a[p].w;
+        s[4] += b[p].x; s[5] += b[p].y; s[6] += b[p].z; s[7] += b[p].w;
     }
     u32x4 o;
 #pragma unroll
