@@ -166,13 +166,17 @@ __device__ inline float wave_sum(float x) {
 // The largest of the lanes' 64-bit keys (h high word, l low word, unsigned),
 // in every lane: a running maximum over the row shifts and row broadcasts of
 // wave_incl_scan (lanes shifted in from outside a row contribute 0, the
-// smallest key), lane 63's result broadcast.
+// smallest key), lane 63's result broadcast.  Each step is one 64-bit
+// compare and two selects: vector instructions only (a compare combined
+// with and/or becomes scalar mask logic, and a CU's waves share one scalar
+// unit).
+__device__ __forceinline__ uint64_t key64(uint32_t h, uint32_t l) { return ((uint64_t)h << 32) | l; }
 __device__ __forceinline__ void wave_max_key(uint32_t& h, uint32_t& l) {
 #define AFD_MAXKEY_STEP(CTRL, ROWS, BOUND)                                                   \
     {                                                                                        \
         const uint32_t nh = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)h, CTRL, ROWS, 0xF, BOUND); \
         const uint32_t nl = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)l, CTRL, ROWS, 0xF, BOUND); \
-        const bool gt = nh > h || (nh == h && nl > l);                                       \
+        const bool gt = key64(nh, nl) > key64(h, l);                                        \
         h = gt ? nh : h;                                                                     \
         l = gt ? nl : l;                                                                     \
     }
@@ -194,12 +198,19 @@ __device__ __forceinline__ void route_token(const float (&v)[EPL], int E, int K,
         // Rank by broadcast: each lane counts the logits that precede its
         // own (larger, or equal with a smaller index).  A logit past E is
         // -inf with an index past every valid one, so it never raises a
-        // valid logit's rank.
+        // valid logit's rank.  Compared as 64-bit keys: the value made
+        // unsigned-orderable (-0 as +0) above the complement of the index,
+        // so "precedes" is one unsigned compare (vector instructions only;
+        // the or/and form becomes scalar mask logic, which the CU's waves
+        // queue for on its one scalar unit).
+        const uint32_t u = __float_as_uint(v[0] + 0.0f);
+        const uint32_t kh = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+        const uint64_t mine = key64(kh, ~(uint32_t)lane);
         rank[0] = 0;
-#pragma unroll 8
+#pragma unroll
         for (int sl = 0; sl < 64; ++sl) {
-            const float x = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v[0]), sl));
-            rank[0] += (x > v[0] || (x == v[0] && sl < lane)) ? 1 : 0;
+            const uint32_t xh = (uint32_t)__builtin_amdgcn_readlane((int)kh, sl);
+            rank[0] += key64(xh, ~(uint32_t)sl) > mine ? 1 : 0;
         }
     } else {
         // K rounds of a wave-wide maximum over the logits not yet taken, in
@@ -220,9 +231,11 @@ __device__ __forceinline__ void route_token(const float (&v)[EPL], int E, int K,
             uint32_t bh = 0u, bl = 0u;  // (a valid key is never (0, 0): finite values)
 #pragma unroll
             for (int j = 0; j < EPL; ++j) {
-                const uint32_t lo = ~(uint32_t)(lane + 64 * j);
-                const bool better = ((live >> j) & 1u) && (kh[j] > bh || (kh[j] == bh && lo > bl));
-                bh = better ? kh[j] : bh;
+                // (a taken or padding entry competes as key 0, which never wins)
+                const uint32_t lo = ((live >> j) & 1u) ? ~(uint32_t)(lane + 64 * j) : 0u;
+                const uint32_t hi = ((live >> j) & 1u) ? kh[j] : 0u;
+                const bool better = key64(hi, lo) > key64(bh, bl);
+                bh = better ? hi : bh;
                 bl = better ? lo : bl;
             }
             wave_max_key(bh, bl);
