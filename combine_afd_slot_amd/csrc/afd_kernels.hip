@@ -2931,31 +2931,65 @@ __global__ __launch_bounds__(256) void k_shsum(DevCtx c, const int* status) {
     }
 }
 
-template <int KK>
-__global__ __launch_bounds__(256) void k_combine(DevCtx c, const int* status, int s, int layer) {
-    const int st = *status;  // loaded together with the token count
-    const int T = *c.Tptr;
-    if (st != AFD_OK) return;
+// NT tokens of a combine workgroup at once (t[1] may repeat t[0]: then
+// only t[0] is written): their pair positions and weights load together,
+// then their rows, so that one token's latency chain overlaps the other's.
+// offq: the fan-in offsets one per lane (see k_combine).
+template <int KK, int NT>
+__device__ __forceinline__ void combine_tokens(const DevCtx& c, const int (&t)[NT], bool two, int offq, int s,
+                                               int npairs) {
     const int H = c.H, H8 = c.H / 8;
-    const int npairs = T * KK;
-    for (int t = blockIdx.x; t < T; t += gridDim.x) {
-        const int p = peer_of(c, t);
-        const int r = t - c.off[p];
-        u32x4* dst = (u32x4*)(slot_ptr(c, c.ret_win, p, s) + c.foff[AFD_FIELD_ROUTED_X] + (int64_t)r * H * 2);
-        int pos[KK];
-        float wk[KK];
+    int pos[NT][KK];
+    float wk[NT][KK];
+    u32x4* dst[NT];
+#pragma unroll
+    for (int u = 0; u < NT; ++u) {
 #pragma unroll
         for (int k = 0; k < KK; ++k) {
-            pos[k] = min(max(c.inv[(int64_t)t * KK + k], 0), npairs - 1);
-            wk[k] = c.wts[(int64_t)t * KK + k];
+            pos[u][k] = min(max(c.inv[(int64_t)t[u] * KK + k], 0), npairs - 1);
+            wk[u][k] = c.wts[(int64_t)t[u] * KK + k];
         }
-        for (int ch = threadIdx.x; ch < H8; ch += blockDim.x) {
-            u32x4 yv[KK];
+        // the token's peer: the peers after the first whose tokens start at
+        // or before it (offsets are nondecreasing, empty peers included)
+        const int p = __popcll(__ballot(offq <= t[u]));
+        const int r = t[u] - (p > 0 ? __builtin_amdgcn_readlane(offq, p - 1) : 0);
+        dst[u] = (u32x4*)(slot_ptr(c, c.ret_win, p, s) + c.foff[AFD_FIELD_ROUTED_X] + (int64_t)r * H * 2);
+    }
+    for (int ch = threadIdx.x; ch < H8; ch += blockDim.x) {
+        u32x4 yv[NT][KK];
+        u32x4 sq[NT];
 #pragma unroll
-            for (int k = 0; k < KK; ++k) yv[k] = *(const u32x4*)(c.y + (int64_t)pos[k] * H + ch * 8);
-            const u32x4 sq = c.has_shared ? shared_chunk(c, t, ch) : (u32x4)0u;
-            __builtin_nontemporal_store(combine_chunk<KK>(yv, wk, sq, c.has_shared, c.rsf), &dst[ch]);
+        for (int u = 0; u < NT; ++u) {
+#pragma unroll
+            for (int k = 0; k < KK; ++k) yv[u][k] = *(const u32x4*)(c.y + (int64_t)pos[u][k] * H + ch * 8);
+            sq[u] = c.has_shared ? shared_chunk(c, t[u], ch) : (u32x4)0u;
         }
+#pragma unroll
+        for (int u = 0; u < NT; ++u)
+            if (u == 0 || two)
+                __builtin_nontemporal_store(combine_chunk<KK>(yv[u], wk[u], sq[u], c.has_shared, c.rsf), &dst[u][ch]);
+    }
+}
+
+template <int KK>
+__global__ __launch_bounds__(256) void k_combine(DevCtx c, const int* status, int s, int layer) {
+    const int st = *status;  // loaded together with the token count and the offsets
+    const int T = *c.Tptr;
+    // lane q: the first token of peer q + 1 (past the last peer: none)
+    const int lane = threadIdx.x & 63;
+    const int offq = lane + 1 < c.P ? c.off[lane + 1] : INT_MAX;
+    if (st != AFD_OK) return;
+    const int npairs = T * KK, G = gridDim.x;
+    if (c.shp > 1) {
+        // (depth-split shared rows: windows of at most kShSplitRows tokens,
+        // one token a workgroup)
+        for (int t = blockIdx.x; t < T; t += G) combine_tokens<KK, 1>(c, {t}, false, offq, s, npairs);
+        return;
+    }
+    // tokens t and t + G of the workgroup together
+    for (int t = blockIdx.x; t < T; t += 2 * G) {
+        const bool two = t + G < T;
+        combine_tokens<KK, 2>(c, {t, two ? t + G : t}, two, offq, s, npairs);
     }
 }
 
