@@ -83,12 +83,6 @@ __device__ inline char* slot_ptr(const DevCtx& c, char* win, int p, int s) {
     return win + c.slots_off + (int64_t)(p * c.R + s) * c.slot_bytes;
 }
 
-__device__ inline int peer_of(const DevCtx& c, int t) {
-    int p = 0;
-    while (p + 1 < c.P && c.off[p + 1] <= t) ++p;
-    return p;
-}
-
 __device__ inline int ld_acquire(int* p) {
     return __hip_atomic_load(p, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -1675,10 +1669,13 @@ __global__ __launch_bounds__(256) void k_gdispatch(DevCtx c, int* status, int s)
     __shared__ long long s_c[2][kMaxExperts + 2];
     __shared__ int s_ord[kMaxExperts + 1];
     __shared__ int s_nh;
+    __shared__ int s_off[kMaxPeers + 1];
     const int st = *status;
     const int T = *c.Tptr;
+    const int toff = (int)threadIdx.x <= c.P ? c.off[threadIdx.x] : 0;
     if (st != AFD_OK) return;
     const int E = c.E, K = c.K, P = c.P, tid = threadIdx.x;
+    if (tid <= P) s_off[tid] = toff;  // (read after the barriers of the scans below)
     {
         const int per = (E + 255) / 256;
         const int e0 = tid * per, e1 = min(E, e0 + per);
@@ -1726,7 +1723,14 @@ __global__ __launch_bounds__(256) void k_gdispatch(DevCtx c, int* status, int s)
     if (c.has_shared) {
         bool bad = false;
         for (int t = (int)blockIdx.x * 256 + tid; t < T; t += stride) {
-            const int p = peer_of(c, t), r = t - c.off[p];
+            // its peer: the last p with off[p] <= t (off[P] = T > t)
+            int pl = 0, ph = P;
+            while (ph - pl > 1) {
+                const int mid = (pl + ph) >> 1;
+                if (s_off[mid] <= t) pl = mid;
+                else ph = mid;
+            }
+            const int p = pl, r = t - s_off[p];
             const char* slot = slot_ptr(c, c.in_win, p, s);
             c.sh_src[t] = (uint64_t)(slot + c.foff[AFD_FIELD_SHARED_X] + (int64_t)r * c.H * 2);
             c.retoffs[t] = (uint32_t)(slot - c.in_win + c.foff[AFD_FIELD_SHARED_X] + (int64_t)r * c.H * 2);
