@@ -949,8 +949,9 @@ __device__ inline bool chunk_range(const DevCtx& c, int b, int& t0, int& t1, int
 // (and shared-row) address, and for the fp8 W1 GEMMs its e4m3 codes and row
 // scale; calls sel(e) in the lane that selected expert e.  Returns whether
 // the token's shared_idx entry is wrong (one FFN replica owns every shared
-// row: shared_idx must be 0..n_p-1).
-template <int EPL, typename Sel>
+// row: shared_idx must be 0..n_p-1).  Q: the fp8 token-row quantisation is
+// compiled in (the bf16 kernels leave it out, and its registers with it).
+template <int EPL, bool Q, typename Sel>
 __device__ __forceinline__ bool route_one(const DevCtx& c, const char* slot, int t, int r, int lane, Sel sel) {
     const int E = c.E, K = c.K;
     float v[EPL];
@@ -985,7 +986,7 @@ __device__ __forceinline__ bool route_one(const DevCtx& c, const char* slot, int
             }
         }
     }
-    if (c.w1_fp8) {
+    if (Q && c.w1_fp8) {
         // fp8 W1: the token row's e4m3 codes and scale (r = 448 / max|x|,
         // code = e4m3(x * r), value = code * max|x| / 448)
         const u32x4* xr = (const u32x4*)(slot + c.foff[AFD_FIELD_ROUTED_X] + (int64_t)r * c.H * 2);
@@ -1041,7 +1042,7 @@ __device__ __forceinline__ bool route_one(const DevCtx& c, const char* slot, int
     return si_bad;
 }
 
-template <int EPL>
+template <int EPL, bool Q>
 __global__ __launch_bounds__(64 * kRouteChunk) void k_route(DevCtx c, int* status, int s) {
     const int st = *status;  // loaded together with the peer offsets of chunk_range
     int t_begin, t_end, p;
@@ -1055,7 +1056,7 @@ __global__ __launch_bounds__(64 * kRouteChunk) void k_route(DevCtx c, int* statu
     const int t = t_begin + (int)(threadIdx.x >> 6);
     __syncthreads();  // hist zeroed
     bool si_bad = false;
-    if (t < t_end) si_bad = route_one<EPL>(c, slot, t, t - c.off[p], lane, [&](int e) { atomicAdd(&hist[e], 1); });
+    if (t < t_end) si_bad = route_one<EPL, Q>(c, slot, t, t - c.off[p], lane, [&](int e) { atomicAdd(&hist[e], 1); });
     if (si_bad) atomicCAS(status, AFD_OK, AFD_ERR_HEADER);
     __syncthreads();
     for (int e = threadIdx.x; e < E; e += blockDim.x) c.blk_counts[(int64_t)e * c.NB + blockIdx.x] = hist[e];
@@ -1486,7 +1487,7 @@ constexpr int kSmallT = AFD_SMALL_T;
 constexpr int kSmallW = kSmallT / 32;  // mask words per expert
 constexpr int kSmallIds = kSmallT * kMaxTopK / (64 * kRouteChunk);  // pair slots per thread
 
-template <int EPL>
+template <int EPL, bool Q>
 __global__ __launch_bounds__(64 * kRouteChunk) void k_route_small(DevCtx c, int* status, int s) {
     __shared__ int sh[16];
     __shared__ long long sh4[64];
@@ -1509,7 +1510,7 @@ __global__ __launch_bounds__(64 * kRouteChunk) void k_route_small(DevCtx c, int*
         const int t = t_begin + (tid >> 6);
         bool bad = false;
         if (st == AFD_OK && have && t < t_end)
-            bad = route_one<EPL>(c, slot_ptr(c, c.in_win, p, s), t, t - c.off[p], lane, [](int) {});
+            bad = route_one<EPL, Q>(c, slot_ptr(c, c.in_win, p, s), t, t - c.off[p], lane, [](int) {});
         if (bad) atomicCAS(status, AFD_OK, AFD_ERR_HEADER);
         __syncthreads();
         if (tid == 0) {
@@ -3122,19 +3123,27 @@ hipError_t launch_ffn(const DevCtx& c, int stage, int layer, const Weights& w, l
     } else if (Tmax <= kSmallT) {
         // small work items: routing, counts, dispatch order and plan in one launch
         // (its time lands in the routing slot)
-        if (c.E <= 64) k_route_small<1><<<c.NB, 64 * kRouteChunk, 0, st>>>(c, status, stage);
-        else if (c.E <= 128) k_route_small<2><<<c.NB, 64 * kRouteChunk, 0, st>>>(c, status, stage);
-        else if (c.E <= 256) k_route_small<4><<<c.NB, 64 * kRouteChunk, 0, st>>>(c, status, stage);
-        else if (c.E <= 512) k_route_small<8><<<c.NB, 64 * kRouteChunk, 0, st>>>(c, status, stage);
-        else k_route_small<16><<<c.NB, 64 * kRouteChunk, 0, st>>>(c, status, stage);
+#define AFD_ROUTE_SMALL(EPL)                                                                 \
+    (c.w1_fp8 ? k_route_small<EPL, true><<<c.NB, 64 * kRouteChunk, 0, st>>>(c, status, stage) \
+              : k_route_small<EPL, false><<<c.NB, 64 * kRouteChunk, 0, st>>>(c, status, stage))
+        if (c.E <= 64) AFD_ROUTE_SMALL(1);
+        else if (c.E <= 128) AFD_ROUTE_SMALL(2);
+        else if (c.E <= 256) AFD_ROUTE_SMALL(4);
+        else if (c.E <= 512) AFD_ROUTE_SMALL(8);
+        else AFD_ROUTE_SMALL(16);
+#undef AFD_ROUTE_SMALL
         mark();
         mark();
     } else {
-        if (c.E <= 64) k_route<1><<<c.NB, 64 * kRouteChunk, 0, st>>>(c, status, stage);
-        else if (c.E <= 128) k_route<2><<<c.NB, 64 * kRouteChunk, 0, st>>>(c, status, stage);
-        else if (c.E <= 256) k_route<4><<<c.NB, 64 * kRouteChunk, 0, st>>>(c, status, stage);
-        else if (c.E <= 512) k_route<8><<<c.NB, 64 * kRouteChunk, 0, st>>>(c, status, stage);
-        else k_route<16><<<c.NB, 64 * kRouteChunk, 0, st>>>(c, status, stage);
+#define AFD_ROUTE(EPL)                                                                 \
+    (c.w1_fp8 ? k_route<EPL, true><<<c.NB, 64 * kRouteChunk, 0, st>>>(c, status, stage) \
+              : k_route<EPL, false><<<c.NB, 64 * kRouteChunk, 0, st>>>(c, status, stage))
+        if (c.E <= 64) AFD_ROUTE(1);
+        else if (c.E <= 128) AFD_ROUTE(2);
+        else if (c.E <= 256) AFD_ROUTE(4);
+        else if (c.E <= 512) AFD_ROUTE(8);
+        else AFD_ROUTE(16);
+#undef AFD_ROUTE
         mark();
         k_scan<<<c.E, 256, 0, st>>>(c, status);
         mark();
