@@ -2936,43 +2936,30 @@ __global__ __launch_bounds__(256) void k_shsum(DevCtx c, const int* status) {
     }
 }
 
-// NT tokens of a combine workgroup at once (t[1] may repeat t[0]: then
-// only t[0] is written): their pair positions and weights load together,
-// then their rows, so that one token's latency chain overlaps the other's.
+// Token t of a combine workgroup: its K pair positions and weights, then
+// its rows (all K loads of a chunk go out together), summed in k order.
 // offq: the fan-in offsets one per lane (see k_combine).
-template <int KK, int NT>
-__device__ __forceinline__ void combine_tokens(const DevCtx& c, const int (&t)[NT], bool two, int offq, int s,
-                                               int npairs) {
+template <int KK>
+__device__ __forceinline__ void combine_token(const DevCtx& c, int t, int offq, int s, int npairs) {
     const int H = c.H, H8 = c.H / 8;
-    int pos[NT][KK];
-    float wk[NT][KK];
-    u32x4* dst[NT];
+    int pos[KK];
+    float wk[KK];
 #pragma unroll
-    for (int u = 0; u < NT; ++u) {
-#pragma unroll
-        for (int k = 0; k < KK; ++k) {
-            pos[u][k] = min(max(c.inv[(int64_t)t[u] * KK + k], 0), npairs - 1);
-            wk[u][k] = c.wts[(int64_t)t[u] * KK + k];
-        }
-        // the token's peer: the peers after the first whose tokens start at
-        // or before it (offsets are nondecreasing, empty peers included)
-        const int p = __popcll(__ballot(offq <= t[u]));
-        const int r = t[u] - (p > 0 ? __builtin_amdgcn_readlane(offq, p - 1) : 0);
-        dst[u] = (u32x4*)(slot_ptr(c, c.ret_win, p, s) + c.foff[AFD_FIELD_ROUTED_X] + (int64_t)r * H * 2);
+    for (int k = 0; k < KK; ++k) {
+        pos[k] = min(max(c.inv[(int64_t)t * KK + k], 0), npairs - 1);
+        wk[k] = c.wts[(int64_t)t * KK + k];
     }
+    // the token's peer: the peers after the first whose tokens start at or
+    // before it (offsets are nondecreasing, empty peers included)
+    const int p = __popcll(__ballot(offq <= t));
+    const int r = t - (p > 0 ? __builtin_amdgcn_readlane(offq, p - 1) : 0);
+    u32x4* dst = (u32x4*)(slot_ptr(c, c.ret_win, p, s) + c.foff[AFD_FIELD_ROUTED_X] + (int64_t)r * H * 2);
     for (int ch = threadIdx.x; ch < H8; ch += blockDim.x) {
-        u32x4 yv[NT][KK];
-        u32x4 sq[NT];
+        u32x4 yv[KK];
 #pragma unroll
-        for (int u = 0; u < NT; ++u) {
-#pragma unroll
-            for (int k = 0; k < KK; ++k) yv[u][k] = *(const u32x4*)(c.y + (int64_t)pos[u][k] * H + ch * 8);
-            sq[u] = c.has_shared ? shared_chunk(c, t[u], ch) : (u32x4)0u;
-        }
-#pragma unroll
-        for (int u = 0; u < NT; ++u)
-            if (u == 0 || two)
-                __builtin_nontemporal_store(combine_chunk<KK>(yv[u], wk[u], sq[u], c.has_shared, c.rsf), &dst[u][ch]);
+        for (int k = 0; k < KK; ++k) yv[k] = *(const u32x4*)(c.y + (int64_t)pos[k] * H + ch * 8);
+        const u32x4 sq = c.has_shared ? shared_chunk(c, t, ch) : (u32x4)0u;
+        __builtin_nontemporal_store(combine_chunk<KK>(yv, wk, sq, c.has_shared, c.rsf), &dst[ch]);
     }
 }
 
@@ -2984,18 +2971,8 @@ __global__ __launch_bounds__(256) void k_combine(DevCtx c, const int* status, in
     const int lane = threadIdx.x & 63;
     const int offq = lane + 1 < c.P ? c.off[lane + 1] : INT_MAX;
     if (st != AFD_OK) return;
-    const int npairs = T * KK, G = gridDim.x;
-    if (c.shp > 1) {
-        // (depth-split shared rows: windows of at most kShSplitRows tokens,
-        // one token a workgroup)
-        for (int t = blockIdx.x; t < T; t += G) combine_tokens<KK, 1>(c, {t}, false, offq, s, npairs);
-        return;
-    }
-    // tokens t and t + G of the workgroup together
-    for (int t = blockIdx.x; t < T; t += 2 * G) {
-        const bool two = t + G < T;
-        combine_tokens<KK, 2>(c, {t, two ? t + G : t}, two, offq, s, npairs);
-    }
+    const int npairs = T * KK;
+    for (int t = blockIdx.x; t < T; t += gridDim.x) combine_token<KK>(c, t, offq, s, npairs);
 }
 
 // Attention-routed runs: no combine on the FFN side ("[RFC]: Async GPU
@@ -3154,7 +3131,7 @@ hipError_t launch_ffn(const DevCtx& c, int stage, int layer, const Weights& w, l
     mark();
     k_gemm<2><<<num_cu, kGemmThreads, 0, st>>>(c, status, w, layer);
     mark();
-    int cgrid = Tmax < num_cu * 8 ? Tmax : num_cu * 8;
+    int cgrid = Tmax < num_cu * 32 ? Tmax : num_cu * 32;  // (one token a workgroup pass)
     if (cgrid < 1) cgrid = 1;
     if (c.attn_routes) {
         // (the down GEMM stored every row into the return slots itself unless the window is too large;
