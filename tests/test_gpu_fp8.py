@@ -139,3 +139,41 @@ def test_fp8_expert_segments_same_bits(F, shared_rank):
     finally:
         for x in sess:
             x.close()
+
+
+@pytest.mark.timeout(900)
+def test_fp8_skew_sampled_rows(orc):
+    """The fp8 W1 path on the full-size skew workload (2 x 4096 tokens, H
+    7168, 256 experts, top-8, Zipf bias): every 16th row of each peer, its
+    last row and every row whose token chose a light expert (1-15 rows),
+    against the oracle's fp8 path over those tokens alone (a token's output
+    row depends on that token only; its token-row scale too)."""
+    import dataclasses
+    from combine_afd_slot_amd.inputs import WORKLOADS
+    wl = dataclasses.replace(WORKLOADS["skew"], w1_fp8=1)
+    say("[fp8-skew] generating inputs")
+    inp = make_inputs(wl)
+    with FfnSession(wl, inp) as s:
+        say("[fp8-skew] GPU run")
+        s.step()
+        st = s.status()
+        assert st.status == 0 and st.total_tokens == wl.total_tokens
+        out = [o.copy() for o in s.outputs_f32()]
+        r = s.routing()
+    counts, ids, off = r["counts"], r["ids"], r["off"]
+    light = np.flatnonzero((counts >= 1) & (counts <= 15))
+    chose_light = np.isin(ids, light).any(axis=1)
+    assert light.size > 0 and chose_light.any()
+    errs = []
+    for p, n in enumerate(wl.seq_lens):
+        rows = np.zeros(n, dtype=bool)
+        rows[::16] = True
+        rows[n - 1] = True
+        rows |= chose_light[off[p]:off[p] + n]
+        idx = np.flatnonzero(rows)
+        say(f"[fp8-skew] peer {p}: oracle fp8 path on {idx.size} of {n} rows")
+        ref = orc.ffn_fp8([inp["x"][p][idx]], [inp["l"][p][idx]], inp["W13"], inp["W2"], inp.get("Ws13"),
+                          inp.get("Ws2"), K=wl.top_k, rsf=wl.routed_scaling_factor, renorm=wl.renormalize)
+        errs.append(row_rel_err(out[p][idx], ref[0]))
+    say(f"[fp8-skew] {int(light.size)} light experts; max row rel err {max(errs):.3e}")
+    assert max(errs) <= ROW_REL_TOL
